@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Throughput of causal kernelized linear attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload long] [--gpus 1]
+
+A step is one la_forward call over the whole workload batch (all three
+kernels: per-span state, span scan, chunked output).  Inputs are seeded
+synthetic tensors already resident in HBM when the timed region starts.  The
+timed region is exactly K steps bracketed by device synchronisation; the
+per-kernel durations come from HIP events recorded on the library's stream
+around each kernel of every timed step.
+
+One JSON line is printed with the metric, the roofline of the dominant kernel
+(the output kernel) and of the whole step, and the fp64 CPU oracle timed on
+this host (single process) on a bounded sample of the same workload.
+
+Workloads (names from kernelized_linear_attention_elu_amd.synth.WORKLOADS):
+long (default: B1 H32 N32768 d64 bf16 causal), prefill, wide, plus
+``decode`` (one decode step for 256 sequences x 32 heads, d = 128) and
+``feature`` (standalone ELU+1 feature map over the long workload's Q).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal LA prefill tokens/s at N=32k,d=64 bf16; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+KERNEL_NAMES = ("la_state_kernel", "la_scan_kernel", "la_output_kernel")
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "kernelized_linear_attention_elu_amd", "csrc")
+
+
+def source_hash():
+    """sha256 over the HIP sources: counter figures taken for other sources
+    are stale and are not reported."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(name.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload, kernel):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current sources."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path, encoding="utf-8") as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    if vals.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="long",
+                   choices=["long", "prefill", "wide", "decode", "feature", "copy"])
+    p.add_argument("--noncausal", action="store_true", help="non-causal prefill")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args(argv)
+
+
+def cpu_info():
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
+
+
+def time_oracle_prefill(q, k, v, causal, max_heads):
+    """fp64 oracle (token recurrence, or the reassociated non-causal form) on
+    the first ``max_heads`` heads of batch 0; returns (seconds, heads, cores)."""
+    from oracle import linear_attention as ora
+    h = min(max_heads, q.shape[1])
+    t0, c0 = time.perf_counter(), time.process_time()
+    if causal:
+        ora.recurrent_attention(q[:1, :h], k[:1, :h], v[:1, :h])
+    else:
+        ora.noncausal_attention(q[:1, :h], k[:1, :h], v[:1, :h])
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    return wall, h, max(1, round(cpu / max(wall, 1e-9)))
+
+
+def bench_prefill(args, torch, la, synth):
+    w = synth.WORKLOADS[args.workload]
+    causal = not args.noncausal
+    dev = torch.device("cuda:0")
+    q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
+
+    def to_dev(x):
+        import numpy as np
+        return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    Q, K, V = to_dev(q), to_dev(k), to_dev(v)
+    O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(la.workspace_bytes(w.B, w.H, w.N, w.d, w.dv, causal=causal, chunk=w.chunk),
+                     dtype=torch.uint8, device=dev)
+
+    def step(events=None):
+        la.forward(Q, K, V, causal=causal, chunk=w.chunk, out=O, workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[la.event_create() for _ in range(2 * la.LA_FORWARD_KERNELS)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = [0.0] * la.LA_FORWARD_KERNELS
+    for e in evs:
+        for j in range(la.LA_FORWARD_KERNELS):
+            kern_ms[j] += la.event_elapsed_ms(e[2 * j], e[2 * j + 1]) / args.steps
+    for e in evs:
+        for x in e:
+            la.event_destroy(x)
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    token_heads = w.B * w.H * w.N
+    alg_bytes = token_heads * (2 * w.d + 2 * w.dv) * 2          # read Q, K, V, write O (bf16)
+    alg_flops = token_heads * (4 * w.d * w.dv + (2 * w.chunk * (w.d + w.dv) if causal else 0))
+    out_ms = kern_ms[2]
+    achieved = alg_bytes / (out_ms * 1e-3) / 1e9
+    traffic = read_traffic(args.workload + ("" if causal else "_noncausal"), "la_output_kernel")
+    step_gbs = alg_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": w.B * w.N / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name} prefill B{w.B} H{w.H} N{w.N} d{w.d} dv{w.dv} bf16 I/O, fp32 state, "
+                        f"phi=elu+1, {'causal' if causal else 'non-causal'}, chunk {w.chunk}",
+            "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv, "chunk": w.chunk, "causal": causal,
+            "phi": "elu1", "accumulate": "fp32",
+        },
+        "roofline": {
+            "kernel": "la_output_kernel",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "path_roofline": {
+            "bound": "hbm",
+            "alg_bytes": alg_bytes,
+            "alg_flops": alg_flops,
+            "achieved_gbs": step_gbs,
+            "frac": step_gbs / HBM_PEAK_GBS,
+            "mfma_frac": alg_flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        },
+        "kernels_us": {n: t * 1e3 for n, t in zip(KERNEL_NAMES, kern_ms)},
+    }
+    if not args.no_cpu_baseline:
+        wall, h, cores = time_oracle_prefill(q, k, v, causal, max_heads=w.H)
+        # the sample covers h of the B*H heads at full length: scale to the job
+        per_job = wall * (w.B * w.H) / h
+        res["cpu_baseline"] = {
+            "value": w.B * w.N / per_job,
+            "unit": "tokens/s",
+            "cores": cores,
+            "kind": "oracle",
+            "sample": f"fp64 {'token recurrence' if causal else 'reassociated form'} over {h} of "
+                      f"{w.B * w.H} heads x {w.N} tokens ({wall:.1f} s), scaled to the full job",
+            "cpu": cpu_info(),
+        }
+    return res
+
+
+def bench_decode(args, torch, la, synth):
+    import numpy as np
+    dw = synth.DECODE_WORKLOAD
+    n, H, d, dv, T = dw["n_seq"], dw["H"], dw["d"], dw["dv"], dw["history"]
+    dev = torch.device("cuda:0")
+
+    def to_dev(x):
+        return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    kh, vh = synth.draw_decode_history(n, H, T, d, dv)
+    # the state comes from a prefill of the history through the library itself
+    _, S, z = la.forward(to_dev(np.zeros_like(kh)), to_dev(kh), to_dev(vh), return_state=True)
+    q, k, v = (to_dev(x) for x in synth.draw_decode_token(n, H, d, dv))
+    o = torch.empty((n, H, dv), dtype=torch.bfloat16, device=dev)
+    for _ in range(args.warmup):
+        la.decode_step(S, z, q, k, v, out=o)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        la.decode_step(S, z, q, k, v, out=o)
+    end.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    kern_ms = start.elapsed_time(end) / args.steps
+    per_head = d * dv * 4 * 2 + d * 4 * 2 + (2 * d + 2 * dv) * 2
+    alg_bytes = n * H * per_head
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    res = {
+        "metric": "decode steps/s (256 sequences x 32 heads, d=dv=128, fp32 state, bf16 tokens)",
+        "value": n / (ms * 1e-3),
+        "unit": "sequence-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"decode step {n} seq x {H} heads d{d} dv{dv}, state from a {T}-token prefill",
+                   "n_seq": n, "H": H, "d": d, "dv": dv},
+        "roofline": {"kernel": "la_decode_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": read_traffic("decode", "la_decode_kernel")},
+    }
+    return res
+
+
+def bench_feature(args, torch, la, synth):
+    import numpy as np
+    w = synth.WORKLOADS["long"]
+    dev = torch.device("cuda:0")
+    q, _, _ = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io="bf16")
+    X = torch.from_numpy(synth.bf16_bits(q).view(np.int16)).view(torch.bfloat16).to(dev)
+    del q
+    for _ in range(args.warmup):
+        Y = la.feature_map(X)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        Y = la.feature_map(X)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    alg_bytes = X.numel() * 2 + Y.numel() * 4
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "ELU+1 feature map rows/s (bf16 in, fp32 out)",
+        "value": X.numel() // w.d / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"phi over Q of the long prefill ({X.numel() // w.d} rows x {w.d})"},
+        "roofline": {"kernel": "la_phi_pointwise_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": read_traffic("feature", "la_phi_pointwise_kernel")},
+    }
+
+
+def bench_copy(args, torch):
+    """Plain device copy of a known size: the reference for scaling the HBM
+    byte counters of the other kernels."""
+    n = 256 * 1024 * 1024
+    a = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(args.warmup):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    return {"metric": "device copy GB/s (read + write)", "value": 2 * n / (ms * 1e-3) / 1e9, "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+            "data": "synthetic", "config": {"workload": f"copy of {n} bytes", "bytes_read": n, "bytes_written": n}}
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (how heads or the sequence "
+              "would shard is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    import kernelized_linear_attention_elu_amd as la
+    from kernelized_linear_attention_elu_amd import synth
+    if args.workload == "copy":
+        res = bench_copy(args, torch)
+    else:
+        la.load_library()
+        if args.workload == "decode":
+            res = bench_decode(args, torch, la, synth)
+        elif args.workload == "feature":
+            res = bench_feature(args, torch, la, synth)
+        else:
+            res = bench_prefill(args, torch, la, synth)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,154 @@
+/*
+ * liblinattn - causal kernelized linear attention on AMD Instinct MI355X
+ * (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * The operation (sources are web pages, cited by title and section):
+ *   - feature map phi: R^d -> R^r; ELU(x)+1 with alpha = 1 ("Choice of phi",
+ *     linear-attention-kernel page; "Efficient attention variants" sec. 4) or
+ *     Performer FAVOR+ positive random features ("Efficient attention
+ *     variants" sec. 6), plus the identity for feeding features directly;
+ *   - causal: S_t = S_{t-1} + phi(k_t) v_t^T, z_t = z_{t-1} + phi(k_t),
+ *     o_t = phi(q_t)^T S_t / phi(q_t)^T z_t with S_0 = 0, z_0 = 0
+ *     ("Efficient attention variants" sec. 5; "Recurrent form" of the
+ *     linear-attention-kernel page; "Why is linear attention an RNN" of the
+ *     linear-attention-and-SSM page).  Token t attends to itself;
+ *   - non-causal: S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j),
+ *     O = phi(Q) S / phi(Q) z ("Efficient attention variants" sec. 4).
+ *
+ * Conventions shared by every call
+ *   - Tensors are contiguous row-major device buffers owned by the caller:
+ *       Q, K [B][H][N][d]; V, O [B][H][N][d_v]; S [B][H][r][d_v]; z [B][H][r];
+ *       decode tokens q, k [B][H][d], v, o [B][H][d_v]; omega [r][d].
+ *     Every pointer must be 16-byte aligned.
+ *   - io_dtype selects the element type of Q, K, V, O, q, k, v, o and X:
+ *     LA_F32 (float) or LA_BF16 (bfloat16).  States S, z and the FAVOR+
+ *     projection omega are always fp32.  Arithmetic is fp32; bf16 data enter
+ *     the matrix cores as bf16 with fp32 accumulation.  Outputs are rounded
+ *     to nearest-even.
+ *   - r: feature dimension.  For LA_PHI_ELU1 and LA_PHI_IDENTITY r must equal d
+ *     (0 is accepted and means d).  For LA_PHI_FAVOR r is the number of omega
+ *     rows.
+ *   - stream: a hipStream_t (NULL = the default stream).  All work is enqueued
+ *     asynchronously on it; the library allocates no memory, keeps no state
+ *     between calls and is re-entrant.
+ *   - The returned status covers argument checks and launch errors
+ *     (LA_ERR_HIP after hipGetLastError).  Numerical results are not errors:
+ *     a zero denominator, possible only with the identity map, yields IEEE
+ *     inf/NaN in that row.
+ *   - Supported shapes (others return LA_ERR_UNSUPPORTED):
+ *       la_forward: d = d_v in {64, 128} with ELU1/IDENTITY (bf16), d = d_v = 64
+ *       (fp32); chunk in {16, 32, 64, 128} (bf16 d = 64), {16, 32, 64} otherwise;
+ *       any N >= 0, any B, H >= 0.
+ *       la_decode_step: d = d_v in {64, 128}; FAVOR+ with r = 256.
+ *       la_feature_map: ELU1/IDENTITY with d % 8 == 0; FAVOR+ with d in {64, 128},
+ *       r = 256.
+ */
+#ifndef LINATTN_LA_H
+#define LINATTN_LA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum la_status {
+  LA_OK = 0,
+  LA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  LA_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, or too large */
+  LA_ERR_UNSUPPORTED = 3, /* valid request outside the supported shapes         */
+  LA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                   */
+  LA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required            */
+  LA_ERR_HIP = 6          /* the HIP runtime reported an error                  */
+} la_status;
+
+typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+typedef enum la_phi_kind { LA_PHI_ELU1 = 0, LA_PHI_FAVOR = 1, LA_PHI_IDENTITY = 2 } la_phi_kind;
+
+/* Number of kernels la_forward enqueues (per-span state, span scan, output). */
+#define LA_FORWARD_KERNELS 3
+
+/*
+ * Workspace bytes la_forward needs for these arguments (fp32 per-span states:
+ * B*H*(n_span+1)*(r*d_v + r)*4 with n_span = ceil(N / span)).  The span is
+ * chosen by the library from B*H and N; the environment variable LA_SPAN
+ * (tokens, a multiple of chunk) overrides it and must not change between this
+ * query and the la_forward call.  Returns 0 for invalid arguments.
+ */
+size_t la_forward_workspace_bytes(int B, int H, int N, int d, int d_v, int phi, int r, int causal, int chunk);
+
+/*
+ * Prefill: O = causal (or non-causal) linear attention of Q, K, V, evaluated
+ * chunkwise ("Efficient attention variants" sec. 8: parallel inside a chunk,
+ * state passed between chunks).  The result equals the token recurrence up to
+ * rounding for every chunk size; chunk = 0 means 64.
+ *
+ *   Q, K, V  in:  device, io_dtype, layouts above.
+ *   O        out: device, io_dtype [B][H][N][d_v]; may not alias Q, K or V.
+ *   omega    in:  device fp32 [r][d] for LA_PHI_FAVOR, else ignored (may be NULL).
+ *   S0, z0   in:  optional initial state (both NULL = zero state, "state reset");
+ *                 if one is given the other must be too.
+ *   S_out, z_out out: optional final state S_N, z_N (fp32), for handing the
+ *                 prefix to la_decode_step or to a later la_forward call.
+ *                 Non-causal: the full sums (including S0, z0).
+ *   workspace    device scratch of at least la_forward_workspace_bytes(...);
+ *                 contents on entry are ignored; owned by the caller.
+ * Errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_UNSUPPORTED, LA_ERR_ALIGN,
+ * LA_ERR_WORKSPACE (nothing enqueued), LA_ERR_HIP (launch failed).
+ */
+la_status la_forward(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int d, int d_v,
+                     int io_dtype, int phi, int r, const float *omega, int causal, int chunk, const float *S0,
+                     const float *z0, float *S_out, float *z_out, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/*
+ * la_forward plus timing: events is NULL or an array of 2*LA_FORWARD_KERNELS
+ * hipEvent_t created by the caller (see la_event_create); events[2i] is
+ * recorded on the stream before kernel i and events[2i+1] after it.  Kernels:
+ * 0 = per-span state, 1 = span scan, 2 = output.
+ */
+la_status la_forward_timed(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int d,
+                           int d_v, int io_dtype, int phi, int r, const float *omega, int causal, int chunk,
+                           const float *S0, const float *z0, float *S_out, float *z_out, void *workspace,
+                           size_t workspace_bytes, void *stream, void *const *events);
+
+/*
+ * Decode step for B*H independent sequences/heads ("Efficient attention
+ * variants" sec. 5; "Recurrent form" of the linear-attention-kernel page):
+ *   S_new = S + phi(k) v^T, z_new = z + phi(k), o = phi(q)^T S_new / phi(q)^T z_new.
+ *   S, z        in:  fp32 [B][H][r][d_v], [B][H][r].
+ *   q, k, v     in:  io_dtype [B][H][d], [B][H][d], [B][H][d_v].
+ *   o           out: io_dtype [B][H][d_v].
+ *   S_new, z_new out: fp32; may alias S, z exactly (in-place update) but must
+ *                not partially overlap them.
+ * Errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_UNSUPPORTED, LA_ERR_ALIGN, LA_ERR_HIP.
+ */
+la_status la_decode_step(const float *S, const float *z, const void *q, const void *k, const void *v, void *o,
+                         float *S_new, float *z_new, int B, int H, int d, int d_v, int io_dtype, int phi, int r,
+                         const float *omega, void *stream);
+
+/*
+ * Standalone feature map: Y[i] = phi(X[i]) for rows i = 0..rows-1.
+ *   X in: io_dtype [rows][d];  Y out: fp32 [rows][r];  omega as in la_forward.
+ * Errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_UNSUPPORTED, LA_ERR_ALIGN, LA_ERR_HIP.
+ */
+la_status la_feature_map(const void *X, float *Y, long long rows, int d, int io_dtype, int phi, int r,
+                         const float *omega, void *stream);
+
+/* Static, human-readable text for a status code. */
+const char *la_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int la_version(void);
+
+/* Event helpers for la_forward_timed (thin wrappers over hipEvent*). */
+la_status la_event_create(void **event);
+la_status la_event_destroy(void *event);
+la_status la_event_elapsed_ms(void *start, void *end, float *ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_LA_H */

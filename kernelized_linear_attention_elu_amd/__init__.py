@@ -1,1 +1,240 @@
-"""MI355X-native causal kernelized linear attention (binding in progress)."""
+"""Causal kernelized linear attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``liblinattn.so`` (declared in
+``include/la.h``).  It only marshals arguments: checks dtypes, shapes and
+contiguity, allocates outputs and the workspace with PyTorch, and passes raw
+device pointers and the current HIP stream to the library.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback, and
+a missing library raises an error.
+
+    forward(Q, K, V, phi="elu1", causal=True, chunk=64, ...)  -> O [, S_N, z_N]
+    decode_step(S, z, q, k, v, phi="elu1", ...)               -> o (S, z updated)
+    feature_map(X, phi="elu1", ...)                           -> Phi (fp32)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "la.h")
+
+LA_F32, LA_BF16 = 0, 1
+PHI = {"elu1": 0, "favor": 1, "identity": 2}
+LA_FORWARD_KERNELS = 3
+STATUS = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_UNSUPPORTED",
+          4: "LA_ERR_ALIGN", 5: "LA_ERR_WORKSPACE", 6: "LA_ERR_HIP"}
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_SIGS = {
+    "la_forward_workspace_bytes": (ctypes.c_size_t, [_i] * 9),
+    "la_forward": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
+    "la_forward_timed": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp, _vp]),
+    "la_decode_step": (_i, [_vp] * 8 + [_i] * 7 + [_vp, _vp]),
+    "la_feature_map": (_i, [_vp, _vp, ctypes.c_longlong, _i, _i, _i, _i, _vp, _vp]),
+    "la_status_string": (ctypes.c_char_p, [_i]),
+    "la_version": (_i, []),
+    "la_event_create": (_i, [ctypes.POINTER(_vp)]),
+    "la_event_destroy": (_i, [_vp]),
+    "la_event_elapsed_ms": (_i, [_vp, _vp, ctypes.POINTER(ctypes.c_float)]),
+}
+
+
+class LinAttnError(RuntimeError):
+    """A non-zero la_status from the library."""
+
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+def load_library(path=None):
+    """Load liblinattn.so (built by ``build.py``).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m kernelized_linear_attention_elu_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def header_functions():
+    """Names of the functions declared in include/la.h."""
+    with open(HEADER_PATH, encoding="utf-8") as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_\w+)\s*\(", text)))
+
+
+def status_string(status):
+    return load_library().la_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != 0:
+        raise LinAttnError(status, where)
+
+
+# ------------------------------------------------------------------ torch marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_bytes(B, H, N, d, dv, phi="elu1", r=0, causal=True, chunk=64):
+    return int(load_library().la_forward_workspace_bytes(B, H, N, d, dv, PHI[phi], r, int(causal), chunk))
+
+
+def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, z0=None,
+            return_state=False, out=None, workspace=None, events=None):
+    """Causal (or non-causal) linear attention over Q, K [B,H,N,d], V [B,H,N,dv].
+
+    Returns O [B,H,N,dv] (same dtype as Q); with ``return_state`` also the
+    final state S_N [B,H,r,dv] and z_N [B,H,r] (fp32).  ``S0``/``z0`` give an
+    initial state.  ``events``: optional list of 2*LA_FORWARD_KERNELS event
+    handles from :func:`event_create` recorded around the library's kernels.
+    """
+    torch = _torch()
+    lib = load_library()
+    if Q.dim() != 4 or K.dim() != 4 or V.dim() != 4:
+        raise ValueError("Q, K, V must be [B, H, N, d]")
+    B, H, N, d = Q.shape
+    dv = V.shape[-1]
+    if K.shape != Q.shape or V.shape[:3] != Q.shape[:3]:
+        raise ValueError("shape mismatch between Q, K, V")
+    dev = Q.device
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        _require(t, name, Q.dtype, dev)
+    io = _io_code(Q)
+    r = omega.shape[0] if (phi == "favor" and omega is not None) else d
+    _require(omega, "omega", torch.float32, dev)
+    if (S0 is None) != (z0 is None):
+        raise ValueError("give both S0 and z0 or neither")
+    _require(S0, "S0", torch.float32, dev)
+    _require(z0, "z0", torch.float32, dev)
+    if S0 is not None and (tuple(S0.shape) != (B, H, r, dv) or tuple(z0.shape) != (B, H, r)):
+        raise ValueError("S0 must be [B,H,r,dv] and z0 [B,H,r]")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=Q.dtype, device=dev)
+    _require(out, "out", Q.dtype, dev)
+    S_out = z_out = None
+    if return_state:
+        S_out = torch.empty((B, H, r, dv), dtype=torch.float32, device=dev)
+        z_out = torch.empty((B, H, r), dtype=torch.float32, device=dev)
+    need = int(lib.la_forward_workspace_bytes(B, H, N, d, dv, PHI[phi], r, int(causal), chunk))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    args = [_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, d, dv, io, PHI[phi], r, _ptr(omega),
+            int(causal), chunk, _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(dev)]
+    if events is None:
+        _check(lib.la_forward(*args), "la_forward")
+    else:
+        arr = (ctypes.c_void_p * (2 * LA_FORWARD_KERNELS))(*events)
+        _check(lib.la_forward_timed(*args, arr), "la_forward_timed")
+    if return_state:
+        return out, S_out, z_out
+    return out
+
+
+def decode_step(S, z, q, k, v, *, phi="elu1", omega=None, inplace=True, out=None):
+    """One decode step for every (batch, head): S, z updated in place (or new
+    tensors when ``inplace=False``).  Returns o, or (o, S_new, z_new)."""
+    torch = _torch()
+    lib = load_library()
+    B, H, d = q.shape
+    dv = v.shape[-1]
+    r = S.shape[-2]
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, q.dtype, dev)
+    _require(S, "S", torch.float32, dev)
+    _require(z, "z", torch.float32, dev)
+    _require(omega, "omega", torch.float32, dev)
+    if tuple(S.shape) != (B, H, r, dv) or tuple(z.shape) != (B, H, r) or tuple(k.shape) != (B, H, d):
+        raise ValueError("decode shapes: S [B,H,r,dv], z [B,H,r], q,k [B,H,d], v [B,H,dv]")
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    S_new, z_new = (S, z) if inplace else (torch.empty_like(S), torch.empty_like(z))
+    st = lib.la_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_new), _ptr(z_new),
+                            B, H, d, dv, _io_code(q), PHI[phi], r, _ptr(omega), _stream(dev))
+    _check(st, "la_decode_step")
+    return out if inplace else (out, S_new, z_new)
+
+
+def feature_map(X, *, phi="elu1", omega=None):
+    """phi applied to the rows of X [..., d]; returns fp32 [..., r]."""
+    torch = _torch()
+    lib = load_library()
+    d = X.shape[-1]
+    rows = X.numel() // d if d else 0
+    _require(X, "X", X.dtype, X.device)
+    _require(omega, "omega", torch.float32, X.device)
+    r = omega.shape[0] if phi == "favor" else d
+    Y = torch.empty(tuple(X.shape[:-1]) + (r,), dtype=torch.float32, device=X.device)
+    st = lib.la_feature_map(_ptr(X), _ptr(Y), rows, d, _io_code(X), PHI[phi], r, _ptr(omega), _stream(X.device))
+    _check(st, "la_feature_map")
+    return Y
+
+
+def event_create():
+    ev = ctypes.c_void_p()
+    _check(load_library().la_event_create(ctypes.byref(ev)), "la_event_create")
+    return ev.value
+
+
+def event_destroy(ev):
+    _check(load_library().la_event_destroy(ev), "la_event_destroy")
+
+
+def event_elapsed_ms(a, b):
+    ms = ctypes.c_float()
+    _check(load_library().la_event_elapsed_ms(a, b, ctypes.byref(ms)), "la_event_elapsed_ms")
+    return ms.value

@@ -1,0 +1,208 @@
+// C-ABI layer: argument validation, span choice, workspace sizing, dispatch.
+// Validation never touches the HIP runtime, so every error path can be
+// exercised on a machine without a GPU.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <hip/hip_runtime.h>
+
+#include "la.h"
+#include "la_prefill.h"
+
+namespace {
+
+constexpr int kMaxDim = 1 << 20;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int norm_r(int phi, int d, int r) {
+  if (phi == LA_PHI_ELU1 || phi == LA_PHI_IDENTITY) return r == 0 ? d : r;
+  return r;
+}
+
+int norm_chunk(int chunk) { return chunk == 0 ? 64 : chunk; }
+
+// Tokens per workgroup: a multiple of the chunk, large enough to amortise the
+// per-span state traffic (r*d_v*4 bytes written, scanned and read back per
+// span) and small enough to give >= 1024 workgroups when the problem allows.
+int choose_span(long long BH, int N, int chunk) {
+  const char* env = getenv("LA_SPAN");
+  if (env && *env) {
+    const long v = strtol(env, nullptr, 10);
+    if (v >= chunk && v % chunk == 0 && v <= (1 << 24)) return static_cast<int>(v);
+  }
+  int span = 256;
+  while (span < 2048 && BH * ((static_cast<long long>(N) + 2 * span - 1) / (2 * span)) >= 1024) span *= 2;
+  if (span < chunk) span = chunk;
+  return span;
+}
+
+struct Shape {
+  int B, H, N, d, dv, r, phi, causal, chunk, span, n_span;
+  long long BH;
+};
+
+la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int phi, int r, int causal, int chunk,
+                              Shape* sh) {
+  if (B < 0 || H < 0 || N < 0 || d <= 0 || d_v <= 0 || r < 0 || chunk < 0) return LA_ERR_SHAPE;
+  if (d > kMaxDim || d_v > kMaxDim || r > kMaxDim) return LA_ERR_SHAPE;
+  if (io != LA_F32 && io != LA_BF16) return LA_ERR_UNSUPPORTED;
+  if (phi != LA_PHI_ELU1 && phi != LA_PHI_FAVOR && phi != LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return LA_ERR_UNSUPPORTED;
+  const int rr = norm_r(phi, d, r);
+  const int ch = norm_chunk(chunk);
+  if (!la::prefill_supported(io, phi, d, d_v, rr, ch)) return LA_ERR_UNSUPPORTED;
+  const long long BH = static_cast<long long>(B) * H;
+  if (BH > (1LL << 30)) return LA_ERR_SHAPE;
+  // element counts must fit the 64-bit indexing used by the kernels, and the
+  // grid (B*H*n_span workgroups) must fit a 32-bit launch
+  const int span = choose_span(BH, N, ch);
+  const long long n_span = (static_cast<long long>(N) + span - 1) / span;
+  if (BH * n_span > 0x7fffffffLL) return LA_ERR_SHAPE;
+  sh->B = B; sh->H = H; sh->N = N; sh->d = d; sh->dv = d_v; sh->r = rr; sh->phi = phi;
+  sh->causal = causal; sh->chunk = ch; sh->span = span; sh->n_span = static_cast<int>(n_span); sh->BH = BH;
+  return LA_OK;
+}
+
+size_t workspace_for(const Shape& sh) {
+  const size_t E = static_cast<size_t>(sh.r) * sh.dv + sh.r;
+  return static_cast<size_t>(sh.BH) * (static_cast<size_t>(sh.n_span) + 1) * E * sizeof(float);
+}
+
+la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+                       int d_v, int io, int phi, int r, const float* omega, int causal, int chunk, const float* S0,
+                       const float* z0, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
+                       void* stream, void* const* events) {
+  Shape sh;
+  la_status st = check_forward_shape(B, H, N, d, d_v, io, phi, r, causal, chunk, &sh);
+  if (st != LA_OK) return st;
+  const bool have_tokens = sh.BH > 0 && N > 0;
+  if (have_tokens && (!Q || !K || !V || !O)) return LA_ERR_NULL;
+  if (phi == LA_PHI_FAVOR && !omega) return LA_ERR_NULL;
+  if ((S0 == nullptr) != (z0 == nullptr)) return LA_ERR_NULL;
+  if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_NULL;
+  const void* ptrs[] = {Q, K, V, O, omega, S0, z0, S_out, z_out, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return LA_ERR_ALIGN;
+  const size_t need = workspace_for(sh);
+  if (sh.BH > 0 && (!workspace || workspace_bytes < need)) return LA_ERR_WORKSPACE;
+  if (sh.BH == 0) return LA_OK;
+
+  la::PrefillArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O;
+  a.B = B; a.H = H; a.N = N; a.d = d; a.dv = d_v; a.r = sh.r;
+  a.io = io; a.phi = phi; a.omega = omega; a.causal = causal;
+  a.chunk = sh.chunk; a.span = sh.span; a.n_span = sh.n_span;
+  a.S0 = S0; a.z0 = z0; a.S_out = S_out; a.z_out = z_out;
+  a.workspace = workspace; a.stream = stream; a.events = events;
+  return la::prefill_launch(a) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t la_forward_workspace_bytes(int B, int H, int N, int d, int d_v, int phi, int r, int causal, int chunk) {
+  Shape sh;
+  // the workspace does not depend on the I/O type; check against bf16 support
+  if (check_forward_shape(B, H, N, d, d_v, LA_BF16, phi, r, causal, chunk, &sh) != LA_OK &&
+      check_forward_shape(B, H, N, d, d_v, LA_F32, phi, r, causal, chunk, &sh) != LA_OK)
+    return 0;
+  return workspace_for(sh);
+}
+
+la_status la_forward(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d, int d_v,
+                     int io_dtype, int phi, int r, const float* omega, int causal, int chunk, const float* S0,
+                     const float* z0, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return forward_impl(Q, K, V, O, B, H, N, d, d_v, io_dtype, phi, r, omega, causal, chunk, S0, z0, S_out, z_out,
+                      workspace, workspace_bytes, stream, nullptr);
+}
+
+la_status la_forward_timed(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+                           int d_v, int io_dtype, int phi, int r, const float* omega, int causal, int chunk,
+                           const float* S0, const float* z0, float* S_out, float* z_out, void* workspace,
+                           size_t workspace_bytes, void* stream, void* const* events) {
+  return forward_impl(Q, K, V, O, B, H, N, d, d_v, io_dtype, phi, r, omega, causal, chunk, S0, z0, S_out, z_out,
+                      workspace, workspace_bytes, stream, events);
+}
+
+la_status la_decode_step(const float* S, const float* z, const void* q, const void* k, const void* v, void* o,
+                         float* S_new, float* z_new, int B, int H, int d, int d_v, int io_dtype, int phi, int r,
+                         const float* omega, void* stream) {
+  if (B < 0 || H < 0 || d <= 0 || d_v <= 0 || r < 0) return LA_ERR_SHAPE;
+  if (static_cast<long long>(B) * H > 0x7fffffffLL) return LA_ERR_SHAPE;
+  if (io_dtype != LA_F32 && io_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  if (phi != LA_PHI_ELU1 && phi != LA_PHI_FAVOR && phi != LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;
+  const int rr = norm_r(phi, d, r);
+  if (!la::decode_supported(io_dtype, phi, d, d_v, rr)) return LA_ERR_UNSUPPORTED;
+  const long long BH = static_cast<long long>(B) * H;
+  if (BH > 0 && (!S || !z || !q || !k || !v || !o || !S_new || !z_new)) return LA_ERR_NULL;
+  if (phi == LA_PHI_FAVOR && !omega) return LA_ERR_NULL;
+  const void* ptrs[] = {S, z, q, k, v, o, S_new, z_new, omega};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return LA_ERR_ALIGN;
+  if (BH == 0) return LA_OK;
+  la::DecodeArgs a;
+  a.S = S; a.z = z; a.q = q; a.k = k; a.v = v; a.o = o; a.S_new = S_new; a.z_new = z_new;
+  a.B = B; a.H = H; a.d = d; a.dv = d_v; a.r = rr; a.io = io_dtype; a.phi = phi; a.omega = omega;
+  a.stream = stream;
+  return la::decode_launch(a) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status la_feature_map(const void* X, float* Y, long long rows, int d, int io_dtype, int phi, int r,
+                         const float* omega, void* stream) {
+  if (rows < 0 || d <= 0 || r < 0 || d > kMaxDim) return LA_ERR_SHAPE;
+  if (io_dtype != LA_F32 && io_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  if (phi != LA_PHI_ELU1 && phi != LA_PHI_FAVOR && phi != LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;
+  const int rr = norm_r(phi, d, r);
+  if (!la::feature_supported(io_dtype, phi, d, rr)) return LA_ERR_UNSUPPORTED;
+  if (rows > (1LL << 40) / (rr > d ? rr : d)) return LA_ERR_SHAPE;
+  if (rows > 0 && (!X || !Y)) return LA_ERR_NULL;
+  if (phi == LA_PHI_FAVOR && !omega) return LA_ERR_NULL;
+  const void* ptrs[] = {X, Y, omega};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return LA_ERR_ALIGN;
+  if (rows == 0) return LA_OK;
+  la::FeatureArgs a;
+  a.X = X; a.Y = Y; a.rows = rows; a.d = d; a.r = rr; a.io = io_dtype; a.phi = phi; a.omega = omega;
+  a.stream = stream;
+  return la::feature_launch(a) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+const char* la_status_string(int status) {
+  switch (status) {
+    case LA_OK: return "ok";
+    case LA_ERR_NULL: return "a required pointer is NULL";
+    case LA_ERR_SHAPE: return "invalid size or shape";
+    case LA_ERR_UNSUPPORTED: return "unsupported dtype, feature map, dimension or chunk";
+    case LA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case LA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int la_version(void) { return 100; }
+
+la_status la_event_create(void** event) {
+  if (!event) return LA_ERR_NULL;
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return LA_ERR_HIP;
+  *event = e;
+  return LA_OK;
+}
+
+la_status la_event_destroy(void* event) {
+  if (!event) return LA_ERR_NULL;
+  return hipEventDestroy(static_cast<hipEvent_t>(event)) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status la_event_elapsed_ms(void* start, void* end, float* ms) {
+  if (!start || !end || !ms) return LA_ERR_NULL;
+  return hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(end)) == hipSuccess
+             ? LA_OK
+             : LA_ERR_HIP;
+}
+
+}  // extern "C"

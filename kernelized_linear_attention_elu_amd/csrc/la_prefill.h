@@ -1,0 +1,67 @@
+// Internal (C++) interface between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace la {
+
+struct PrefillArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  int B, H, N, d, dv, r;
+  int io;      // 0 = fp32, 1 = bf16
+  int phi;     // PhiKind
+  const float* omega;
+  int causal;
+  int chunk;
+  int span;    // tokens per workgroup (multiple of chunk)
+  int n_span;  // ceil(N / span)
+  const float* S0;
+  const float* z0;
+  float* S_out;
+  float* z_out;
+  void* workspace;
+  void* stream;
+  void* const* events;  // optional: 6 hipEvent_t recorded around the three kernels
+};
+
+bool prefill_supported(int io, int phi, int d, int dv, int r, int chunk);
+hipError_t prefill_launch(const PrefillArgs& a);
+
+struct DecodeArgs {
+  const float* S;
+  const float* z;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* S_new;
+  float* z_new;
+  int B, H, d, dv, r;
+  int io;
+  int phi;
+  const float* omega;
+  void* stream;
+};
+
+bool decode_supported(int io, int phi, int d, int dv, int r);
+hipError_t decode_launch(const DecodeArgs& a);
+
+struct FeatureArgs {
+  const void* X;
+  float* Y;
+  long long rows;
+  int d, r;
+  int io;
+  int phi;
+  const float* omega;
+  void* stream;
+};
+
+bool feature_supported(int io, int phi, int d, int r);
+hipError_t feature_launch(const FeatureArgs& a);
+
+}  // namespace la

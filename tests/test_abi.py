@@ -1,0 +1,121 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load, export every function declared in include/la.h, and
+reject invalid arguments before touching the HIP runtime.  The pointers used
+here are never dereferenced: every call below fails validation first.
+"""
+
+import ctypes
+import os
+
+import pytest
+
+import kernelized_linear_attention_elu_amd as la
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(la.LIB_PATH):
+        from kernelized_linear_attention_elu_amd import build
+        build.build()
+    return la.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = la.header_functions()
+    assert {"la_forward", "la_decode_step", "la_forward_workspace_bytes", "la_status_string",
+            "la_feature_map"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in la.h but not exported"
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.la_status_string(code).decode()
+    assert lib.la_status_string(99).decode() == "unknown status"
+    assert lib.la_version() >= 100
+
+
+def _ws(B, H, N, d=64, dv=64, phi=0, r=0, causal=1, chunk=64):
+    return la.load_library().la_forward_workspace_bytes(B, H, N, d, dv, phi, r, causal, chunk)
+
+
+def test_workspace_sizes(lib, monkeypatch):
+    monkeypatch.delenv("LA_SPAN", raising=False)
+    E = 64 * 64 + 64
+    # long prefill B1 H32 N32768: 1024-token spans -> 32 spans per head
+    assert _ws(1, 32, 32768) == 32 * 33 * E * 4
+    # prefill B4 H16 N4096: 256-token spans -> 16 spans per head
+    assert _ws(4, 16, 4096) == 64 * 17 * E * 4
+    # wide heads B2 H16 N65536 d128: 2048-token spans -> 32 spans
+    assert _ws(2, 16, 65536, 128, 128) == 32 * 33 * (128 * 128 + 128) * 4
+    # N = 0 still needs one slot per head for the (initial = final) state
+    assert _ws(1, 2, 0) == 2 * 1 * E * 4
+    monkeypatch.setenv("LA_SPAN", "64")
+    assert _ws(1, 1, 256) == 1 * 5 * E * 4
+    monkeypatch.setenv("LA_SPAN", "48")  # not a multiple of the chunk: ignored
+    assert _ws(1, 1, 256) == 1 * 2 * E * 4
+    # unsupported shapes report 0
+    assert _ws(1, 1, 16, 96, 96) == 0
+    assert _ws(1, 1, 16, 64, 64, chunk=24) == 0
+
+
+FAKE = ctypes.c_void_p(0x100000)      # aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x100008)
+
+
+def _fwd(lib, Q=FAKE, K=FAKE, V=FAKE, O=FAKE, B=1, H=1, N=64, d=64, dv=64, io=1, phi=0, r=0, omega=None,
+         causal=1, chunk=64, S0=None, z0=None, S_out=None, z_out=None, ws=FAKE, ws_bytes=1 << 30):
+    return lib.la_forward(Q, K, V, O, B, H, N, d, dv, io, phi, r, omega, causal, chunk, S0, z0, S_out, z_out,
+                          ws, ws_bytes, None)
+
+
+def test_forward_argument_errors(lib):
+    assert _fwd(lib, Q=None) == 1                       # LA_ERR_NULL
+    assert _fwd(lib, N=-1) == 2                         # LA_ERR_SHAPE
+    assert _fwd(lib, d=0) == 2
+    assert _fwd(lib, d=96, dv=96) == 3                  # LA_ERR_UNSUPPORTED
+    assert _fwd(lib, chunk=48) == 3
+    assert _fwd(lib, io=7) == 3
+    assert _fwd(lib, phi=9) == 3
+    assert _fwd(lib, causal=2) == 3
+    assert _fwd(lib, r=32) == 3                         # ELU+1 keeps r = d
+    assert _fwd(lib, O=MISALIGNED) == 4                 # LA_ERR_ALIGN
+    assert _fwd(lib, ws=None) == 5                      # LA_ERR_WORKSPACE
+    assert _fwd(lib, ws_bytes=16) == 5
+    assert _fwd(lib, S0=FAKE, z0=None) == 1             # S0 without z0
+    assert _fwd(lib, S_out=FAKE, z_out=None) == 1
+    assert _fwd(lib, io=0, d=128, dv=128) == 3          # fp32 I/O only at d = 64
+    assert _fwd(lib, chunk=128, d=128, dv=128) == 3
+    # nothing to do: B*H == 0 succeeds without touching any pointer
+    assert _fwd(lib, Q=None, K=None, V=None, O=None, B=0, ws=None) == 0
+
+
+def test_decode_argument_errors(lib):
+    def dec(S=FAKE, z=FAKE, q=FAKE, k=FAKE, v=FAKE, o=FAKE, Sn=FAKE, zn=FAKE, B=1, H=1, d=64, dv=64, io=1,
+            phi=0, r=0, omega=None):
+        return lib.la_decode_step(S, z, q, k, v, o, Sn, zn, B, H, d, dv, io, phi, r, omega, None)
+    assert dec(S=None) == 1
+    assert dec(B=-1) == 2
+    assert dec(d=32, dv=32) == 3
+    assert dec(phi=1, r=256) == 1                        # FAVOR+ needs omega
+    assert dec(phi=1, r=128, omega=FAKE) == 3
+    assert dec(o=MISALIGNED) == 4
+    assert dec(B=0, S=None, z=None) == 0
+
+
+def test_feature_map_argument_errors(lib):
+    def fm(X=FAKE, Y=FAKE, rows=10, d=64, io=1, phi=0, r=0, omega=None):
+        return lib.la_feature_map(X, Y, rows, d, io, phi, r, omega, None)
+    assert fm(X=None) == 1
+    assert fm(rows=-1) == 2
+    assert fm(d=12) == 3
+    assert fm(phi=1, r=256) == 1
+    assert fm(Y=MISALIGNED) == 4
+    assert fm(rows=0, X=None, Y=None) == 0
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(la, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        la.load_library(str(tmp_path / "nope.so"))
