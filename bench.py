@@ -114,14 +114,14 @@ def time_oracle_prefill(q, k, v, causal, max_heads):
 
 
 def bench_prefill(args, torch, la, synth):
+    from kernelized_linear_attention_elu_amd import hostio
     w = synth.WORKLOADS[args.workload]
     causal = not args.noncausal
     dev = torch.device("cuda:0")
     q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
 
     def to_dev(x):
-        import numpy as np
-        return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return hostio.upload_bf16_bits(synth.bf16_bits(x), dev)
 
     Q, K, V = to_dev(q), to_dev(k), to_dev(v)
     O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.bfloat16, device=dev)
@@ -211,13 +211,14 @@ def bench_prefill(args, torch, la, synth):
 
 
 def bench_decode(args, torch, la, synth):
+    from kernelized_linear_attention_elu_amd import hostio
     import numpy as np
     dw = synth.DECODE_WORKLOAD
     n, H, d, dv, T = dw["n_seq"], dw["H"], dw["d"], dw["dv"], dw["history"]
     dev = torch.device("cuda:0")
 
     def to_dev(x):
-        return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return hostio.upload_bf16_bits(synth.bf16_bits(x), dev)
 
     kh, vh = synth.draw_decode_history(n, H, T, d, dv)
     # the state comes from a prefill of the history through the library itself
@@ -257,11 +258,12 @@ def bench_decode(args, torch, la, synth):
 
 
 def bench_feature(args, torch, la, synth):
+    from kernelized_linear_attention_elu_amd import hostio
     import numpy as np
     w = synth.WORKLOADS["long"]
     dev = torch.device("cuda:0")
     q, _, _ = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io="bf16")
-    X = torch.from_numpy(synth.bf16_bits(q).view(np.int16)).view(torch.bfloat16).to(dev)
+    X = hostio.upload_bf16_bits(synth.bf16_bits(q), dev)
     del q
     for _ in range(args.warmup):
         Y = la.feature_map(X)

@@ -31,6 +31,10 @@
  *   - stream: a hipStream_t (NULL = the default stream).  All work is enqueued
  *     asynchronously on it; the library allocates no memory, keeps no state
  *     between calls and is re-entrant.
+ *   - The library links the HIP runtime by its soname (libamdhip64.so.7).  In a
+ *     process that also uses PyTorch, load PyTorch first so that both share
+ *     the runtime PyTorch brings (the Python binding does this); otherwise two
+ *     HIP runtimes end up in one process.
  *   - The returned status covers argument checks and launch errors
  *     (LA_ERR_HIP after hipGetLastError).  Numerical results are not errors:
  *     a zero denominator, possible only with the identity map, yields IEEE
@@ -138,6 +142,10 @@ la_status la_feature_map(const void *X, float *Y, long long rows, int d, int io_
 
 /* Static, human-readable text for a status code. */
 const char *la_status_string(int status);
+
+/* Text of the HIP runtime error behind the most recent LA_ERR_HIP returned
+ * to the calling thread ("" if none).  Static storage; do not free. */
+const char *la_hip_error_string(void);
 
 /* Library ABI version (major * 100 + minor). */
 int la_version(void);

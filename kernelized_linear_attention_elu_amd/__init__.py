@@ -40,6 +40,7 @@ _SIGS = {
     "la_feature_map": (_i, [_vp, _vp, ctypes.c_longlong, _i, _i, _i, _i, _vp, _vp]),
     "la_status_string": (ctypes.c_char_p, [_i]),
     "la_version": (_i, []),
+    "la_hip_error_string": (ctypes.c_char_p, []),
     "la_event_create": (_i, [ctypes.POINTER(_vp)]),
     "la_event_destroy": (_i, [_vp]),
     "la_event_elapsed_ms": (_i, [_vp, _vp, ctypes.POINTER(ctypes.c_float)]),
@@ -51,7 +52,10 @@ class LinAttnError(RuntimeError):
 
     def __init__(self, status, where):
         self.status = status
-        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+        detail = status_string(status)
+        if status == 6:
+            detail += ": " + load_library().la_hip_error_string().decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({detail})")
 
 
 def load_library(path=None):
@@ -64,6 +68,14 @@ def load_library(path=None):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m kernelized_linear_attention_elu_amd.build` "
             "(there is no non-HIP fallback)")
+    # PyTorch ships its own HIP runtime and links it by a different file name
+    # than the system one this library was linked against.  Loading torch
+    # first lets the library bind to the runtime already in the process;
+    # the other order would put two HIP/HSA runtimes in one process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)

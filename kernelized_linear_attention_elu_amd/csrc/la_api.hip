@@ -13,6 +13,15 @@ namespace {
 
 constexpr int kMaxDim = 1 << 20;
 
+// Text of the most recent HIP failure seen by a call on this thread.
+thread_local const char* t_last_hip_error = "";
+
+la_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return LA_OK;
+  t_last_hip_error = hipGetErrorString(e);
+  return LA_ERR_HIP;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int norm_r(int phi, int d, int r) {
@@ -95,7 +104,7 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
   a.chunk = sh.chunk; a.span = sh.span; a.n_span = sh.n_span;
   a.S0 = S0; a.z0 = z0; a.S_out = S_out; a.z_out = z_out;
   a.workspace = workspace; a.stream = stream; a.events = events;
-  return la::prefill_launch(a) == hipSuccess ? LA_OK : LA_ERR_HIP;
+  return hip_status(la::prefill_launch(a));
 }
 
 }  // namespace
@@ -147,7 +156,7 @@ la_status la_decode_step(const float* S, const float* z, const void* q, const vo
   a.S = S; a.z = z; a.q = q; a.k = k; a.v = v; a.o = o; a.S_new = S_new; a.z_new = z_new;
   a.B = B; a.H = H; a.d = d; a.dv = d_v; a.r = rr; a.io = io_dtype; a.phi = phi; a.omega = omega;
   a.stream = stream;
-  return la::decode_launch(a) == hipSuccess ? LA_OK : LA_ERR_HIP;
+  return hip_status(la::decode_launch(a));
 }
 
 la_status la_feature_map(const void* X, float* Y, long long rows, int d, int io_dtype, int phi, int r,
@@ -167,7 +176,7 @@ la_status la_feature_map(const void* X, float* Y, long long rows, int d, int io_
   la::FeatureArgs a;
   a.X = X; a.Y = Y; a.rows = rows; a.d = d; a.r = rr; a.io = io_dtype; a.phi = phi; a.omega = omega;
   a.stream = stream;
-  return la::feature_launch(a) == hipSuccess ? LA_OK : LA_ERR_HIP;
+  return hip_status(la::feature_launch(a));
 }
 
 const char* la_status_string(int status) {
@@ -185,10 +194,12 @@ const char* la_status_string(int status) {
 
 int la_version(void) { return 100; }
 
+const char* la_hip_error_string(void) { return t_last_hip_error; }
+
 la_status la_event_create(void** event) {
   if (!event) return LA_ERR_NULL;
   hipEvent_t e;
-  if (hipEventCreate(&e) != hipSuccess) return LA_ERR_HIP;
+  if (hipEventCreate(&e) != hipSuccess) return hip_status(hipErrorUnknown);
   *event = e;
   return LA_OK;
 }

@@ -137,6 +137,7 @@ template <typename T, int D, int R, int DV, int PHI>
 static hipError_t launch_decode(const DecodeArgs& a) {
   const int BH = a.B * a.H;
   if (BH == 0) return hipSuccess;
+  (void)hipGetLastError();  // drop a stale error left by an unrelated earlier runtime call
   hipLaunchKernelGGL((la_decode_kernel<T, D, R, DV, PHI>), dim3(BH), dim3(kThreads), 0,
                      static_cast<hipStream_t>(a.stream), a.S, a.z, static_cast<const T*>(a.q),
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<T*>(a.o), a.S_new,

@@ -91,6 +91,7 @@ template <typename T>
 static hipError_t feature_io(const FeatureArgs& a) {
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   if (a.rows == 0) return hipSuccess;
+  (void)hipGetLastError();  // drop a stale error left by an unrelated earlier runtime call
   if (a.phi == PHI_FAVOR) {
     const long long blocks = (a.rows + 15) / 16;
     const int grid = static_cast<int>(blocks < 4096 ? blocks : 4096);

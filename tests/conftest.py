@@ -18,3 +18,10 @@ def lib():
     import kernelized_linear_attention_elu_amd as la
     la.load_library()
     return la
+
+
+def pytest_runtest_logreport(report):
+    """Print a failing test's report at once, so that it survives even if a
+    later test takes the process down."""
+    if report.failed:
+        print(f"\n---- {report.nodeid} ({report.when}) failed ----\n{report.longreprtext}\n", flush=True)

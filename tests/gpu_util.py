@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from kernelized_linear_attention_elu_amd import synth
+from kernelized_linear_attention_elu_amd import hostio, synth
 
 TOL_F32_ABS = 1e-4
 TOL_BF16_ABS = 2e-2
@@ -18,23 +18,20 @@ TOL_BF16_REL = 2e-2
 
 
 def to_dev(x, io, device="cuda"):
-    """float32 numpy array (already representable in ``io``) -> device tensor."""
-    import torch
+    """float32 numpy array (already representable in ``io``) -> device tensor
+    (copied through pinned staging memory)."""
     if io == "bf16":
-        bits = synth.bf16_bits(x)
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
-    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+        return hostio.upload_bf16_bits(synth.bf16_bits(x), device)
+    return hostio.upload_f32(x, device)
 
 
 def f32_dev(x, device="cuda"):
-    import torch
-    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+    return hostio.upload_f32(x, device)
 
 
 def to_host(t):
     """Device tensor -> float64 numpy array (exact for bf16 and fp32)."""
-    import torch
-    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+    return hostio.download_f64(t.detach())
 
 
 def check_close(got, ref, io, what=""):
