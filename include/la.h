@@ -75,12 +75,15 @@ typedef enum la_phi_kind { LA_PHI_ELU1 = 0, LA_PHI_FAVOR = 1, LA_PHI_IDENTITY = 
 
 /*
  * Workspace bytes la_forward needs for these arguments (fp32 per-span states:
- * B*H*(n_span+1)*(r*d_v + r)*4 with n_span = ceil(N / span)).  The span is
- * chosen by the library from B*H and N; the environment variable LA_SPAN
- * (tokens, a multiple of chunk) overrides it and must not change between this
- * query and the la_forward call.  Returns 0 for invalid arguments.
+ * B*H*(n_span+1)*(r*d_v + r)*4).  A head's chunks are split as evenly as
+ * possible over n_span spans (one workgroup each); n_span is chosen by the
+ * library from B*H, N, d, chunk and the I/O type so that the workgroups fill
+ * the GPU in one round.  The environment variable LA_SPAN (tokens, a multiple
+ * of chunk) overrides the span length and must not change between this query
+ * and the la_forward call.  Returns 0 for invalid or unsupported arguments.
  */
-size_t la_forward_workspace_bytes(int B, int H, int N, int d, int d_v, int phi, int r, int causal, int chunk);
+size_t la_forward_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int causal,
+                                  int chunk);
 
 /*
  * Prefill: O = causal (or non-causal) linear attention of Q, K, V, evaluated

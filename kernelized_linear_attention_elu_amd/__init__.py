@@ -33,7 +33,7 @@ _lib = None
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _SIGS = {
-    "la_forward_workspace_bytes": (ctypes.c_size_t, [_i] * 9),
+    "la_forward_workspace_bytes": (ctypes.c_size_t, [_i] * 10),
     "la_forward": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
     "la_forward_timed": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp, _vp]),
     "la_decode_step": (_i, [_vp] * 8 + [_i] * 7 + [_vp, _vp]),
@@ -140,8 +140,9 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def workspace_bytes(B, H, N, d, dv, phi="elu1", r=0, causal=True, chunk=64):
-    return int(load_library().la_forward_workspace_bytes(B, H, N, d, dv, PHI[phi], r, int(causal), chunk))
+def workspace_bytes(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64):
+    io_code = LA_BF16 if io == "bf16" else LA_F32
+    return int(load_library().la_forward_workspace_bytes(B, H, N, d, dv, io_code, PHI[phi], r, int(causal), chunk))
 
 
 def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, z0=None,
@@ -180,7 +181,7 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
     if return_state:
         S_out = torch.empty((B, H, r, dv), dtype=torch.float32, device=dev)
         z_out = torch.empty((B, H, r), dtype=torch.float32, device=dev)
-    need = int(lib.la_forward_workspace_bytes(B, H, N, d, dv, PHI[phi], r, int(causal), chunk))
+    need = int(lib.la_forward_workspace_bytes(B, H, N, d, dv, io, PHI[phi], r, int(causal), chunk))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     args = [_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, d, dv, io, PHI[phi], r, _ptr(omega),

@@ -31,23 +31,43 @@ int norm_r(int phi, int d, int r) {
 
 int norm_chunk(int chunk) { return chunk == 0 ? 64 : chunk; }
 
-// Tokens per workgroup: a multiple of the chunk, large enough to amortise the
-// per-span state traffic (r*d_v*4 bytes written, scanned and read back per
-// span) and small enough to give >= 1024 workgroups when the problem allows.
-int choose_span(long long BH, int N, int chunk) {
+// Spans per head.  Both prefill kernels run one workgroup per (head, span)
+// and a span's chunks are contiguous; spans of a head differ by at most one
+// chunk.  The default fills one round of workgroup slots of the output
+// kernel (256 CUs x workgroups per CU at its occupancy for this
+// configuration) so that no CU runs a partial second round, but keeps at
+// least 4 chunks per span so that the per-span state traffic (r*d_v*4 bytes
+// written, scanned and read back) stays small next to the span's data.  The
+// environment variable LA_SPAN (tokens, a multiple of the chunk) overrides
+// the span length.
+constexpr int kCUs = 256;
+
+int output_occupancy(int io, int d, int chunk) {
+  if (d == 64) {
+    if (io == LA_BF16) return chunk <= 16 ? 4 : (chunk <= 64 ? 3 : 1);
+    return chunk <= 16 ? 3 : (chunk == 32 ? 2 : 1);
+  }
+  return 1;
+}
+
+int choose_n_span(long long BH, int N, int chunk, int d, int io) {
+  if (N <= 0) return 0;
+  const long long n_chunks = (static_cast<long long>(N) + chunk - 1) / chunk;
   const char* env = getenv("LA_SPAN");
   if (env && *env) {
     const long v = strtol(env, nullptr, 10);
-    if (v >= chunk && v % chunk == 0 && v <= (1 << 24)) return static_cast<int>(v);
+    if (v >= chunk && v % chunk == 0 && v <= (1 << 24)) return static_cast<int>((N + v - 1) / v);
   }
-  int span = 256;
-  while (span < 2048 && BH * ((static_cast<long long>(N) + 2 * span - 1) / (2 * span)) >= 1024) span *= 2;
-  if (span < chunk) span = chunk;
-  return span;
+  const long long slots = static_cast<long long>(kCUs) * output_occupancy(io, d, chunk);
+  long long n = (slots + BH - 1) / (BH > 0 ? BH : 1);
+  const long long cap = n_chunks / 4 > 0 ? n_chunks / 4 : 1;
+  if (n > cap) n = cap;
+  if (n < 1) n = 1;
+  return static_cast<int>(n);
 }
 
 struct Shape {
-  int B, H, N, d, dv, r, phi, causal, chunk, span, n_span;
+  int B, H, N, d, dv, r, phi, causal, chunk, n_span;
   long long BH;
 };
 
@@ -63,13 +83,15 @@ la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int p
   if (!la::prefill_supported(io, phi, d, d_v, rr, ch)) return LA_ERR_UNSUPPORTED;
   const long long BH = static_cast<long long>(B) * H;
   if (BH > (1LL << 30)) return LA_ERR_SHAPE;
-  // element counts must fit the 64-bit indexing used by the kernels, and the
-  // grid (B*H*n_span workgroups) must fit a 32-bit launch
-  const int span = choose_span(BH, N, ch);
-  const long long n_span = (static_cast<long long>(N) + span - 1) / span;
+  // a head's Q/K/V/O must fit a 32-bit buffer range (the kernels address
+  // each head through a buffer resource), and the grid (B*H*n_span
+  // workgroups) must fit a 32-bit launch
+  const long long row = static_cast<long long>(d > d_v ? d : d_v) * (io == LA_BF16 ? 2 : 4);
+  if (static_cast<long long>(N) * row >= (1LL << 31)) return LA_ERR_SHAPE;
+  const int n_span = choose_n_span(BH, N, ch, d, io);
   if (BH * n_span > 0x7fffffffLL) return LA_ERR_SHAPE;
   sh->B = B; sh->H = H; sh->N = N; sh->d = d; sh->dv = d_v; sh->r = rr; sh->phi = phi;
-  sh->causal = causal; sh->chunk = ch; sh->span = span; sh->n_span = static_cast<int>(n_span); sh->BH = BH;
+  sh->causal = causal; sh->chunk = ch; sh->n_span = n_span; sh->BH = BH;
   return LA_OK;
 }
 
@@ -101,7 +123,7 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
   a.Q = Q; a.K = K; a.V = V; a.O = O;
   a.B = B; a.H = H; a.N = N; a.d = d; a.dv = d_v; a.r = sh.r;
   a.io = io; a.phi = phi; a.omega = omega; a.causal = causal;
-  a.chunk = sh.chunk; a.span = sh.span; a.n_span = sh.n_span;
+  a.chunk = sh.chunk; a.n_span = sh.n_span;
   a.S0 = S0; a.z0 = z0; a.S_out = S_out; a.z_out = z_out;
   a.workspace = workspace; a.stream = stream; a.events = events;
   return hip_status(la::prefill_launch(a));
@@ -111,12 +133,10 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
 
 extern "C" {
 
-size_t la_forward_workspace_bytes(int B, int H, int N, int d, int d_v, int phi, int r, int causal, int chunk) {
+size_t la_forward_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int causal,
+                                  int chunk) {
   Shape sh;
-  // the workspace does not depend on the I/O type; check against bf16 support
-  if (check_forward_shape(B, H, N, d, d_v, LA_BF16, phi, r, causal, chunk, &sh) != LA_OK &&
-      check_forward_shape(B, H, N, d, d_v, LA_F32, phi, r, causal, chunk, &sh) != LA_OK)
-    return 0;
+  if (check_forward_shape(B, H, N, d, d_v, io_dtype, phi, r, causal, chunk, &sh) != LA_OK) return 0;
   return workspace_for(sh);
 }
 

@@ -17,8 +17,7 @@ struct PrefillArgs {
   const float* omega;
   int causal;
   int chunk;
-  int span;    // tokens per workgroup (multiple of chunk)
-  int n_span;  // ceil(N / span)
+  int n_span;  // spans per head (a head's chunks split evenly over them)
   const float* S0;
   const float* z0;
   float* S_out;

@@ -29,10 +29,18 @@
 // gfx950 transposing LDS read ds_read_b64_tr_b16: inside each 16-lane group,
 // lane i reads 4 consecutive elements of row r0 + i/4 starting at column
 // col_start(i%4), and output lane o receives rows r0..r0+3 of column
-// col_start(o/4) + o%4.
+// col_start(o/4) + o%4.  bf16 tiles are unpadded and XOR-swizzled (see
+// Tile) so that none of these access patterns has LDS bank conflicts.
+//
+// Global loads and stores go through buffer resources sized to the head, so
+// tokens beyond N read as zero and their stores are dropped by the hardware:
+// no branches guard memory operations, which lets the compiler wait for a
+// prefetched chunk without draining the later ones.
 //
 // Data layout: Q, K [B*H][N][D], V, O [B*H][N][DV] (I/O type T), workspace
 // fp32 [B*H][n_span+1][R*DV + R] holding S (row-major [R][DV]) then z.
+#include <type_traits>
+
 #include "la_common.h"
 #include "la_prefill.h"
 
@@ -44,10 +52,6 @@ struct Cfg {
   using OP = T;                               // MFMA operand type
   static constexpr int D = D_, R = R_, DV = DV_, C = C_, PHI = PHI_;
   static constexpr int EPL = Vec16<T>::N;     // elements per 16-byte vector
-  static constexpr int PAD = EPL;             // LDS row padding (elements)
-  static constexpr int QS = R + PAD;          // row stride of phi(Q), phi(K)  [C][QS]
-  static constexpr int VS = DV + PAD;         // row stride of V               [C][VS]
-  static constexpr int SS = DV + PAD;         // row stride of the state copy  [R][SS]
   static constexpr int KS = Op<OP>::K;
   static constexpr int PL = Op<OP>::PL;
   static constexpr int RB = C / 16;           // 16-token row blocks per chunk
@@ -71,6 +75,47 @@ struct Cfg {
   static_assert(CT % WPR == 0, "value tiles must split over the waves of a row block");
 };
 
+// ------------------------------------------------------------------ LDS tiles
+
+// Row-major LDS tile of RL-element rows.  fp32 tiles are padded by one
+// 16-byte vector per row.  bf16 tiles are unpadded; the 16-byte unit index of
+// a row is XORed with a hash of the row number (bits r3..r0):
+//   RL = 64  (8 units):  h = 4 r1 + 2 (r2 ^ r3) + r2
+//   RL = 128 (16 units): h = 8 r1 + 4 r0 + 2 (r2 ^ r3) + r2
+// With it, each of the access patterns below touches every LDS bank equally
+// often per hardware pass: 16 consecutive rows at one 16-byte unit (row reads
+// of phi(Q)/phi(K) and 8-byte state writes), rows {b..b+3, b+8..b+11} at 32
+// contiguous bytes (transposing reads over k-steps), rows {b..b+7} at 32
+// contiguous bytes (transposing reads of value blocks), and whole rows
+// (staging writes).  An 8-byte piece never straddles a 16-byte unit, so the
+// transposing reads see contiguous 4-element pieces.
+template <typename OP, int RL>
+struct Tile {
+  static constexpr int kStride = sizeof(OP) == 2 ? RL : RL + 16 / (int)sizeof(OP);
+  static constexpr int elems(int rows) { return rows * kStride; }
+  __device__ static __forceinline__ int hash(int r) {
+    if constexpr (RL == 64) {
+      return (((r >> 1) & 1) << 2) | ((((r >> 2) ^ (r >> 3)) & 1) << 1) | ((r >> 2) & 1);
+    } else {
+      static_assert(RL == 128, "bf16 tiles of 64 or 128 elements per row");
+      return (((r >> 1) & 1) << 3) | ((r & 1) << 2) | ((((r >> 2) ^ (r >> 3)) & 1) << 1) | ((r >> 2) & 1);
+    }
+  }
+  __device__ static __forceinline__ int off(int row, int col) {
+    if constexpr (sizeof(OP) == 2) {
+      return row * RL + ((((col >> 3) ^ hash(row)) << 3) | (col & 7));
+    } else {
+      return row * kStride + col;
+    }
+  }
+};
+
+// Buffer resource over [base, base + bytes): out-of-range loads return zero
+// and out-of-range stores are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
 // ------------------------------------------------------------------ LDS fragments
 
 __device__ __forceinline__ bf16x4 ds_read_tr4(const bf16* p) {
@@ -79,20 +124,22 @@ __device__ __forceinline__ bf16x4 ds_read_tr4(const bf16* p) {
 
 // bf16 operand fragment whose 8 k-slots run down two groups of 4 rows of a
 // row-major LDS tile (slots 0-3: rows ra..ra+3, slots 4-7: rows rb..rb+3) at
-// this lane's column col_base + a_stride*(li/4) + li%4.
-__device__ __forceinline__ bf16x8 tr_frag(const bf16* base, int stride, int ra, int rb, int col_base,
-                                          int a_stride, int li) {
-  const int off = (li >> 2) * stride + col_base + a_stride * (li & 3);
-  const bf16x4 x = ds_read_tr4(base + ra * stride + off);
-  const bf16x4 y = ds_read_tr4(base + rb * stride + off);
+// this lane's column col_base + li (lane li reads row ra + li/4 at column
+// col_base + 4 (li%4)).
+template <int RL>
+__device__ __forceinline__ bf16x8 tr_frag(const bf16* base, int ra, int rb, int col_base, int li) {
+  using TL = Tile<bf16, RL>;
+  const int col = col_base + 4 * (li & 3);
+  const bf16x4 x = ds_read_tr4(base + TL::off(ra + (li >> 2), col));
+  const bf16x4 y = ds_read_tr4(base + TL::off(rb + (li >> 2), col));
   return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // The same fragment with the upper 4 slots zero (a 16-token chunk).
-__device__ __forceinline__ bf16x8 tr_frag_lo(const bf16* base, int stride, int ra, int col_base, int a_stride,
-                                             int li) {
-  const int off = (li >> 2) * stride + col_base + a_stride * (li & 3);
-  const bf16x4 x = ds_read_tr4(base + ra * stride + off);
+template <int RL>
+__device__ __forceinline__ bf16x8 tr_frag_lo(const bf16* base, int ra, int col_base, int li) {
+  using TL = Tile<bf16, RL>;
+  const bf16x4 x = ds_read_tr4(base + TL::off(ra + (li >> 2), col_base + 4 * (li & 3)));
   const bf16x4 z4 = bf16x4{0, 0, 0, 0};
   return __builtin_shufflevector(x, z4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -106,36 +153,37 @@ struct ChunkRegs {
   u32x4 v[CF::LV];
 };
 
-// Global -> registers for the chunk starting at token t0 (zero beyond N).
+// Buffer resources of one head's Q, K (N x D) and V, O (N x DV).
+struct HeadBufs {
+  __amdgpu_buffer_rsrc_t q, k, v, o;
+};
+
+// Global -> registers for the chunk starting at token t0.  Rows beyond N
+// read as zero (buffer bounds); no load is predicated.
 template <class CF, bool WITH_Q>
-__device__ __forceinline__ void load_chunk(ChunkRegs<CF, WITH_Q>& cr, const typename CF::IO* Qh,
-                                           const typename CF::IO* Kh, const typename CF::IO* Vh,
-                                           int t0, int N) {
+__device__ __forceinline__ void load_chunk(ChunkRegs<CF, WITH_Q>& cr, const HeadBufs& hb, int t0) {
   const int tid = threadIdx.x;
+  using T = typename CF::IO;
   constexpr int QV = CF::D / CF::EPL;   // vectors per Q/K row
   constexpr int VVR = CF::DV / CF::EPL; // vectors per V row
+  // (a chunk smaller than one vector per thread, 16 tokens at d = 64, is
+  // the only case that needs the vi guard; it folds away otherwise)
 #pragma unroll
   for (int i = 0; i < CF::LQ; ++i) {
     const int vi = tid + i * kThreads;
-    u32x4 kq = u32x4{0, 0, 0, 0}, qq = u32x4{0, 0, 0, 0};
-    const int t = t0 + vi / QV;
-    const int col = (vi % QV) * CF::EPL;
-    if ((CF::VQ % kThreads == 0 || vi < CF::VQ) && t < N) {
-      kq = *reinterpret_cast<const u32x4*>(Kh + (size_t)t * CF::D + col);
-      if constexpr (WITH_Q) qq = *reinterpret_cast<const u32x4*>(Qh + (size_t)t * CF::D + col);
+    if (CF::VQ % kThreads == 0 || vi < CF::VQ) {
+      const int off = ((t0 + vi / QV) * CF::D + (vi % QV) * CF::EPL) * (int)sizeof(T);
+      cr.k[i] = __builtin_amdgcn_raw_buffer_load_b128(hb.k, off, 0, 0);
+      if constexpr (WITH_Q) cr.q[i] = __builtin_amdgcn_raw_buffer_load_b128(hb.q, off, 0, 0);
     }
-    cr.k[i] = kq;
-    if constexpr (WITH_Q) cr.q[i] = qq;
   }
 #pragma unroll
   for (int i = 0; i < CF::LV; ++i) {
     const int vi = tid + i * kThreads;
-    u32x4 vv = u32x4{0, 0, 0, 0};
-    const int t = t0 + vi / VVR;
-    const int col = (vi % VVR) * CF::EPL;
-    if ((CF::VV % kThreads == 0 || vi < CF::VV) && t < N)
-      vv = *reinterpret_cast<const u32x4*>(Vh + (size_t)t * CF::DV + col);
-    cr.v[i] = vv;
+    if (CF::VV % kThreads == 0 || vi < CF::VV) {
+      const int off = ((t0 + vi / VVR) * CF::DV + (vi % VVR) * CF::EPL) * (int)sizeof(T);
+      cr.v[i] = __builtin_amdgcn_raw_buffer_load_b128(hb.v, off, 0, 0);
+    }
   }
 }
 
@@ -150,45 +198,43 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typ
                                             typename CF::OP* sv, int t0, int N) {
   using T = typename CF::IO;
   using OP = typename CF::OP;
+  using TQ = Tile<OP, CF::R>;
+  using TV = Tile<OP, CF::DV>;
   const int tid = threadIdx.x;
   constexpr int QV = CF::D / CF::EPL;
   constexpr int VVR = CF::DV / CF::EPL;
 #pragma unroll
   for (int i = 0; i < CF::LQ; ++i) {
     const int vi = tid + i * kThreads;
-    if (CF::VQ % kThreads == 0 || vi < CF::VQ) {
-      const int tok = vi / QV;
-      const int col = (vi % QV) * CF::EPL;
-      const bool valid = t0 + tok < N;
-      float f[CF::EPL];
-      if constexpr (WITH_Q) {
-        unpack16<T>(cr.q[i], f);
+    if (!(CF::VQ % kThreads == 0 || vi < CF::VQ)) continue;
+    const int tok = vi / QV;
+    const int col = (vi % QV) * CF::EPL;
+    const bool valid = t0 + tok < N;
+    float f[CF::EPL];
+    if constexpr (WITH_Q) {
+      unpack16<T>(cr.q[i], f);
 #pragma unroll
-        for (int e = 0; e < CF::EPL; ++e) f[e] = phi_pointwise<CF::PHI>(f[e]);
-        *reinterpret_cast<u32x4*>(sq + tok * CF::QS + col) = pack16<OP>(f);
-      }
-      unpack16<T>(cr.k[i], f);
+      for (int e = 0; e < CF::EPL; ++e) f[e] = phi_pointwise<CF::PHI>(f[e]);
+      *reinterpret_cast<u32x4*>(sq + TQ::off(tok, col)) = pack16<OP>(f);
+    }
+    unpack16<T>(cr.k[i], f);
 #pragma unroll
-      for (int e = 0; e < CF::EPL; ++e) f[e] = valid ? phi_pointwise<CF::PHI>(f[e]) : 0.f;
-      *reinterpret_cast<u32x4*>(sk + tok * CF::QS + col) = pack16<OP>(f);
-      if constexpr (sizeof(OP) == 2) {
-        if (sk_lo) {
-          float lo[CF::EPL];
+    for (int e = 0; e < CF::EPL; ++e) f[e] = valid ? phi_pointwise<CF::PHI>(f[e]) : 0.f;
+    *reinterpret_cast<u32x4*>(sk + TQ::off(tok, col)) = pack16<OP>(f);
+    if constexpr (sizeof(OP) == 2) {
+      if (sk_lo) {
+        float lo[CF::EPL];
 #pragma unroll
-          for (int e = 0; e < CF::EPL; ++e) lo[e] = f[e] - round_op<OP>(f[e]);
-          *reinterpret_cast<u32x4*>(sk_lo + tok * CF::QS + col) = pack16<OP>(lo);
-        }
+        for (int e = 0; e < CF::EPL; ++e) lo[e] = f[e] - round_op<OP>(f[e]);
+        *reinterpret_cast<u32x4*>(sk_lo + TQ::off(tok, col)) = pack16<OP>(lo);
       }
     }
   }
 #pragma unroll
   for (int i = 0; i < CF::LV; ++i) {
     const int vi = tid + i * kThreads;
-    if (CF::VV % kThreads == 0 || vi < CF::VV) {
-      const int tok = vi / VVR;
-      const int col = (vi % VVR) * CF::EPL;
-      *reinterpret_cast<u32x4*>(sv + tok * CF::VS + col) = cr.v[i];
-    }
+    if (CF::VV % kThreads == 0 || vi < CF::VV)
+      *reinterpret_cast<u32x4*>(sv + TV::off(vi / VVR, (vi % VVR) * CF::EPL)) = cr.v[i];
   }
 }
 
@@ -205,46 +251,35 @@ __device__ __forceinline__ void state_mfma(f32x4 (&acc)[CF::TPW], f32x4 (&zt)[CF
                                            const typename CF::OP* sk, const typename CF::OP* sk_lo,
                                            const typename CF::OP* sv, int w, int g, int li) {
   using OP = typename CF::OP;
+  constexpr int R = CF::R, DV = CF::DV;
   if constexpr (sizeof(OP) == 2) {
     const bf16 one = static_cast<bf16>(1.0f);
     const bf16x8 ones = bf16x8{one, one, one, one, one, one, one, one};
     constexpr int NK = (CF::C + 31) / 32;  // k-steps of 32 tokens
+    auto kfrag = [&](const OP* base, int ra, int ft) {
+      return CF::C >= 32 ? tr_frag<R>(base, ra, ra + 4, 16 * ft, li) : tr_frag_lo<R>(base, 4 * g, 16 * ft, li);
+    };
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
-      const int ra = ks * 32 + 8 * g, rb = ra + 4;
+      const int ra = ks * 32 + 8 * g;
 #pragma unroll
       for (int i = 0; i < CF::TPW; ++i) {
         const int t = w + kWaves * i;
         const int ct = t % CF::CT, ft = t / CF::CT;
-        bf16x8 a, b;
-        if constexpr (CF::C >= 32) {
-          a = tr_frag(sv, CF::VS, ra, rb, 16 * ct, 4, li);
-          b = tr_frag(sk, CF::QS, ra, rb, 16 * ft, 4, li);
-        } else {  // 16 tokens: slots 0-3 = rows 4g..4g+3, upper half zero
-          a = tr_frag_lo(sv, CF::VS, 4 * g, 16 * ct, 4, li);
-          b = tr_frag_lo(sk, CF::QS, 4 * g, 16 * ft, 4, li);
-        }
-        acc[i] = mfma16(a, b, acc[i]);
-        if (sk_lo) {
-          const bf16x8 blo = CF::C >= 32 ? tr_frag(sk_lo, CF::QS, ra, rb, 16 * ft, 4, li)
-                                         : tr_frag_lo(sk_lo, CF::QS, 4 * g, 16 * ft, 4, li);
-          acc[i] = mfma16(a, blo, acc[i]);
-        }
+        const bf16x8 a = CF::C >= 32 ? tr_frag<DV>(sv, ra, ra + 4, 16 * ct, li) : tr_frag_lo<DV>(sv, 4 * g, 16 * ct, li);
+        acc[i] = mfma16(a, kfrag(sk, ra, ft), acc[i]);
+        if (sk_lo) acc[i] = mfma16(a, kfrag(sk_lo, ra, ft), acc[i]);
       }
 #pragma unroll
       for (int k = 0; k < CF::ZPW; ++k) {
         const int ft = w + kWaves * k;
-        const bf16x8 b = CF::C >= 32 ? tr_frag(sk, CF::QS, ra, rb, 16 * ft, 4, li)
-                                     : tr_frag_lo(sk, CF::QS, 4 * g, 16 * ft, 4, li);
-        zt[k] = mfma16(ones, b, zt[k]);
-        if (sk_lo) {
-          const bf16x8 blo = CF::C >= 32 ? tr_frag(sk_lo, CF::QS, ra, rb, 16 * ft, 4, li)
-                                         : tr_frag_lo(sk_lo, CF::QS, 4 * g, 16 * ft, 4, li);
-          zt[k] = mfma16(ones, blo, zt[k]);
-        }
+        zt[k] = mfma16(ones, kfrag(sk, ra, ft), zt[k]);
+        if (sk_lo) zt[k] = mfma16(ones, kfrag(sk_lo, ra, ft), zt[k]);
       }
     }
   } else {
+    using TQ = Tile<OP, R>;
+    using TV = Tile<OP, DV>;
 #pragma unroll
     for (int ks = 0; ks < CF::C / 4; ++ks) {
       const int row = ks * 4 + g;
@@ -252,12 +287,12 @@ __device__ __forceinline__ void state_mfma(f32x4 (&acc)[CF::TPW], f32x4 (&zt)[CF
       for (int i = 0; i < CF::TPW; ++i) {
         const int t = w + kWaves * i;
         const int ct = t % CF::CT, ft = t / CF::CT;
-        acc[i] = mfma16(sv[row * CF::VS + 16 * ct + li], sk[row * CF::QS + 16 * ft + li], acc[i]);
+        acc[i] = mfma16(sv[TV::off(row, 16 * ct + li)], sk[TQ::off(row, 16 * ft + li)], acc[i]);
       }
 #pragma unroll
       for (int k = 0; k < CF::ZPW; ++k) {
         const int ft = w + kWaves * k;
-        zt[k] = mfma16(1.0f, sk[row * CF::QS + 16 * ft + li], zt[k]);
+        zt[k] = mfma16(1.0f, sk[TQ::off(row, 16 * ft + li)], zt[k]);
       }
     }
   }
@@ -265,42 +300,95 @@ __device__ __forceinline__ void state_mfma(f32x4 (&acc)[CF::TPW], f32x4 (&zt)[CF
 
 // ------------------------------------------------------------------ outputs
 
+// phi(Q) MFMA fragments of this wave's query rows, loaded straight from
+// global memory (no LDS round trip).  k-slot -> feature mapping: bf16 lane
+// group g owns features 32 ks + 8 g .. +7 (one 16-byte vector per k-step);
+// fp32 lane group g owns features 16 g .. 16 g + 15 (k-step ks -> 16 g + ks),
+// so its slots are also contiguous 16-byte vectors.  The same mapping is used
+// for every operand contracted against phi(Q).
+template <class CF>
+struct QRegs {
+  using OP = typename CF::OP;
+  using frag = typename Op<OP>::frag;
+  static constexpr int NV = CF::PL == 8 ? CF::R / 32 : CF::R / 16;  // 16-byte vectors per row block
+  u32x4 raw[CF::RBW][NV];
+  __device__ static __forceinline__ int feature(int ks, int g) { return CF::PL == 8 ? 32 * ks + 8 * g : 16 * g + ks; }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t q, int t0, int w, int g, int li) {
+    using T = typename CF::IO;
+#pragma unroll
+    for (int rbi = 0; rbi < CF::RBW; ++rbi) {
+      const int ib = (CF::RB >= kWaves) ? (w + kWaves * rbi) : (w % CF::RB);
+      const int row = t0 + 16 * ib + li;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int col = CF::PL == 8 ? 32 * v + 8 * g : 16 * g + 4 * v;
+        raw[rbi][v] = __builtin_amdgcn_raw_buffer_load_b128(q, (row * CF::D + col) * (int)sizeof(T), 0, 0);
+      }
+    }
+  }
+  // apply phi in fp32 and round to the operand type
+  __device__ __forceinline__ void to_frags(frag (&qf)[CF::RBW][CF::R / CF::KS]) const {
+    using T = typename CF::IO;
+#pragma unroll
+    for (int rbi = 0; rbi < CF::RBW; ++rbi) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        float f[CF::EPL];
+        unpack16<T>(raw[rbi][v], f);
+        if constexpr (CF::PL == 8) {
+          bf16x8 x;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = to_op<bf16>(phi_pointwise<CF::PHI>(f[e]));
+          qf[rbi][v] = x;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qf[rbi][4 * v + e] = phi_pointwise<CF::PHI>(f[e]);
+        }
+      }
+    }
+  }
+};
+
+// Finished output values of one lane for one chunk (row 16 ib + li, value
+// columns 16 ct + 4 g .. +3 for each of its CTW value tiles), already rounded
+// to the I/O type, kept in registers until they are stored.
+template <class CF>
+struct OutRegs {
+  using vec = typename std::conditional<sizeof(typename CF::IO) == 2, bf16x4, f32x4>::type;
+  vec v[CF::RBW][CF::CTW];
+};
+
 // Output rows of one chunk.  For row block ib (query tokens 16 ib .. +15):
 //  * weights: tiles a[jb] = phi(K_jb) phi(Q_ib)^T for key blocks jb <= ib;
 //    lane (g, li) holds A[i = li][j = 16 jb + 4 g + r]; the diagonal block is
 //    masked to j <= i by selection (never by multiplication, so non-finite
 //    future keys cannot leak);
-//  * numerator O^T = V^T A^T + S^T phi(Q)^T (MFMA), where the accumulator row
-//    m of value tile ct maps to value column (DV/4)(m/4) + 4 ct + m%4, so that
-//    every lane ends with 4*CTW consecutive columns of one row;
+//  * numerator O^T = V^T A^T + S^T phi(Q)^T (MFMA): lane (g, li) ends with
+//    O[i = li][c = 16 ct + 4 g + r];
 //  * denominator = rowsum(A) + phi(q_i).z  (fp32), then one divide per value.
 // The weights and phi(Q) enter both sums exactly as rounded for the MFMA.
 template <class CF, bool CAUSAL>
-__device__ __forceinline__ void chunk_outputs(const typename CF::OP* sq, const typename CF::OP* sk,
-                                              const typename CF::OP* sv, const typename CF::OP* ss,
-                                              const float* sz, typename CF::IO* Oh, int t0, int N, int w,
-                                              int g, int li) {
+__device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&qf)[CF::RBW][CF::R / CF::KS],
+                                              const typename CF::OP* sk, const typename CF::OP* sv,
+                                              const typename CF::OP* ss, const float* sz, OutRegs<CF>& out,
+                                              int w, int g, int li) {
   using OP = typename CF::OP;
-  using T = typename CF::IO;
-  using frag = typename Op<OP>::frag;
-  constexpr int KS = CF::KS, PL = CF::PL, RB = CF::RB, CTW = CF::CTW;
-  constexpr int AST = CF::DV / 4;  // column step between lane quads (permuted value columns)
+  using TQ = Tile<OP, CF::R>;
+  using TV = Tile<OP, CF::DV>;
+  constexpr int KS = CF::KS, PL = CF::PL, RB = CF::RB, CTW = CF::CTW, R = CF::R, DV = CF::DV;
 #pragma unroll
   for (int rbi = 0; rbi < CF::RBW; ++rbi) {
     const int ib = (RB >= kWaves) ? (w + kWaves * rbi) : (w % RB);
     const int ct0 = (RB >= kWaves) ? 0 : (w / RB) * CTW;
-    frag qf[CF::R / KS];
-#pragma unroll
-    for (int ks = 0; ks < CF::R / KS; ++ks) qf[ks] = load_frag(sq + (16 * ib + li) * CF::QS + ks * KS + g * PL);
 
     float den = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < CF::R / KS; ++ks) {
+    for (int ks = 0; ks < R / KS; ++ks) {
       if constexpr (PL == 1) {
-        den += qf[ks] * sz[ks * KS + g];
+        den += qf[rbi][ks] * sz[QRegs<CF>::feature(ks, g)];
       } else {
 #pragma unroll
-        for (int e = 0; e < PL; ++e) den += static_cast<float>(qf[ks][e]) * sz[ks * KS + g * PL + e];
+        for (int e = 0; e < PL; ++e) den += static_cast<float>(qf[rbi][ks][e]) * sz[ks * KS + g * PL + e];
       }
     }
 
@@ -309,55 +397,52 @@ __device__ __forceinline__ void chunk_outputs(const typename CF::OP* sq, const t
     for (int c = 0; c < CTW; ++c) o[c] = zero4();
 
     if constexpr (CAUSAL) {
-      f32x4 a[RB];
+      // key blocks are taken in pairs (one K = 32 MFMA step for bf16); only
+      // the pair's two weight tiles are live at a time
+      auto weights = [&](int jb) {
+        f32x4 t = zero4();
 #pragma unroll
-      for (int jb = 0; jb < RB; ++jb) {
-        a[jb] = zero4();
-        if (jb <= ib) {
-#pragma unroll
-          for (int ks = 0; ks < CF::R / KS; ++ks)
-            a[jb] = mfma16(load_frag(sk + (16 * jb + li) * CF::QS + ks * KS + g * PL), qf[ks], a[jb]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float x = a[jb][r];
-            x = (jb == ib && 4 * g + r > li) ? 0.f : x;
-            x = round_op<OP>(x);
-            a[jb][r] = x;
-            den += x;
+        for (int ks = 0; ks < R / KS; ++ks) {
+          if constexpr (PL == 8) {
+            t = mfma16(load_frag(sk + TQ::off(16 * jb + li, ks * KS + g * PL)), qf[rbi][ks], t);
+          } else {
+            t = mfma16(sk[TQ::off(16 * jb + li, QRegs<CF>::feature(ks, g))], qf[rbi][ks], t);
           }
         }
-      }
 #pragma unroll
-      for (int cti = 0; cti < CTW; ++cti) {
-        const int ct = ct0 + cti;
+        for (int r = 0; r < 4; ++r) {
+          float x = (jb == ib && 4 * g + r > li) ? 0.f : t[r];
+          x = round_op<OP>(x);
+          t[r] = x;
+          den += x;
+        }
+        return t;
+      };
+#pragma unroll
+      for (int jp = 0; jp < (RB + 1) / 2; ++jp) {
+        const int jb0 = 2 * jp, jb1 = 2 * jp + 1;
+        if (jb0 > ib) continue;
+        const f32x4 a0 = weights(jb0);
+        const bool two = jb1 < RB && jb1 <= ib;
+        const f32x4 a1 = two ? weights(jb1) : zero4();
         if constexpr (PL == 8) {
+          const bf16x8 bv = bf16x8{to_op<bf16>(a0[0]), to_op<bf16>(a0[1]), to_op<bf16>(a0[2]), to_op<bf16>(a0[3]),
+                                   to_op<bf16>(a1[0]), to_op<bf16>(a1[1]), to_op<bf16>(a1[2]), to_op<bf16>(a1[3])};
 #pragma unroll
-          for (int jp = 0; jp < (RB + 1) / 2; ++jp) {
-            const int jb0 = 2 * jp, jb1 = 2 * jp + 1;
-            if (jb0 <= ib) {
-              const bf16x4 blo = bf16x4{to_op<bf16>(a[jb0][0]), to_op<bf16>(a[jb0][1]),
-                                        to_op<bf16>(a[jb0][2]), to_op<bf16>(a[jb0][3])};
-              bf16x8 av, bv;
-              if (jb1 < RB && jb1 <= ib) {
-                av = tr_frag(sv, CF::VS, 16 * jb0 + 4 * g, 16 * jb1 + 4 * g, 4 * ct, AST, li);
-                const bf16x4 bhi = bf16x4{to_op<bf16>(a[jb1][0]), to_op<bf16>(a[jb1][1]),
-                                          to_op<bf16>(a[jb1][2]), to_op<bf16>(a[jb1][3])};
-                bv = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
-              } else {
-                av = tr_frag_lo(sv, CF::VS, 16 * jb0 + 4 * g, 4 * ct, AST, li);
-                const bf16x4 z4 = bf16x4{0, 0, 0, 0};
-                bv = __builtin_shufflevector(blo, z4, 0, 1, 2, 3, 4, 5, 6, 7);
-              }
-              o[cti] = mfma16(av, bv, o[cti]);
-            }
+          for (int cti = 0; cti < CTW; ++cti) {
+            const int ct = ct0 + cti;
+            const bf16x8 av = two ? tr_frag<DV>(sv, 16 * jb0 + 4 * g, 16 * jb1 + 4 * g, 16 * ct, li)
+                                  : tr_frag_lo<DV>(sv, 16 * jb0 + 4 * g, 16 * ct, li);
+            o[cti] = mfma16(av, bv, o[cti]);
           }
         } else {
-          const int c = AST * (li >> 2) + 4 * ct + (li & 3);
 #pragma unroll
-          for (int jb = 0; jb < RB; ++jb) {
-            if (jb <= ib) {
+          for (int cti = 0; cti < CTW; ++cti) {
+            const int ct = ct0 + cti;
 #pragma unroll
-              for (int r = 0; r < 4; ++r) o[cti] = mfma16(sv[(16 * jb + 4 * g + r) * CF::VS + c], a[jb][r], o[cti]);
+            for (int r = 0; r < 4; ++r) {
+              o[cti] = mfma16(sv[TV::off(16 * jb0 + 4 * g + r, 16 * ct + li)], a0[r], o[cti]);
+              if (two) o[cti] = mfma16(sv[TV::off(16 * jb1 + 4 * g + r, 16 * ct + li)], a1[r], o[cti]);
             }
           }
         }
@@ -371,32 +456,47 @@ __device__ __forceinline__ void chunk_outputs(const typename CF::OP* sq, const t
       const int ct = ct0 + cti;
       if constexpr (PL == 8) {
 #pragma unroll
-        for (int ks = 0; ks < CF::R / KS; ++ks)
-          o[cti] = mfma16(tr_frag(ss, CF::SS, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, 4 * ct, AST, li), qf[ks], o[cti]);
+        for (int ks = 0; ks < R / KS; ++ks)
+          o[cti] = mfma16(tr_frag<DV>(ss, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, 16 * ct, li), qf[rbi][ks], o[cti]);
       } else {
-        const int c = AST * (li >> 2) + 4 * ct + (li & 3);
 #pragma unroll
-        for (int ks = 0; ks < CF::R / KS; ++ks) o[cti] = mfma16(ss[(ks * 4 + g) * CF::SS + c], qf[ks], o[cti]);
+        for (int ks = 0; ks < R / KS; ++ks)
+          o[cti] = mfma16(ss[TV::off(QRegs<CF>::feature(ks, g), 16 * ct + li)], qf[rbi][ks], o[cti]);
       }
     }
 
-    const int tok = t0 + 16 * ib + li;
-    if (tok < N) {
-      float vals[4 * CTW];
+    const float rden = __builtin_amdgcn_rcpf(den);  // one reciprocal per row (<= 1 ulp)
 #pragma unroll
-      for (int cti = 0; cti < CTW; ++cti)
+    for (int cti = 0; cti < CTW; ++cti) {
+      if constexpr (sizeof(typename CF::IO) == 2) {
+        out.v[rbi][cti] = bf16x4{to_op<bf16>(o[cti][0] * rden), to_op<bf16>(o[cti][1] * rden),
+                                 to_op<bf16>(o[cti][2] * rden), to_op<bf16>(o[cti][3] * rden)};
+      } else {
+        out.v[rbi][cti] = o[cti] * rden;
+      }
+    }
+  }
+}
+
+// Store one chunk's outputs (rows beyond N are dropped by the buffer bounds).
+template <class CF>
+__device__ __forceinline__ void store_outputs(const OutRegs<CF>& out, __amdgpu_buffer_rsrc_t orsrc, int t0,
+                                              int w, int g, int li) {
+  using T = typename CF::IO;
+  constexpr int RB = CF::RB, CTW = CF::CTW;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vals[4 * cti + r] = o[cti][r] / den;
-      T* dst = Oh + (size_t)tok * CF::DV + AST * g + 4 * ct0;
-      constexpr int NV = 4 * CTW;                 // values per lane
-      if constexpr (NV % CF::EPL == 0) {
+  for (int rbi = 0; rbi < CF::RBW; ++rbi) {
+    const int ib = (RB >= kWaves) ? (w + kWaves * rbi) : (w % RB);
+    const int ct0 = (RB >= kWaves) ? 0 : (w / RB) * CTW;
+    const int row = t0 + 16 * ib + li;
 #pragma unroll
-        for (int vv = 0; vv < NV / CF::EPL; ++vv)
-          *reinterpret_cast<u32x4*>(dst + vv * CF::EPL) = pack16<T>(vals + vv * CF::EPL);
-      } else {  // bf16 with 4 values per lane
-        const bf16x4 h = bf16x4{to_op<bf16>(vals[0]), to_op<bf16>(vals[1]), to_op<bf16>(vals[2]),
-                                to_op<bf16>(vals[3])};
-        *reinterpret_cast<bf16x4*>(dst) = h;
+    for (int cti = 0; cti < CTW; ++cti) {
+      const int off = (row * CF::DV + 16 * (ct0 + cti) + 4 * g) * (int)sizeof(T);
+      if constexpr (sizeof(T) == 2) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out.v[rbi][cti]), orsrc, off, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out.v[rbi][cti]), orsrc, off, 0, 0);
       }
     }
   }
@@ -407,11 +507,12 @@ template <class CF>
 __device__ __forceinline__ void publish_state(const f32x4 (&sacc)[CF::TPW], const f32x4 (&zt)[CF::ZPW],
                                               typename CF::OP* ss, float* sz, int w, int g, int li) {
   using OP = typename CF::OP;
+  using TS = Tile<OP, CF::DV>;
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
     const int t = w + kWaves * i;
     const int ct = t % CF::CT, ft = t / CF::CT;
-    OP* dst = ss + (16 * ft + li) * CF::SS + 16 * ct + 4 * g;
+    OP* dst = ss + TS::off(16 * ft + li, 16 * ct + 4 * g);
     if constexpr (sizeof(OP) == 2) {
       *reinterpret_cast<bf16x4*>(dst) = bf16x4{to_op<bf16>(sacc[i][0]), to_op<bf16>(sacc[i][1]),
                                                to_op<bf16>(sacc[i][2]), to_op<bf16>(sacc[i][3])};
@@ -427,39 +528,63 @@ __device__ __forceinline__ void publish_state(const f32x4 (&sacc)[CF::TPW], cons
 
 // ------------------------------------------------------------------ kernels
 
+// LDS of the state kernel: two chunk buffers (staging of chunk c+1 overlaps
+// the MFMA work on chunk c; one barrier per chunk).
 template <class CF>
 struct SmemState {
-  typename CF::OP k[CF::C * CF::QS];
-  typename CF::OP k_lo[sizeof(typename CF::OP) == 2 ? CF::C * CF::QS : 1];
-  typename CF::OP v[CF::C * CF::VS];
+  using OP = typename CF::OP;
+  static constexpr int KE = Tile<OP, CF::R>::elems(CF::C);
+  static constexpr int VE = Tile<OP, CF::DV>::elems(CF::C);
+  OP k[2][KE];
+  OP k_lo[2][sizeof(OP) == 2 ? KE : 1];
+  OP v[2][VE];
 };
 
+// LDS of the output kernel: two chunk buffers of phi(K), V and of the
+// carried state (S as an MFMA operand, z in fp32).
 template <class CF>
 struct SmemOut {
-  typename CF::OP q[CF::C * CF::QS];
-  typename CF::OP k[CF::C * CF::QS];
-  typename CF::OP v[CF::C * CF::VS];
-  typename CF::OP s[CF::R * CF::SS];
-  float z[CF::R];
+  using OP = typename CF::OP;
+  OP k[2][Tile<OP, CF::R>::elems(CF::C)];
+  OP v[2][Tile<OP, CF::DV>::elems(CF::C)];
+  OP s[2][Tile<OP, CF::DV>::elems(CF::R)];
+  float z[2][CF::R];
 };
 
+// First token of span s when a head's ceil(N/C) chunks are split as evenly as
+// possible over n_span spans (span lengths differ by at most one chunk).
+template <class CF>
+__device__ __forceinline__ int span_begin(int s, int n_span, int N) {
+  const long long n_chunks = (N + CF::C - 1) / CF::C;
+  return (int)min((long long)N, CF::C * ((long long)s * n_chunks / n_span));
+}
+
+template <class CF>
+__device__ __forceinline__ HeadBufs head_bufs(const typename CF::IO* Q, const typename CF::IO* K,
+                                              const typename CF::IO* V, typename CF::IO* O, int bh, int N) {
+  using T = typename CF::IO;
+  const size_t qk = (size_t)N * CF::D, vo = (size_t)N * CF::DV;
+  HeadBufs hb;
+  hb.q = make_rsrc(Q ? Q + bh * qk : nullptr, (unsigned)(qk * sizeof(T)));
+  hb.k = make_rsrc(K + bh * qk, (unsigned)(qk * sizeof(T)));
+  hb.v = make_rsrc(V + bh * vo, (unsigned)(vo * sizeof(T)));
+  hb.o = make_rsrc(O ? O + bh * vo : nullptr, (unsigned)(vo * sizeof(T)));
+  return hb;
+}
+
 // Per-span state: dS = phi(K_span)^T V_span, dz = sum phi(K_span) -> ws slot s.
-// Two chunks of loads are kept in flight (register double buffering).
 template <class CF>
 __global__ __launch_bounds__(kThreads) void la_state_kernel(const typename CF::IO* __restrict__ K,
                                                             const typename CF::IO* __restrict__ V,
-                                                            float* __restrict__ ws, int N, int span,
-                                                            int n_span) {
+                                                            float* __restrict__ ws, int N, int n_span) {
   using OP = typename CF::OP;
   __shared__ SmemState<CF> sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
   const int bh = blockIdx.x / n_span;
   const int s = blockIdx.x % n_span;
-  const int t_begin = s * span;
-  const int t_end = min(t_begin + span, N);
-  const typename CF::IO* Kh = K + (size_t)bh * N * CF::D;
-  const typename CF::IO* Vh = V + (size_t)bh * N * CF::DV;
-  OP* klo = sizeof(OP) == 2 ? sm.k_lo : nullptr;
+  const int t_begin = span_begin<CF>(s, n_span, N);
+  const int t_end = span_begin<CF>(s + 1, n_span, N);
+  const HeadBufs hb = head_bufs<CF>(nullptr, K, V, nullptr, bh, N);
 
   f32x4 acc[CF::TPW];
 #pragma unroll
@@ -468,22 +593,16 @@ __global__ __launch_bounds__(kThreads) void la_state_kernel(const typename CF::I
 #pragma unroll
   for (int k = 0; k < CF::ZPW; ++k) zt[k] = zero4();
 
-  ChunkRegs<CF, false> ca, cb;
-  load_chunk<CF, false>(ca, nullptr, Kh, Vh, t_begin, N);
-  if (t_begin + CF::C < t_end) load_chunk<CF, false>(cb, nullptr, Kh, Vh, t_begin + CF::C, N);
-  for (int t0 = t_begin; t0 < t_end; t0 += 2 * CF::C) {
+  // one batch of loads is in flight while the previous chunk is computed
+  ChunkRegs<CF, false> cr;
+  load_chunk<CF, false>(cr, hb, t_begin);
+  int buf = 0;
+  for (int t0 = t_begin; t0 < t_end; t0 += CF::C, buf ^= 1) {
+    OP* lo = sizeof(OP) == 2 ? sm.k_lo[buf] : nullptr;
+    stage_chunk<CF, false>(cr, nullptr, sm.k[buf], lo, sm.v[buf], t0, N);
+    if (t0 + CF::C < t_end) load_chunk<CF, false>(cr, hb, t0 + CF::C);
     __syncthreads();
-    stage_chunk<CF, false>(ca, nullptr, sm.k, klo, sm.v, t0, N);
-    __syncthreads();
-    if (t0 + 2 * CF::C < t_end) load_chunk<CF, false>(ca, nullptr, Kh, Vh, t0 + 2 * CF::C, N);
-    state_mfma<CF>(acc, zt, sm.k, klo, sm.v, w, g, li);
-    const int t1 = t0 + CF::C;
-    if (t1 >= t_end) break;
-    __syncthreads();
-    stage_chunk<CF, false>(cb, nullptr, sm.k, klo, sm.v, t1, N);
-    __syncthreads();
-    if (t1 + 2 * CF::C < t_end) load_chunk<CF, false>(cb, nullptr, Kh, Vh, t1 + 2 * CF::C, N);
-    state_mfma<CF>(acc, zt, sm.k, klo, sm.v, w, g, li);
+    state_mfma<CF>(acc, zt, sm.k[buf], lo, sm.v[buf], w, g, li);
   }
 
   constexpr int E = CF::R * CF::DV + CF::R;
@@ -521,19 +640,18 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
     if (z0) acc = z0[(size_t)bh * R + (e - R * DV)];
   }
   float* p = ws + (size_t)bh * (n_span + 1) * E + e;
-  int s = 0;
-  for (; s + 4 <= n_span; s += 4) {
-    const float x0 = p[(size_t)(s + 0) * E], x1 = p[(size_t)(s + 1) * E];
-    const float x2 = p[(size_t)(s + 2) * E], x3 = p[(size_t)(s + 3) * E];
-    p[(size_t)(s + 0) * E] = acc; acc += x0;
-    p[(size_t)(s + 1) * E] = acc; acc += x1;
-    p[(size_t)(s + 2) * E] = acc; acc += x2;
-    p[(size_t)(s + 3) * E] = acc; acc += x3;
-  }
-  for (; s < n_span; ++s) {
-    const float x = p[(size_t)s * E];
-    p[(size_t)s * E] = acc;
-    acc += x;
+  // all loads of a batch are issued before the dependent adds, so a span
+  // scan costs ceil(n_span / 16) memory round trips instead of n_span
+  constexpr int kBatch = 16;
+  for (int s0 = 0; s0 < n_span; s0 += kBatch) {
+    float x[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) x[j] = s0 + j < n_span ? p[(size_t)(s0 + j) * E] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (s0 + j < n_span) p[(size_t)(s0 + j) * E] = acc;
+      acc += x[j];
+    }
   }
   p[(size_t)n_span * E] = acc;
   if (is_s) {
@@ -544,24 +662,23 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
 }
 
 // Outputs of one span, carrying (S, z) from the span's prefix (causal) or
-// reading the full-sequence sums (non-causal).
+// reading the full-sequence sums (non-causal).  Chunk c+1 is loaded while
+// chunk c is computed (LDS double buffering, one barrier per chunk), and the
+// outputs of chunk c are stored while chunk c+1 is computed, so that the wait
+// for prefetched data never also waits for just-issued stores.
 template <class CF, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void la_output_kernel(const typename CF::IO* __restrict__ Q,
-                                                             const typename CF::IO* __restrict__ K,
-                                                             const typename CF::IO* __restrict__ V,
-                                                             typename CF::IO* __restrict__ O,
-                                                             const float* __restrict__ ws, int N, int span,
-                                                             int n_span) {
+__global__ __launch_bounds__(kThreads, 3) void la_output_kernel(const typename CF::IO* __restrict__ Q,
+                                                                const typename CF::IO* __restrict__ K,
+                                                                const typename CF::IO* __restrict__ V,
+                                                                typename CF::IO* __restrict__ O,
+                                                                const float* __restrict__ ws, int N, int n_span) {
   __shared__ SmemOut<CF> sm;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
   const int bh = blockIdx.x / n_span;
   const int s = blockIdx.x % n_span;
-  const int t_begin = s * span;
-  const int t_end = min(t_begin + span, N);
-  const typename CF::IO* Qh = Q + (size_t)bh * N * CF::D;
-  const typename CF::IO* Kh = K + (size_t)bh * N * CF::D;
-  const typename CF::IO* Vh = V + (size_t)bh * N * CF::DV;
-  typename CF::IO* Oh = O + (size_t)bh * N * CF::DV;
+  const int t_begin = span_begin<CF>(s, n_span, N);
+  const int t_end = span_begin<CF>(s + 1, n_span, N);
+  const HeadBufs hb = head_bufs<CF>(Q, K, V, O, bh, N);
 
   // carried state: this wave's tiles of S (fp32) and its z tiles
   constexpr int E = CF::R * CF::DV + CF::R;
@@ -580,16 +697,30 @@ __global__ __launch_bounds__(kThreads) void la_output_kernel(const typename CF::
     zt[k] = f32x4{zv, zv, zv, zv};
   }
 
-  ChunkRegs<CF, true> cr;
-  load_chunk<CF, true>(cr, Qh, Kh, Vh, t_begin, N);
-  for (int t0 = t_begin; t0 < t_end; t0 += CF::C) {
-    if (CAUSAL || t0 == t_begin) publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
-    stage_chunk<CF, true>(cr, sm.q, sm.k, nullptr, sm.v, t0, N);
+  ChunkRegs<CF, false> cr;
+  QRegs<CF> qr;
+  OutRegs<CF> out;
+  load_chunk<CF, false>(cr, hb, t_begin);
+  qr.load(hb.q, t_begin, w, g, li);
+  int buf = 0;
+  for (int t0 = t_begin; t0 < t_end; t0 += CF::C, buf ^= 1) {
+    const int sb = CAUSAL ? buf : 0;  // non-causal: one state for every chunk
+    if (CAUSAL || t0 == t_begin) publish_state<CF>(sacc, zt, sm.s[sb], sm.z[sb], w, g, li);
+    stage_chunk<CF, false>(cr, nullptr, sm.k[buf], nullptr, sm.v[buf], t0, N);
+    typename QRegs<CF>::frag qf[CF::RBW][CF::R / CF::KS];
+    qr.to_frags(qf);
+    if (t0 != t_begin) store_outputs<CF>(out, hb.o, t0 - CF::C, w, g, li);
+    if (t0 + CF::C < t_end) {
+      load_chunk<CF, false>(cr, hb, t0 + CF::C);
+      qr.load(hb.q, t0 + CF::C, w, g, li);
+    }
     __syncthreads();
-    if (t0 + CF::C < t_end) load_chunk<CF, true>(cr, Qh, Kh, Vh, t0 + CF::C, N);
-    chunk_outputs<CF, CAUSAL>(sm.q, sm.k, sm.v, sm.s, sm.z, Oh, t0, N, w, g, li);
-    if constexpr (CAUSAL) state_mfma<CF>(sacc, zt, sm.k, nullptr, sm.v, w, g, li);
-    __syncthreads();
+    chunk_outputs<CF, CAUSAL>(qf, sm.k[buf], sm.v[buf], sm.s[sb], sm.z[sb], out, w, g, li);
+    if constexpr (CAUSAL) state_mfma<CF>(sacc, zt, sm.k[buf], nullptr, sm.v[buf], w, g, li);
+  }
+  if (t_end > t_begin) {
+    const int last = t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C;
+    store_outputs<CF>(out, hb.o, last, w, g, li);
   }
 }
 
@@ -614,8 +745,7 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
   };
   rec(0);
   if (n_span > 0 && BH > 0) {
-    hipLaunchKernelGGL((la_state_kernel<CF>), dim3(BH * n_span), dim3(kThreads), 0, st, K, V, ws, a.N, a.span,
-                       n_span);
+    hipLaunchKernelGGL((la_state_kernel<CF>), dim3(BH * n_span), dim3(kThreads), 0, st, K, V, ws, a.N, n_span);
   }
   rec(1);
   rec(2);
@@ -628,10 +758,10 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
   if (n_span > 0 && BH > 0) {
     if (a.causal)
       hipLaunchKernelGGL((la_output_kernel<CF, true>), dim3(BH * n_span), dim3(kThreads), 0, st, Q, K, V, O, ws,
-                         a.N, a.span, n_span);
+                         a.N, n_span);
     else
       hipLaunchKernelGGL((la_output_kernel<CF, false>), dim3(BH * n_span), dim3(kThreads), 0, st, Q, K, V, O, ws,
-                         a.N, a.span, n_span);
+                         a.N, n_span);
   }
   rec(5);
   return hipGetLastError();

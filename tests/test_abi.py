@@ -36,19 +36,25 @@ def test_status_strings(lib):
     assert lib.la_version() >= 100
 
 
-def _ws(B, H, N, d=64, dv=64, phi=0, r=0, causal=1, chunk=64):
-    return la.load_library().la_forward_workspace_bytes(B, H, N, d, dv, phi, r, causal, chunk)
+def _ws(B, H, N, d=64, dv=64, phi=0, r=0, causal=1, chunk=64, io=1):
+    return la.load_library().la_forward_workspace_bytes(B, H, N, d, dv, io, phi, r, causal, chunk)
 
 
 def test_workspace_sizes(lib, monkeypatch):
     monkeypatch.delenv("LA_SPAN", raising=False)
     E = 64 * 64 + 64
-    # long prefill B1 H32 N32768: 1024-token spans -> 32 spans per head
-    assert _ws(1, 32, 32768) == 32 * 33 * E * 4
-    # prefill B4 H16 N4096: 256-token spans -> 16 spans per head
-    assert _ws(4, 16, 4096) == 64 * 17 * E * 4
-    # wide heads B2 H16 N65536 d128: 2048-token spans -> 32 spans
-    assert _ws(2, 16, 65536, 128, 128) == 32 * 33 * (128 * 128 + 128) * 4
+    # long prefill B1 H32 N32768 (512 chunks per head): 768 output workgroups
+    # (256 CUs x 3) -> 24 spans per head
+    assert _ws(1, 32, 32768) == 32 * 25 * E * 4
+    # prefill B4 H16 N4096 (64 chunks per head): 12 spans per head
+    assert _ws(4, 16, 4096) == 64 * 13 * E * 4
+    # wide heads B2 H16 N65536 d128 (one workgroup per CU): 8 spans per head
+    assert _ws(2, 16, 65536, 128, 128) == 32 * 9 * (128 * 128 + 128) * 4
+    # short sequences keep at least 4 chunks per span
+    assert _ws(1, 1, 256) == 1 * 2 * E * 4
+    assert _ws(1, 2, 4096) == 2 * 17 * E * 4
+    # fp32 I/O at chunk 64 runs one workgroup per CU: 256 slots
+    assert _ws(1, 8, 65536, io=0) == 8 * 33 * E * 4
     # N = 0 still needs one slot per head for the (initial = final) state
     assert _ws(1, 2, 0) == 2 * 1 * E * 4
     monkeypatch.setenv("LA_SPAN", "64")
