@@ -321,8 +321,9 @@ def main(argv=None):
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (how heads or the sequence "
-              "would shard is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (heads shard across GPUs "
+              "with no exchange; the sequence would shard with one exchange of span states); "
+              "run with --gpus 1", file=sys.stderr)
         return 2
     import torch
     if not torch.cuda.is_available():

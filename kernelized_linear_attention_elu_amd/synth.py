@@ -4,7 +4,7 @@ This module only draws random numbers and rounds them to the I/O format; it
 holds none of the linear-attention arithmetic, so that the HIP path and the
 CPU oracle can consume identical inputs while sharing no computation.
 
-Recipe ("Inputs"):
+Recipe:
 
 * ``numpy.random.default_rng(seed)``; float32 standard normals drawn in the
   order Q, K, V, each over its full [B, H, N, d] (or [B, H, N, d_v]) shape;

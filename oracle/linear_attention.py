@@ -33,7 +33,7 @@ What is computed (plain definitions, written out; no blocking, no fusion):
 * single output rows of the causal / non-causal definition (for sampled parity
   checks at sizes where the full forms are too slow).
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
 normalised read-out; the causal mask keeps j == t; no scaling of q, k before
 ELU+1; alpha = 1; no epsilon in the denominator; S_0 = 0, z_0 = 0 unless a
 state is given; FAVOR+ keeps the 1/sqrt(r) factor and uses x = u / d**(1/4);
