@@ -39,6 +39,7 @@ METRIC = "causal LA prefill tokens/s at N=32k,d=64 bf16; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 KERNEL_NAMES = ("la_state_kernel", "la_scan_kernel", "la_output_kernel")
+FAVOR_KERNEL_NAMES = ("la_state_favor_kernel", "la_scan_kernel", "la_output_favor_kernel")
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "kernelized_linear_attention_elu_amd", "csrc")
 
@@ -80,7 +81,7 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="long",
-                   choices=["long", "prefill", "wide", "decode", "feature", "copy"])
+                   choices=["long", "prefill", "wide", "favor", "decode", "feature", "copy"])
     p.add_argument("--noncausal", action="store_true", help="non-causal prefill")
     p.add_argument("--no-cpu-baseline", action="store_true")
     return p.parse_args(argv)
@@ -99,16 +100,16 @@ def cpu_info():
     return model
 
 
-def time_oracle_prefill(q, k, v, causal, max_heads):
+def time_oracle_prefill(q, k, v, causal, max_heads, phi="elu1", omega=None):
     """fp64 oracle (token recurrence, or the reassociated non-causal form) on
     the first ``max_heads`` heads of batch 0; returns (seconds, heads, cores)."""
     from oracle import linear_attention as ora
     h = min(max_heads, q.shape[1])
     t0, c0 = time.perf_counter(), time.process_time()
     if causal:
-        ora.recurrent_attention(q[:1, :h], k[:1, :h], v[:1, :h])
+        ora.recurrent_attention(q[:1, :h], k[:1, :h], v[:1, :h], phi=phi, omega=omega)
     else:
-        ora.noncausal_attention(q[:1, :h], k[:1, :h], v[:1, :h])
+        ora.noncausal_attention(q[:1, :h], k[:1, :h], v[:1, :h], phi=phi, omega=omega)
     wall = time.perf_counter() - t0
     cpu = time.process_time() - c0
     return wall, h, max(1, round(cpu / max(wall, 1e-9)))
@@ -125,12 +126,16 @@ def bench_prefill(args, torch, la, synth):
         return hostio.upload_bf16_bits(synth.bf16_bits(x), dev)
 
     Q, K, V = to_dev(q), to_dev(k), to_dev(v)
+    omega = synth.draw_omega(w.r, w.d) if w.phi == "favor" else None
+    om_dev = hostio.upload_f32(omega, dev) if omega is not None else None
     O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(la.workspace_bytes(w.B, w.H, w.N, w.d, w.dv, io=w.io, causal=causal, chunk=w.chunk),
+    ws = torch.empty(la.workspace_bytes(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
+                                        chunk=w.chunk),
                      dtype=torch.uint8, device=dev)
 
     def step(events=None):
-        la.forward(Q, K, V, causal=causal, chunk=w.chunk, out=O, workspace=ws, events=events)
+        la.forward(Q, K, V, phi=w.phi, omega=om_dev, causal=causal, chunk=w.chunk, out=O, workspace=ws,
+                   events=events)
 
     for _ in range(args.warmup):
         step()
@@ -159,10 +164,25 @@ def bench_prefill(args, torch, la, synth):
     ms = (t1 - t0) * 1e3 / args.steps
     token_heads = w.B * w.H * w.N
     alg_bytes = token_heads * (2 * w.d + 2 * w.dv) * 2          # read Q, K, V, write O (bf16)
-    alg_flops = token_heads * (4 * w.d * w.dv + (2 * w.chunk * (w.d + w.dv) if causal else 0))
+    # features (FAVOR+: two d x r projections), state build + read-out
+    # (4 r dv), intra-chunk products over full C x C tiles
+    feat_flops = 2 * 2 * w.d * w.r if w.phi == "favor" else 0
+    alg_flops = token_heads * (feat_flops + 4 * w.r * w.dv + (2 * w.chunk * (w.r + w.dv) if causal else 0))
     out_ms = kern_ms[2]
-    achieved = alg_bytes / (out_ms * 1e-3) / 1e9
-    traffic = read_traffic(args.workload + ("" if causal else "_noncausal"), "la_output_kernel")
+    out_kernel = "la_output_favor_kernel" if w.phi == "favor" else "la_output_kernel"
+    traffic = read_traffic(args.workload + ("" if causal else "_noncausal"), out_kernel)
+    if w.phi == "favor":
+        # the output kernel's own work: phi(Q) and phi(K) projections, the
+        # read-out and the state carry (2 r dv each), the intra-chunk products
+        out_flops = token_heads * (2 * 2 * w.d * w.r + 2 * 2 * w.r * w.dv
+                                   + (2 * w.chunk * (w.r + w.dv) if causal else 0))
+        achieved = out_flops / (out_ms * 1e-3) / 1e12
+        roof = {"kernel": out_kernel, "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic}
+    else:
+        achieved = alg_bytes / (out_ms * 1e-3) / 1e9
+        roof = {"kernel": out_kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
     step_gbs = alg_bytes / (ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -179,19 +199,12 @@ def bench_prefill(args, torch, la, synth):
         "data": "synthetic",
         "config": {
             "workload": f"{w.name} prefill B{w.B} H{w.H} N{w.N} d{w.d} dv{w.dv} bf16 I/O, fp32 state, "
-                        f"phi=elu+1, {'causal' if causal else 'non-causal'}, chunk {w.chunk}",
-            "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv, "chunk": w.chunk, "causal": causal,
-            "phi": "elu1", "accumulate": "fp32",
+                        f"phi={'FAVOR+ r=%d' % w.r if w.phi == 'favor' else 'elu+1'}, "
+                        f"{'causal' if causal else 'non-causal'}, chunk {w.chunk}",
+            "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv, "r": w.r, "chunk": w.chunk, "causal": causal,
+            "phi": w.phi, "accumulate": "fp32",
         },
-        "roofline": {
-            "kernel": "la_output_kernel",
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
-        },
+        "roofline": roof,
         "path_roofline": {
             "bound": "hbm",
             "alg_bytes": alg_bytes,
@@ -200,10 +213,11 @@ def bench_prefill(args, torch, la, synth):
             "frac": step_gbs / HBM_PEAK_GBS,
             "mfma_frac": alg_flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         },
-        "kernels_us": {n: t * 1e3 for n, t in zip(KERNEL_NAMES, kern_ms)},
+        "kernels_us": {n: t * 1e3 for n, t in zip(FAVOR_KERNEL_NAMES if w.phi == "favor" else KERNEL_NAMES,
+                                                   kern_ms)},
     }
     if not args.no_cpu_baseline:
-        wall, h, cores = time_oracle_prefill(q, k, v, causal, max_heads=w.H)
+        wall, h, cores = time_oracle_prefill(q, k, v, causal, max_heads=w.H, phi=w.phi, omega=omega)
         # the sample covers h of the B*H heads at full length: scale to the job
         per_job = wall * (w.B * w.H) / h
         res["cpu_baseline"] = {

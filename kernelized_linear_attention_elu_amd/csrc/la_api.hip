@@ -42,7 +42,8 @@ int norm_chunk(int chunk) { return chunk == 0 ? 64 : chunk; }
 // the span length.
 constexpr int kCUs = 256;
 
-int output_occupancy(int io, int d, int chunk) {
+int output_occupancy(int io, int phi, int d, int chunk) {
+  if (phi == LA_PHI_FAVOR) return 1;
   if (d == 64) {
     if (io == LA_BF16) return chunk <= 16 ? 4 : (chunk <= 64 ? 3 : 1);
     return chunk <= 16 ? 3 : (chunk == 32 ? 2 : 1);
@@ -50,7 +51,7 @@ int output_occupancy(int io, int d, int chunk) {
   return 1;
 }
 
-int choose_n_span(long long BH, int N, int chunk, int d, int io) {
+int choose_n_span(long long BH, int N, int chunk, int d, int io, int phi) {
   if (N <= 0) return 0;
   const long long n_chunks = (static_cast<long long>(N) + chunk - 1) / chunk;
   const char* env = getenv("LA_SPAN");
@@ -58,7 +59,7 @@ int choose_n_span(long long BH, int N, int chunk, int d, int io) {
     const long v = strtol(env, nullptr, 10);
     if (v >= chunk && v % chunk == 0 && v <= (1 << 24)) return static_cast<int>((N + v - 1) / v);
   }
-  const long long slots = static_cast<long long>(kCUs) * output_occupancy(io, d, chunk);
+  const long long slots = static_cast<long long>(kCUs) * output_occupancy(io, phi, d, chunk);
   long long n = (slots + BH - 1) / (BH > 0 ? BH : 1);
   const long long cap = n_chunks / 4 > 0 ? n_chunks / 4 : 1;
   if (n > cap) n = cap;
@@ -88,7 +89,7 @@ la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int p
   // workgroups) must fit a 32-bit launch
   const long long row = static_cast<long long>(d > d_v ? d : d_v) * (io == LA_BF16 ? 2 : 4);
   if (static_cast<long long>(N) * row >= (1LL << 31)) return LA_ERR_SHAPE;
-  const int n_span = choose_n_span(BH, N, ch, d, io);
+  const int n_span = choose_n_span(BH, N, ch, d, io, phi);
   if (BH * n_span > 0x7fffffffLL) return LA_ERR_SHAPE;
   sh->B = B; sh->H = H; sh->N = N; sh->d = d; sh->dv = d_v; sh->r = rr; sh->phi = phi;
   sh->causal = causal; sh->chunk = ch; sh->n_span = n_span; sh->BH = BH;

@@ -30,6 +30,14 @@ struct PrefillArgs {
 bool prefill_supported(int io, int phi, int d, int dv, int r, int chunk);
 hipError_t prefill_launch(const PrefillArgs& a);
 
+// FAVOR+ prefill (la_prefill_favor.hip).
+bool favor_prefill_supported(int io, int d, int dv, int r, int chunk);
+hipError_t favor_prefill_launch(const PrefillArgs& a);
+
+// Span scan over a workspace of R x DV states (la_prefill.hip).
+hipError_t scan_launch(float* ws, int BH, int R, int DV, int n_span, const float* S0, const float* z0,
+                       float* S_out, float* z_out, hipStream_t stream);
+
 struct DecodeArgs {
   const float* S;
   const float* z;

@@ -1,0 +1,528 @@
+// Chunked prefill with FAVOR+ positive random features fused in (gfx950).
+//
+// FAVOR+ ("Efficient attention variants", sec. 6): with x = u / d^(1/4),
+//   phi(u)_f = exp(w_f . x - |x|^2 / 2) / sqrt(r),   f = 0 .. r-1,
+// where w_f is row f of the projection omega [r][d].  The method is the
+// chunked causal linear attention of the pointwise feature maps (same span
+// state / span scan / output split, same workspace layout); only the
+// features change: they come from a projection instead of a pointwise map.
+// Supported: bf16 I/O, d = d_v = 64, r = 256, chunk 64.
+//
+// The projection X omega^T is a bf16 MFMA.  X is exact in bf16.  For the span
+// state, omega (fp32) enters as a bf16 hi + lo pair, so the projection is
+// accurate to ~2^-16 relative and the fp32 state that later spans read is
+// accurate; the output kernel rounds its feature tiles to bf16 anyway and
+// uses omega's hi part only.  Each wave owns 64 of the 256 features and
+// keeps its omega fragments in registers for the whole kernel.  The squared norm |u|^2 of
+// every token is summed in fp32 while the chunk is staged.  phi itself is
+// evaluated in fp32 as one exp2; features of tokens beyond N are zero.
+//
+//   la_state_favor_kernel  - per span: dS = phi(K)^T V, dz = sum phi(K).
+//                            The projection tiles come out of the MFMA with
+//                            tokens along the k-slot direction, so they feed
+//                            the state MFMA directly as bf16 hi + lo
+//                            operands (no LDS round trip); dz is summed from
+//                            the fp32 features.
+//   la_output_favor_kernel - per span, chunk by chunk: phi(Q), phi(K) tiles
+//                            -> LDS, then the masked intra-chunk product,
+//                            read-out of the carried state and divide, and
+//                            the state carry (as for the pointwise maps).
+//                            phi(Q) and phi(K) are contracted over features
+//                            in a permuted order: k-slot e of lane group g
+//                            at k-step ks is feature 32 ks + 16 (e / 4) +
+//                            4 g + e % 4, which is how the projection
+//                            accumulators lay them out.  S and z are read in
+//                            the same order.
+#include "la_common.h"
+#include "la_prefill.h"
+#include "la_tiles.h"
+
+namespace la {
+namespace {
+
+constexpr int FD = 64;                    // head dimension d
+constexpr int FR = 256;                   // random features r
+constexpr int FDV = 64;                   // value dimension
+constexpr int FC = 64;                    // chunk
+constexpr int FFT = FR / 16;              // feature tiles
+constexpr int FCT = FDV / 16;             // value tiles
+constexpr int FPW = FFT / kWaves;         // feature tiles owned by a wave in the projections
+constexpr int FE = FR * FDV + FR;         // floats per workspace slot
+constexpr int FVQ = FC * FD / 8;          // 16-byte vectors per raw chunk
+constexpr int FLQ = FVQ / kThreads;       // ... per thread
+static_assert(FVQ % kThreads == 0 && FDV == FD, "raw chunk tiles are 64 x 64 bf16");
+
+using T64 = Tile<bf16, 64>;
+using T256 = Tile<bf16, 256>;
+
+// exp2 argument constants of phi: log2(e) d^(-1/4), log2(e) / (2 sqrt(d)),
+// and log2(sqrt(r)).
+struct FavorConsts {
+  float a1, a2, a3;
+};
+__device__ __forceinline__ FavorConsts favor_consts() {
+  const float log2e = 1.4426950408889634f;
+  return FavorConsts{log2e * 0.35355339059327373f /* 64^(-1/4) */, log2e / 16.0f /* 1 / (2 sqrt(64)) */,
+                     4.0f /* log2(sqrt(256)) */};
+}
+__device__ __forceinline__ float favor_phi(const FavorConsts& c, float proj, float norm2) {
+  return __builtin_amdgcn_exp2f(proj * c.a1 - norm2 * c.a2 - c.a3);
+}
+
+// omega fragments of the 4 feature tiles a wave owns (features 64 w + 16 j +
+// li), for the two 32-wide k-steps over d: lane (g, li) holds
+// omega[f][32 ks + 8 g .. +7] as bf16 hi and lo = round(x - hi).  The same
+// fragment serves as an A operand (features along M) or a B operand
+// (features along N).
+template <bool LO>
+struct OmegaFrags {
+  bf16x8 hi[FPW][2], lo[LO ? FPW : 1][2];
+  __device__ __forceinline__ void load(const float* __restrict__ omega, int w, int g, int li) {
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const float* p = omega + (size_t)(16 * (FPW * w + j) + li) * FD + 32 * ks + 8 * g;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = e < 4 ? a[e] : b[e - 4];
+          const bf16 h = static_cast<bf16>(x);
+          hi[j][ks][e] = h;
+          if constexpr (LO) lo[j][ks][e] = static_cast<bf16>(x - static_cast<float>(h));
+        }
+      }
+    }
+  }
+};
+
+// Raw (unmapped) chunk rows held in registers between load and staging.
+template <int NS>
+struct RawRegs {
+  u32x4 x[NS][FLQ];
+};
+
+// Global -> registers: raw rows of the given streams for the chunk at t0
+// (rows beyond N read as zero through the buffer bounds).
+template <int NS>
+__device__ __forceinline__ void load_raw(RawRegs<NS>& rr, const __amdgpu_buffer_rsrc_t (&src)[NS], int t0) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < FLQ; ++i) {
+    const int vi = tid + i * kThreads;
+    const int off = ((t0 + vi / 8) * FD + (vi % 8) * 8) * 2;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) rr.x[s][i] = __builtin_amdgcn_raw_buffer_load_b128(src[s], off, 0, 0);
+  }
+}
+
+// Registers -> LDS (row-major swizzled 64 x 64 tiles).  For the streams
+// flagged in `norms`, the squared norm of each token row is summed in fp32
+// (8 threads hold one row: a 3-step butterfly) and written to nrm.
+template <int NS>
+__device__ __forceinline__ void stage_raw(const RawRegs<NS>& rr, bf16* const (&dst)[NS], float* const (&nrm)[NS],
+                                          int norms) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < FLQ; ++i) {
+    const int vi = tid + i * kThreads;
+    const int tok = vi / 8, col = (vi % 8) * 8;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      *reinterpret_cast<u32x4*>(dst[s] + T64::off(tok, col)) = rr.x[s][i];
+      if (norms & (1 << s)) {
+        float f[8];
+        unpack16<bf16>(rr.x[s][i], f);
+        float n2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) n2 += f[e] * f[e];
+        n2 += __shfl_xor(n2, 1);
+        n2 += __shfl_xor(n2, 2);
+        n2 += __shfl_xor(n2, 4);
+        if ((tid & 7) == 0) nrm[s][tok] = n2;
+      }
+    }
+  }
+}
+
+// Projection tile of 16 tokens (block tb of a staged raw chunk) against the
+// feature tile j of this wave: acc += X_tb omega_j^T in one of two
+// orientations.  TOKENS_ON_M: lane (g, li) ends with tokens 16 tb + 4 g + r
+// of feature li; otherwise features 4 g + r of token 16 tb + li.
+template <bool TOKENS_ON_M, bool LO>
+__device__ __forceinline__ f32x4 project(const bf16* raw, const OmegaFrags<LO>& om, int j, int tb, int g, int li) {
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const bf16x8 x = load_frag(raw + T64::off(16 * tb + li, 32 * ks + 8 * g));
+    if constexpr (TOKENS_ON_M) {
+      acc = mfma16(x, om.hi[j][ks], acc);
+      if constexpr (LO) acc = mfma16(x, om.lo[j][ks], acc);
+    } else {
+      acc = mfma16(om.hi[j][ks], x, acc);
+      if constexpr (LO) acc = mfma16(om.lo[j][ks], x, acc);
+    }
+  }
+  return acc;
+}
+
+__device__ __forceinline__ int span_begin64(int s, int n_span, int N) {
+  const long long n_chunks = (N + FC - 1) / FC;
+  return (int)min((long long)N, FC * ((long long)s * n_chunks / n_span));
+}
+
+__device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ------------------------------------------------------------------ span state
+
+// dS = phi(K_span)^T V_span, dz = sum phi(K_span) -> workspace slot s.  Wave w
+// owns features 64 w .. 64 w + 63 (tiles j = 0..3) for all value tiles ct:
+// acc[j][ct] lane (g, li) holds S[f = 64 w + 16 j + li][c = 16 ct + 4 g + r].
+__global__ __launch_bounds__(kThreads, 1) void la_state_favor_kernel(const bf16* __restrict__ K,
+                                                                     const bf16* __restrict__ V,
+                                                                     const float* __restrict__ omega,
+                                                                     float* __restrict__ ws, int N, int n_span) {
+  __shared__ bf16 kraw[2][FC * FD];
+  __shared__ bf16 vt[2][FC * FDV];
+  __shared__ float kn[2][FC];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  const int bh = blockIdx.x / n_span;
+  const int s = blockIdx.x % n_span;
+  const int t_begin = span_begin64(s, n_span, N);
+  const int t_end = span_begin64(s + 1, n_span, N);
+  const size_t head = (size_t)N * FD;
+  const __amdgpu_buffer_rsrc_t src[2] = {make_rsrc(K + bh * head, (unsigned)(head * 2)),
+                                         make_rsrc(V + bh * head, (unsigned)(head * 2))};
+  const FavorConsts fc = favor_consts();
+  OmegaFrags<true> om;
+  om.load(omega, w, g, li);
+
+  f32x4 acc[FPW][FCT];
+  float zacc[FPW];
+#pragma unroll
+  for (int j = 0; j < FPW; ++j) {
+    zacc[j] = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < FCT; ++ct) acc[j][ct] = zero4();
+  }
+
+  RawRegs<2> rr;
+  load_raw<2>(rr, src, t_begin);
+  int buf = 0;
+  for (int t0 = t_begin; t0 < t_end; t0 += FC, buf ^= 1) {
+    {
+      bf16* const dst[2] = {kraw[buf], vt[buf]};
+      float* const nrm[2] = {kn[buf], nullptr};
+      stage_raw<2>(rr, dst, nrm, 1);
+    }
+    if (t0 + FC < t_end) load_raw<2>(rr, src, t0 + FC);
+    __syncthreads();
+
+    // V^T fragments (A operands): k-slots 0-3 = tokens 32 kp + 4 g + r,
+    // 4-7 = tokens 32 kp + 16 + 4 g + r, matching the projection tiles of
+    // token blocks 2 kp and 2 kp + 1.
+    bf16x8 va[2][FCT];
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+      for (int ct = 0; ct < FCT; ++ct) va[kp][ct] = tr_frag<64>(vt[buf], 32 * kp + 4 * g, 32 * kp + 16 + 4 * g, 16 * ct, li);
+
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) {
+      bf16x4 ph[4], pl[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const f32x4 p = project<true, true>(kraw[buf], om, j, tb, g, li);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = 16 * tb + 4 * g + r;
+          const float f = t0 + tok < N ? favor_phi(fc, p[r], kn[buf][tok]) : 0.f;
+          const bf16 h = static_cast<bf16>(f);
+          ph[tb][r] = h;
+          pl[tb][r] = static_cast<bf16>(f - static_cast<float>(h));
+          zacc[j] += f;
+        }
+      }
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        const bf16x8 bh8 = cat4(ph[2 * kp], ph[2 * kp + 1]);
+        const bf16x8 bl8 = cat4(pl[2 * kp], pl[2 * kp + 1]);
+#pragma unroll
+        for (int ct = 0; ct < FCT; ++ct) {
+          acc[j][ct] = mfma16(va[kp][ct], bh8, acc[j][ct]);
+          acc[j][ct] = mfma16(va[kp][ct], bl8, acc[j][ct]);
+        }
+      }
+    }
+  }
+
+  float* slot = ws + ((size_t)bh * (n_span + 1) + s) * FE;
+#pragma unroll
+  for (int j = 0; j < FPW; ++j) {
+    const int f = 16 * (FPW * w + j) + li;
+#pragma unroll
+    for (int ct = 0; ct < FCT; ++ct) *reinterpret_cast<f32x4*>(slot + f * FDV + 16 * ct + 4 * g) = acc[j][ct];
+    const float zs = xor_sum16_32(zacc[j]);
+    if (g == 0) slot[FR * FDV + f] = zs;
+  }
+}
+
+// ------------------------------------------------------------------ outputs
+
+struct SmemOutFavor {
+  bf16 qraw[2][FC * FD];
+  bf16 kraw[2][FC * FD];
+  bf16 v[2][FC * FDV];
+  float qn[2][FC];
+  float kn[2][FC];
+  bf16 sq[FC * FR];   // phi(Q) of the chunk, [token][feature]
+  bf16 sk[FC * FR];   // phi(K) of the chunk
+  bf16 ss[FR * FDV];  // carried S, [feature][value]
+  float sz[FR];       // carried z
+};
+
+// Feature of k-slot e of lane group g at k-step ks in the permuted order.
+__device__ __forceinline__ int pfeat(int ks, int g, int e) { return 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3); }
+
+// Operand fragment of one row of a [token][feature] phi tile in the permuted
+// feature order (two 8-byte LDS reads).
+__device__ __forceinline__ bf16x8 prow_frag(const bf16* t, int row, int ks, int g) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(t + T256::off(row, 32 * ks + 4 * g));
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(t + T256::off(row, 32 * ks + 16 + 4 * g));
+  return cat4(a, b);
+}
+
+// Outputs of one span (carried state from the scanned slot when causal, the
+// full-sequence sums otherwise).  Per chunk: stage raw Q, K, V (double
+// buffered) -> barrier -> feature tiles of phi(Q), phi(K) and the carried
+// state -> LDS -> barrier -> outputs of row block w, then the state carry.
+// The carried state tiles follow the pointwise kernels' ownership: tile i of
+// wave w is value tile w, feature tile i.
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void la_output_favor_kernel(const bf16* __restrict__ Q,
+                                                                      const bf16* __restrict__ K,
+                                                                      const bf16* __restrict__ V,
+                                                                      bf16* __restrict__ O,
+                                                                      const float* __restrict__ omega,
+                                                                      const float* __restrict__ ws, int N,
+                                                                      int n_span) {
+  __shared__ SmemOutFavor sm;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  const int bh = blockIdx.x / n_span;
+  const int s = blockIdx.x % n_span;
+  const int t_begin = span_begin64(s, n_span, N);
+  const int t_end = span_begin64(s + 1, n_span, N);
+  const size_t head = (size_t)N * FD;
+  const unsigned hbytes = (unsigned)(head * 2);
+  const __amdgpu_buffer_rsrc_t src[3] = {make_rsrc(Q + bh * head, hbytes), make_rsrc(K + bh * head, hbytes),
+                                         make_rsrc(V + bh * head, hbytes)};
+  const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(O + bh * head, hbytes);
+  const FavorConsts fc = favor_consts();
+  OmegaFrags<false> om;  // phi tiles are rounded to bf16 here: omega hi suffices
+  om.load(omega, w, g, li);
+
+  constexpr int TPW = FFT * FCT / kWaves;  // carried state tiles per wave (16)
+  constexpr int ZPW = FFT / kWaves;        // z tiles per wave (4)
+  const float* pre = ws + ((size_t)bh * (n_span + 1) + (CAUSAL ? s : n_span)) * FE;
+  f32x4 sacc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) sacc[i] = *reinterpret_cast<const f32x4*>(pre + (16 * i + li) * FDV + 16 * w + 4 * g);
+  f32x4 zt[ZPW];
+#pragma unroll
+  for (int k = 0; k < ZPW; ++k) {
+    const float zv = pre[FR * FDV + 16 * (w + kWaves * k) + li];
+    zt[k] = f32x4{zv, zv, zv, zv};
+  }
+  const bf16 one = static_cast<bf16>(1.0f);
+  const bf16x8 ones = bf16x8{one, one, one, one, one, one, one, one};
+
+  RawRegs<3> rr;
+  load_raw<3>(rr, src, t_begin);
+  bf16x4 out[FCT];
+  int buf = 0;
+  for (int t0 = t_begin; t0 < t_end; t0 += FC, buf ^= 1) {
+    {
+      bf16* const dst[3] = {sm.qraw[buf], sm.kraw[buf], sm.v[buf]};
+      float* const nrm[3] = {sm.qn[buf], sm.kn[buf], nullptr};
+      stage_raw<3>(rr, dst, nrm, CAUSAL ? 3 : 1);
+    }
+    if (t0 != t_begin) {
+      const int row = t0 - FC + 16 * w + li;
+#pragma unroll
+      for (int ct = 0; ct < FCT; ++ct) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out[ct]), orsrc,
+                                              (row * FDV + 16 * ct + 4 * g) * 2, 0, 0);
+      }
+    }
+    if (t0 + FC < t_end) load_raw<3>(rr, src, t0 + FC);
+    __syncthreads();
+
+    // feature tiles: wave w computes features 64 w .. +63 of every token;
+    // lane (g, li) gets features 16 ft + 4 g + r of token 16 tb + li
+#pragma unroll
+    for (int j = 0; j < FPW; ++j) {
+      const int ft = FPW * w + j;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const int tok = 16 * tb + li;
+        const f32x4 pq = project<false, false>(sm.qraw[buf], om, j, tb, g, li);
+        const float nq = sm.qn[buf][tok];
+        bf16x4 hq;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hq[r] = static_cast<bf16>(favor_phi(fc, pq[r], nq));
+        *reinterpret_cast<bf16x4*>(sm.sq + T256::off(tok, 16 * ft + 4 * g)) = hq;
+        if constexpr (CAUSAL) {
+          const f32x4 pk = project<false, false>(sm.kraw[buf], om, j, tb, g, li);
+          const float nk = sm.kn[buf][tok];
+          const bool valid = t0 + tok < N;
+          bf16x4 hk;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) hk[r] = static_cast<bf16>(valid ? favor_phi(fc, pk[r], nk) : 0.f);
+          *reinterpret_cast<bf16x4*>(sm.sk + T256::off(tok, 16 * ft + 4 * g)) = hk;
+        }
+      }
+    }
+    if (CAUSAL || t0 == t_begin) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+        *reinterpret_cast<bf16x4*>(sm.ss + T64::off(16 * i + li, 16 * w + 4 * g)) =
+            bf16x4{static_cast<bf16>(sacc[i][0]), static_cast<bf16>(sacc[i][1]), static_cast<bf16>(sacc[i][2]),
+                   static_cast<bf16>(sacc[i][3])};
+      if (g == 0) {
+#pragma unroll
+        for (int k = 0; k < ZPW; ++k) sm.sz[16 * (w + kWaves * k) + li] = zt[k][0];
+      }
+    }
+    __syncthreads();
+
+    // ---- outputs of row block ib = w (query tokens 16 w + li)
+    const int ib = w;
+    bf16x8 qf[FR / 32];
+    float den = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < FR / 32; ++ks) {
+      qf[ks] = prow_frag(sm.sq, 16 * ib + li, ks, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) den += static_cast<float>(qf[ks][e]) * sm.sz[pfeat(ks, g, e)];
+    }
+    f32x4 o[FCT];
+#pragma unroll
+    for (int ct = 0; ct < FCT; ++ct) o[ct] = zero4();
+    if constexpr (CAUSAL) {
+      // weights of key block jb: lane (g, li) holds A[i = li][j = 16 jb + 4 g + r];
+      // the diagonal block is masked to j <= i by selection
+      auto weights = [&](int jb) {
+        f32x4 t = zero4();
+#pragma unroll
+        for (int ks = 0; ks < FR / 32; ++ks) t = mfma16(prow_frag(sm.sk, 16 * jb + li, ks, g), qf[ks], t);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = (jb == ib && 4 * g + r > li) ? 0.f : t[r];
+          x = round_op<bf16>(x);
+          t[r] = x;
+          den += x;
+        }
+        return t;
+      };
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) {
+        const int jb0 = 2 * jp, jb1 = 2 * jp + 1;
+        if (jb0 > ib) continue;
+        const f32x4 a0 = weights(jb0);
+        const bool two = jb1 <= ib;
+        const f32x4 a1 = two ? weights(jb1) : zero4();
+        const bf16x8 bv = bf16x8{static_cast<bf16>(a0[0]), static_cast<bf16>(a0[1]), static_cast<bf16>(a0[2]),
+                                 static_cast<bf16>(a0[3]), static_cast<bf16>(a1[0]), static_cast<bf16>(a1[1]),
+                                 static_cast<bf16>(a1[2]), static_cast<bf16>(a1[3])};
+#pragma unroll
+        for (int ct = 0; ct < FCT; ++ct) {
+          const bf16x8 av = two ? tr_frag<64>(sm.v[buf], 16 * jb0 + 4 * g, 16 * jb1 + 4 * g, 16 * ct, li)
+                                : tr_frag_lo<64>(sm.v[buf], 16 * jb0 + 4 * g, 16 * ct, li);
+          o[ct] = mfma16(av, bv, o[ct]);
+        }
+      }
+    }
+    den = xor_sum16_32(den);
+#pragma unroll
+    for (int ct = 0; ct < FCT; ++ct)
+#pragma unroll
+      for (int ks = 0; ks < FR / 32; ++ks)
+        o[ct] = mfma16(tr_frag<64>(sm.ss, 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * ct, li), qf[ks], o[ct]);
+    const float rden = __builtin_amdgcn_rcpf(den);
+#pragma unroll
+    for (int ct = 0; ct < FCT; ++ct)
+      out[ct] = bf16x4{static_cast<bf16>(o[ct][0] * rden), static_cast<bf16>(o[ct][1] * rden),
+                       static_cast<bf16>(o[ct][2] * rden), static_cast<bf16>(o[ct][3] * rden)};
+
+    // ---- state carry: S += phi(K_c)^T V_c, z += phi(K_c)^T 1 (bf16 features)
+    if constexpr (CAUSAL) {
+#pragma unroll
+      for (int ks = 0; ks < FC / 32; ++ks) {
+        const int ra = 32 * ks + 8 * g;
+        const bf16x8 a = tr_frag<64>(sm.v[buf], ra, ra + 4, 16 * w, li);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) sacc[i] = mfma16(a, tr_frag<256>(sm.sk, ra, ra + 4, 16 * i, li), sacc[i]);
+#pragma unroll
+        for (int k = 0; k < ZPW; ++k)
+          zt[k] = mfma16(ones, tr_frag<256>(sm.sk, ra, ra + 4, 16 * (w + kWaves * k), li), zt[k]);
+      }
+    }
+  }
+  if (t_end > t_begin) {
+    const int last = t_begin + ((t_end - t_begin - 1) / FC) * FC;
+    const int row = last + 16 * w + li;
+#pragma unroll
+    for (int ct = 0; ct < FCT; ++ct) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out[ct]), orsrc,
+                                            (row * FDV + 16 * ct + 4 * g) * 2, 0, 0);
+    }
+  }
+}
+
+}  // namespace
+
+bool favor_prefill_supported(int io, int d, int dv, int r, int chunk) {
+  return io == 1 && d == FD && dv == FDV && r == FR && chunk == FC;
+}
+
+hipError_t favor_prefill_launch(const PrefillArgs& a) {
+  const bf16* Q = static_cast<const bf16*>(a.Q);
+  const bf16* K = static_cast<const bf16*>(a.K);
+  const bf16* V = static_cast<const bf16*>(a.V);
+  bf16* O = static_cast<bf16*>(a.O);
+  float* ws = static_cast<float*>(a.workspace);
+  const int BH = a.B * a.H;
+  hipStream_t st = static_cast<hipStream_t>(a.stream);
+  const int n_span = a.n_span;
+  (void)hipGetLastError();
+  auto rec = [&](int i) {
+    if (a.events && a.events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a.events[i]), st);
+  };
+  rec(0);
+  if (n_span > 0 && BH > 0)
+    hipLaunchKernelGGL(la_state_favor_kernel, dim3(BH * n_span), dim3(kThreads), 0, st, K, V, a.omega, ws, a.N,
+                       n_span);
+  rec(1);
+  rec(2);
+  hipError_t e = scan_launch(ws, BH, FR, FDV, n_span, a.S0, a.z0, a.S_out, a.z_out, st);
+  if (e != hipSuccess) return e;
+  rec(3);
+  rec(4);
+  if (n_span > 0 && BH > 0) {
+    if (a.causal)
+      hipLaunchKernelGGL((la_output_favor_kernel<true>), dim3(BH * n_span), dim3(kThreads), 0, st, Q, K, V, O,
+                         a.omega, ws, a.N, n_span);
+    else
+      hipLaunchKernelGGL((la_output_favor_kernel<false>), dim3(BH * n_span), dim3(kThreads), 0, st, Q, K, V, O,
+                         a.omega, ws, a.N, n_span);
+  }
+  rec(5);
+  return hipGetLastError();
+}
+
+}  // namespace la

@@ -64,6 +64,12 @@ def test_workspace_sizes(lib, monkeypatch):
     # unsupported shapes report 0
     assert _ws(1, 1, 16, 96, 96) == 0
     assert _ws(1, 1, 16, 64, 64, chunk=24) == 0
+    # FAVOR+ (r = 256, one output workgroup per CU): B2 H16 N16384 -> 8 spans
+    EF = 256 * 64 + 256
+    assert _ws(2, 16, 16384, phi=1, r=256) == 32 * 9 * EF * 4
+    assert _ws(1, 1, 100, phi=1, r=128) == 0
+    assert _ws(1, 1, 100, phi=1, r=256, chunk=32) == 0
+    assert _ws(1, 1, 100, phi=1, r=256, io=0) == 0
 
 
 FAKE = ctypes.c_void_p(0x100000)      # aligned, never dereferenced
@@ -86,6 +92,9 @@ def test_forward_argument_errors(lib):
     assert _fwd(lib, phi=9) == 3
     assert _fwd(lib, causal=2) == 3
     assert _fwd(lib, r=32) == 3                         # ELU+1 keeps r = d
+    assert _fwd(lib, phi=1, r=256) == 1                 # FAVOR+ needs omega
+    assert _fwd(lib, phi=1, r=256, omega=MISALIGNED) == 4
+    assert _fwd(lib, phi=1, r=64, omega=FAKE) == 3
     assert _fwd(lib, O=MISALIGNED) == 4                 # LA_ERR_ALIGN
     assert _fwd(lib, ws=None) == 5                      # LA_ERR_WORKSPACE
     assert _fwd(lib, ws_bytes=16) == 5
