@@ -40,6 +40,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 KERNEL_NAMES = ("la_state_kernel", "la_scan_kernel", "la_output_kernel")
 FAVOR_KERNEL_NAMES = ("la_state_favor_kernel", "la_scan_kernel", "la_output_favor_kernel")
+FUSED_KERNEL_NAMES = ("la_fused_reset_kernel", None, "la_fused_kernel")
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "kernelized_linear_attention_elu_amd", "csrc")
 
@@ -169,7 +170,10 @@ def bench_prefill(args, torch, la, synth):
     feat_flops = 2 * 2 * w.d * w.r if w.phi == "favor" else 0
     alg_flops = token_heads * (feat_flops + 4 * w.r * w.dv + (2 * w.chunk * (w.r + w.dv) if causal else 0))
     out_ms = kern_ms[2]
-    out_kernel = "la_output_favor_kernel" if w.phi == "favor" else "la_output_kernel"
+    n_span, single_pass = la.forward_config(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
+                                            chunk=w.chunk)
+    names = (FAVOR_KERNEL_NAMES if w.phi == "favor" else FUSED_KERNEL_NAMES if single_pass else KERNEL_NAMES)
+    out_kernel = names[2]
     traffic = read_traffic(args.workload + ("" if causal else "_noncausal"), out_kernel)
     if w.phi == "favor":
         # the output kernel's own work: phi(Q) and phi(K) projections, the
@@ -213,8 +217,8 @@ def bench_prefill(args, torch, la, synth):
             "frac": step_gbs / HBM_PEAK_GBS,
             "mfma_frac": alg_flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         },
-        "kernels_us": {n: t * 1e3 for n, t in zip(FAVOR_KERNEL_NAMES if w.phi == "favor" else KERNEL_NAMES,
-                                                   kern_ms)},
+        "kernels_us": {n: t * 1e3 for n, t in zip(names, kern_ms) if n},
+        "path": {"single_pass": single_pass, "spans_per_head": n_span},
     }
     if not args.no_cpu_baseline:
         wall, h, cores = time_oracle_prefill(q, k, v, causal, max_heads=w.H, phi=w.phi, omega=omega)

@@ -86,6 +86,21 @@ size_t la_forward_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dt
                                   int chunk);
 
 /*
+ * How la_forward will run this shape (no device work): *n_span receives the
+ * number of spans per head (workgroups per head), *single_pass 1 when the
+ * single-pass kernel serves it (if selected; causal, bf16, d = d_v = 64,
+ * chunk 64, N >= 1:
+ * each workgroup keeps its 256-token span of phi(K), V in LDS and takes the
+ * prefix of the earlier spans from their published sums), 0 for the
+ * three-kernel path (span states, span scan, outputs).  The three-kernel
+ * path is the default; LA_FUSED=1 in the environment selects the single
+ * pass where it applies.  Either pointer may be NULL.  Errors as
+ * la_forward's shape checks.
+ */
+la_status la_forward_config(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int causal, int chunk,
+                            int *n_span, int *single_pass);
+
+/*
  * Prefill: O = causal (or non-causal) linear attention of Q, K, V, evaluated
  * chunkwise ("Efficient attention variants" sec. 8: parallel inside a chunk,
  * state passed between chunks).  The result equals the token recurrence up to
@@ -112,8 +127,10 @@ la_status la_forward(const void *Q, const void *K, const void *V, void *O, int B
 /*
  * la_forward plus timing: events is NULL or an array of 2*LA_FORWARD_KERNELS
  * hipEvent_t created by the caller (see la_event_create); events[2i] is
- * recorded on the stream before kernel i and events[2i+1] after it.  Kernels:
- * 0 = per-span state, 1 = span scan, 2 = output.
+ * recorded on the stream before kernel i and events[2i+1] after it.  Kernels
+ * of the three-kernel path: 0 = per-span state, 1 = span scan, 2 = output;
+ * of the single-pass path: 0 = workspace flag reset, 1 = none (empty
+ * interval), 2 = the single-pass kernel.
  */
 la_status la_forward_timed(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int d,
                            int d_v, int io_dtype, int phi, int r, const float *omega, int causal, int chunk,

@@ -34,6 +34,7 @@ _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _SIGS = {
     "la_forward_workspace_bytes": (ctypes.c_size_t, [_i] * 10),
+    "la_forward_config": (_i, [_i] * 10 + [ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "la_forward": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
     "la_forward_timed": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp, _vp]),
     "la_decode_step": (_i, [_vp] * 8 + [_i] * 7 + [_vp, _vp]),
@@ -143,6 +144,15 @@ def _stream(device):
 def workspace_bytes(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64):
     io_code = LA_BF16 if io == "bf16" else LA_F32
     return int(load_library().la_forward_workspace_bytes(B, H, N, d, dv, io_code, PHI[phi], r, int(causal), chunk))
+
+
+def forward_config(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64):
+    """(n_span, single_pass) that la_forward uses for this shape."""
+    io_code = LA_BF16 if io == "bf16" else LA_F32
+    n, sp = ctypes.c_int(), ctypes.c_int()
+    _check(load_library().la_forward_config(B, H, N, d, dv, io_code, PHI[phi], r, int(causal), chunk,
+                                            ctypes.byref(n), ctypes.byref(sp)), "la_forward_config")
+    return n.value, bool(sp.value)
 
 
 def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, z0=None,

@@ -68,9 +68,31 @@ int choose_n_span(long long BH, int N, int chunk, int d, int io, int phi) {
 }
 
 struct Shape {
-  int B, H, N, d, dv, r, phi, causal, chunk, n_span;
+  int B, H, N, d, dv, r, phi, causal, chunk, n_span, fused;
   long long BH;
 };
+
+// Spans per look-back block of the single-pass kernel (LA_FUSED_GROUP
+// overrides the default; 1 .. 64).
+int fused_group() {
+  const char* env = getenv("LA_FUSED_GROUP");
+  if (env && *env) {
+    const long v = strtol(env, nullptr, 10);
+    if (v >= 1 && v <= 64) return static_cast<int>(v);
+  }
+  return la::kFusedGroup;
+}
+
+// The single-pass kernel can serve causal bf16 prefill at d = d_v = 64,
+// chunk 64, for any N >= 1.  It is selected with LA_FUSED=1 in the
+// environment; the three-kernel path is the default (on MI355X it is the
+// faster of the two at the long-sequence shapes: both are bound by per-chunk
+// work on the CUs, and the single pass adds the exchange of span states).
+bool use_fused(int io, int phi, int d, int d_v, int r, int causal, int chunk, int N) {
+  if (N <= 0 || !la::fused_supported(io, phi, d, d_v, r, chunk, causal)) return false;
+  const char* env = getenv("LA_FUSED");
+  return env && env[0] == '1';
+}
 
 la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int phi, int r, int causal, int chunk,
                               Shape* sh) {
@@ -89,14 +111,16 @@ la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int p
   // workgroups) must fit a 32-bit launch
   const long long row = static_cast<long long>(d > d_v ? d : d_v) * (io == LA_BF16 ? 2 : 4);
   if (static_cast<long long>(N) * row >= (1LL << 31)) return LA_ERR_SHAPE;
-  const int n_span = choose_n_span(BH, N, ch, d, io, phi);
+  const int fused = use_fused(io, phi, d, d_v, rr, causal, ch, N) ? 1 : 0;
+  const int n_span = fused ? (N + la::kFusedSpan - 1) / la::kFusedSpan : choose_n_span(BH, N, ch, d, io, phi);
   if (BH * n_span > 0x7fffffffLL) return LA_ERR_SHAPE;
   sh->B = B; sh->H = H; sh->N = N; sh->d = d; sh->dv = d_v; sh->r = rr; sh->phi = phi;
-  sh->causal = causal; sh->chunk = ch; sh->n_span = n_span; sh->BH = BH;
+  sh->causal = causal; sh->chunk = ch; sh->n_span = n_span; sh->fused = fused; sh->BH = BH;
   return LA_OK;
 }
 
 size_t workspace_for(const Shape& sh) {
+  if (sh.fused) return la::fused_workspace_bytes(sh.BH, sh.n_span, sh.r, sh.dv);
   const size_t E = static_cast<size_t>(sh.r) * sh.dv + sh.r;
   return static_cast<size_t>(sh.BH) * (static_cast<size_t>(sh.n_span) + 1) * E * sizeof(float);
 }
@@ -124,7 +148,7 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
   a.Q = Q; a.K = K; a.V = V; a.O = O;
   a.B = B; a.H = H; a.N = N; a.d = d; a.dv = d_v; a.r = sh.r;
   a.io = io; a.phi = phi; a.omega = omega; a.causal = causal;
-  a.chunk = sh.chunk; a.n_span = sh.n_span;
+  a.chunk = sh.chunk; a.n_span = sh.n_span; a.fused = sh.fused; a.group = fused_group();
   a.S0 = S0; a.z0 = z0; a.S_out = S_out; a.z_out = z_out;
   a.workspace = workspace; a.stream = stream; a.events = events;
   return hip_status(la::prefill_launch(a));
@@ -139,6 +163,16 @@ size_t la_forward_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dt
   Shape sh;
   if (check_forward_shape(B, H, N, d, d_v, io_dtype, phi, r, causal, chunk, &sh) != LA_OK) return 0;
   return workspace_for(sh);
+}
+
+la_status la_forward_config(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int causal, int chunk,
+                            int* n_span, int* single_pass) {
+  Shape sh;
+  const la_status st = check_forward_shape(B, H, N, d, d_v, io_dtype, phi, r, causal, chunk, &sh);
+  if (st != LA_OK) return st;
+  if (n_span) *n_span = sh.n_span;
+  if (single_pass) *single_pass = sh.fused;
+  return LA_OK;
 }
 
 la_status la_forward(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d, int d_v,

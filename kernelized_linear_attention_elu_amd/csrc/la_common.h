@@ -126,6 +126,10 @@ __device__ __forceinline__ float phi_pointwise(float x) {
 
 // ------------------------------------------------------------------ wave helpers
 
+// Index of this wave in its workgroup, as a wave-uniform (scalar) value, so
+// that branches on it are scalar branches rather than exec-mask regions.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ float xor_sum16_32(float v) {
   v += __shfl_xor(v, 16);
   v += __shfl_xor(v, 32);

@@ -25,7 +25,22 @@ struct PrefillArgs {
   void* workspace;
   void* stream;
   void* const* events;  // optional: 6 hipEvent_t recorded around the three kernels
+  int fused;            // single-pass kernel (n_span = ceil(N / kFusedSpan))
+  int group;            // single pass: spans per look-back block
 };
+
+// Single-pass causal prefill (la_prefill.hip): tokens per workgroup and the
+// default number of spans per look-back block.
+constexpr int kFusedSpan = 256;
+constexpr int kFusedGroup = 8;
+bool fused_supported(int io, int phi, int d, int dv, int r, int chunk, int causal);
+// Workspace: 256-byte header, one flag word per (head, span) rounded up to
+// 256 bytes, then two fp32 state slots of r*d_v + r per (head, span).
+inline size_t fused_slots_offset(long long n_flags) { return 256 + (size_t)((n_flags * 4 + 255) / 256) * 256; }
+inline size_t fused_workspace_bytes(long long BH, int n_span, int r, int dv) {
+  const long long n = BH * n_span;
+  return fused_slots_offset(n) + (size_t)n * 2 * ((size_t)r * dv + r) * sizeof(float);
+}
 
 bool prefill_supported(int io, int phi, int d, int dv, int r, int chunk);
 hipError_t prefill_launch(const PrefillArgs& a);

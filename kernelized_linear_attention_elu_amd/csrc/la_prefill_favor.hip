@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_state_favor_kernel(const bf16*
   __shared__ bf16 kraw[2][FC * FD];
   __shared__ bf16 vt[2][FC * FDV];
   __shared__ float kn[2][FC];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
   const int bh = blockIdx.x / n_span;
   const int s = blockIdx.x % n_span;
   const int t_begin = span_begin64(s, n_span, N);
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_output_favor_kernel(const bf16
                                                                       const float* __restrict__ ws, int N,
                                                                       int n_span) {
   __shared__ SmemOutFavor sm;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, li = l & 15;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
   const int bh = blockIdx.x / n_span;
   const int s = blockIdx.x % n_span;
   const int t_begin = span_begin64(s, n_span, N);

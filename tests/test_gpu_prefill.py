@@ -19,6 +19,15 @@ from tests.gpu_util import check_close, f32_dev, rel_rms_error, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(autouse=True, params=["single_pass", "three_kernel"])
+def path(request, monkeypatch):
+    """Every test runs on both prefill paths: the single-pass kernel (causal
+    bf16 d = 64, chunk 64) and the three-kernel path (everything else, and
+    everything when LA_FUSED=0)."""
+    monkeypatch.setenv("LA_FUSED", "1" if request.param == "single_pass" else "0")
+    return request.param
+
+
 @pytest.fixture
 def span(monkeypatch):
     """Set the LA_SPAN override (tokens per workgroup) for one test."""
@@ -272,3 +281,26 @@ def test_split_prefill_equals_one_shot(lib, span, causal):
         # queries after the split see every key: earlier ones through the state
         ref, _, _ = ora.noncausal_attention(q[..., n1:, :], k, v)
         check_close(to_host(b), ref, "bf16", "non-causal with state")
+
+
+def test_single_pass_is_used_and_never_times_out(lib, path):
+    """With the single pass selected, the long causal shape runs on it, and
+    none of its bounded waits for earlier spans expires (the kernel counts
+    expiries in word 1 of its workspace)."""
+    import torch
+    w = synth.WORKLOADS["long"]
+    n_span, single = lib.forward_config(w.B, w.H, w.N, w.d, w.dv)
+    assert single == (path == "single_pass")
+    if not single:
+        return
+    q, k, v = synth.draw_qkv(w.B, 4, 8192, w.d, w.dv, io=w.io)
+    ws = torch.empty(lib.workspace_bytes(w.B, 4, 8192, w.d, w.dv), dtype=torch.uint8, device="cuda")
+    Q, K, V = (to_dev(x, "bf16") for x in (q, k, v))
+    O = lib.forward(Q, K, V, workspace=ws)
+    torch.cuda.synchronize()
+    hdr = ws[:8].cpu().numpy().view(np.uint32)
+    assert hdr[0] == 4 * 8192 // 256          # every workgroup took one ticket
+    assert hdr[1] == 0                        # no expired wait
+    rows = [0, 255, 256, 4095, 8191]
+    for h in range(4):
+        check_close(to_host(O)[0, h, rows], ora.causal_rows(q[0, h], k[0, h], v[0, h], rows), "bf16", f"h{h}")
