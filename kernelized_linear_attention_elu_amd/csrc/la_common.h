@@ -96,15 +96,22 @@ template <> __device__ __forceinline__ float from_op<float>(float x) { return x;
 // Value after a round trip through OP (what an MFMA operand really holds).
 template <typename OP> __device__ __forceinline__ float round_op(float x) { return from_op<OP>(to_op<OP>(x)); }
 
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// Round-to-nearest-even conversions of whole vectors (v_cvt_pk_bf16_f32:
+// two elements per instruction).
+__device__ __forceinline__ bf16x8 cvt_bf16x8(const float* f) {
+  const f32x8 v = {f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]};
+  return __builtin_convertvector(v, bf16x8);
+}
+__device__ __forceinline__ bf16x4 cvt_bf16x4(f32x4 v) { return __builtin_convertvector(v, bf16x4); }
+
 // Pack 16 bytes worth of floats (8 for bf16, 4 for fp32) into one vector.
 template <typename OP>
 __device__ __forceinline__ u32x4 pack16(const float* f);
 template <>
 __device__ __forceinline__ u32x4 pack16<bf16>(const float* f) {
-  bf16x8 v;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = static_cast<bf16>(f[e]);
-  return *reinterpret_cast<u32x4*>(&v);
+  return __builtin_bit_cast(u32x4, cvt_bf16x8(f));
 }
 template <>
 __device__ __forceinline__ u32x4 pack16<float>(const float* f) {

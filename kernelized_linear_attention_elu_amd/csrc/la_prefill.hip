@@ -70,6 +70,10 @@ struct Cfg {
   static constexpr int WPR = RB >= kWaves ? 1 : kWaves / RB;
   static constexpr int RBW = RB >= kWaves ? RB / kWaves : 1;
   static constexpr int CTW = CT / WPR;
+  // carried z as published in LDS: fp32 for fp32 operands; for bf16 three
+  // rows of R bf16 (hi, lo = z - hi, zeros), read as an MFMA operand
+  using ZT = typename std::conditional<sizeof(T) == 2, bf16, float>::type;
+  static constexpr int ZE = sizeof(T) == 2 ? 3 * R : R;
   static_assert(R == D, "pointwise feature maps keep the dimension");
   static_assert(NTILE % kWaves == 0 && FT % kWaves == 0, "state tiles must split evenly over waves");
   static_assert(C % 16 == 0 && C <= 128, "chunk must be 16, 32, 64 or 128");
@@ -130,33 +134,51 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typ
   const int tid = threadIdx.x;
   constexpr int QV = CF::D / CF::EPL;
   constexpr int VVR = CF::DV / CF::EPL;
+  // only a chunk that reaches past N has keys to mask (a uniform branch)
+  auto keys = [&](auto tail) {
 #pragma unroll
-  for (int i = 0; i < CF::LQ; ++i) {
-    const int vi = tid + i * kThreads;
-    if (!(CF::VQ % kThreads == 0 || vi < CF::VQ)) continue;
-    const int tok = vi / QV;
-    const int col = (vi % QV) * CF::EPL;
-    const bool valid = t0 + tok < N;
-    float f[CF::EPL];
-    if constexpr (WITH_Q) {
-      unpack16<T>(cr.q[i], f);
+    for (int i = 0; i < CF::LQ; ++i) {
+      const int vi = tid + i * kThreads;
+      if (!(CF::VQ % kThreads == 0 || vi < CF::VQ)) continue;
+      const int tok = vi / QV;
+      const int col = (vi % QV) * CF::EPL;
+      float f[CF::EPL];
+      if constexpr (WITH_Q) {
+        unpack16<T>(cr.q[i], f);
+#pragma unroll
+        for (int e = 0; e < CF::EPL; ++e) f[e] = phi_pointwise<CF::PHI>(f[e]);
+        *reinterpret_cast<u32x4*>(sq + TQ::off(tok, col)) = pack16<OP>(f);
+      }
+      unpack16<T>(cr.k[i], f);
 #pragma unroll
       for (int e = 0; e < CF::EPL; ++e) f[e] = phi_pointwise<CF::PHI>(f[e]);
-      *reinterpret_cast<u32x4*>(sq + TQ::off(tok, col)) = pack16<OP>(f);
-    }
-    unpack16<T>(cr.k[i], f);
+      u32x4 hi = pack16<OP>(f);
+      u32x4 lo = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (sizeof(OP) == 2) {
+        if (sk_lo) {
+          float h[CF::EPL], r[CF::EPL];
+          unpack16<bf16>(hi, h);
 #pragma unroll
-    for (int e = 0; e < CF::EPL; ++e) f[e] = valid ? phi_pointwise<CF::PHI>(f[e]) : 0.f;
-    *reinterpret_cast<u32x4*>(sk + TQ::off(tok, col)) = pack16<OP>(f);
-    if constexpr (sizeof(OP) == 2) {
-      if (sk_lo) {
-        float lo[CF::EPL];
-#pragma unroll
-        for (int e = 0; e < CF::EPL; ++e) lo[e] = f[e] - round_op<OP>(f[e]);
-        *reinterpret_cast<u32x4*>(sk_lo + TQ::off(tok, col)) = pack16<OP>(lo);
+          for (int e = 0; e < CF::EPL; ++e) r[e] = f[e] - h[e];
+          lo = pack16<OP>(r);
+        }
+      }
+      if constexpr (decltype(tail)::value) {
+        // keys at or beyond N get zero features (selected on the packed words)
+        const bool valid = t0 + tok < N;
+        hi = valid ? hi : u32x4{0u, 0u, 0u, 0u};
+        lo = valid ? lo : u32x4{0u, 0u, 0u, 0u};
+      }
+      *reinterpret_cast<u32x4*>(sk + TQ::off(tok, col)) = hi;
+      if constexpr (sizeof(OP) == 2) {
+        if (sk_lo) *reinterpret_cast<u32x4*>(sk_lo + TQ::off(tok, col)) = lo;
       }
     }
-  }
+  };
+  if (t0 + CF::C > N)
+    keys(std::true_type{});
+  else
+    keys(std::false_type{});
 #pragma unroll
   for (int i = 0; i < CF::LV; ++i) {
     const int vi = tid + i * kThreads;
@@ -263,10 +285,9 @@ struct QRegs {
         float f[CF::EPL];
         unpack16<T>(raw[rbi][v], f);
         if constexpr (CF::PL == 8) {
-          bf16x8 x;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = to_op<bf16>(phi_pointwise<CF::PHI>(f[e]));
-          qf[rbi][v] = x;
+          for (int e = 0; e < 8; ++e) f[e] = phi_pointwise<CF::PHI>(f[e]);
+          qf[rbi][v] = cvt_bf16x8(f);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) qf[rbi][4 * v + e] = phi_pointwise<CF::PHI>(f[e]);
@@ -292,30 +313,40 @@ struct OutRegs {
 //    future keys cannot leak);
 //  * numerator O^T = V^T A^T + S^T phi(Q)^T (MFMA): lane (g, li) ends with
 //    O[i = li][c = 16 ct + 4 g + r];
-//  * denominator = rowsum(A) + phi(q_i).z  (fp32), then one divide per value.
+//  * denominator = rowsum(A) + phi(q_i).z, then one reciprocal per row.
+//    bf16: both terms on the MFMA as well, into one accumulator dacc: an A
+//    operand whose rows 4m hold z_hi and rows 4m+1 z_lo (the published z
+//    rows; other rows read the zero row) against phi(Q), and an A operand
+//    of ones on rows 4m against the weights, so that every lane ends with
+//    dacc[0] = z_hi.phi(q) + rowsum(A) and dacc[1] = z_lo.phi(q).
+//    fp32: in VALU.
 // The weights and phi(Q) enter both sums exactly as rounded for the MFMA.
 template <class CF, bool CAUSAL>
 __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&qf)[CF::RBW][CF::R / CF::KS],
                                               const typename CF::OP* sk, const typename CF::OP* sv,
-                                              const typename CF::OP* ss, const float* sz, OutRegs<CF>& out,
-                                              int w, int g, int li) {
+                                              const typename CF::OP* ss, const typename CF::ZT* sz,
+                                              OutRegs<CF>& out, int w, int g, int li) {
   using OP = typename CF::OP;
   using TQ = Tile<OP, CF::R>;
   using TV = Tile<OP, CF::DV>;
   constexpr int KS = CF::KS, PL = CF::PL, RB = CF::RB, CTW = CF::CTW, R = CF::R, DV = CF::DV;
+  const bf16 one = static_cast<bf16>(1.0f), zero = static_cast<bf16>(0.0f);
+  const bf16 o1 = (li & 3) == 0 ? one : zero;
+  const bf16x8 ones_rows = bf16x8{o1, o1, o1, o1, o1, o1, o1, o1};  // rows 4m of the ones operand
+  const int zrow = min(li & 3, 2);                                    // z_hi, z_lo or zeros
 #pragma unroll
   for (int rbi = 0; rbi < CF::RBW; ++rbi) {
     const int ib = (RB >= kWaves) ? (w + kWaves * rbi) : (w % RB);
     const int ct0 = (RB >= kWaves) ? 0 : (w / RB) * CTW;
 
     float den = 0.f;
+    f32x4 dacc = zero4();
 #pragma unroll
     for (int ks = 0; ks < R / KS; ++ks) {
       if constexpr (PL == 1) {
         den += qf[rbi][ks] * sz[QRegs<CF>::feature(ks, g)];
       } else {
-#pragma unroll
-        for (int e = 0; e < PL; ++e) den += static_cast<float>(qf[rbi][ks][e]) * sz[ks * KS + g * PL + e];
+        dacc = mfma16(load_frag(sz + zrow * R + ks * KS + g * PL), qf[rbi][ks], dacc);
       }
     }
 
@@ -336,12 +367,18 @@ __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&q
             t = mfma16(sk[TQ::off(16 * jb + li, QRegs<CF>::feature(ks, g))], qf[rbi][ks], t);
           }
         }
+        if constexpr (PL == 8) {
+          if (jb == ib) {  // wave-uniform: only the diagonal block is masked
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = (jb == ib && 4 * g + r > li) ? 0.f : t[r];
-          x = round_op<OP>(x);
-          t[r] = x;
-          den += x;
+            for (int r = 0; r < 4; ++r) t[r] = 4 * g + r > li ? 0.f : t[r];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float x = (jb == ib && 4 * g + r > li) ? 0.f : t[r];
+            t[r] = x;
+            den += x;
+          }
         }
         return t;
       };
@@ -353,8 +390,9 @@ __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&q
         const bool two = jb1 < RB && jb1 <= ib;
         const f32x4 a1 = two ? weights(jb1) : zero4();
         if constexpr (PL == 8) {
-          const bf16x8 bv = bf16x8{to_op<bf16>(a0[0]), to_op<bf16>(a0[1]), to_op<bf16>(a0[2]), to_op<bf16>(a0[3]),
-                                   to_op<bf16>(a1[0]), to_op<bf16>(a1[1]), to_op<bf16>(a1[2]), to_op<bf16>(a1[3])};
+          const float w8[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          const bf16x8 bv = cvt_bf16x8(w8);
+          dacc = mfma16(ones_rows, bv, dacc);
 #pragma unroll
           for (int cti = 0; cti < CTW; ++cti) {
             const int ct = ct0 + cti;
@@ -376,7 +414,11 @@ __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&q
       }
     }
 
-    den = xor_sum16_32(den);
+    if constexpr (PL == 8) {
+      den = dacc[0] + dacc[1];
+    } else {
+      den = xor_sum16_32(den);
+    }
 
 #pragma unroll
     for (int cti = 0; cti < CTW; ++cti) {
@@ -396,8 +438,7 @@ __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&q
 #pragma unroll
     for (int cti = 0; cti < CTW; ++cti) {
       if constexpr (sizeof(typename CF::IO) == 2) {
-        out.v[rbi][cti] = bf16x4{to_op<bf16>(o[cti][0] * rden), to_op<bf16>(o[cti][1] * rden),
-                                 to_op<bf16>(o[cti][2] * rden), to_op<bf16>(o[cti][3] * rden)};
+        out.v[rbi][cti] = cvt_bf16x4(o[cti] * rden);
       } else {
         out.v[rbi][cti] = o[cti] * rden;
       }
@@ -429,10 +470,11 @@ __device__ __forceinline__ void store_outputs(const OutRegs<CF>& out, __amdgpu_b
   }
 }
 
-// Carried state -> LDS: S (operand type, row-major [R][DV]) and z (fp32).
+// Carried state -> LDS: S (operand type, row-major [R][DV]) and z (fp32, or
+// for bf16 the hi / lo / zero rows read by chunk_outputs).
 template <class CF>
 __device__ __forceinline__ void publish_state(const f32x4 (&sacc)[CF::TPW], const f32x4 (&zt)[CF::ZPW],
-                                              typename CF::OP* ss, float* sz, int w, int g, int li) {
+                                              typename CF::OP* ss, typename CF::ZT* sz, int w, int g, int li) {
   using OP = typename CF::OP;
   using TS = Tile<OP, CF::DV>;
 #pragma unroll
@@ -441,15 +483,27 @@ __device__ __forceinline__ void publish_state(const f32x4 (&sacc)[CF::TPW], cons
     const int ct = t % CF::CT, ft = t / CF::CT;
     OP* dst = ss + TS::off(16 * ft + li, 16 * ct + 4 * g);
     if constexpr (sizeof(OP) == 2) {
-      *reinterpret_cast<bf16x4*>(dst) = bf16x4{to_op<bf16>(sacc[i][0]), to_op<bf16>(sacc[i][1]),
-                                               to_op<bf16>(sacc[i][2]), to_op<bf16>(sacc[i][3])};
+      *reinterpret_cast<bf16x4*>(dst) = cvt_bf16x4(sacc[i]);
     } else {
       *reinterpret_cast<f32x4*>(dst) = sacc[i];
     }
   }
-  if (g == 0) {
+  if constexpr (sizeof(OP) == 2) {
+    // lane group 0 writes z_hi, group 1 z_lo, group 2 the zero row
+    if (g < 3) {
 #pragma unroll
-    for (int k = 0; k < CF::ZPW; ++k) sz[16 * (w + kWaves * k) + li] = zt[k][0];
+      for (int k = 0; k < CF::ZPW; ++k) {
+        const float z = zt[k][0];
+        const bf16 h = static_cast<bf16>(z);
+        const bf16 v = g == 0 ? h : g == 1 ? static_cast<bf16>(z - static_cast<float>(h)) : static_cast<bf16>(0.f);
+        sz[g * CF::R + 16 * (w + kWaves * k) + li] = v;
+      }
+    }
+  } else {
+    if (g == 0) {
+#pragma unroll
+      for (int k = 0; k < CF::ZPW; ++k) sz[16 * (w + kWaves * k) + li] = zt[k][0];
+    }
   }
 }
 
@@ -475,7 +529,7 @@ struct SmemOut {
   OP k[2][Tile<OP, CF::R>::elems(CF::C)];
   OP v[2][Tile<OP, CF::DV>::elems(CF::C)];
   OP s[2][Tile<OP, CF::DV>::elems(CF::R)];
-  float z[2][CF::R];
+  alignas(16) typename CF::ZT z[2][CF::ZE];
 };
 
 // First token of span s when a head's ceil(N/C) chunks are split as evenly as
@@ -770,7 +824,7 @@ __global__ __launch_bounds__(kThreads, 2) void la_fused_kernel(
   constexpr int E = CF::R * CF::DV + CF::R;
   struct P3 {
     OP s[Tile<OP, CF::DV>::elems(CF::R)];
-    float z[CF::R];
+    alignas(16) typename CF::ZT z[CF::ZE];
   };
   union X {
     OP klo[TE];  // lo words of the chunk being accumulated (step 1)
