@@ -5,11 +5,12 @@
 
 A step is one la_forward call over the whole workload batch (all three
 kernels: per-span state, span scan, chunked output).  Inputs are seeded
-synthetic tensors already resident in HBM when the timed region starts.  The
+synthetic tensors already resident in HBM when the timed region starts;
+three copies of the inputs and outputs are used in turn, so that no step
+finds its data in the 256 MB memory-side cache left by the step before.  The
 timed region is exactly K steps bracketed by device synchronisation; the
-per-kernel durations come from HIP events recorded on the library's stream
-around each kernel during K further steps (events add small gaps between
-kernels, so they are kept out of the headline timing).
+per-kernel durations come from HIP events that the library records on its
+stream around each kernel during those same steps.
 
 One JSON line is printed with the metric, the roofline of the dominant kernel
 (the output kernel) and of the whole step, and the fp64 CPU oracle timed on
@@ -24,6 +25,7 @@ long (default: B1 H32 N32768 d64 bf16 causal), prefill, wide, plus
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -43,6 +45,7 @@ FAVOR_KERNEL_NAMES = ("la_state_favor_kernel", "la_scan_kernel", "la_output_favo
 FUSED_KERNEL_NAMES = ("la_fused_reset_kernel", None, "la_fused_kernel")
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "kernelized_linear_attention_elu_amd", "csrc")
+ROTATE = 3                     # input/output copies used in turn by the prefill bench
 
 
 def source_hash():
@@ -84,6 +87,8 @@ def parse_args(argv=None):
     p.add_argument("--workload", default="long",
                    choices=["long", "prefill", "wide", "favor", "decode", "feature", "copy"])
     p.add_argument("--noncausal", action="store_true", help="non-causal prefill")
+    p.add_argument("--chunk", type=int, default=None,
+                   help="chunk size (default: the workload's, 0 = the library's choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     return p.parse_args(argv)
 
@@ -119,6 +124,8 @@ def time_oracle_prefill(q, k, v, causal, max_heads, phi="elu1", omega=None):
 def bench_prefill(args, torch, la, synth):
     from kernelized_linear_attention_elu_amd import hostio
     w = synth.WORKLOADS[args.workload]
+    if args.chunk is not None:
+        w = dataclasses.replace(w, chunk=args.chunk)
     causal = not args.noncausal
     dev = torch.device("cuda:0")
     q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
@@ -126,33 +133,44 @@ def bench_prefill(args, torch, la, synth):
     def to_dev(x):
         return hostio.upload_bf16_bits(synth.bf16_bits(x), dev)
 
-    Q, K, V = to_dev(q), to_dev(k), to_dev(v)
+    # ROTATE copies of the inputs and outputs, used in turn, so that no step
+    # finds its data in the 256 MB memory-side cache left by the previous
+    # step: every step streams its inputs from HBM
+    Q0, K0, V0 = to_dev(q), to_dev(k), to_dev(v)
+    sets = [(Q0, K0, V0)] + [(Q0.clone(), K0.clone(), V0.clone()) for _ in range(ROTATE - 1)]
+    outs = [torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.bfloat16, device=dev) for _ in range(ROTATE)]
     omega = synth.draw_omega(w.r, w.d) if w.phi == "favor" else None
     om_dev = hostio.upload_f32(omega, dev) if omega is not None else None
-    O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(la.workspace_bytes(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
                                         chunk=w.chunk),
                      dtype=torch.uint8, device=dev)
 
-    def step(events=None):
-        la.forward(Q, K, V, phi=w.phi, omega=om_dev, causal=causal, chunk=w.chunk, out=O, workspace=ws,
-                   events=events)
+    def step(i, events=None):
+        Q, K, V = sets[i % ROTATE]
+        la.forward(Q, K, V, phi=w.phi, omega=om_dev, causal=causal, chunk=w.chunk, out=outs[i % ROTATE],
+                   workspace=ws, events=events)
 
-    for _ in range(args.warmup):
-        step()
-    # timed region: exactly K steps, nothing else on the stream
+    for i in range(args.warmup):
+        step(i)
+    nk = la.LA_FORWARD_KERNELS
+    evs = [[la.event_create() for _ in range(2 * nk)] for _ in range(args.steps)]
+    # timed region: exactly K steps; two HIP events per step, recorded by the
+    # library on its stream around the dominant (output) kernel, give that
+    # kernel's duration live
+    live = [[None] * (2 * nk - 2) + e[2 * nk - 2:] for e in evs]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i, live[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    # per-kernel durations: K more steps with HIP events recorded on the
-    # library's stream around each of its kernels
-    evs = [[la.event_create() for _ in range(2 * la.LA_FORWARD_KERNELS)] for _ in range(args.steps)]
+    out_live_ms = sum(la.event_elapsed_ms(e[2 * nk - 2], e[2 * nk - 1]) for e in evs) / args.steps
+    # breakdown of the whole step: K more steps with events around every
+    # kernel (these add gaps between kernels, so they are kept out of the
+    # timed region)
     torch.cuda.synchronize()
     for i in range(args.steps):
-        step(evs[i])
+        step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     kern_ms = [0.0] * la.LA_FORWARD_KERNELS
     for e in evs:
@@ -169,7 +187,7 @@ def bench_prefill(args, torch, la, synth):
     # (4 r dv), intra-chunk products over full C x C tiles
     feat_flops = 2 * 2 * w.d * w.r if w.phi == "favor" else 0
     alg_flops = token_heads * (feat_flops + 4 * w.r * w.dv + (2 * w.chunk * (w.r + w.dv) if causal else 0))
-    out_ms = kern_ms[2]
+    out_ms = out_live_ms
     n_span, single_pass = la.forward_config(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
                                             chunk=w.chunk)
     names = (FAVOR_KERNEL_NAMES if w.phi == "favor" else FUSED_KERNEL_NAMES if single_pass else KERNEL_NAMES)
@@ -184,7 +202,10 @@ def bench_prefill(args, torch, la, synth):
         roof = {"kernel": out_kernel, "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic}
     else:
-        achieved = alg_bytes / (out_ms * 1e-3) / 1e9
+        # the output kernel reads Q, K, V and writes O (causal); non-causal it
+        # reads Q and writes O only
+        out_bytes = alg_bytes if causal else token_heads * (w.d + w.dv) * 2
+        achieved = out_bytes / (out_ms * 1e-3) / 1e9
         roof = {"kernel": out_kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
     step_gbs = alg_bytes / (ms * 1e-3) / 1e9
@@ -218,6 +239,7 @@ def bench_prefill(args, torch, la, synth):
             "mfma_frac": alg_flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         },
         "kernels_us": {n: t * 1e3 for n, t in zip(names, kern_ms) if n},
+        "dominant_kernel_us_live": out_live_ms * 1e3,
         "path": {"single_pass": single_pass, "spans_per_head": n_span},
     }
     if not args.no_cpu_baseline:

@@ -42,8 +42,10 @@ int norm_chunk(int chunk) { return chunk == 0 ? 64 : chunk; }
 // the span length.
 constexpr int kCUs = 256;
 
-int output_occupancy(int io, int phi, int d, int chunk) {
+int output_occupancy(int io, int phi, int d, int chunk, int causal) {
   if (phi == LA_PHI_FAVOR) return 1;
+  // the non-causal output kernel holds only Q chunks and the shared sums
+  if (!causal && io == LA_BF16 && d == 64) return 6;
   if (d == 64) {
     if (io == LA_BF16) return chunk <= 16 ? 4 : (chunk <= 64 ? 3 : 1);
     return chunk <= 16 ? 3 : (chunk == 32 ? 2 : 1);
@@ -51,7 +53,7 @@ int output_occupancy(int io, int phi, int d, int chunk) {
   return 1;
 }
 
-int choose_n_span(long long BH, int N, int chunk, int d, int io, int phi) {
+int choose_n_span(long long BH, int N, int chunk, int d, int io, int phi, int causal) {
   if (N <= 0) return 0;
   const long long n_chunks = (static_cast<long long>(N) + chunk - 1) / chunk;
   const char* env = getenv("LA_SPAN");
@@ -59,7 +61,7 @@ int choose_n_span(long long BH, int N, int chunk, int d, int io, int phi) {
     const long v = strtol(env, nullptr, 10);
     if (v >= chunk && v % chunk == 0 && v <= (1 << 24)) return static_cast<int>((N + v - 1) / v);
   }
-  const long long slots = static_cast<long long>(kCUs) * output_occupancy(io, phi, d, chunk);
+  const long long slots = static_cast<long long>(kCUs) * output_occupancy(io, phi, d, chunk, causal);
   long long n = (slots + BH - 1) / (BH > 0 ? BH : 1);
   const long long cap = n_chunks / 4 > 0 ? n_chunks / 4 : 1;
   if (n > cap) n = cap;
@@ -112,7 +114,7 @@ la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int p
   const long long row = static_cast<long long>(d > d_v ? d : d_v) * (io == LA_BF16 ? 2 : 4);
   if (static_cast<long long>(N) * row >= (1LL << 31)) return LA_ERR_SHAPE;
   const int fused = use_fused(io, phi, d, d_v, rr, causal, ch, N) ? 1 : 0;
-  const int n_span = fused ? (N + la::kFusedSpan - 1) / la::kFusedSpan : choose_n_span(BH, N, ch, d, io, phi);
+  const int n_span = fused ? (N + la::kFusedSpan - 1) / la::kFusedSpan : choose_n_span(BH, N, ch, d, io, phi, causal);
   if (BH * n_span > 0x7fffffffLL) return LA_ERR_SHAPE;
   sh->B = B; sh->H = H; sh->N = N; sh->d = d; sh->dv = d_v; sh->r = rr; sh->phi = phi;
   sh->causal = causal; sh->chunk = ch; sh->n_span = n_span; sh->fused = fused; sh->BH = BH;

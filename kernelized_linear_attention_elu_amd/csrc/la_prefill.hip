@@ -249,52 +249,102 @@ __device__ __forceinline__ void state_mfma(f32x4 (&acc)[CF::TPW], f32x4 (&zt)[CF
 
 // ------------------------------------------------------------------ outputs
 
-// phi(Q) MFMA fragments of this wave's query rows, loaded straight from
-// global memory (no LDS round trip).  k-slot -> feature mapping: bf16 lane
-// group g owns features 32 ks + 8 g .. +7 (one 16-byte vector per k-step);
-// fp32 lane group g owns features 16 g .. 16 g + 15 (k-step ks -> 16 g + ks),
-// so its slots are also contiguous 16-byte vectors.  The same mapping is used
-// for every operand contracted against phi(Q).
-template <class CF>
+// phi(Q) MFMA fragments of this wave's query rows.  k-slot -> feature
+// mapping: bf16 lane group g owns features 32 ks + 8 g .. +7 (one 16-byte
+// vector per k-step); fp32 lane group g owns features 16 g .. 16 g + 15
+// (k-step ks -> 16 g + ks).  The same mapping is used for every operand
+// contracted against phi(Q).
+//
+// bf16 with one wave per row block (kRows): the wave's rows are loaded as
+// whole 128/256-byte rows (consecutive lanes read consecutive 16 bytes, so
+// every load instruction covers whole cache lines), written to the wave's
+// own LDS scratch and read back in fragment layout.  A fragment-layout
+// global load would touch 16 half lines per instruction, which streams
+// about a third slower.  Otherwise the fragments are loaded from global
+// memory directly.
+template <class CF, bool ROWS = true>
 struct QRegs {
   using OP = typename CF::OP;
   using frag = typename Op<OP>::frag;
-  static constexpr int NV = CF::PL == 8 ? CF::R / 32 : CF::R / 16;  // 16-byte vectors per row block
+  static constexpr bool kRows = ROWS && CF::PL == 8 && CF::WPR == 1;
+  static constexpr int NV = CF::PL == 8 ? CF::R / 32 : CF::R / 16;  // 16-byte vectors per lane per row block
+  static constexpr int UPR = CF::D / 8;                              // 16-byte units per bf16 row
   u32x4 raw[CF::RBW][NV];
   __device__ static __forceinline__ int feature(int ks, int g) { return CF::PL == 8 ? 32 * ks + 8 * g : 16 * g + ks; }
+  __device__ static __forceinline__ int row_block(int rbi, int w) {
+    return (CF::RB >= kWaves) ? (w + kWaves * rbi) : (w % CF::RB);
+  }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t q, int t0, int w, int g, int li) {
     using T = typename CF::IO;
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int rbi = 0; rbi < CF::RBW; ++rbi) {
-      const int ib = (CF::RB >= kWaves) ? (w + kWaves * rbi) : (w % CF::RB);
-      const int row = t0 + 16 * ib + li;
+      const int ib = row_block(rbi, w);
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const int col = CF::PL == 8 ? 32 * v + 8 * g : 16 * g + 4 * v;
+        int row, col;
+        if constexpr (kRows) {
+          const int qi = v * 64 + lane;
+          row = t0 + 16 * ib + qi / UPR;
+          col = 8 * (qi % UPR);
+        } else {
+          row = t0 + 16 * ib + li;
+          col = CF::PL == 8 ? 32 * v + 8 * g : 16 * g + 4 * v;
+        }
         raw[rbi][v] = __builtin_amdgcn_raw_buffer_load_b128(q, (row * CF::D + col) * (int)sizeof(T), 0, 0);
       }
     }
   }
-  // apply phi in fp32 and round to the operand type
-  __device__ __forceinline__ void to_frags(frag (&qf)[CF::RBW][CF::R / CF::KS]) const {
+  // apply phi in fp32 and round to the operand type (scr: this wave's LDS
+  // scratch of RBW x 16 rows, used when kRows)
+  __device__ __forceinline__ void to_frags(frag (&qf)[CF::RBW][CF::R / CF::KS], OP* scr, int g, int li) const {
     using T = typename CF::IO;
+    if constexpr (kRows) {
+      using TS = Tile<OP, CF::D>;
+      const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int rbi = 0; rbi < CF::RBW; ++rbi) {
+      for (int rbi = 0; rbi < CF::RBW; ++rbi)
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        float f[CF::EPL];
-        unpack16<T>(raw[rbi][v], f);
-        if constexpr (CF::PL == 8) {
+        for (int v = 0; v < NV; ++v) {
+          const int qi = v * 64 + lane;
+          *reinterpret_cast<u32x4*>(scr + TS::off(16 * rbi + qi / UPR, 8 * (qi % UPR))) = raw[rbi][v];
+        }
+#pragma unroll
+      for (int rbi = 0; rbi < CF::RBW; ++rbi)
+#pragma unroll
+        for (int ks = 0; ks < NV; ++ks) {
+          float f[8];
+          unpack16<bf16>(*reinterpret_cast<const u32x4*>(scr + TS::off(16 * rbi + li, 32 * ks + 8 * g)), f);
 #pragma unroll
           for (int e = 0; e < 8; ++e) f[e] = phi_pointwise<CF::PHI>(f[e]);
-          qf[rbi][v] = cvt_bf16x8(f);
-        } else {
+          qf[rbi][ks] = cvt_bf16x8(f);
+        }
+    } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) qf[rbi][4 * v + e] = phi_pointwise<CF::PHI>(f[e]);
+      for (int rbi = 0; rbi < CF::RBW; ++rbi) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          float f[CF::EPL];
+          unpack16<T>(raw[rbi][v], f);
+          if constexpr (CF::PL == 8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = phi_pointwise<CF::PHI>(f[e]);
+            qf[rbi][v] = cvt_bf16x8(f);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qf[rbi][4 * v + e] = phi_pointwise<CF::PHI>(f[e]);
+          }
         }
       }
     }
   }
+};
+
+// Per-wave LDS scratch of the output kernels (bf16 row staging of Q and O).
+template <class CF>
+struct Scratch {
+  static constexpr int PER_WAVE = QRegs<CF>::kRows ? CF::RBW * 16 * (CF::D > CF::DV ? CF::D : CF::DV) : 8;
+  static constexpr int ELEMS = kWaves * PER_WAVE;
 };
 
 // Finished output values of one lane for one chunk (row 16 ib + li, value
@@ -447,24 +497,53 @@ __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&q
 }
 
 // Store one chunk's outputs (rows beyond N are dropped by the buffer bounds).
-template <class CF>
+// Store one chunk's outputs (rows beyond N are dropped by the buffer bounds).
+// With drop set, every store gets an offset past the buffer and the hardware
+// discards it: the store instructions are still issued, so that the memory
+// counter waits of the surrounding loop stay exact.  bf16 with one wave per
+// row block: the wave's finished rows go through its LDS scratch and leave as
+// whole rows, 16 bytes per lane (consecutive lanes, consecutive addresses).
+template <class CF, bool ROWS = true>
 __device__ __forceinline__ void store_outputs(const OutRegs<CF>& out, __amdgpu_buffer_rsrc_t orsrc, int t0,
-                                              int w, int g, int li) {
+                                              int w, int g, int li, bool drop, typename CF::OP* scr) {
   using T = typename CF::IO;
   constexpr int RB = CF::RB, CTW = CF::CTW;
+  if constexpr (QRegs<CF, ROWS>::kRows) {
+    using TS = Tile<typename CF::OP, CF::DV>;
+    constexpr int UPR = CF::DV / 8;               // 16-byte units per output row
+    constexpr int NVO = 16 * UPR / 64;            // row units per lane per row block
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int rbi = 0; rbi < CF::RBW; ++rbi) {
-    const int ib = (RB >= kWaves) ? (w + kWaves * rbi) : (w % RB);
-    const int ct0 = (RB >= kWaves) ? 0 : (w / RB) * CTW;
-    const int row = t0 + 16 * ib + li;
+    for (int rbi = 0; rbi < CF::RBW; ++rbi)
 #pragma unroll
-    for (int cti = 0; cti < CTW; ++cti) {
-      const int off = (row * CF::DV + 16 * (ct0 + cti) + 4 * g) * (int)sizeof(T);
-      if constexpr (sizeof(T) == 2) {
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out.v[rbi][cti]), orsrc, off, 0, 0);
-      } else {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out.v[rbi][cti]), orsrc, off, 0, 0);
+      for (int cti = 0; cti < CTW; ++cti)
+        *reinterpret_cast<bf16x4*>(scr + TS::off(16 * rbi + li, 16 * cti + 4 * g)) = out.v[rbi][cti];
+#pragma unroll
+    for (int rbi = 0; rbi < CF::RBW; ++rbi) {
+      const int ib = QRegs<CF>::row_block(rbi, w);
+#pragma unroll
+      for (int v = 0; v < NVO; ++v) {
+        const int qi = v * 64 + lane;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(scr + TS::off(16 * rbi + qi / UPR, 8 * (qi % UPR)));
+        const int off = drop ? 0x7ffffff0 : ((t0 + 16 * ib + qi / UPR) * CF::DV + 8 * (qi % UPR)) * 2;
+        __builtin_amdgcn_raw_buffer_store_b128(x, orsrc, off, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int rbi = 0; rbi < CF::RBW; ++rbi) {
+      const int ib = QRegs<CF>::row_block(rbi, w);
+      const int ct0 = (RB >= kWaves) ? 0 : (w / RB) * CTW;
+      const int row = t0 + 16 * ib + li;
+#pragma unroll
+      for (int cti = 0; cti < CTW; ++cti) {
+        const int off = drop ? 0x7ffffff0 : (row * CF::DV + 16 * (ct0 + cti) + 4 * g) * (int)sizeof(T);
+        if constexpr (sizeof(T) == 2) {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out.v[rbi][cti]), orsrc, off, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out.v[rbi][cti]), orsrc, off, 0, 0);
+        }
       }
     }
   }
@@ -521,15 +600,25 @@ struct SmemState {
   OP v[2][VE];
 };
 
-// LDS of the output kernel: two chunk buffers of phi(K), V and of the
-// carried state (S as an MFMA operand, z in fp32).
+// LDS of the output kernel: two chunk buffers of phi(K) and V, the carried
+// state (S as an MFMA operand, z), and the per-wave row scratch.
 template <class CF>
 struct SmemOut {
   using OP = typename CF::OP;
   OP k[2][Tile<OP, CF::R>::elems(CF::C)];
   OP v[2][Tile<OP, CF::DV>::elems(CF::C)];
-  OP s[2][Tile<OP, CF::DV>::elems(CF::R)];
-  alignas(16) typename CF::ZT z[2][CF::ZE];
+  OP s[Tile<OP, CF::DV>::elems(CF::R)];
+  alignas(16) typename CF::ZT z[CF::ZE];
+  alignas(16) OP scr[Scratch<CF>::ELEMS];
+};
+
+// LDS of the non-causal output kernel: the full-sequence sums only.
+template <class CF>
+struct SmemOutNC {
+  using OP = typename CF::OP;
+  OP s[Tile<OP, CF::DV>::elems(CF::R)];
+  alignas(16) typename CF::ZT z[CF::ZE];
+  alignas(16) OP scr[Scratch<CF>::ELEMS];
 };
 
 // First token of span s when a head's ceil(N/C) chunks are split as evenly as
@@ -574,16 +663,32 @@ __global__ __launch_bounds__(kThreads) void la_state_kernel(const typename CF::I
 #pragma unroll
   for (int k = 0; k < CF::ZPW; ++k) zt[k] = zero4();
 
-  // one batch of loads is in flight while the previous chunk is computed
-  ChunkRegs<CF, false> cr;
-  load_chunk<CF, false>(cr, hb, t_begin);
+  // two chunks of loads in flight: chunk c+2 is requested as soon as chunk
+  // c has been staged (LDS double buffering, one barrier per chunk).  Every
+  // load is issued unconditionally (past the span's last chunk it re-reads
+  // that chunk, from L2), so that no loop path differs in the number of
+  // memory operations and the counter waits stay exact.
+  const int last = t_end > t_begin ? t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C : t_begin;
+  ChunkRegs<CF, false> ca, cb;
+  load_chunk<CF, false>(ca, hb, t_begin);
+  load_chunk<CF, false>(cb, hb, min(t_begin + CF::C, last));
   int buf = 0;
-  for (int t0 = t_begin; t0 < t_end; t0 += CF::C, buf ^= 1) {
+  for (int t0 = t_begin; t0 < t_end; t0 += 2 * CF::C) {
     OP* lo = sizeof(OP) == 2 ? sm.k_lo[buf] : nullptr;
-    stage_chunk<CF, false>(cr, nullptr, sm.k[buf], lo, sm.v[buf], t0, N);
-    if (t0 + CF::C < t_end) load_chunk<CF, false>(cr, hb, t0 + CF::C);
+    stage_chunk<CF, false>(ca, nullptr, sm.k[buf], lo, sm.v[buf], t0, N);
+    load_chunk<CF, false>(ca, hb, min(t0 + 2 * CF::C, last));
     __syncthreads();
     state_mfma<CF>(acc, zt, sm.k[buf], lo, sm.v[buf], w, g, li);
+    buf ^= 1;
+    const bool second = t0 + CF::C < t_end;  // workgroup-uniform
+    lo = sizeof(OP) == 2 ? sm.k_lo[buf] : nullptr;
+    if (second) stage_chunk<CF, false>(cb, nullptr, sm.k[buf], lo, sm.v[buf], t0 + CF::C, N);
+    load_chunk<CF, false>(cb, hb, min(t0 + 3 * CF::C, last));
+    if (second) {
+      __syncthreads();
+      state_mfma<CF>(acc, zt, sm.k[buf], lo, sm.v[buf], w, g, li);
+      buf ^= 1;
+    }
   }
 
   constexpr int E = CF::R * CF::DV + CF::R;
@@ -643,17 +748,17 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
 }
 
 // Outputs of one span, carrying (S, z) from the span's prefix (causal) or
-// reading the full-sequence sums (non-causal).  Chunk c+1 is loaded while
-// chunk c is computed (LDS double buffering, one barrier per chunk), and the
-// outputs of chunk c are stored while chunk c+1 is computed, so that the wait
-// for prefetched data never also waits for just-issued stores.
+// reading the full-sequence sums (non-causal: only Q is read).  Causal: chunk
+// c+1 is loaded while chunk c is computed (LDS double buffering of phi(K) and
+// V; the carried state is single-buffered, hence a second barrier per
+// chunk), and chunk c's outputs are stored before the state update.
 template <class CF, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 3) void la_output_kernel(const typename CF::IO* __restrict__ Q,
                                                                 const typename CF::IO* __restrict__ K,
                                                                 const typename CF::IO* __restrict__ V,
                                                                 typename CF::IO* __restrict__ O,
                                                                 const float* __restrict__ ws, int N, int n_span) {
-  __shared__ SmemOut<CF> sm;
+  __shared__ typename std::conditional<CAUSAL, SmemOut<CF>, SmemOutNC<CF>>::type sm;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
   // heads in the reverse order of la_state_kernel: the keys and values
   // that kernel read last are the likeliest to still sit in the
@@ -681,30 +786,52 @@ __global__ __launch_bounds__(kThreads, 3) void la_output_kernel(const typename C
     zt[k] = f32x4{zv, zv, zv, zv};
   }
 
-  ChunkRegs<CF, false> cr;
-  QRegs<CF> qr;
   OutRegs<CF> out;
-  load_chunk<CF, false>(cr, hb, t_begin);
-  qr.load(hb.q, t_begin, w, g, li);
-  int buf = 0;
-  for (int t0 = t_begin; t0 < t_end; t0 += CF::C, buf ^= 1) {
-    const int sb = CAUSAL ? buf : 0;  // non-causal: one state for every chunk
-    if (CAUSAL || t0 == t_begin) publish_state<CF>(sacc, zt, sm.s[sb], sm.z[sb], w, g, li);
-    stage_chunk<CF, false>(cr, nullptr, sm.k[buf], nullptr, sm.v[buf], t0, N);
-    typename QRegs<CF>::frag qf[CF::RBW][CF::R / CF::KS];
-    qr.to_frags(qf);
-    if (t0 != t_begin) store_outputs<CF>(out, hb.o, t0 - CF::C, w, g, li);
-    if (t0 + CF::C < t_end) {
-      load_chunk<CF, false>(cr, hb, t0 + CF::C);
-      qr.load(hb.q, t0 + CF::C, w, g, li);
-    }
+  if constexpr (!CAUSAL) {
+    // non-causal: the full-sequence sums serve every row; only Q is read,
+    // two chunks ahead, and each chunk's outputs are stored right away
+    publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
     __syncthreads();
-    chunk_outputs<CF, CAUSAL>(qf, sm.k[buf], sm.v[buf], sm.s[sb], sm.z[sb], out, w, g, li);
-    if constexpr (CAUSAL) state_mfma<CF>(sacc, zt, sm.k[buf], nullptr, sm.v[buf], w, g, li);
-  }
-  if (t_end > t_begin) {
-    const int last = t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C;
-    store_outputs<CF>(out, hb.o, last, w, g, li);
+    QRegs<CF> qa, qb;
+    qa.load(hb.q, t_begin, w, g, li);
+    qb.load(hb.q, t_begin + CF::C, w, g, li);  // beyond N: zeros, never stored
+    typename CF::OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
+    auto step = [&](QRegs<CF>& q, int t0) {
+      typename QRegs<CF>::frag qf[CF::RBW][CF::R / CF::KS];
+      q.to_frags(qf, scr, g, li);
+      if (t0 + 2 * CF::C < t_end) q.load(hb.q, t0 + 2 * CF::C, w, g, li);
+      chunk_outputs<CF, false>(qf, nullptr, nullptr, sm.s, sm.z, out, w, g, li);
+      store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
+    };
+    for (int t0 = t_begin; t0 < t_end; t0 += 2 * CF::C) {
+      step(qa, t0);
+      if (t0 + CF::C < t_end) step(qb, t0 + CF::C);
+    }
+  } else {
+    // every memory operation is issued on every iteration (loads past the
+    // span re-read its last chunk from L2; the first iteration's store of
+    // "the previous chunk" is dropped), so the counter waits stay exact
+    const int last = t_end > t_begin ? t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C : t_begin;
+    ChunkRegs<CF, false> cr;
+    QRegs<CF> qr;
+    load_chunk<CF, false>(cr, hb, t_begin);
+    qr.load(hb.q, t_begin, w, g, li);
+    int buf = 0;
+    typename CF::OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
+    for (int t0 = t_begin; t0 < t_end; t0 += CF::C, buf ^= 1) {
+      __syncthreads();  // every wave is done with the previous chunk's S, z
+      publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
+      stage_chunk<CF, false>(cr, nullptr, sm.k[buf], nullptr, sm.v[buf], t0, N);
+      typename QRegs<CF>::frag qf[CF::RBW][CF::R / CF::KS];
+      qr.to_frags(qf, scr, g, li);
+      const int tn = min(t0 + CF::C, last);
+      load_chunk<CF, false>(cr, hb, tn);
+      qr.load(hb.q, tn, w, g, li);
+      __syncthreads();
+      chunk_outputs<CF, true>(qf, sm.k[buf], sm.v[buf], sm.s, sm.z, out, w, g, li);
+      store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
+      state_mfma<CF>(sacc, zt, sm.k[buf], nullptr, sm.v[buf], w, g, li);
+    }
   }
 }
 
@@ -849,7 +976,7 @@ __global__ __launch_bounds__(kThreads, 2) void la_fused_kernel(
 
   // ---- 1. all loads of the span, then the span's own sums
   ChunkRegs<CF, false> cr[NC];
-  QRegs<CF> qr[NC];
+  QRegs<CF, false> qr[NC];  // fragments loaded directly (no LDS room for row staging)
 #pragma unroll
   for (int c = 0; c < NC; ++c) load_chunk<CF, false>(cr[c], hb, t_begin + c * C);
 #pragma unroll
@@ -931,9 +1058,9 @@ __global__ __launch_bounds__(kThreads, 2) void la_fused_kernel(
       publish_state<CF>(sacc, zc, sx.p.s, sx.p.z, w, g, li);
       __syncthreads();
       typename QRegs<CF>::frag qf[CF::RBW][CF::R / CF::KS];
-      qr[c].to_frags(qf);
+      qr[c].to_frags(qf, nullptr, g, li);
       chunk_outputs<CF, true>(qf, sk + c * TE, sv + c * TV, sx.p.s, sx.p.z, out, w, g, li);
-      store_outputs<CF>(out, hb.o, t_begin + c * C, w, g, li);
+      store_outputs<CF, false>(out, hb.o, t_begin + c * C, w, g, li, false, nullptr);
       if (c + 1 < nck) {
         state_mfma<CF>(sacc, zc, sk + c * TE, nullptr, sv + c * TV, w, g, li);
         __syncthreads();
