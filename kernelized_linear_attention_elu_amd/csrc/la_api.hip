@@ -47,10 +47,10 @@ int output_occupancy(int io, int phi, int d, int chunk, int causal) {
   // the non-causal output kernel holds only Q chunks and the shared sums
   if (!causal && io == LA_BF16 && d == 64) return 6;
   if (d == 64) {
-    if (io == LA_BF16) return chunk <= 16 ? 4 : (chunk <= 64 ? 3 : 1);
-    return chunk <= 16 ? 3 : (chunk == 32 ? 2 : 1);
+    if (io == LA_BF16) return chunk <= 32 ? 4 : (chunk == 64 ? 3 : 1);
+    return chunk <= 32 ? 4 : 3;
   }
-  return 1;
+  return 1;  // d = 128: one workgroup of eight waves per CU
 }
 
 int choose_n_span(long long BH, int N, int chunk, int d, int io, int phi, int causal) {

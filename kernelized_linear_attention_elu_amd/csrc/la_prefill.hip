@@ -47,11 +47,15 @@
 
 namespace la {
 
-template <typename T, int D_, int R_, int DV_, int C_, int PHI_>
+template <typename T, int D_, int R_, int DV_, int C_, int PHI_, int NW_ = kWaves>
 struct Cfg {
   using IO = T;
   using OP = T;                               // MFMA operand type
   static constexpr int D = D_, R = R_, DV = DV_, C = C_, PHI = PHI_;
+  static constexpr int NW = NW_;              // waves per workgroup
+  static constexpr int NT = 64 * NW_;         // threads per workgroup
+  // workgroups per CU the output kernel's registers are sized for
+  static constexpr int MINB = (NW_ == 4 && D_ == 64) ? 3 : 1;
   static constexpr int EPL = Vec16<T>::N;     // elements per 16-byte vector
   static constexpr int KS = Op<OP>::K;
   static constexpr int PL = Op<OP>::PL;
@@ -59,23 +63,23 @@ struct Cfg {
   static constexpr int CT = DV / 16;          // 16-wide value-column tiles
   static constexpr int FT = R / 16;           // 16-wide feature tiles
   static constexpr int NTILE = CT * FT;       // 16x16 tiles of the state
-  static constexpr int TPW = NTILE / kWaves;  // state tiles owned per wave
-  static constexpr int ZPW = FT / kWaves;     // z tiles owned per wave
+  static constexpr int TPW = NTILE / NW;  // state tiles owned per wave
+  static constexpr int ZPW = FT / NW;     // z tiles owned per wave
   static constexpr int VQ = C * D / EPL;      // 16-byte vectors of one Q/K chunk
   static constexpr int VV = C * DV / EPL;     // ... of one V chunk
-  static constexpr int LQ = (VQ + kThreads - 1) / kThreads;
-  static constexpr int LV = (VV + kThreads - 1) / kThreads;
+  static constexpr int LQ = (VQ + NT - 1) / NT;
+  static constexpr int LV = (VV + NT - 1) / NT;
   // causal output work split: waves per row block, row blocks per wave,
   // value-column tiles per wave
-  static constexpr int WPR = RB >= kWaves ? 1 : kWaves / RB;
-  static constexpr int RBW = RB >= kWaves ? RB / kWaves : 1;
+  static constexpr int WPR = RB >= NW ? 1 : NW / RB;
+  static constexpr int RBW = RB >= NW ? RB / NW : 1;
   static constexpr int CTW = CT / WPR;
   // carried z as published in LDS: fp32 for fp32 operands; for bf16 three
   // rows of R bf16 (hi, lo = z - hi, zeros), read as an MFMA operand
   using ZT = typename std::conditional<sizeof(T) == 2, bf16, float>::type;
   static constexpr int ZE = sizeof(T) == 2 ? 3 * R : R;
   static_assert(R == D, "pointwise feature maps keep the dimension");
-  static_assert(NTILE % kWaves == 0 && FT % kWaves == 0, "state tiles must split evenly over waves");
+  static_assert(NTILE % NW == 0 && FT % NW == 0, "state tiles must split evenly over waves");
   static_assert(C % 16 == 0 && C <= 128, "chunk must be 16, 32, 64 or 128");
   static_assert(CT % WPR == 0, "value tiles must split over the waves of a row block");
 };
@@ -101,8 +105,8 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<CF, WITH_Q>& cr, const Head
   // the only case that needs the vi guard; it folds away otherwise)
 #pragma unroll
   for (int i = 0; i < CF::LQ; ++i) {
-    const int vi = tid + i * kThreads;
-    if (CF::VQ % kThreads == 0 || vi < CF::VQ) {
+    const int vi = tid + i * CF::NT;
+    if (CF::VQ % CF::NT == 0 || vi < CF::VQ) {
       const int off = ((t0 + vi / QV) * CF::D + (vi % QV) * CF::EPL) * (int)sizeof(T);
       cr.k[i] = __builtin_amdgcn_raw_buffer_load_b128(hb.k, off, 0, 0);
       if constexpr (WITH_Q) cr.q[i] = __builtin_amdgcn_raw_buffer_load_b128(hb.q, off, 0, 0);
@@ -110,8 +114,8 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<CF, WITH_Q>& cr, const Head
   }
 #pragma unroll
   for (int i = 0; i < CF::LV; ++i) {
-    const int vi = tid + i * kThreads;
-    if (CF::VV % kThreads == 0 || vi < CF::VV) {
+    const int vi = tid + i * CF::NT;
+    if (CF::VV % CF::NT == 0 || vi < CF::VV) {
       const int off = ((t0 + vi / VVR) * CF::DV + (vi % VVR) * CF::EPL) * (int)sizeof(T);
       cr.v[i] = __builtin_amdgcn_raw_buffer_load_b128(hb.v, off, 0, 0);
     }
@@ -138,8 +142,8 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typ
   auto keys = [&](auto tail) {
 #pragma unroll
     for (int i = 0; i < CF::LQ; ++i) {
-      const int vi = tid + i * kThreads;
-      if (!(CF::VQ % kThreads == 0 || vi < CF::VQ)) continue;
+      const int vi = tid + i * CF::NT;
+      if (!(CF::VQ % CF::NT == 0 || vi < CF::VQ)) continue;
       const int tok = vi / QV;
       const int col = (vi % QV) * CF::EPL;
       float f[CF::EPL];
@@ -181,8 +185,8 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typ
     keys(std::false_type{});
 #pragma unroll
   for (int i = 0; i < CF::LV; ++i) {
-    const int vi = tid + i * kThreads;
-    if (CF::VV % kThreads == 0 || vi < CF::VV)
+    const int vi = tid + i * CF::NT;
+    if (CF::VV % CF::NT == 0 || vi < CF::VV)
       *reinterpret_cast<u32x4*>(sv + TV::off(vi / VVR, (vi % VVR) * CF::EPL)) = cr.v[i];
   }
 }
@@ -213,7 +217,7 @@ __device__ __forceinline__ void state_mfma(f32x4 (&acc)[CF::TPW], f32x4 (&zt)[CF
       const int ra = ks * 32 + 8 * g;
 #pragma unroll
       for (int i = 0; i < CF::TPW; ++i) {
-        const int t = w + kWaves * i;
+        const int t = w + CF::NW * i;
         const int ct = t % CF::CT, ft = t / CF::CT;
         const bf16x8 a = CF::C >= 32 ? tr_frag<DV>(sv, ra, ra + 4, 16 * ct, li) : tr_frag_lo<DV>(sv, 4 * g, 16 * ct, li);
         acc[i] = mfma16(a, kfrag(sk, ra, ft), acc[i]);
@@ -221,7 +225,7 @@ __device__ __forceinline__ void state_mfma(f32x4 (&acc)[CF::TPW], f32x4 (&zt)[CF
       }
 #pragma unroll
       for (int k = 0; k < CF::ZPW; ++k) {
-        const int ft = w + kWaves * k;
+        const int ft = w + CF::NW * k;
         zt[k] = mfma16(ones, kfrag(sk, ra, ft), zt[k]);
         if (sk_lo) zt[k] = mfma16(ones, kfrag(sk_lo, ra, ft), zt[k]);
       }
@@ -234,13 +238,13 @@ __device__ __forceinline__ void state_mfma(f32x4 (&acc)[CF::TPW], f32x4 (&zt)[CF
       const int row = ks * 4 + g;
 #pragma unroll
       for (int i = 0; i < CF::TPW; ++i) {
-        const int t = w + kWaves * i;
+        const int t = w + CF::NW * i;
         const int ct = t % CF::CT, ft = t / CF::CT;
         acc[i] = mfma16(sv[TV::off(row, 16 * ct + li)], sk[TQ::off(row, 16 * ft + li)], acc[i]);
       }
 #pragma unroll
       for (int k = 0; k < CF::ZPW; ++k) {
-        const int ft = w + kWaves * k;
+        const int ft = w + CF::NW * k;
         zt[k] = mfma16(1.0f, sk[TQ::off(row, 16 * ft + li)], zt[k]);
       }
     }
@@ -255,24 +259,27 @@ __device__ __forceinline__ void state_mfma(f32x4 (&acc)[CF::TPW], f32x4 (&zt)[CF
 // (k-step ks -> 16 g + ks).  The same mapping is used for every operand
 // contracted against phi(Q).
 //
-// bf16 with one wave per row block (kRows): the wave's rows are loaded as
-// whole 128/256-byte rows (consecutive lanes read consecutive 16 bytes, so
-// every load instruction covers whole cache lines), written to the wave's
-// own LDS scratch and read back in fragment layout.  A fragment-layout
-// global load would touch 16 half lines per instruction, which streams
-// about a third slower.  Otherwise the fragments are loaded from global
-// memory directly.
+// bf16 (kRows): the wave's query rows are loaded as whole 128/256-byte rows
+// (consecutive lanes read consecutive 16 bytes, so every load instruction
+// covers whole cache lines), written to the wave's own LDS scratch and read
+// back in fragment layout.  A fragment-layout global load would touch 16
+// partial lines per instruction, which streams about a third slower.  (Waves
+// that share a row block each load it; the second read hits L2.)  fp32: the
+// fragments are loaded from global memory directly.
 template <class CF, bool ROWS = true>
 struct QRegs {
   using OP = typename CF::OP;
   using frag = typename Op<OP>::frag;
-  static constexpr bool kRows = ROWS && CF::PL == 8 && CF::WPR == 1;
+  static constexpr bool kRows = ROWS && CF::PL == 8;
+  // output rows leave whole when this wave's columns span 64 or 128 values
+  static constexpr int OCOLS = CF::CTW * 16;
+  static constexpr bool kRowsOut = kRows && (OCOLS == 64 || OCOLS == 128);
   static constexpr int NV = CF::PL == 8 ? CF::R / 32 : CF::R / 16;  // 16-byte vectors per lane per row block
   static constexpr int UPR = CF::D / 8;                              // 16-byte units per bf16 row
   u32x4 raw[CF::RBW][NV];
   __device__ static __forceinline__ int feature(int ks, int g) { return CF::PL == 8 ? 32 * ks + 8 * g : 16 * g + ks; }
   __device__ static __forceinline__ int row_block(int rbi, int w) {
-    return (CF::RB >= kWaves) ? (w + kWaves * rbi) : (w % CF::RB);
+    return (CF::RB >= CF::NW) ? (w + CF::NW * rbi) : (w % CF::RB);
   }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t q, int t0, int w, int g, int li) {
     using T = typename CF::IO;
@@ -343,8 +350,10 @@ struct QRegs {
 // Per-wave LDS scratch of the output kernels (bf16 row staging of Q and O).
 template <class CF>
 struct Scratch {
-  static constexpr int PER_WAVE = QRegs<CF>::kRows ? CF::RBW * 16 * (CF::D > CF::DV ? CF::D : CF::DV) : 8;
-  static constexpr int ELEMS = kWaves * PER_WAVE;
+  static constexpr int QE = CF::RBW * 16 * CF::D;
+  static constexpr int OE = QRegs<CF>::kRowsOut ? CF::RBW * 16 * QRegs<CF>::OCOLS : 0;
+  static constexpr int PER_WAVE = QRegs<CF>::kRows ? (QE > OE ? QE : OE) : 8;
+  static constexpr int ELEMS = CF::NW * PER_WAVE;
 };
 
 // Finished output values of one lane for one chunk (row 16 ib + li, value
@@ -386,8 +395,8 @@ __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&q
   const int zrow = min(li & 3, 2);                                    // z_hi, z_lo or zeros
 #pragma unroll
   for (int rbi = 0; rbi < CF::RBW; ++rbi) {
-    const int ib = (RB >= kWaves) ? (w + kWaves * rbi) : (w % RB);
-    const int ct0 = (RB >= kWaves) ? 0 : (w / RB) * CTW;
+    const int ib = (RB >= CF::NW) ? (w + CF::NW * rbi) : (w % RB);
+    const int ct0 = (RB >= CF::NW) ? 0 : (w / RB) * CTW;
 
     float den = 0.f;
     f32x4 dacc = zero4();
@@ -508,11 +517,14 @@ __device__ __forceinline__ void store_outputs(const OutRegs<CF>& out, __amdgpu_b
                                               int w, int g, int li, bool drop, typename CF::OP* scr) {
   using T = typename CF::IO;
   constexpr int RB = CF::RB, CTW = CF::CTW;
-  if constexpr (QRegs<CF, ROWS>::kRows) {
-    using TS = Tile<typename CF::OP, CF::DV>;
-    constexpr int UPR = CF::DV / 8;               // 16-byte units per output row
-    constexpr int NVO = 16 * UPR / 64;            // row units per lane per row block
+  if constexpr (QRegs<CF, ROWS>::kRowsOut) {
+    // this wave's columns [16 ct0, 16 ct0 + OCOLS) of its rows
+    constexpr int OC = QRegs<CF, ROWS>::OCOLS;
+    using TS = Tile<typename CF::OP, OC>;
+    constexpr int UPR = OC / 8;                   // 16-byte units per row piece
+    constexpr int NVO = 16 * UPR / 64;            // units per lane per row block
     const int lane = threadIdx.x & 63;
+    const int ct0 = (RB >= CF::NW) ? 0 : (w / RB) * CTW;
 #pragma unroll
     for (int rbi = 0; rbi < CF::RBW; ++rbi)
 #pragma unroll
@@ -525,7 +537,8 @@ __device__ __forceinline__ void store_outputs(const OutRegs<CF>& out, __amdgpu_b
       for (int v = 0; v < NVO; ++v) {
         const int qi = v * 64 + lane;
         const u32x4 x = *reinterpret_cast<const u32x4*>(scr + TS::off(16 * rbi + qi / UPR, 8 * (qi % UPR)));
-        const int off = drop ? 0x7ffffff0 : ((t0 + 16 * ib + qi / UPR) * CF::DV + 8 * (qi % UPR)) * 2;
+        const int off =
+            drop ? 0x7ffffff0 : ((t0 + 16 * ib + qi / UPR) * CF::DV + 16 * ct0 + 8 * (qi % UPR)) * 2;
         __builtin_amdgcn_raw_buffer_store_b128(x, orsrc, off, 0, 0);
       }
     }
@@ -533,7 +546,7 @@ __device__ __forceinline__ void store_outputs(const OutRegs<CF>& out, __amdgpu_b
 #pragma unroll
     for (int rbi = 0; rbi < CF::RBW; ++rbi) {
       const int ib = QRegs<CF>::row_block(rbi, w);
-      const int ct0 = (RB >= kWaves) ? 0 : (w / RB) * CTW;
+      const int ct0 = (RB >= CF::NW) ? 0 : (w / RB) * CTW;
       const int row = t0 + 16 * ib + li;
 #pragma unroll
       for (int cti = 0; cti < CTW; ++cti) {
@@ -558,7 +571,7 @@ __device__ __forceinline__ void publish_state(const f32x4 (&sacc)[CF::TPW], cons
   using TS = Tile<OP, CF::DV>;
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
-    const int t = w + kWaves * i;
+    const int t = w + CF::NW * i;
     const int ct = t % CF::CT, ft = t / CF::CT;
     OP* dst = ss + TS::off(16 * ft + li, 16 * ct + 4 * g);
     if constexpr (sizeof(OP) == 2) {
@@ -575,13 +588,13 @@ __device__ __forceinline__ void publish_state(const f32x4 (&sacc)[CF::TPW], cons
         const float z = zt[k][0];
         const bf16 h = static_cast<bf16>(z);
         const bf16 v = g == 0 ? h : g == 1 ? static_cast<bf16>(z - static_cast<float>(h)) : static_cast<bf16>(0.f);
-        sz[g * CF::R + 16 * (w + kWaves * k) + li] = v;
+        sz[g * CF::R + 16 * (w + CF::NW * k) + li] = v;
       }
     }
   } else {
     if (g == 0) {
 #pragma unroll
-      for (int k = 0; k < CF::ZPW; ++k) sz[16 * (w + kWaves * k) + li] = zt[k][0];
+      for (int k = 0; k < CF::ZPW; ++k) sz[16 * (w + CF::NW * k) + li] = zt[k][0];
     }
   }
 }
@@ -600,13 +613,14 @@ struct SmemState {
   OP v[2][VE];
 };
 
-// LDS of the output kernel: two chunk buffers of phi(K) and V, the carried
-// state (S as an MFMA operand, z), and the per-wave row scratch.
+// LDS of the output kernel: phi(K) and V of the chunk, the carried state (S
+// as an MFMA operand, z), and the per-wave row scratch.  All single buffers:
+// the barrier at the top of each chunk orders every reuse.
 template <class CF>
 struct SmemOut {
   using OP = typename CF::OP;
-  OP k[2][Tile<OP, CF::R>::elems(CF::C)];
-  OP v[2][Tile<OP, CF::DV>::elems(CF::C)];
+  OP k[Tile<OP, CF::R>::elems(CF::C)];
+  OP v[Tile<OP, CF::DV>::elems(CF::C)];
   OP s[Tile<OP, CF::DV>::elems(CF::R)];
   alignas(16) typename CF::ZT z[CF::ZE];
   alignas(16) OP scr[Scratch<CF>::ELEMS];
@@ -644,7 +658,7 @@ __device__ __forceinline__ HeadBufs head_bufs(const typename CF::IO* Q, const ty
 
 // Per-span state: dS = phi(K_span)^T V_span, dz = sum phi(K_span) -> ws slot s.
 template <class CF>
-__global__ __launch_bounds__(kThreads) void la_state_kernel(const typename CF::IO* __restrict__ K,
+__global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO* __restrict__ K,
                                                             const typename CF::IO* __restrict__ V,
                                                             float* __restrict__ ws, int N, int n_span) {
   using OP = typename CF::OP;
@@ -695,13 +709,13 @@ __global__ __launch_bounds__(kThreads) void la_state_kernel(const typename CF::I
   float* slot = ws + ((size_t)bh * (n_span + 1) + s) * E;
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
-    const int t = w + kWaves * i;
+    const int t = w + CF::NW * i;
     const int ct = t % CF::CT, ft = t / CF::CT;
     *reinterpret_cast<f32x4*>(slot + (16 * ft + li) * CF::DV + 16 * ct + 4 * g) = acc[i];
   }
   if (g == 0) {
 #pragma unroll
-    for (int k = 0; k < CF::ZPW; ++k) slot[CF::R * CF::DV + 16 * (w + kWaves * k) + li] = zt[k][0];
+    for (int k = 0; k < CF::ZPW; ++k) slot[CF::R * CF::DV + 16 * (w + CF::NW * k) + li] = zt[k][0];
   }
 }
 
@@ -749,11 +763,11 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
 
 // Outputs of one span, carrying (S, z) from the span's prefix (causal) or
 // reading the full-sequence sums (non-causal: only Q is read).  Causal: chunk
-// c+1 is loaded while chunk c is computed (LDS double buffering of phi(K) and
-// V; the carried state is single-buffered, hence a second barrier per
-// chunk), and chunk c's outputs are stored before the state update.
+// c+1 is loaded into registers while chunk c is computed; LDS holds one
+// chunk, with a barrier before it is overwritten and one after it is written;
+// chunk c's outputs are stored before the state update.
 template <class CF, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 3) void la_output_kernel(const typename CF::IO* __restrict__ Q,
+__global__ __launch_bounds__(CF::NT, CF::MINB) void la_output_kernel(const typename CF::IO* __restrict__ Q,
                                                                 const typename CF::IO* __restrict__ K,
                                                                 const typename CF::IO* __restrict__ V,
                                                                 typename CF::IO* __restrict__ O,
@@ -775,14 +789,14 @@ __global__ __launch_bounds__(kThreads, 3) void la_output_kernel(const typename C
   f32x4 sacc[CF::TPW];
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
-    const int t = w + kWaves * i;
+    const int t = w + CF::NW * i;
     const int ct = t % CF::CT, ft = t / CF::CT;
     sacc[i] = *reinterpret_cast<const f32x4*>(pre + (16 * ft + li) * CF::DV + 16 * ct + 4 * g);
   }
   f32x4 zt[CF::ZPW];
 #pragma unroll
   for (int k = 0; k < CF::ZPW; ++k) {
-    const float zv = pre[CF::R * CF::DV + 16 * (w + kWaves * k) + li];
+    const float zv = pre[CF::R * CF::DV + 16 * (w + CF::NW * k) + li];
     zt[k] = f32x4{zv, zv, zv, zv};
   }
 
@@ -816,21 +830,20 @@ __global__ __launch_bounds__(kThreads, 3) void la_output_kernel(const typename C
     QRegs<CF> qr;
     load_chunk<CF, false>(cr, hb, t_begin);
     qr.load(hb.q, t_begin, w, g, li);
-    int buf = 0;
     typename CF::OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
-    for (int t0 = t_begin; t0 < t_end; t0 += CF::C, buf ^= 1) {
-      __syncthreads();  // every wave is done with the previous chunk's S, z
+    for (int t0 = t_begin; t0 < t_end; t0 += CF::C) {
+      __syncthreads();  // every wave is done with the previous chunk's S, z, phi(K), V
       publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
-      stage_chunk<CF, false>(cr, nullptr, sm.k[buf], nullptr, sm.v[buf], t0, N);
+      stage_chunk<CF, false>(cr, nullptr, sm.k, nullptr, sm.v, t0, N);
       typename QRegs<CF>::frag qf[CF::RBW][CF::R / CF::KS];
       qr.to_frags(qf, scr, g, li);
       const int tn = min(t0 + CF::C, last);
       load_chunk<CF, false>(cr, hb, tn);
       qr.load(hb.q, tn, w, g, li);
       __syncthreads();
-      chunk_outputs<CF, true>(qf, sm.k[buf], sm.v[buf], sm.s, sm.z, out, w, g, li);
+      chunk_outputs<CF, true>(qf, sm.k, sm.v, sm.s, sm.z, out, w, g, li);
       store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
-      state_mfma<CF>(sacc, zt, sm.k[buf], nullptr, sm.v[buf], w, g, li);
+      state_mfma<CF>(sacc, zt, sm.k, nullptr, sm.v, w, g, li);
     }
   }
 }
@@ -888,7 +901,7 @@ __device__ __forceinline__ void slot_store(float* slot, const f32x4 (&S)[CF::TPW
   const __amdgpu_buffer_rsrc_t r = make_rsrc(slot, (CF::R * CF::DV + CF::R) * 4);
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
-    const int t = w + kWaves * i;
+    const int t = w + CF::NW * i;
     const int ct = t % CF::CT, ft = t / CF::CT;
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S[i]), r,
                                            ((16 * ft + li) * CF::DV + 16 * ct + 4 * g) * 4, 0, kDeviceScope);
@@ -897,7 +910,7 @@ __device__ __forceinline__ void slot_store(float* slot, const f32x4 (&S)[CF::TPW
 #pragma unroll
     for (int k = 0; k < CF::ZPW; ++k)
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z[k][0]), r,
-                                            (CF::R * CF::DV + 16 * (w + kWaves * k) + li) * 4, 0, kDeviceScope);
+                                            (CF::R * CF::DV + 16 * (w + CF::NW * k) + li) * 4, 0, kDeviceScope);
   }
 }
 
@@ -908,7 +921,7 @@ __device__ __forceinline__ void slot_add(const float* slot, f32x4 (&S)[CF::TPW],
   const __amdgpu_buffer_rsrc_t r = make_rsrc(slot, (CF::R * CF::DV + CF::R) * 4);
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
-    const int t = w + kWaves * i;
+    const int t = w + CF::NW * i;
     const int ct = t % CF::CT, ft = t / CF::CT;
     S[i] += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                           r, ((16 * ft + li) * CF::DV + 16 * ct + 4 * g) * 4, 0, kDeviceScope));
@@ -916,7 +929,7 @@ __device__ __forceinline__ void slot_add(const float* slot, f32x4 (&S)[CF::TPW],
 #pragma unroll
   for (int k = 0; k < CF::ZPW; ++k) {
     const float v = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(r, (CF::R * CF::DV + 16 * (w + kWaves * k) + li) * 4, 0, kDeviceScope));
+        __builtin_amdgcn_raw_buffer_load_b32(r, (CF::R * CF::DV + 16 * (w + CF::NW * k) + li) * 4, 0, kDeviceScope));
     z[k] += f32x4{v, v, v, v};
   }
 }
@@ -927,19 +940,19 @@ __device__ __forceinline__ void state_add(const float* Sm, const float* zv, f32x
                                           f32x4 (&z)[CF::ZPW], int w, int g, int li) {
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
-    const int t = w + kWaves * i;
+    const int t = w + CF::NW * i;
     const int ct = t % CF::CT, ft = t / CF::CT;
     S[i] += *reinterpret_cast<const f32x4*>(Sm + (16 * ft + li) * CF::DV + 16 * ct + 4 * g);
   }
 #pragma unroll
   for (int k = 0; k < CF::ZPW; ++k) {
-    const float v = zv[16 * (w + kWaves * k) + li];
+    const float v = zv[16 * (w + CF::NW * k) + li];
     z[k] += f32x4{v, v, v, v};
   }
 }
 
 template <class CF>
-__global__ __launch_bounds__(kThreads, 2) void la_fused_kernel(
+__global__ __launch_bounds__(CF::NT, 2) void la_fused_kernel(
     const typename CF::IO* __restrict__ Q, const typename CF::IO* __restrict__ K,
     const typename CF::IO* __restrict__ V, typename CF::IO* __restrict__ O, float* __restrict__ slots,
     unsigned* __restrict__ hdr, int N, int n_span, int BH, int group, const float* __restrict__ S0,
@@ -1035,14 +1048,14 @@ __global__ __launch_bounds__(kThreads, 2) void la_fused_kernel(
       // the final state S_N, z_N (z_out rows use the same ownership)
 #pragma unroll
       for (int i = 0; i < CF::TPW; ++i) {
-        const int t = w + kWaves * i;
+        const int t = w + CF::NW * i;
         const int ct = t % CF::CT, ft = t / CF::CT;
         *reinterpret_cast<f32x4*>(S_out + (size_t)bh * CF::R * CF::DV + (16 * ft + li) * CF::DV + 16 * ct + 4 * g) =
             is[i];
       }
       if (g == 0) {
 #pragma unroll
-        for (int k = 0; k < CF::ZPW; ++k) z_out[(size_t)bh * CF::R + 16 * (w + kWaves * k) + li] = iz[k][0];
+        for (int k = 0; k < CF::ZPW; ++k) z_out[(size_t)bh * CF::R + 16 * (w + CF::NW * k) + li] = iz[k][0];
       }
     }
     wait_stores();
@@ -1088,7 +1101,7 @@ static hipError_t launch_fused(const PrefillArgs& a) {
   rec(2);
   rec(3);
   rec(4);
-  hipLaunchKernelGGL((la_fused_kernel<CF>), dim3(BH * a.n_span), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((la_fused_kernel<CF>), dim3(BH * a.n_span), dim3(CF::NT), 0, st,
                      static_cast<const T*>(a.Q), static_cast<const T*>(a.K), static_cast<const T*>(a.V),
                      static_cast<T*>(a.O), slots, hdr, a.N, a.n_span, BH, a.group, a.S0, a.z0, a.S_out, a.z_out);
   rec(5);
@@ -1115,7 +1128,7 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
   };
   rec(0);
   if (n_span > 0 && BH > 0) {
-    hipLaunchKernelGGL((la_state_kernel<CF>), dim3(BH * n_span), dim3(kThreads), 0, st, K, V, ws, a.N, n_span);
+    hipLaunchKernelGGL((la_state_kernel<CF>), dim3(BH * n_span), dim3(CF::NT), 0, st, K, V, ws, a.N, n_span);
   }
   rec(1);
   rec(2);
@@ -1125,10 +1138,10 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
   rec(4);
   if (n_span > 0 && BH > 0) {
     if (a.causal)
-      hipLaunchKernelGGL((la_output_kernel<CF, true>), dim3(BH * n_span), dim3(kThreads), 0, st, Q, K, V, O, ws,
+      hipLaunchKernelGGL((la_output_kernel<CF, true>), dim3(BH * n_span), dim3(CF::NT), 0, st, Q, K, V, O, ws,
                          a.N, n_span);
     else
-      hipLaunchKernelGGL((la_output_kernel<CF, false>), dim3(BH * n_span), dim3(kThreads), 0, st, Q, K, V, O, ws,
+      hipLaunchKernelGGL((la_output_kernel<CF, false>), dim3(BH * n_span), dim3(CF::NT), 0, st, Q, K, V, O, ws,
                          a.N, n_span);
   }
   rec(5);
@@ -1137,10 +1150,13 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
 
 template <typename T, int D, int PHI>
 static hipError_t dispatch_chunk(const PrefillArgs& a) {
+  // wide heads run eight waves per workgroup: half the state tiles and
+  // registers per wave, and twice the waves per CU
+  constexpr int NW = D == 128 ? 8 : kWaves;
   switch (a.chunk) {
-    case 16: return launch_prefill<Cfg<T, D, D, D, 16, PHI>>(a);
-    case 32: return launch_prefill<Cfg<T, D, D, D, 32, PHI>>(a);
-    case 64: return launch_prefill<Cfg<T, D, D, D, 64, PHI>>(a);
+    case 16: return launch_prefill<Cfg<T, D, D, D, 16, PHI, NW>>(a);
+    case 32: return launch_prefill<Cfg<T, D, D, D, 32, PHI, NW>>(a);
+    case 64: return launch_prefill<Cfg<T, D, D, D, 64, PHI, NW>>(a);
     case 128:
       if constexpr (sizeof(T) == 2 && D == 64) return launch_prefill<Cfg<T, D, D, D, 128, PHI>>(a);
       return hipErrorInvalidValue;

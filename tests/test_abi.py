@@ -73,8 +73,8 @@ def test_workspace_sizes(lib, monkeypatch):
     # short sequences keep at least 4 chunks per span
     assert _ws(1, 1, 256) == 1 * 2 * E * 4
     assert _ws(1, 2, 4096) == 2 * 17 * E * 4
-    # fp32 I/O at chunk 64 runs one workgroup per CU: 256 slots
-    assert _ws(1, 8, 65536, io=0) == 8 * 33 * E * 4
+    # fp32 I/O at chunk 64: three workgroups per CU, 768 slots
+    assert _ws(1, 8, 65536, io=0) == 8 * 97 * E * 4
     # N = 0 still needs one slot per head for the (initial = final) state
     assert _ws(1, 2, 0) == 2 * 1 * E * 4
     monkeypatch.setenv("LA_SPAN", "64")
