@@ -2,7 +2,7 @@
 //
 // ELU(x)+1 (alpha = 1) and the identity are pointwise ("Choice of phi" on the
 // linear-attention-kernel page; "Efficient attention variants" sec. 4), so the
-// kernel is a pure stream: 16-byte vector loads, 32/16-byte stores, grid
+// kernel is a pure stream: contiguous vector loads and 16-byte stores, grid
 // stride, HBM-bound.
 //
 // FAVOR+ ("Efficient attention variants" sec. 6): x = u / D^(1/4),
@@ -13,21 +13,28 @@
 
 namespace la {
 
+// One group of 4 elements per lane and step: the loads (8 bytes per lane for
+// bf16, 16 for fp32) and the 16-byte fp32 stores are both contiguous across
+// the lanes of every instruction, so each instruction covers whole cache
+// lines in both directions.
 template <typename T, int PHI>
 __global__ __launch_bounds__(kThreads) void la_phi_pointwise_kernel(const T* __restrict__ X,
-                                                                    float* __restrict__ Y, long long n_vec) {
-  constexpr int EPL = Vec16<T>::N;
+                                                                    float* __restrict__ Y, long long n_quad) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   const long long stride = (long long)gridDim.x * kThreads;
-  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n_vec; i += stride) {
-    const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X) + i);
-    float f[EPL];
-    unpack16<T>(u, f);
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n_quad; i += stride) {
+    float f[4];
+    if constexpr (sizeof(T) == 2) {
+      const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(X) + i);
+      f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x);
+      f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
+    } else {
+      const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X) + i);
+      unpack16<float>(u, f);
+    }
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) f[e] = phi_pointwise<PHI>(f[e]);
-    f32x4* dst = reinterpret_cast<f32x4*>(Y + i * EPL);
-#pragma unroll
-    for (int e = 0; e < EPL / 4; ++e)
-      __builtin_nontemporal_store(f32x4{f[4 * e], f[4 * e + 1], f[4 * e + 2], f[4 * e + 3]}, dst + e);
+    for (int e = 0; e < 4; ++e) f[e] = phi_pointwise<PHI>(f[e]);
+    __builtin_nontemporal_store(f32x4{f[0], f[1], f[2], f[3]}, reinterpret_cast<f32x4*>(Y) + i);
   }
 }
 
@@ -103,15 +110,15 @@ static hipError_t feature_io(const FeatureArgs& a) {
                          static_cast<const T*>(a.X), a.Y, a.rows, a.omega);
     return hipGetLastError();
   }
-  const long long n_vec = a.rows * a.d / Vec16<T>::N;
-  const long long blocks = (n_vec + kThreads - 1) / kThreads;
+  const long long n_quad = a.rows * a.d / 4;
+  const long long blocks = (n_quad + kThreads - 1) / kThreads;
   const int grid = static_cast<int>(blocks < 8192 ? blocks : 8192);
   if (a.phi == PHI_ELU1)
     hipLaunchKernelGGL((la_phi_pointwise_kernel<T, PHI_ELU1>), dim3(grid), dim3(kThreads), 0, st,
-                       static_cast<const T*>(a.X), a.Y, n_vec);
+                       static_cast<const T*>(a.X), a.Y, n_quad);
   else
     hipLaunchKernelGGL((la_phi_pointwise_kernel<T, PHI_IDENTITY>), dim3(grid), dim3(kThreads), 0, st,
-                       static_cast<const T*>(a.X), a.Y, n_vec);
+                       static_cast<const T*>(a.X), a.Y, n_quad);
   return hipGetLastError();
 }
 

@@ -65,8 +65,12 @@ __device__ __forceinline__ FavorConsts favor_consts() {
   return FavorConsts{log2e * 0.35355339059327373f /* 64^(-1/4) */, log2e / 16.0f /* 1 / (2 sqrt(64)) */,
                      4.0f /* log2(sqrt(256)) */};
 }
-__device__ __forceinline__ float favor_phi(const FavorConsts& c, float proj, float norm2) {
-  return __builtin_amdgcn_exp2f(proj * c.a1 - norm2 * c.a2 - c.a3);
+// Per-token part of the exponent, formed once per token when its squared
+// norm is summed: -(|u|^2 log2(e) / (2 sqrt(d)) + log2(sqrt(r))).
+__device__ __forceinline__ float favor_bias(const FavorConsts& c, float norm2) { return -(norm2 * c.a2 + c.a3); }
+// phi for one feature: exp2(proj log2(e) d^(-1/4) + bias) - one FMA and one exp2.
+__device__ __forceinline__ float favor_phi(const FavorConsts& c, float proj, float bias) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(proj, c.a1, bias));
 }
 
 // omega fragments of the 4 feature tiles a wave owns (features 64 w + 16 j +
@@ -119,7 +123,8 @@ __device__ __forceinline__ void load_raw(RawRegs<NS>& rr, const __amdgpu_buffer_
 
 // Registers -> LDS (row-major swizzled 64 x 64 tiles).  For the streams
 // flagged in `norms`, the squared norm of each token row is summed in fp32
-// (8 threads hold one row: a 3-step butterfly) and written to nrm.
+// (8 threads hold one row: a 3-step butterfly) and its exponent bias is
+// written to nrm.
 template <int NS>
 __device__ __forceinline__ void stage_raw(const RawRegs<NS>& rr, bf16* const (&dst)[NS], float* const (&nrm)[NS],
                                           int norms) {
@@ -140,7 +145,7 @@ __device__ __forceinline__ void stage_raw(const RawRegs<NS>& rr, bf16* const (&d
         n2 += __shfl_xor(n2, 1);
         n2 += __shfl_xor(n2, 2);
         n2 += __shfl_xor(n2, 4);
-        if ((tid & 7) == 0) nrm[s][tok] = n2;
+        if ((tid & 7) == 0) nrm[s][tok] = favor_bias(favor_consts(), n2);
       }
     }
   }
