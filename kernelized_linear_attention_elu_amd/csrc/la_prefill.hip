@@ -298,7 +298,7 @@ struct QRegs {
           row = t0 + 16 * ib + li;
           col = CF::PL == 8 ? 32 * v + 8 * g : 16 * g + 4 * v;
         }
-        raw[rbi][v] = __builtin_amdgcn_raw_buffer_load_b128(q, (row * CF::D + col) * (int)sizeof(T), 0, 0);
+        raw[rbi][v] = __builtin_amdgcn_raw_buffer_load_b128(q, (row * CF::D + col) * (int)sizeof(T), 0, kStreamLoad);
       }
     }
   }
@@ -539,7 +539,7 @@ __device__ __forceinline__ void store_outputs(const OutRegs<CF>& out, __amdgpu_b
         const u32x4 x = *reinterpret_cast<const u32x4*>(scr + TS::off(16 * rbi + qi / UPR, 8 * (qi % UPR)));
         const int off =
             drop ? 0x7ffffff0 : ((t0 + 16 * ib + qi / UPR) * CF::DV + 16 * ct0 + 8 * (qi % UPR)) * 2;
-        __builtin_amdgcn_raw_buffer_store_b128(x, orsrc, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(x, orsrc, off, 0, kStreamStore);
       }
     }
   } else {
@@ -553,9 +553,11 @@ __device__ __forceinline__ void store_outputs(const OutRegs<CF>& out, __amdgpu_b
         const int off = drop ? 0x7ffffff0 : (row * CF::DV + 16 * (ct0 + cti) + 4 * g) * (int)sizeof(T);
         if constexpr (sizeof(T) == 2) {
           typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out.v[rbi][cti]), orsrc, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out.v[rbi][cti]), orsrc, off, 0,
+                                                kStreamStore);
         } else {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out.v[rbi][cti]), orsrc, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out.v[rbi][cti]), orsrc, off, 0,
+                                                 kStreamStore);
         }
       }
     }

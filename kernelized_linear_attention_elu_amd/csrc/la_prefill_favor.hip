@@ -360,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_output_favor_kernel(const bf16
       for (int ct = 0; ct < FCT; ++ct) {
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out[ct]), orsrc,
-                                              (row * FDV + 16 * ct + 4 * g) * 2, 0, 0);
+                                              (row * FDV + 16 * ct + 4 * g) * 2, 0, kStreamStore);
       }
     }
     if (t0 + FC < t_end) load_raw<3>(rr, src, t0 + FC);
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_output_favor_kernel(const bf16
     for (int ct = 0; ct < FCT; ++ct) {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out[ct]), orsrc,
-                                            (row * FDV + 16 * ct + 4 * g) * 2, 0, 0);
+                                            (row * FDV + 16 * ct + 4 * g) * 2, 0, kStreamStore);
     }
   }
 }

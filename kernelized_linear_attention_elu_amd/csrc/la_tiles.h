@@ -49,6 +49,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
+// Cache policy of the output stores: nt (streaming).  O is written once and
+// not read again by the path; with this policy its lines do not linger dirty
+// in the memory-side cache, where the next kernel of a step (the next span
+// state pass) would otherwise pay for their write-back while it reads K and V.
+constexpr int kStreamStore = 2;
+// The same policy on the output pass's Q loads (Q is read once): measured
+// faster for the output kernel, while on the state pass's K and V loads it
+// slows the output pass that re-reads them.
+constexpr int kStreamLoad = 2;
+
 // ------------------------------------------------------------------ LDS fragments
 
 __device__ __forceinline__ bf16x4 ds_read_tr4(const bf16* p) {
