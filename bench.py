@@ -9,8 +9,13 @@ synthetic tensors already resident in HBM when the timed region starts;
 three copies of the inputs and outputs are used in turn, so that no step
 finds its data in the 256 MB memory-side cache left by the step before.  The
 timed region is exactly K steps bracketed by device synchronisation; the
-per-kernel durations come from HIP events that the library records on its
-stream around each kernel during those same steps.
+dominant kernel's duration comes from HIP events that the library records on
+its stream around that kernel during those same steps.
+
+Before timing, after the W warm-up steps, untimed steps continue for a fixed
+wall time (--settle, 0.3 s by default): the GPU's clock and power control
+takes about 10 ms of sustained load to reach its steady state, and a step
+timed before that runs up to 25 % slower.
 
 One JSON line is printed with the metric, the roofline of the dominant kernel
 (the output kernel) and of the whole step, and the fp64 CPU oracle timed on
@@ -46,6 +51,21 @@ FUSED_KERNEL_NAMES = ("la_fused_reset_kernel", None, "la_fused_kernel")
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "kernelized_linear_attention_elu_amd", "csrc")
 ROTATE = 3                     # input/output copies used in turn by the prefill bench
+SETTLE_S = 0.3                 # untimed run after the warm-up steps (clock/power steady state)
+
+
+def settle(torch, run, seconds):
+    """Keep calling run(i) (untimed) until `seconds` of wall time have passed,
+    synchronising every 16 calls; returns the number of calls."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            run(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
 
 
 def source_hash():
@@ -82,13 +102,15 @@ def read_traffic(workload, kernel):
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="long",
                    choices=["long", "prefill", "wide", "favor", "decode", "feature", "copy"])
     p.add_argument("--noncausal", action="store_true", help="non-causal prefill")
     p.add_argument("--chunk", type=int, default=None,
                    help="chunk size (default: the workload's, 0 = the library's choice)")
+    p.add_argument("--settle", type=float, default=SETTLE_S,
+                   help="seconds of untimed steps after the warm-up steps (clock/power steady state)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     return p.parse_args(argv)
 
@@ -152,6 +174,7 @@ def bench_prefill(args, torch, la, synth):
 
     for i in range(args.warmup):
         step(i)
+    settled = settle(torch, step, args.settle)
     nk = la.LA_FORWARD_KERNELS
     evs = [[la.event_create() for _ in range(2 * nk)] for _ in range(args.steps)]
     # timed region: exactly K steps; two HIP events per step, recorded by the
@@ -241,6 +264,7 @@ def bench_prefill(args, torch, la, synth):
         "kernels_us": {n: t * 1e3 for n, t in zip(names, kern_ms) if n},
         "dominant_kernel_us_live": out_live_ms * 1e3,
         "path": {"single_pass": single_pass, "spans_per_head": n_span},
+        "settle": {"seconds": args.settle, "untimed_steps": settled},
     }
     if not args.no_cpu_baseline:
         wall, h, cores = time_oracle_prefill(q, k, v, causal, max_heads=w.H, phi=w.phi, omega=omega)
@@ -275,7 +299,7 @@ def bench_decode(args, torch, la, synth):
     o = torch.empty((n, H, dv), dtype=torch.bfloat16, device=dev)
     for _ in range(args.warmup):
         la.decode_step(S, z, q, k, v, out=o)
-    torch.cuda.synchronize()
+    settled = settle(torch, lambda i: la.decode_step(S, z, q, k, v, out=o), args.settle)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
@@ -301,6 +325,7 @@ def bench_decode(args, torch, la, synth):
         "roofline": {"kernel": "la_decode_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": read_traffic("decode", "la_decode_kernel")},
+        "settle": {"seconds": args.settle, "untimed_steps": settled},
     }
     return res
 
@@ -313,13 +338,14 @@ def bench_feature(args, torch, la, synth):
     q, _, _ = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io="bf16")
     X = hostio.upload_bf16_bits(synth.bf16_bits(q), dev)
     del q
+    Y = torch.empty(tuple(X.shape), dtype=torch.float32, device=dev)
     for _ in range(args.warmup):
-        Y = la.feature_map(X)
-    torch.cuda.synchronize()
+        la.feature_map(X, out=Y)
+    settled = settle(torch, lambda i: la.feature_map(X, out=Y), args.settle)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(args.steps):
-        Y = la.feature_map(X)
+        la.feature_map(X, out=Y)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
@@ -334,6 +360,7 @@ def bench_feature(args, torch, la, synth):
         "roofline": {"kernel": "la_phi_pointwise_kernel", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": read_traffic("feature", "la_phi_pointwise_kernel")},
+        "settle": {"seconds": args.settle, "untimed_steps": settled},
     }
 
 
@@ -345,7 +372,7 @@ def bench_copy(args, torch):
     b = torch.empty_like(a)
     for _ in range(args.warmup):
         b.copy_(a)
-    torch.cuda.synchronize()
+    settled = settle(torch, lambda i: b.copy_(a), args.settle)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         b.copy_(a)
@@ -354,7 +381,8 @@ def bench_copy(args, torch):
     return {"metric": "device copy GB/s (read + write)", "value": 2 * n / (ms * 1e-3) / 1e9, "unit": "GB/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
-            "data": "synthetic", "config": {"workload": f"copy of {n} bytes", "bytes_read": n, "bytes_written": n}}
+            "data": "synthetic", "config": {"workload": f"copy of {n} bytes", "bytes_read": n, "bytes_written": n},
+            "settle": {"seconds": args.settle, "untimed_steps": settled}}
 
 
 def main(argv=None):
