@@ -136,6 +136,16 @@ def _require(t, name, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _omega_rows(omega, phi, d):
+    """Feature count r: omega's rows for FAVOR+ (omega must be [r, d]), else d."""
+    if phi != "favor":
+        return d
+    if omega is None or omega.dim() != 2 or omega.shape[1] != d:
+        raise ValueError(f"FAVOR+ needs omega of shape [r, {d}], got "
+                         f"{None if omega is None else tuple(omega.shape)}")
+    return omega.shape[0]
+
+
 def _stream(device):
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
@@ -176,8 +186,8 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
     for name, t in (("Q", Q), ("K", K), ("V", V)):
         _require(t, name, Q.dtype, dev)
     io = _io_code(Q)
-    r = omega.shape[0] if (phi == "favor" and omega is not None) else d
     _require(omega, "omega", torch.float32, dev)
+    r = _omega_rows(omega, phi, d)
     if (S0 is None) != (z0 is None):
         raise ValueError("give both S0 and z0 or neither")
     _require(S0, "S0", torch.float32, dev)
@@ -187,6 +197,8 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
     if out is None:
         out = torch.empty((B, H, N, dv), dtype=Q.dtype, device=dev)
     _require(out, "out", Q.dtype, dev)
+    if tuple(out.shape) != (B, H, N, dv):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, N, dv)}")
     S_out = z_out = None
     if return_state:
         S_out = torch.empty((B, H, r, dv), dtype=torch.float32, device=dev)
@@ -221,10 +233,16 @@ def decode_step(S, z, q, k, v, *, phi="elu1", omega=None, inplace=True, out=None
     _require(S, "S", torch.float32, dev)
     _require(z, "z", torch.float32, dev)
     _require(omega, "omega", torch.float32, dev)
-    if tuple(S.shape) != (B, H, r, dv) or tuple(z.shape) != (B, H, r) or tuple(k.shape) != (B, H, d):
+    if _omega_rows(omega, phi, d) != r:
+        raise ValueError(f"S has {r} feature rows; phi={phi} gives {_omega_rows(omega, phi, d)}")
+    if (tuple(S.shape) != (B, H, r, dv) or tuple(z.shape) != (B, H, r) or tuple(k.shape) != (B, H, d)
+            or tuple(v.shape) != (B, H, dv)):
         raise ValueError("decode shapes: S [B,H,r,dv], z [B,H,r], q,k [B,H,d], v [B,H,dv]")
     if out is None:
         out = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    _require(out, "out", q.dtype, dev)
+    if tuple(out.shape) != (B, H, dv):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, dv)}")
     S_new, z_new = (S, z) if inplace else (torch.empty_like(S), torch.empty_like(z))
     st = lib.la_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_new), _ptr(z_new),
                             B, H, d, dv, _io_code(q), PHI[phi], r, _ptr(omega), _stream(dev))
@@ -232,16 +250,24 @@ def decode_step(S, z, q, k, v, *, phi="elu1", omega=None, inplace=True, out=None
     return out if inplace else (out, S_new, z_new)
 
 
-def feature_map(X, *, phi="elu1", omega=None):
-    """phi applied to the rows of X [..., d]; returns fp32 [..., r]."""
+def feature_map(X, *, phi="elu1", omega=None, out=None):
+    """phi applied to the rows of X [..., d]; returns fp32 [..., r] (written
+    into ``out`` when given: contiguous fp32 of that shape on X's device)."""
     torch = _torch()
     lib = load_library()
     d = X.shape[-1]
     rows = X.numel() // d if d else 0
     _require(X, "X", X.dtype, X.device)
     _require(omega, "omega", torch.float32, X.device)
-    r = omega.shape[0] if phi == "favor" else d
-    Y = torch.empty(tuple(X.shape[:-1]) + (r,), dtype=torch.float32, device=X.device)
+    r = _omega_rows(omega, phi, d)
+    shape = tuple(X.shape[:-1]) + (r,)
+    if out is None:
+        Y = torch.empty(shape, dtype=torch.float32, device=X.device)
+    else:
+        _require(out, "out", torch.float32, X.device)
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
+        Y = out
     st = lib.la_feature_map(_ptr(X), _ptr(Y), rows, d, _io_code(X), PHI[phi], r, _ptr(omega), _stream(X.device))
     _check(st, "la_feature_map")
     return Y
