@@ -506,7 +506,6 @@ __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&q
 }
 
 // Store one chunk's outputs (rows beyond N are dropped by the buffer bounds).
-// Store one chunk's outputs (rows beyond N are dropped by the buffer bounds).
 // With drop set, every store gets an offset past the buffer and the hardware
 // discards it: the store instructions are still issued, so that the memory
 // counter waits of the surrounding loop stay exact.  bf16 with one wave per
@@ -538,7 +537,7 @@ __device__ __forceinline__ void store_outputs(const OutRegs<CF>& out, __amdgpu_b
         const int qi = v * 64 + lane;
         const u32x4 x = *reinterpret_cast<const u32x4*>(scr + TS::off(16 * rbi + qi / UPR, 8 * (qi % UPR)));
         const int off =
-            drop ? 0x7ffffff0 : ((t0 + 16 * ib + qi / UPR) * CF::DV + 16 * ct0 + 8 * (qi % UPR)) * 2;
+            drop ? kDropOffset : ((t0 + 16 * ib + qi / UPR) * CF::DV + 16 * ct0 + 8 * (qi % UPR)) * 2;
         __builtin_amdgcn_raw_buffer_store_b128(x, orsrc, off, 0, kStreamStore);
       }
     }
@@ -550,7 +549,7 @@ __device__ __forceinline__ void store_outputs(const OutRegs<CF>& out, __amdgpu_b
       const int row = t0 + 16 * ib + li;
 #pragma unroll
       for (int cti = 0; cti < CTW; ++cti) {
-        const int off = drop ? 0x7ffffff0 : (row * CF::DV + 16 * (ct0 + cti) + 4 * g) * (int)sizeof(T);
+        const int off = drop ? kDropOffset : (row * CF::DV + 16 * (ct0 + cti) + 4 * g) * (int)sizeof(T);
         if constexpr (sizeof(T) == 2) {
           typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
           __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out.v[rbi][cti]), orsrc, off, 0,
@@ -559,6 +558,35 @@ __device__ __forceinline__ void store_outputs(const OutRegs<CF>& out, __amdgpu_b
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out.v[rbi][cti]), orsrc, off, 0,
                                                  kStreamStore);
         }
+      }
+    }
+  }
+}
+
+// The store instructions of store_outputs<CF, ROWS> (same count, width and
+// policy), all aimed past the buffer, where the hardware drops them.  Issued
+// once ahead of a loop whose iterations end with store_outputs, they make
+// the memory operations outstanding at the loop head the same on entry as
+// on the back edge, so that the compiler's counter wait there covers only
+// the prefetched loads and not the previous chunk's stores.
+template <class CF, bool ROWS = true>
+__device__ __forceinline__ void dummy_stores(__amdgpu_buffer_rsrc_t orsrc) {
+  constexpr int CTW = CF::CTW;
+  if constexpr (QRegs<CF, ROWS>::kRowsOut) {
+    constexpr int NVO = 16 * (QRegs<CF, ROWS>::OCOLS / 8) / 64;
+    static_assert(CF::RBW * NVO <= 4, "distinct drop offsets");
+#pragma unroll
+    for (int i = 0; i < CF::RBW * NVO; ++i)  // distinct offsets: no store is merged away
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, orsrc, kDropOffset - 16 * i, 0, kStreamStore);
+  } else {
+    static_assert(CF::RBW * CTW <= 4, "distinct drop offsets");
+#pragma unroll
+    for (int i = 0; i < CF::RBW * CTW; ++i) {
+      if constexpr (sizeof(typename CF::IO) == 2) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, orsrc, kDropOffset - 16 * i, 0, kStreamStore);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, orsrc, kDropOffset - 16 * i, 0, kStreamStore);
       }
     }
   }
@@ -687,6 +715,7 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
   const int last = t_end > t_begin ? t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C : t_begin;
   ChunkRegs<CF, false> ca, cb;
   load_chunk<CF, false>(ca, hb, t_begin);
+  mem_order_fence();  // ca's loads first, as in the loop: exact counter waits
   load_chunk<CF, false>(cb, hb, min(t_begin + CF::C, last));
   int buf = 0;
   for (int t0 = t_begin; t0 < t_end; t0 += 2 * CF::C) {
@@ -825,15 +854,24 @@ __global__ __launch_bounds__(CF::NT, CF::MINB) void la_output_kernel(const typen
     }
   } else {
     // every memory operation is issued on every iteration (loads past the
-    // span re-read its last chunk from L2; the first iteration's store of
-    // "the previous chunk" is dropped), so the counter waits stay exact
-    const int last = t_end > t_begin ? t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C : t_begin;
+    // span re-read its last chunk from L2), and the prologue issues the
+    // loop's memory operations in the loop's order (K and V, Q, then the
+    // stores, dropped), so the counter wait at the loop head is exact: it
+    // waits for the prefetched chunk, not for the previous chunk's stores
+    // (an empty span returns here, so that the prologue and the loop entry
+    // are one block and the compiler keeps the prologue's issue order)
+    if (t_begin >= t_end) return;
+    const int last = t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C;
     ChunkRegs<CF, false> cr;
     QRegs<CF> qr;
     load_chunk<CF, false>(cr, hb, t_begin);
+    mem_order_fence();
     qr.load(hb.q, t_begin, w, g, li);
+    mem_order_fence();
+    dummy_stores<CF>(hb.o);
     typename CF::OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
-    for (int t0 = t_begin; t0 < t_end; t0 += CF::C) {
+    int t0 = t_begin;
+    do {
       __syncthreads();  // every wave is done with the previous chunk's S, z, phi(K), V
       publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
       stage_chunk<CF, false>(cr, nullptr, sm.k, nullptr, sm.v, t0, N);
@@ -846,7 +884,8 @@ __global__ __launch_bounds__(CF::NT, CF::MINB) void la_output_kernel(const typen
       chunk_outputs<CF, true>(qf, sm.k, sm.v, sm.s, sm.z, out, w, g, li);
       store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
       state_mfma<CF>(sacc, zt, sm.k, nullptr, sm.v, w, g, li);
-    }
+      t0 += CF::C;
+    } while (t0 < t_end);
   }
 }
 

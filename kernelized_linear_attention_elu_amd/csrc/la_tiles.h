@@ -49,6 +49,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
+// A store offset that is past the end of every buffer the kernels address:
+// the entry points refuse heads whose Q/K/V/O reach 2^31 bytes, and every
+// supported row is at least 128 bytes, so a head buffer ends at or below
+// 2^31 - 128 = 0x7fffff80.  Stores at kDropOffset - 16 i (i < 4) are
+// dropped by the buffer range check.
+constexpr int kDropOffset = 0x7ffffff0;
+
+// Compiler-only ordering point: memory operations are not moved across it
+// (no instruction is emitted).  Used where the issue order of loads decides
+// how exactly the compiler can count outstanding memory operations.
+__device__ __forceinline__ void mem_order_fence() { asm volatile("" ::: "memory"); }
+
 // Cache policy of the output stores: nt (streaming).  O is written once and
 // not read again by the path; with this policy its lines do not linger dirty
 // in the memory-side cache, where the next kernel of a step (the next span
