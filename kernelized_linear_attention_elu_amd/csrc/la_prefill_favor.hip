@@ -12,8 +12,9 @@
 // state, omega (fp32) enters as a bf16 hi + lo pair, so the projection is
 // accurate to ~2^-16 relative and the fp32 state that later spans read is
 // accurate; the output kernel rounds its feature tiles to bf16 anyway and
-// uses omega's hi part only.  Each wave owns 64 of the 256 features and
-// keeps its omega fragments in registers for the whole kernel.  The squared norm |u|^2 of
+// uses omega's hi part only.  Eight waves per workgroup (two per SIMD); each
+// wave owns 32 of the 256 features and keeps its omega fragments in
+// registers for the whole kernel.  The squared norm |u|^2 of
 // every token is summed in fp32 while the chunk is staged.  phi itself is
 // evaluated in fp32 as one exp2; features of tokens beyond N are zero.
 //
@@ -46,11 +47,13 @@ constexpr int FDV = 64;                   // value dimension
 constexpr int FC = 64;                    // chunk
 constexpr int FFT = FR / 16;              // feature tiles
 constexpr int FCT = FDV / 16;             // value tiles
-constexpr int FPW = FFT / kWaves;         // feature tiles owned by a wave in the projections
+constexpr int FNW = 8;                    // waves per workgroup (two per SIMD)
+constexpr int FNT = 64 * FNW;             // threads per workgroup
+constexpr int FPW = FFT / FNW;            // feature tiles owned by a wave in the projections
 constexpr int FE = FR * FDV + FR;         // floats per workspace slot
 constexpr int FVQ = FC * FD / 8;          // 16-byte vectors per raw chunk
-constexpr int FLQ = FVQ / kThreads;       // ... per thread
-static_assert(FVQ % kThreads == 0 && FDV == FD, "raw chunk tiles are 64 x 64 bf16");
+constexpr int FLQ = FVQ / FNT;            // ... per thread
+static_assert(FVQ % FNT == 0 && FDV == FD, "raw chunk tiles are 64 x 64 bf16");
 
 using T64 = Tile<bf16, 64>;
 using T256 = Tile<bf16, 256>;
@@ -114,7 +117,7 @@ __device__ __forceinline__ void load_raw(RawRegs<NS>& rr, const __amdgpu_buffer_
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < FLQ; ++i) {
-    const int vi = tid + i * kThreads;
+    const int vi = tid + i * FNT;
     const int off = ((t0 + vi / 8) * FD + (vi % 8) * 8) * 2;
 #pragma unroll
     for (int s = 0; s < NS; ++s) rr.x[s][i] = __builtin_amdgcn_raw_buffer_load_b128(src[s], off, 0, 0);
@@ -131,7 +134,7 @@ __device__ __forceinline__ void stage_raw(const RawRegs<NS>& rr, bf16* const (&d
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < FLQ; ++i) {
-    const int vi = tid + i * kThreads;
+    const int vi = tid + i * FNT;
     const int tok = vi / 8, col = (vi % 8) * 8;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -184,9 +187,9 @@ __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
 // ------------------------------------------------------------------ span state
 
 // dS = phi(K_span)^T V_span, dz = sum phi(K_span) -> workspace slot s.  Wave w
-// owns features 64 w .. 64 w + 63 (tiles j = 0..3) for all value tiles ct:
-// acc[j][ct] lane (g, li) holds S[f = 64 w + 16 j + li][c = 16 ct + 4 g + r].
-__global__ __launch_bounds__(kThreads, 1) void la_state_favor_kernel(const bf16* __restrict__ K,
+// owns features 32 w .. 32 w + 31 (tiles j = 0, 1) for all value tiles ct:
+// acc[j][ct] lane (g, li) holds S[f = 32 w + 16 j + li][c = 16 ct + 4 g + r].
+__global__ __launch_bounds__(FNT, 1) void la_state_favor_kernel(const bf16* __restrict__ K,
                                                                      const bf16* __restrict__ V,
                                                                      const float* __restrict__ omega,
                                                                      float* __restrict__ ws, int N, int n_span) {
@@ -286,11 +289,8 @@ struct SmemOutFavor {
   bf16 sq[FC * FR];   // phi(Q) of the chunk, [token][feature]
   bf16 sk[FC * FR];   // phi(K) of the chunk
   bf16 ss[FR * FDV];  // carried S, [feature][value]
-  float sz[FR];       // carried z
+  bf16 sz[3 * FR];    // carried z as rows: bf16 hi, lo = z - hi, zeros
 };
-
-// Feature of k-slot e of lane group g at k-step ks in the permuted order.
-__device__ __forceinline__ int pfeat(int ks, int g, int e) { return 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3); }
 
 // Operand fragment of one row of a [token][feature] phi tile in the permuted
 // feature order (two 8-byte LDS reads).
@@ -300,22 +300,33 @@ __device__ __forceinline__ bf16x8 prow_frag(const bf16* t, int row, int ks, int 
   return cat4(a, b);
 }
 
+// The same for one of the three (unswizzled) z rows.
+__device__ __forceinline__ bf16x8 zrow_frag(const bf16* z, int row, int ks, int g) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(z + row * FR + 32 * ks + 4 * g);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(z + row * FR + 32 * ks + 16 + 4 * g);
+  return cat4(a, b);
+}
+
 // Outputs of one span (carried state from the scanned slot when causal, the
 // full-sequence sums otherwise).  Per chunk: stage raw Q, K, V (double
-// buffered) -> barrier -> feature tiles of phi(Q), phi(K) and the carried
-// state -> LDS -> barrier -> outputs of row block w, then the state carry.
-// The carried state tiles follow the pointwise kernels' ownership: tile i of
-// wave w is value tile w, feature tile i.
+// buffered) -> barrier -> feature tiles of phi(Q), phi(K) (wave w: features
+// 32 w .. +31 of every token) and the carried state -> LDS -> barrier ->
+// outputs, then the state carry.  Outputs: the two waves w and w + 4 share
+// row block ib = w mod 4 (query tokens 16 ib + li); each forms the row
+// block's weights and denominator and produces value tiles 2 (w / 4) and
+// 2 (w / 4) + 1.  Carried state: wave w owns value tile w mod 4 and feature
+// tiles 8 (w / 4) .. +7, and z tiles w and w + 8.
 template <bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void la_output_favor_kernel(const bf16* __restrict__ Q,
-                                                                      const bf16* __restrict__ K,
-                                                                      const bf16* __restrict__ V,
-                                                                      bf16* __restrict__ O,
-                                                                      const float* __restrict__ omega,
-                                                                      const float* __restrict__ ws, int N,
-                                                                      int n_span) {
+__global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __restrict__ Q,
+                                                                 const bf16* __restrict__ K,
+                                                                 const bf16* __restrict__ V,
+                                                                 bf16* __restrict__ O,
+                                                                 const float* __restrict__ omega,
+                                                                 const float* __restrict__ ws, int N,
+                                                                 int n_span) {
   __shared__ SmemOutFavor sm;
-  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63;
+  int g = l >> 4, li = l & 15;
   const int bh = blockIdx.x / n_span;
   const int s = blockIdx.x % n_span;
   const int t_begin = span_begin64(s, n_span, N);
@@ -329,45 +340,58 @@ __global__ __launch_bounds__(kThreads, 1) void la_output_favor_kernel(const bf16
   OmegaFrags<false> om;  // phi tiles are rounded to bf16 here: omega hi suffices
   om.load(omega, w, g, li);
 
-  constexpr int TPW = FFT * FCT / kWaves;  // carried state tiles per wave (16)
-  constexpr int ZPW = FFT / kWaves;        // z tiles per wave (4)
+  constexpr int TPW = FFT * FCT / FNW;  // carried state tiles per wave (8)
+  constexpr int ZPW = FFT / FNW;        // z tiles per wave (2)
+  constexpr int OCT = FCT / 2;          // value tiles per wave in the outputs (2)
+  const int sct = w % FCT;              // value tile of this wave's carried state tiles
+  const int sft0 = TPW * (w / FCT);     // first feature tile of them
+  const int ib = w % 4;                 // output row block
+  const int oct0 = OCT * (w / 4);       // first output value tile
   const float* pre = ws + ((size_t)bh * (n_span + 1) + (CAUSAL ? s : n_span)) * FE;
   f32x4 sacc[TPW];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) sacc[i] = *reinterpret_cast<const f32x4*>(pre + (16 * i + li) * FDV + 16 * w + 4 * g);
+  for (int i = 0; i < TPW; ++i)
+    sacc[i] = *reinterpret_cast<const f32x4*>(pre + (16 * (sft0 + i) + li) * FDV + 16 * sct + 4 * g);
   f32x4 zt[ZPW];
 #pragma unroll
   for (int k = 0; k < ZPW; ++k) {
-    const float zv = pre[FR * FDV + 16 * (w + kWaves * k) + li];
+    const float zv = pre[FR * FDV + 16 * (w + FNW * k) + li];
     zt[k] = f32x4{zv, zv, zv, zv};
   }
-  const bf16 one = static_cast<bf16>(1.0f);
+  const bf16 one = static_cast<bf16>(1.0f), zero = static_cast<bf16>(0.0f);
   const bf16x8 ones = bf16x8{one, one, one, one, one, one, one, one};
+  const bf16 o1 = (li & 3) == 0 ? one : zero;
+  const bf16x8 ones_rows = bf16x8{o1, o1, o1, o1, o1, o1, o1, o1};  // rows 4m of the ones operand
+  const int zrow = min(li & 3, 2);                                    // z_hi, z_lo or zeros
 
   RawRegs<3> rr;
   load_raw<3>(rr, src, t_begin);
-  bf16x4 out[FCT];
+  bf16x4 out[OCT];
   int buf = 0;
   for (int t0 = t_begin; t0 < t_end; t0 += FC, buf ^= 1) {
+    // the lane coordinates are made opaque to the compiler once per chunk,
+    // so that the many per-lane LDS addresses derived from them are formed
+    // where they are used instead of being hoisted out of the loop and
+    // spilled (registers are tight at two waves per SIMD)
+    asm volatile("" : "+v"(g), "+v"(li));
     {
       bf16* const dst[3] = {sm.qraw[buf], sm.kraw[buf], sm.v[buf]};
       float* const nrm[3] = {sm.qn[buf], sm.kn[buf], nullptr};
       stage_raw<3>(rr, dst, nrm, CAUSAL ? 3 : 1);
     }
     if (t0 != t_begin) {
-      const int row = t0 - FC + 16 * w + li;
+      const int row = t0 - FC + 16 * ib + li;
 #pragma unroll
-      for (int ct = 0; ct < FCT; ++ct) {
+      for (int c = 0; c < OCT; ++c) {
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out[ct]), orsrc,
-                                              (row * FDV + 16 * ct + 4 * g) * 2, 0, kStreamStore);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out[c]), orsrc,
+                                              (row * FDV + 16 * (oct0 + c) + 4 * g) * 2, 0, kStreamStore);
       }
     }
     if (t0 + FC < t_end) load_raw<3>(rr, src, t0 + FC);
     __syncthreads();
 
-    // feature tiles: wave w computes features 64 w .. +63 of every token;
-    // lane (g, li) gets features 16 ft + 4 g + r of token 16 tb + li
+    // feature tiles: lane (g, li) gets features 16 ft + 4 g + r of token 16 tb + li
 #pragma unroll
     for (int j = 0; j < FPW; ++j) {
       const int ft = FPW * w + j;
@@ -394,29 +418,31 @@ __global__ __launch_bounds__(kThreads, 1) void la_output_favor_kernel(const bf16
     if (CAUSAL || t0 == t_begin) {
 #pragma unroll
       for (int i = 0; i < TPW; ++i)
-        *reinterpret_cast<bf16x4*>(sm.ss + T64::off(16 * i + li, 16 * w + 4 * g)) =
-            bf16x4{static_cast<bf16>(sacc[i][0]), static_cast<bf16>(sacc[i][1]), static_cast<bf16>(sacc[i][2]),
-                   static_cast<bf16>(sacc[i][3])};
-      if (g == 0) {
+        *reinterpret_cast<bf16x4*>(sm.ss + T64::off(16 * (sft0 + i) + li, 16 * sct + 4 * g)) = cvt_bf16x4(sacc[i]);
+      // lane group 0 writes z_hi, group 1 z_lo, group 2 the zero row
+      if (g < 3) {
 #pragma unroll
-        for (int k = 0; k < ZPW; ++k) sm.sz[16 * (w + kWaves * k) + li] = zt[k][0];
+        for (int k = 0; k < ZPW; ++k) {
+          const float z = zt[k][0];
+          const bf16 h = static_cast<bf16>(z);
+          const bf16 v = g == 0 ? h : g == 1 ? static_cast<bf16>(z - static_cast<float>(h)) : zero;
+          sm.sz[g * FR + 16 * (w + FNW * k) + li] = v;
+        }
       }
     }
     __syncthreads();
 
-    // ---- outputs of row block ib = w (query tokens 16 w + li)
-    const int ib = w;
+    // ---- outputs of row block ib, value tiles oct0, oct0 + 1
     bf16x8 qf[FR / 32];
-    float den = 0.f;
+    f32x4 dacc = zero4();  // [0] = z_hi . phi(q) + rowsum(weights), [1] = z_lo . phi(q)
 #pragma unroll
     for (int ks = 0; ks < FR / 32; ++ks) {
       qf[ks] = prow_frag(sm.sq, 16 * ib + li, ks, g);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) den += static_cast<float>(qf[ks][e]) * sm.sz[pfeat(ks, g, e)];
+      dacc = mfma16(zrow_frag(sm.sz, zrow, ks, g), qf[ks], dacc);
     }
-    f32x4 o[FCT];
+    f32x4 o[OCT];
 #pragma unroll
-    for (int ct = 0; ct < FCT; ++ct) o[ct] = zero4();
+    for (int c = 0; c < OCT; ++c) o[c] = zero4();
     if constexpr (CAUSAL) {
       // weights of key block jb: lane (g, li) holds A[i = li][j = 16 jb + 4 g + r];
       // the diagonal block is masked to j <= i by selection
@@ -424,12 +450,9 @@ __global__ __launch_bounds__(kThreads, 1) void la_output_favor_kernel(const bf16
         f32x4 t = zero4();
 #pragma unroll
         for (int ks = 0; ks < FR / 32; ++ks) t = mfma16(prow_frag(sm.sk, 16 * jb + li, ks, g), qf[ks], t);
+        if (jb == ib) {  // wave-uniform: only the diagonal block is masked
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = (jb == ib && 4 * g + r > li) ? 0.f : t[r];
-          x = round_op<bf16>(x);
-          t[r] = x;
-          den += x;
+          for (int r = 0; r < 4; ++r) t[r] = 4 * g + r > li ? 0.f : t[r];
         }
         return t;
       };
@@ -440,51 +463,50 @@ __global__ __launch_bounds__(kThreads, 1) void la_output_favor_kernel(const bf16
         const f32x4 a0 = weights(jb0);
         const bool two = jb1 <= ib;
         const f32x4 a1 = two ? weights(jb1) : zero4();
-        const bf16x8 bv = bf16x8{static_cast<bf16>(a0[0]), static_cast<bf16>(a0[1]), static_cast<bf16>(a0[2]),
-                                 static_cast<bf16>(a0[3]), static_cast<bf16>(a1[0]), static_cast<bf16>(a1[1]),
-                                 static_cast<bf16>(a1[2]), static_cast<bf16>(a1[3])};
+        const float w8[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        const bf16x8 bv = cvt_bf16x8(w8);
+        dacc = mfma16(ones_rows, bv, dacc);
 #pragma unroll
-        for (int ct = 0; ct < FCT; ++ct) {
+        for (int c = 0; c < OCT; ++c) {
+          const int ct = oct0 + c;
           const bf16x8 av = two ? tr_frag<64>(sm.v[buf], 16 * jb0 + 4 * g, 16 * jb1 + 4 * g, 16 * ct, li)
                                 : tr_frag_lo<64>(sm.v[buf], 16 * jb0 + 4 * g, 16 * ct, li);
-          o[ct] = mfma16(av, bv, o[ct]);
+          o[c] = mfma16(av, bv, o[c]);
         }
       }
     }
-    den = xor_sum16_32(den);
 #pragma unroll
-    for (int ct = 0; ct < FCT; ++ct)
+    for (int c = 0; c < OCT; ++c)
 #pragma unroll
       for (int ks = 0; ks < FR / 32; ++ks)
-        o[ct] = mfma16(tr_frag<64>(sm.ss, 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * ct, li), qf[ks], o[ct]);
-    const float rden = __builtin_amdgcn_rcpf(den);
+        o[c] = mfma16(tr_frag<64>(sm.ss, 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * (oct0 + c), li), qf[ks], o[c]);
+    const float rden = __builtin_amdgcn_rcpf(dacc[0] + dacc[1]);
 #pragma unroll
-    for (int ct = 0; ct < FCT; ++ct)
-      out[ct] = bf16x4{static_cast<bf16>(o[ct][0] * rden), static_cast<bf16>(o[ct][1] * rden),
-                       static_cast<bf16>(o[ct][2] * rden), static_cast<bf16>(o[ct][3] * rden)};
+    for (int c = 0; c < OCT; ++c) out[c] = cvt_bf16x4(o[c] * rden);
 
     // ---- state carry: S += phi(K_c)^T V_c, z += phi(K_c)^T 1 (bf16 features)
     if constexpr (CAUSAL) {
 #pragma unroll
       for (int ks = 0; ks < FC / 32; ++ks) {
         const int ra = 32 * ks + 8 * g;
-        const bf16x8 a = tr_frag<64>(sm.v[buf], ra, ra + 4, 16 * w, li);
+        const bf16x8 a = tr_frag<64>(sm.v[buf], ra, ra + 4, 16 * sct, li);
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) sacc[i] = mfma16(a, tr_frag<256>(sm.sk, ra, ra + 4, 16 * i, li), sacc[i]);
+        for (int i = 0; i < TPW; ++i)
+          sacc[i] = mfma16(a, tr_frag<256>(sm.sk, ra, ra + 4, 16 * (sft0 + i), li), sacc[i]);
 #pragma unroll
         for (int k = 0; k < ZPW; ++k)
-          zt[k] = mfma16(ones, tr_frag<256>(sm.sk, ra, ra + 4, 16 * (w + kWaves * k), li), zt[k]);
+          zt[k] = mfma16(ones, tr_frag<256>(sm.sk, ra, ra + 4, 16 * (w + FNW * k), li), zt[k]);
       }
     }
   }
   if (t_end > t_begin) {
     const int last = t_begin + ((t_end - t_begin - 1) / FC) * FC;
-    const int row = last + 16 * w + li;
+    const int row = last + 16 * ib + li;
 #pragma unroll
-    for (int ct = 0; ct < FCT; ++ct) {
+    for (int c = 0; c < OCT; ++c) {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out[ct]), orsrc,
-                                            (row * FDV + 16 * ct + 4 * g) * 2, 0, kStreamStore);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out[c]), orsrc,
+                                            (row * FDV + 16 * (oct0 + c) + 4 * g) * 2, 0, kStreamStore);
     }
   }
 }
@@ -510,7 +532,7 @@ hipError_t favor_prefill_launch(const PrefillArgs& a) {
   };
   rec(0);
   if (n_span > 0 && BH > 0)
-    hipLaunchKernelGGL(la_state_favor_kernel, dim3(BH * n_span), dim3(kThreads), 0, st, K, V, a.omega, ws, a.N,
+    hipLaunchKernelGGL(la_state_favor_kernel, dim3(BH * n_span), dim3(FNT), 0, st, K, V, a.omega, ws, a.N,
                        n_span);
   rec(1);
   rec(2);
@@ -520,10 +542,10 @@ hipError_t favor_prefill_launch(const PrefillArgs& a) {
   rec(4);
   if (n_span > 0 && BH > 0) {
     if (a.causal)
-      hipLaunchKernelGGL((la_output_favor_kernel<true>), dim3(BH * n_span), dim3(kThreads), 0, st, Q, K, V, O,
+      hipLaunchKernelGGL((la_output_favor_kernel<true>), dim3(BH * n_span), dim3(FNT), 0, st, Q, K, V, O,
                          a.omega, ws, a.N, n_span);
     else
-      hipLaunchKernelGGL((la_output_favor_kernel<false>), dim3(BH * n_span), dim3(kThreads), 0, st, Q, K, V, O,
+      hipLaunchKernelGGL((la_output_favor_kernel<false>), dim3(BH * n_span), dim3(FNT), 0, st, Q, K, V, O,
                          a.omega, ws, a.N, n_span);
   }
   rec(5);
