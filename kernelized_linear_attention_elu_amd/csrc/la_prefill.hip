@@ -84,6 +84,18 @@ struct Cfg {
   static_assert(CT % WPR == 0, "value tiles must split over the waves of a row block");
 };
 
+// State tile i of wave w: feature tile ft = w (the wave's own), value tile
+// ct = i.  Lane (g, li) of that tile holds S[f = 16 ft + li][c = 16 ct + 4 g
+// + r]; the wave's z tile is its feature tile too.  With its feature tile
+// fixed, a wave reads one phi(K) fragment per k-step and uses it for all of
+// its value tiles and its z tile.
+template <class CF>
+__device__ __forceinline__ void state_tile(int w, int i, int& ct, int& ft) {
+  static_assert(CF::NW == CF::FT && CF::TPW == CF::CT && CF::ZPW == 1, "one feature tile per wave");
+  ft = w;
+  ct = i;
+}
+
 // ------------------------------------------------------------------ staging
 
 template <class CF, bool WITH_Q>
@@ -193,12 +205,10 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typ
 
 // ------------------------------------------------------------------ state update
 
-// acc[i] += V_c^T phi(K_c) for the state tiles this wave owns, and
-// zt[k] += 1^T phi(K_c) for its z tiles.  Tile i of wave w is t = w + 4 i
-// with value tile ct = t % CT and feature tile ft = t / CT; lane (g, li)
-// ends up holding S[f = 16 ft + li][c = 16 ct + 4 g + r].  z tile k of wave w
-// covers features 16 (w + 4 k) + li (all four r hold the same sum).  With
-// sk_lo, the lo words are contracted as well (hi + lo = phi to ~2^-16).
+// acc[i] += V_c^T phi(K_c) for the state tiles this wave owns (state_tile:
+// feature tile w, value tile i), and zt[k] += 1^T phi(K_c) for its z tile
+// (features 16 w + li; all four r hold the same sum).  With sk_lo, the lo
+// words are contracted as well (hi + lo = phi to ~2^-16).
 template <class CF>
 __device__ __forceinline__ void state_mfma(f32x4 (&acc)[CF::TPW], f32x4 (&zt)[CF::ZPW],
                                            const typename CF::OP* sk, const typename CF::OP* sk_lo,
@@ -215,20 +225,20 @@ __device__ __forceinline__ void state_mfma(f32x4 (&acc)[CF::TPW], f32x4 (&zt)[CF
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
       const int ra = ks * 32 + 8 * g;
+      // the wave's feature tile (state_tile): one phi(K) fragment (and its
+      // lo word) per k-step, shared by every value tile and the z tile
+      const bf16x8 kh = kfrag(sk, ra, w);
+      const bf16x8 kl = sk_lo ? kfrag(sk_lo, ra, w) : kh;
 #pragma unroll
       for (int i = 0; i < CF::TPW; ++i) {
-        const int t = w + CF::NW * i;
-        const int ct = t % CF::CT, ft = t / CF::CT;
+        int ct, ft;
+        state_tile<CF>(w, i, ct, ft);
         const bf16x8 a = CF::C >= 32 ? tr_frag<DV>(sv, ra, ra + 4, 16 * ct, li) : tr_frag_lo<DV>(sv, 4 * g, 16 * ct, li);
-        acc[i] = mfma16(a, kfrag(sk, ra, ft), acc[i]);
-        if (sk_lo) acc[i] = mfma16(a, kfrag(sk_lo, ra, ft), acc[i]);
+        acc[i] = mfma16(a, kh, acc[i]);
+        if (sk_lo) acc[i] = mfma16(a, kl, acc[i]);
       }
-#pragma unroll
-      for (int k = 0; k < CF::ZPW; ++k) {
-        const int ft = w + CF::NW * k;
-        zt[k] = mfma16(ones, kfrag(sk, ra, ft), zt[k]);
-        if (sk_lo) zt[k] = mfma16(ones, kfrag(sk_lo, ra, ft), zt[k]);
-      }
+      zt[0] = mfma16(ones, kh, zt[0]);
+      if (sk_lo) zt[0] = mfma16(ones, kl, zt[0]);
     }
   } else {
     using TQ = Tile<OP, R>;
@@ -238,8 +248,8 @@ __device__ __forceinline__ void state_mfma(f32x4 (&acc)[CF::TPW], f32x4 (&zt)[CF
       const int row = ks * 4 + g;
 #pragma unroll
       for (int i = 0; i < CF::TPW; ++i) {
-        const int t = w + CF::NW * i;
-        const int ct = t % CF::CT, ft = t / CF::CT;
+        int ct, ft;
+        state_tile<CF>(w, i, ct, ft);
         acc[i] = mfma16(sv[TV::off(row, 16 * ct + li)], sk[TQ::off(row, 16 * ft + li)], acc[i]);
       }
 #pragma unroll
@@ -601,8 +611,8 @@ __device__ __forceinline__ void publish_state(const f32x4 (&sacc)[CF::TPW], cons
   using TS = Tile<OP, CF::DV>;
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
-    const int t = w + CF::NW * i;
-    const int ct = t % CF::CT, ft = t / CF::CT;
+    int ct, ft;
+    state_tile<CF>(w, i, ct, ft);
     OP* dst = ss + TS::off(16 * ft + li, 16 * ct + 4 * g);
     if constexpr (sizeof(OP) == 2) {
       *reinterpret_cast<bf16x4*>(dst) = cvt_bf16x4(sacc[i]);
@@ -740,8 +750,8 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
   float* slot = ws + ((size_t)bh * (n_span + 1) + s) * E;
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
-    const int t = w + CF::NW * i;
-    const int ct = t % CF::CT, ft = t / CF::CT;
+    int ct, ft;
+    state_tile<CF>(w, i, ct, ft);
     *reinterpret_cast<f32x4*>(slot + (16 * ft + li) * CF::DV + 16 * ct + 4 * g) = acc[i];
   }
   if (g == 0) {
@@ -820,8 +830,8 @@ __global__ __launch_bounds__(CF::NT, CF::MINB) void la_output_kernel(const typen
   f32x4 sacc[CF::TPW];
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
-    const int t = w + CF::NW * i;
-    const int ct = t % CF::CT, ft = t / CF::CT;
+    int ct, ft;
+    state_tile<CF>(w, i, ct, ft);
     sacc[i] = *reinterpret_cast<const f32x4*>(pre + (16 * ft + li) * CF::DV + 16 * ct + 4 * g);
   }
   f32x4 zt[CF::ZPW];
@@ -942,8 +952,8 @@ __device__ __forceinline__ void slot_store(float* slot, const f32x4 (&S)[CF::TPW
   const __amdgpu_buffer_rsrc_t r = make_rsrc(slot, (CF::R * CF::DV + CF::R) * 4);
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
-    const int t = w + CF::NW * i;
-    const int ct = t % CF::CT, ft = t / CF::CT;
+    int ct, ft;
+    state_tile<CF>(w, i, ct, ft);
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S[i]), r,
                                            ((16 * ft + li) * CF::DV + 16 * ct + 4 * g) * 4, 0, kDeviceScope);
   }
@@ -962,8 +972,8 @@ __device__ __forceinline__ void slot_add(const float* slot, f32x4 (&S)[CF::TPW],
   const __amdgpu_buffer_rsrc_t r = make_rsrc(slot, (CF::R * CF::DV + CF::R) * 4);
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
-    const int t = w + CF::NW * i;
-    const int ct = t % CF::CT, ft = t / CF::CT;
+    int ct, ft;
+    state_tile<CF>(w, i, ct, ft);
     S[i] += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                           r, ((16 * ft + li) * CF::DV + 16 * ct + 4 * g) * 4, 0, kDeviceScope));
   }
@@ -981,8 +991,8 @@ __device__ __forceinline__ void state_add(const float* Sm, const float* zv, f32x
                                           f32x4 (&z)[CF::ZPW], int w, int g, int li) {
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
-    const int t = w + CF::NW * i;
-    const int ct = t % CF::CT, ft = t / CF::CT;
+    int ct, ft;
+    state_tile<CF>(w, i, ct, ft);
     S[i] += *reinterpret_cast<const f32x4*>(Sm + (16 * ft + li) * CF::DV + 16 * ct + 4 * g);
   }
 #pragma unroll
@@ -1089,8 +1099,8 @@ __global__ __launch_bounds__(CF::NT, 2) void la_fused_kernel(
       // the final state S_N, z_N (z_out rows use the same ownership)
 #pragma unroll
       for (int i = 0; i < CF::TPW; ++i) {
-        const int t = w + CF::NW * i;
-        const int ct = t % CF::CT, ft = t / CF::CT;
+        int ct, ft;
+        state_tile<CF>(w, i, ct, ft);
         *reinterpret_cast<f32x4*>(S_out + (size_t)bh * CF::R * CF::DV + (16 * ft + li) * CF::DV + 16 * ct + 4 * g) =
             is[i];
       }
