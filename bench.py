@@ -107,6 +107,8 @@ def parse_args(argv=None):
     p.add_argument("--workload", default="long",
                    choices=["long", "prefill", "wide", "favor", "decode", "feature", "copy"])
     p.add_argument("--noncausal", action="store_true", help="non-causal prefill")
+    p.add_argument("--decay", action="store_true",
+                   help="causal prefill with a fixed per-head decay (RetNet form, la_forward_decay)")
     p.add_argument("--chunk", type=int, default=None,
                    help="chunk size (default: the workload's, 0 = the library's choice)")
     p.add_argument("--settle", type=float, default=SETTLE_S,
@@ -128,13 +130,17 @@ def cpu_info():
     return model
 
 
-def time_oracle_prefill(q, k, v, causal, max_heads, phi="elu1", omega=None):
-    """fp64 oracle (token recurrence, or the reassociated non-causal form) on
-    the first ``max_heads`` heads of batch 0; returns (seconds, heads, cores)."""
+def time_oracle_prefill(q, k, v, causal, max_heads, phi="elu1", omega=None, gamma=None):
+    """fp64 oracle (token recurrence, decayed when ``gamma`` is given, or the
+    reassociated non-causal form) on the first ``max_heads`` heads of batch 0;
+    returns (seconds, heads, cores)."""
     from oracle import linear_attention as ora
+    from oracle import decay as dec
     h = min(max_heads, q.shape[1])
     t0, c0 = time.perf_counter(), time.process_time()
-    if causal:
+    if gamma is not None:
+        dec.recurrent_decay(q[:1, :h], k[:1, :h], v[:1, :h], gamma[:h].astype("float64"), phi=phi)
+    elif causal:
         ora.recurrent_attention(q[:1, :h], k[:1, :h], v[:1, :h], phi=phi, omega=omega)
     else:
         ora.noncausal_attention(q[:1, :h], k[:1, :h], v[:1, :h], phi=phi, omega=omega)
@@ -149,8 +155,11 @@ def bench_prefill(args, torch, la, synth):
     if args.chunk is not None:
         w = dataclasses.replace(w, chunk=args.chunk)
     causal = not args.noncausal
+    if args.decay and (not causal or w.phi == "favor"):
+        raise SystemExit("--decay: causal pointwise-feature workloads only")
     dev = torch.device("cuda:0")
     q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
+    gamma = synth.decay_gammas(w.H) if args.decay else None
 
     def to_dev(x):
         return hostio.upload_bf16_bits(synth.bf16_bits(x), dev)
@@ -163,6 +172,7 @@ def bench_prefill(args, torch, la, synth):
     outs = [torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.bfloat16, device=dev) for _ in range(ROTATE)]
     omega = synth.draw_omega(w.r, w.d) if w.phi == "favor" else None
     om_dev = hostio.upload_f32(omega, dev) if omega is not None else None
+    gamma_dev = hostio.upload_f32(gamma, dev) if gamma is not None else None
     ws = torch.empty(la.workspace_bytes(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
                                         chunk=w.chunk),
                      dtype=torch.uint8, device=dev)
@@ -170,7 +180,7 @@ def bench_prefill(args, torch, la, synth):
     def step(i, events=None):
         Q, K, V = sets[i % ROTATE]
         la.forward(Q, K, V, phi=w.phi, omega=om_dev, causal=causal, chunk=w.chunk, out=outs[i % ROTATE],
-                   workspace=ws, events=events)
+                   workspace=ws, events=events, gamma=gamma_dev)
 
     for i in range(args.warmup):
         step(i)
@@ -212,7 +222,7 @@ def bench_prefill(args, torch, la, synth):
     alg_flops = token_heads * (feat_flops + 4 * w.r * w.dv + (2 * w.chunk * (w.r + w.dv) if causal else 0))
     out_ms = out_live_ms
     n_span, single_pass = la.forward_config(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
-                                            chunk=w.chunk)
+                                            chunk=w.chunk, decay=gamma is not None)
     names = (FAVOR_KERNEL_NAMES if w.phi == "favor" else FUSED_KERNEL_NAMES if single_pass else KERNEL_NAMES)
     out_kernel = names[2]
     traffic = read_traffic(args.workload + ("" if causal else "_noncausal"), out_kernel)
@@ -248,9 +258,10 @@ def bench_prefill(args, torch, la, synth):
         "config": {
             "workload": f"{w.name} prefill B{w.B} H{w.H} N{w.N} d{w.d} dv{w.dv} bf16 I/O, fp32 state, "
                         f"phi={'FAVOR+ r=%d' % w.r if w.phi == 'favor' else 'elu+1'}, "
-                        f"{'causal' if causal else 'non-causal'}, chunk {w.chunk}",
+                        f"{'causal' if causal else 'non-causal'}, chunk {w.chunk}"
+                        + (", per-head decay gamma_h = 1 - 2^-(5 + 7h/(H-1)) (RetNet form)" if gamma is not None else ""),
             "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv, "r": w.r, "chunk": w.chunk, "causal": causal,
-            "phi": w.phi, "accumulate": "fp32",
+            "phi": w.phi, "accumulate": "fp32", "decay": gamma is not None,
         },
         "roofline": roof,
         "path_roofline": {
@@ -267,7 +278,7 @@ def bench_prefill(args, torch, la, synth):
         "settle": {"seconds": args.settle, "untimed_steps": settled},
     }
     if not args.no_cpu_baseline:
-        wall, h, cores = time_oracle_prefill(q, k, v, causal, max_heads=w.H, phi=w.phi, omega=omega)
+        wall, h, cores = time_oracle_prefill(q, k, v, causal, max_heads=w.H, phi=w.phi, omega=omega, gamma=gamma)
         # the sample covers h of the B*H heads at full length: scale to the job
         per_job = wall * (w.B * w.H) / h
         res["cpu_baseline"] = {
@@ -275,7 +286,7 @@ def bench_prefill(args, torch, la, synth):
             "unit": "tokens/s",
             "cores": cores,
             "kind": "oracle",
-            "sample": f"fp64 {'token recurrence' if causal else 'reassociated form'} over {h} of "
+            "sample": f"fp64 {('decayed token recurrence' if gamma is not None else 'token recurrence') if causal else 'reassociated form'} over {h} of "
                       f"{w.B * w.H} heads x {w.N} tokens ({wall:.1f} s), scaled to the full job",
             "cpu": cpu_info(),
         }

@@ -13,7 +13,12 @@
  *     linear-attention-kernel page; "Why is linear attention an RNN" of the
  *     linear-attention-and-SSM page).  Token t attends to itself;
  *   - non-causal: S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j),
- *     O = phi(Q) S / phi(Q) z ("Efficient attention variants" sec. 4).
+ *     O = phi(Q) S / phi(Q) z ("Efficient attention variants" sec. 4);
+ *   - causal with a fixed per-head decay gamma (RetNet form, "Efficient
+ *     attention variants" sec. 7.1): S_t = gamma S_{t-1} + phi(k_t) v_t^T,
+ *     z_t = gamma z_{t-1} + phi(k_t), read out normalised as above or, with
+ *     normalize = 0, as o_t = phi(q_t)^T S_t (the page's form with the
+ *     identity map).
  *
  * Conventions shared by every call
  *   - Tensors are contiguous row-major device buffers owned by the caller:
@@ -43,7 +48,9 @@
  *       la_forward: d = d_v in {64, 128} with ELU1/IDENTITY (bf16), d = d_v = 64
  *       (fp32); chunk in {16, 32, 64, 128} (bf16 d = 64), {16, 32, 64} otherwise;
  *       any N >= 0, any B, H >= 0.
+ *       la_forward_decay: as la_forward for ELU1/IDENTITY (no FAVOR+).
  *       la_decode_step: d = d_v in {64, 128}; FAVOR+ with r = 256.
+ *       la_decode_step_decay: d = d_v in {64, 128}, ELU1/IDENTITY.
  *       la_feature_map: ELU1/IDENTITY with d % 8 == 0; FAVOR+ with d in {64, 128},
  *       r = 256.
  */
@@ -151,6 +158,51 @@ la_status la_forward_timed(const void *Q, const void *K, const void *V, void *O,
 la_status la_decode_step(const float *S, const float *z, const void *q, const void *k, const void *v, void *o,
                          float *S_new, float *z_new, int B, int H, int d, int d_v, int io_dtype, int phi, int r,
                          const float *omega, void *stream);
+
+/*
+ * Causal prefill with a fixed per-head decay ("Efficient attention variants"
+ * sec. 7.1, RetNet): S_t = gamma_h S_{t-1} + phi(k_t) v_t^T,
+ * z_t = gamma_h z_{t-1} + phi(k_t), so that token j enters o_t with weight
+ * gamma_h^(t-j) phi(q_t).phi(k_j); o_t = phi(q_t)^T S_t / phi(q_t)^T z_t, or
+ * phi(q_t)^T S_t when normalize = 0.  gamma_h = 1 gives la_forward's causal
+ * result.  An initial state S0, z0 is decayed like any earlier token: it
+ * enters o_t (0-based) with gamma_h^(t+1).
+ *   gamma     in: device fp32 [H], one decay per head (shared by the B
+ *             sequences), each in (0, 1]; other values are not rejected
+ *             (they are not read on the host) and give undefined results.
+ *   normalize 1 (divide by phi(q)^T z) or 0.
+ *   The other arguments are la_forward's with causal = 1 and no omega
+ *   (FAVOR+ returns LA_ERR_UNSUPPORTED).  The workspace
+ *   la_forward_workspace_bytes(..., causal = 1, chunk) returns is enough.
+ * Errors: as la_forward; LA_ERR_NULL for a NULL gamma.
+ */
+la_status la_forward_decay(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int d,
+                           int d_v, int io_dtype, int phi, int r, const float *gamma, int normalize, int chunk,
+                           const float *S0, const float *z0, float *S_out, float *z_out, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Spans per head la_forward_decay uses for this shape (*n_span; may be NULL);
+ * errors as its shape checks.  No device work. */
+la_status la_forward_decay_config(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk,
+                                  int *n_span);
+
+/* la_forward_decay plus timing events, as la_forward_timed. */
+la_status la_forward_decay_timed(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int d,
+                                 int d_v, int io_dtype, int phi, int r, const float *gamma, int normalize, int chunk,
+                                 const float *S0, const float *z0, float *S_out, float *z_out, void *workspace,
+                                 size_t workspace_bytes, void *stream, void *const *events);
+
+/*
+ * Decode step with a fixed per-head decay (sec. 7.1):
+ *   S_new = gamma_h S + phi(k) v^T, z_new = gamma_h z + phi(k),
+ *   o = phi(q)^T S_new / phi(q)^T z_new (normalize = 1) or phi(q)^T S_new.
+ * gamma: device fp32 [H] in (0, 1]; other arguments as la_decode_step
+ * (ELU1/IDENTITY only).
+ * Errors: as la_decode_step; LA_ERR_NULL for a NULL gamma.
+ */
+la_status la_decode_step_decay(const float *S, const float *z, const void *q, const void *k, const void *v,
+                               void *o, float *S_new, float *z_new, int B, int H, int d, int d_v, int io_dtype,
+                               int phi, int r, const float *gamma, int normalize, void *stream);
 
 /*
  * Standalone feature map: Y[i] = phi(X[i]) for rows i = 0..rows-1.

@@ -38,6 +38,10 @@ _SIGS = {
     "la_forward": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
     "la_forward_timed": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp, _vp]),
     "la_decode_step": (_i, [_vp] * 8 + [_i] * 7 + [_vp, _vp]),
+    "la_forward_decay_config": (_i, [_i] * 9 + [ctypes.POINTER(_i)]),
+    "la_forward_decay": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
+    "la_forward_decay_timed": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp, _vp]),
+    "la_decode_step_decay": (_i, [_vp] * 8 + [_i] * 7 + [_vp, _i, _vp]),
     "la_feature_map": (_i, [_vp, _vp, ctypes.c_longlong, _i, _i, _i, _i, _vp, _vp]),
     "la_status_string": (ctypes.c_char_p, [_i]),
     "la_version": (_i, []),
@@ -156,23 +160,44 @@ def workspace_bytes(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chu
     return int(load_library().la_forward_workspace_bytes(B, H, N, d, dv, io_code, PHI[phi], r, int(causal), chunk))
 
 
-def forward_config(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64):
-    """(n_span, single_pass) that la_forward uses for this shape."""
+def forward_config(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64, decay=False):
+    """(n_span, single_pass) that la_forward (la_forward_decay with
+    ``decay``) uses for this shape."""
     io_code = LA_BF16 if io == "bf16" else LA_F32
     n, sp = ctypes.c_int(), ctypes.c_int()
+    if decay:
+        _check(load_library().la_forward_decay_config(B, H, N, d, dv, io_code, PHI[phi], r, chunk, ctypes.byref(n)),
+               "la_forward_decay_config")
+        return n.value, False
     _check(load_library().la_forward_config(B, H, N, d, dv, io_code, PHI[phi], r, int(causal), chunk,
                                             ctypes.byref(n), ctypes.byref(sp)), "la_forward_config")
     return n.value, bool(sp.value)
 
 
+def _gamma_arg(gamma, H, dev, causal=True):
+    """Per-head decay: a fp32 device tensor of H values (or None)."""
+    if gamma is None:
+        return None
+    torch = _torch()
+    if not causal:
+        raise ValueError("the decay is defined for the causal form only")
+    _require(gamma, "gamma", torch.float32, dev)
+    if tuple(gamma.shape) != (H,):
+        raise ValueError(f"gamma must have shape ({H},), got {tuple(gamma.shape)}")
+    return gamma
+
+
 def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, z0=None,
-            return_state=False, out=None, workspace=None, events=None):
+            return_state=False, out=None, workspace=None, events=None, gamma=None, normalize=True):
     """Causal (or non-causal) linear attention over Q, K [B,H,N,d], V [B,H,N,dv].
 
     Returns O [B,H,N,dv] (same dtype as Q); with ``return_state`` also the
     final state S_N [B,H,r,dv] and z_N [B,H,r] (fp32).  ``S0``/``z0`` give an
     initial state.  ``events``: optional list of 2*LA_FORWARD_KERNELS event
     handles from :func:`event_create` recorded around the library's kernels.
+    ``gamma``: optional fp32 device tensor [H] of per-head decays in (0, 1]
+    (causal only; la_forward_decay), with ``normalize=False`` for the
+    unnormalised read-out.
     """
     torch = _torch()
     lib = load_library()
@@ -203,25 +228,39 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
     if return_state:
         S_out = torch.empty((B, H, r, dv), dtype=torch.float32, device=dev)
         z_out = torch.empty((B, H, r), dtype=torch.float32, device=dev)
+    gamma = _gamma_arg(gamma, H, dev, causal)
+    if gamma is None and not normalize:
+        raise ValueError("normalize=False is available with a decay (gamma) only")
     need = int(lib.la_forward_workspace_bytes(B, H, N, d, dv, io, PHI[phi], r, int(causal), chunk))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    args = [_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, d, dv, io, PHI[phi], r, _ptr(omega),
-            int(causal), chunk, _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(workspace),
+    tail = [chunk, _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(dev)]
+    head = [_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, d, dv, io, PHI[phi], r]
+    if gamma is None:
+        args = head + [_ptr(omega), int(causal)] + tail
+        fn, name = (lib.la_forward, "la_forward") if events is None else (lib.la_forward_timed, "la_forward_timed")
+    else:
+        if phi == "favor":
+            raise ValueError("the decay is available for the pointwise feature maps only")
+        args = head + [_ptr(gamma), int(bool(normalize))] + tail
+        fn, name = ((lib.la_forward_decay, "la_forward_decay") if events is None
+                    else (lib.la_forward_decay_timed, "la_forward_decay_timed"))
     if events is None:
-        _check(lib.la_forward(*args), "la_forward")
+        _check(fn(*args), name)
     else:
         arr = (ctypes.c_void_p * (2 * LA_FORWARD_KERNELS))(*events)
-        _check(lib.la_forward_timed(*args, arr), "la_forward_timed")
+        _check(fn(*args, arr), name)
     if return_state:
         return out, S_out, z_out
     return out
 
 
-def decode_step(S, z, q, k, v, *, phi="elu1", omega=None, inplace=True, out=None):
+def decode_step(S, z, q, k, v, *, phi="elu1", omega=None, inplace=True, out=None, gamma=None, normalize=True):
     """One decode step for every (batch, head): S, z updated in place (or new
-    tensors when ``inplace=False``).  Returns o, or (o, S_new, z_new)."""
+    tensors when ``inplace=False``).  Returns o, or (o, S_new, z_new).
+    ``gamma``: optional fp32 device tensor [H] of per-head decays
+    (la_decode_step_decay), with ``normalize=False`` for o = phi(q)^T S'."""
     torch = _torch()
     lib = load_library()
     B, H, d = q.shape
@@ -243,10 +282,19 @@ def decode_step(S, z, q, k, v, *, phi="elu1", omega=None, inplace=True, out=None
     _require(out, "out", q.dtype, dev)
     if tuple(out.shape) != (B, H, dv):
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, dv)}")
+    gamma = _gamma_arg(gamma, H, dev)
+    if gamma is None and not normalize:
+        raise ValueError("normalize=False is available with a decay (gamma) only")
     S_new, z_new = (S, z) if inplace else (torch.empty_like(S), torch.empty_like(z))
-    st = lib.la_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_new), _ptr(z_new),
-                            B, H, d, dv, _io_code(q), PHI[phi], r, _ptr(omega), _stream(dev))
-    _check(st, "la_decode_step")
+    if gamma is None:
+        st = lib.la_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_new),
+                                _ptr(z_new), B, H, d, dv, _io_code(q), PHI[phi], r, _ptr(omega), _stream(dev))
+        _check(st, "la_decode_step")
+    else:
+        st = lib.la_decode_step_decay(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_new),
+                                      _ptr(z_new), B, H, d, dv, _io_code(q), PHI[phi], r, _ptr(gamma),
+                                      int(bool(normalize)), _stream(dev))
+        _check(st, "la_decode_step_decay")
     return out if inplace else (out, S_new, z_new)
 
 

@@ -42,8 +42,10 @@ int norm_chunk(int chunk) { return chunk == 0 ? 64 : chunk; }
 // the span length.
 constexpr int kCUs = 256;
 
-int output_occupancy(int io, int phi, int d, int chunk, int causal) {
+int output_occupancy(int io, int phi, int d, int chunk, int causal, int decay) {
   if (phi == LA_PHI_FAVOR) return 1;
+  // with a decay the output kernel runs two workgroups per CU at d = 64
+  if (decay) return (d == 64 && chunk <= 64) ? 2 : 1;
   // the non-causal output kernel holds only Q chunks and the shared sums
   if (!causal && io == LA_BF16 && d == 64) return 6;
   if (d == 64) {
@@ -53,7 +55,7 @@ int output_occupancy(int io, int phi, int d, int chunk, int causal) {
   return 1;  // d = 128: one workgroup of eight waves per CU
 }
 
-int choose_n_span(long long BH, int N, int chunk, int d, int io, int phi, int causal) {
+int choose_n_span(long long BH, int N, int chunk, int d, int io, int phi, int causal, int decay) {
   if (N <= 0) return 0;
   const long long n_chunks = (static_cast<long long>(N) + chunk - 1) / chunk;
   const char* env = getenv("LA_SPAN");
@@ -61,7 +63,7 @@ int choose_n_span(long long BH, int N, int chunk, int d, int io, int phi, int ca
     const long v = strtol(env, nullptr, 10);
     if (v >= chunk && v % chunk == 0 && v <= (1 << 24)) return static_cast<int>((N + v - 1) / v);
   }
-  const long long slots = static_cast<long long>(kCUs) * output_occupancy(io, phi, d, chunk, causal);
+  const long long slots = static_cast<long long>(kCUs) * output_occupancy(io, phi, d, chunk, causal, decay);
   long long n = (slots + BH - 1) / (BH > 0 ? BH : 1);
   const long long cap = n_chunks / 4 > 0 ? n_chunks / 4 : 1;
   if (n > cap) n = cap;
@@ -96,13 +98,15 @@ bool use_fused(int io, int phi, int d, int d_v, int r, int causal, int chunk, in
   return env && env[0] == '1';
 }
 
+// decay: a fixed per-head decay is requested (causal, pointwise maps only).
 la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int phi, int r, int causal, int chunk,
-                              Shape* sh) {
+                              Shape* sh, int decay = 0) {
   if (B < 0 || H < 0 || N < 0 || d <= 0 || d_v <= 0 || r < 0 || chunk < 0) return LA_ERR_SHAPE;
   if (d > kMaxDim || d_v > kMaxDim || r > kMaxDim) return LA_ERR_SHAPE;
   if (io != LA_F32 && io != LA_BF16) return LA_ERR_UNSUPPORTED;
   if (phi != LA_PHI_ELU1 && phi != LA_PHI_FAVOR && phi != LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return LA_ERR_UNSUPPORTED;
+  if (decay && (phi == LA_PHI_FAVOR || !causal)) return LA_ERR_UNSUPPORTED;
   const int rr = norm_r(phi, d, r);
   const int ch = norm_chunk(chunk);
   if (!la::prefill_supported(io, phi, d, d_v, rr, ch)) return LA_ERR_UNSUPPORTED;
@@ -113,8 +117,9 @@ la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int p
   // workgroups) must fit a 32-bit launch
   const long long row = static_cast<long long>(d > d_v ? d : d_v) * (io == LA_BF16 ? 2 : 4);
   if (static_cast<long long>(N) * row >= (1LL << 31)) return LA_ERR_SHAPE;
-  const int fused = use_fused(io, phi, d, d_v, rr, causal, ch, N) ? 1 : 0;
-  const int n_span = fused ? (N + la::kFusedSpan - 1) / la::kFusedSpan : choose_n_span(BH, N, ch, d, io, phi, causal);
+  const int fused = !decay && use_fused(io, phi, d, d_v, rr, causal, ch, N) ? 1 : 0;
+  const int n_span =
+      fused ? (N + la::kFusedSpan - 1) / la::kFusedSpan : choose_n_span(BH, N, ch, d, io, phi, causal, decay);
   if (BH * n_span > 0x7fffffffLL) return LA_ERR_SHAPE;
   sh->B = B; sh->H = H; sh->N = N; sh->d = d; sh->dv = d_v; sh->r = rr; sh->phi = phi;
   sh->causal = causal; sh->chunk = ch; sh->n_span = n_span; sh->fused = fused; sh->BH = BH;
@@ -130,16 +135,17 @@ size_t workspace_for(const Shape& sh) {
 la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
                        int d_v, int io, int phi, int r, const float* omega, int causal, int chunk, const float* S0,
                        const float* z0, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
-                       void* stream, void* const* events) {
+                       void* stream, void* const* events, const float* gamma = nullptr, int normalize = 1) {
   Shape sh;
-  la_status st = check_forward_shape(B, H, N, d, d_v, io, phi, r, causal, chunk, &sh);
+  const int decay = gamma != nullptr;
+  la_status st = check_forward_shape(B, H, N, d, d_v, io, phi, r, causal, chunk, &sh, decay);
   if (st != LA_OK) return st;
   const bool have_tokens = sh.BH > 0 && N > 0;
   if (have_tokens && (!Q || !K || !V || !O)) return LA_ERR_NULL;
   if (phi == LA_PHI_FAVOR && !omega) return LA_ERR_NULL;
   if ((S0 == nullptr) != (z0 == nullptr)) return LA_ERR_NULL;
   if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_NULL;
-  const void* ptrs[] = {Q, K, V, O, omega, S0, z0, S_out, z_out, workspace};
+  const void* ptrs[] = {Q, K, V, O, omega, S0, z0, S_out, z_out, workspace, gamma};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return LA_ERR_ALIGN;
   const size_t need = workspace_for(sh);
@@ -153,6 +159,7 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
   a.chunk = sh.chunk; a.n_span = sh.n_span; a.fused = sh.fused; a.group = fused_group();
   a.S0 = S0; a.z0 = z0; a.S_out = S_out; a.z_out = z_out;
   a.workspace = workspace; a.stream = stream; a.events = events;
+  a.gamma = gamma; a.normalize = normalize;
   return hip_status(la::prefill_launch(a));
 }
 
@@ -177,6 +184,15 @@ la_status la_forward_config(int B, int H, int N, int d, int d_v, int io_dtype, i
   return LA_OK;
 }
 
+la_status la_forward_decay_config(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk,
+                                  int* n_span) {
+  Shape sh;
+  const la_status st = check_forward_shape(B, H, N, d, d_v, io_dtype, phi, r, 1, chunk, &sh, 1);
+  if (st != LA_OK) return st;
+  if (n_span) *n_span = sh.n_span;
+  return LA_OK;
+}
+
 la_status la_forward(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d, int d_v,
                      int io_dtype, int phi, int r, const float* omega, int causal, int chunk, const float* S0,
                      const float* z0, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
@@ -193,9 +209,11 @@ la_status la_forward_timed(const void* Q, const void* K, const void* V, void* O,
                       workspace, workspace_bytes, stream, events);
 }
 
-la_status la_decode_step(const float* S, const float* z, const void* q, const void* k, const void* v, void* o,
-                         float* S_new, float* z_new, int B, int H, int d, int d_v, int io_dtype, int phi, int r,
-                         const float* omega, void* stream) {
+namespace {
+
+la_status decode_impl(const float* S, const float* z, const void* q, const void* k, const void* v, void* o,
+                      float* S_new, float* z_new, int B, int H, int d, int d_v, int io_dtype, int phi, int r,
+                      const float* omega, void* stream, const float* gamma, int normalize) {
   if (B < 0 || H < 0 || d <= 0 || d_v <= 0 || r < 0) return LA_ERR_SHAPE;
   if (static_cast<long long>(B) * H > 0x7fffffffLL) return LA_ERR_SHAPE;
   if (io_dtype != LA_F32 && io_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
@@ -205,15 +223,53 @@ la_status la_decode_step(const float* S, const float* z, const void* q, const vo
   const long long BH = static_cast<long long>(B) * H;
   if (BH > 0 && (!S || !z || !q || !k || !v || !o || !S_new || !z_new)) return LA_ERR_NULL;
   if (phi == LA_PHI_FAVOR && !omega) return LA_ERR_NULL;
-  const void* ptrs[] = {S, z, q, k, v, o, S_new, z_new, omega};
+  const void* ptrs[] = {S, z, q, k, v, o, S_new, z_new, omega, gamma};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return LA_ERR_ALIGN;
   if (BH == 0) return LA_OK;
   la::DecodeArgs a;
   a.S = S; a.z = z; a.q = q; a.k = k; a.v = v; a.o = o; a.S_new = S_new; a.z_new = z_new;
   a.B = B; a.H = H; a.d = d; a.dv = d_v; a.r = rr; a.io = io_dtype; a.phi = phi; a.omega = omega;
-  a.stream = stream;
+  a.stream = stream; a.gamma = gamma; a.normalize = normalize;
   return hip_status(la::decode_launch(a));
+}
+
+}  // namespace
+
+la_status la_decode_step(const float* S, const float* z, const void* q, const void* k, const void* v, void* o,
+                         float* S_new, float* z_new, int B, int H, int d, int d_v, int io_dtype, int phi, int r,
+                         const float* omega, void* stream) {
+  return decode_impl(S, z, q, k, v, o, S_new, z_new, B, H, d, d_v, io_dtype, phi, r, omega, stream, nullptr, 1);
+}
+
+la_status la_forward_decay(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+                           int d_v, int io_dtype, int phi, int r, const float* gamma, int normalize, int chunk,
+                           const float* S0, const float* z0, float* S_out, float* z_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!gamma) return LA_ERR_NULL;
+  if (normalize != 0 && normalize != 1) return LA_ERR_UNSUPPORTED;
+  return forward_impl(Q, K, V, O, B, H, N, d, d_v, io_dtype, phi, r, nullptr, 1, chunk, S0, z0, S_out, z_out,
+                      workspace, workspace_bytes, stream, nullptr, gamma, normalize);
+}
+
+la_status la_forward_decay_timed(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+                                 int d_v, int io_dtype, int phi, int r, const float* gamma, int normalize, int chunk,
+                                 const float* S0, const float* z0, float* S_out, float* z_out, void* workspace,
+                                 size_t workspace_bytes, void* stream, void* const* events) {
+  if (!gamma) return LA_ERR_NULL;
+  if (normalize != 0 && normalize != 1) return LA_ERR_UNSUPPORTED;
+  return forward_impl(Q, K, V, O, B, H, N, d, d_v, io_dtype, phi, r, nullptr, 1, chunk, S0, z0, S_out, z_out,
+                      workspace, workspace_bytes, stream, events, gamma, normalize);
+}
+
+la_status la_decode_step_decay(const float* S, const float* z, const void* q, const void* k, const void* v,
+                               void* o, float* S_new, float* z_new, int B, int H, int d, int d_v, int io_dtype,
+                               int phi, int r, const float* gamma, int normalize, void* stream) {
+  if (!gamma) return LA_ERR_NULL;
+  if (normalize != 0 && normalize != 1) return LA_ERR_UNSUPPORTED;
+  if (phi == LA_PHI_FAVOR) return LA_ERR_UNSUPPORTED;
+  return decode_impl(S, z, q, k, v, o, S_new, z_new, B, H, d, d_v, io_dtype, phi, r, nullptr, stream, gamma,
+                     normalize);
 }
 
 la_status la_feature_map(const void* X, float* Y, long long rows, int d, int io_dtype, int phi, int r,

@@ -5,6 +5,10 @@
 //   S' = S + phi(k) v^T,  z' = z + phi(k),  o = phi(q)^T S' / phi(q)^T z'
 // ("Efficient attention variants" sec. 5: write the token first, then read;
 // the state is O(R*DV) and a step costs O(R*DV) work).
+// With a fixed per-head decay gamma ("Efficient attention variants" sec. 7.1)
+// the old state is multiplied by gamma first: S' = gamma S + phi(k) v^T,
+// z' = gamma z + phi(k); without one gamma = 1, which changes no bit.  With
+// normalize = 0 the read-out is phi(q)^T S' (no division).
 //
 // The step streams S once (read 4*R*DV bytes, write 4*R*DV bytes); its
 // arithmetic intensity is ~0.5 flop/byte, so it is HBM-bound and runs on the
@@ -78,7 +82,9 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
                                                              const T* __restrict__ q, const T* __restrict__ k,
                                                              const T* __restrict__ v, T* __restrict__ o,
                                                              float* S_new, float* z_new,
-                                                             const float* __restrict__ omega) {
+                                                             const float* __restrict__ omega,
+                                                             const float* __restrict__ gamma, int H,
+                                                             int normalize) {
   constexpr int TPR = DV / 4;          // threads per state row
   constexpr int RPP = kThreads / TPR;  // rows per pass
   static_assert(R % RPP == 0, "state rows must split evenly");
@@ -87,6 +93,7 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
   __shared__ float scratch[2][kWaves];
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
+  const float gm = gamma ? gamma[bh % H] : 1.f;
 
   features_to_lds<T, D, R, PHI>(q + (size_t)bh * D, omega, fq, xbuf, scratch[0]);
   features_to_lds<T, D, R, PHI>(k + (size_t)bh * D, omega, fk, xbuf, scratch[1]);
@@ -108,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
 #pragma unroll
   for (int it = 0; it < R / RPP; ++it) {
     const int f = r0 + it * RPP;
-    s[it] += fk[f] * v4;
+    s[it] = s[it] * gm + fk[f] * v4;
     __builtin_nontemporal_store(s[it], reinterpret_cast<f32x4*>(Sn + (size_t)f * DV));
     num += fq[f] * s[it];
   }
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
 
   float dpart = 0.f;
   for (int f = tid; f < R; f += kThreads) {
-    const float zn = z[(size_t)bh * R + f] + fk[f];
+    const float zn = z[(size_t)bh * R + f] * gm + fk[f];
     z_new[(size_t)bh * R + f] = zn;
     dpart += fq[f] * zn;
   }
@@ -129,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
     float n = 0.f;
 #pragma unroll
     for (int rr = 0; rr < RPP; ++rr) n += red[rr * DV + c];
-    store_io<T>(o + (size_t)bh * DV + c, n / den);
+    store_io<T>(o + (size_t)bh * DV + c, normalize ? n / den : n);
   }
 }
 
@@ -141,7 +148,7 @@ static hipError_t launch_decode(const DecodeArgs& a) {
   hipLaunchKernelGGL((la_decode_kernel<T, D, R, DV, PHI>), dim3(BH), dim3(kThreads), 0,
                      static_cast<hipStream_t>(a.stream), a.S, a.z, static_cast<const T*>(a.q),
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<T*>(a.o), a.S_new,
-                     a.z_new, a.omega);
+                     a.z_new, a.omega, a.gamma, a.H > 0 ? a.H : 1, a.normalize);
   return hipGetLastError();
 }
 

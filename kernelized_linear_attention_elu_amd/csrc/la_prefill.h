@@ -27,6 +27,10 @@ struct PrefillArgs {
   void* const* events;  // optional: 6 hipEvent_t recorded around the three kernels
   int fused;            // single-pass kernel (n_span = ceil(N / kFusedSpan))
   int group;            // single pass: spans per look-back block
+  // fixed per-head decay (device [H] fp32 in (0, 1]; null: none), causal
+  // pointwise maps only: S_t = gamma S_{t-1} + phi(k_t) v_t^T, z likewise
+  const float* gamma = nullptr;
+  int normalize = 1;    // 0: o_t = phi(q_t)^T S_t (no division by phi(q_t)^T z_t)
 };
 
 // Single-pass causal prefill (la_prefill.hip): tokens per workgroup and the
@@ -49,9 +53,12 @@ hipError_t prefill_launch(const PrefillArgs& a);
 bool favor_prefill_supported(int io, int d, int dv, int r, int chunk);
 hipError_t favor_prefill_launch(const PrefillArgs& a);
 
-// Span scan over a workspace of R x DV states (la_prefill.hip).
+// Span scan over a workspace of R x DV states (la_prefill.hip).  With a decay
+// (gamma, H heads), a span of L tokens multiplies the running state by
+// gamma^L; span lengths follow from N, the chunk and n_span.
 hipError_t scan_launch(float* ws, int BH, int R, int DV, int n_span, const float* S0, const float* z0,
-                       float* S_out, float* z_out, hipStream_t stream);
+                       float* S_out, float* z_out, hipStream_t stream, const float* gamma = nullptr, int H = 1,
+                       int N = 0, int chunk = 64);
 
 struct DecodeArgs {
   const float* S;
@@ -67,6 +74,8 @@ struct DecodeArgs {
   int phi;
   const float* omega;
   void* stream;
+  const float* gamma = nullptr;  // per-head decay (device [H]); null: none
+  int normalize = 1;
 };
 
 bool decode_supported(int io, int phi, int d, int dv, int r);

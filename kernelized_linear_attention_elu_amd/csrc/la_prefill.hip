@@ -56,6 +56,9 @@ struct Cfg {
   static constexpr int NT = 64 * NW_;         // threads per workgroup
   // workgroups per CU the output kernel's registers are sized for
   static constexpr int MINB = (NW_ == 4 && D_ == 64) ? 3 : 1;
+  // ... and with a decay (the weighted feature tile and the decay factors
+  // need more registers than three workgroups per CU leave)
+  static constexpr int MINB_DECAY = (NW_ == 4 && D_ == 64 && C_ <= 64) ? 2 : 1;
   static constexpr int EPL = Vec16<T>::N;     // elements per 16-byte vector
   static constexpr int KS = Op<OP>::K;
   static constexpr int PL = Op<OP>::PL;
@@ -139,10 +142,15 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<CF, WITH_Q>& cr, const Head
 // features so that they add nothing to the state.  With a non-null sk_lo the
 // rounding residual phi - round(phi) of the keys is stored too (a bf16 lo
 // word), so that hi + lo carries phi(K) to ~2^-16 relative.
-template <class CF, bool WITH_Q>
+// Decay (DECAY, lg = log2 gamma): key j of the chunk (0-based) is weighted
+// by gamma^(len - 1 - j), its age at the end of the chunk's len tokens.  The
+// weighted features go to sk (and sk_lo) when skw is null, otherwise sk
+// keeps the plain features and skw receives the weighted ones.
+template <class CF, bool WITH_Q, bool DECAY = false>
 __device__ __forceinline__ void stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typename CF::OP* sq,
                                             typename CF::OP* sk, typename CF::OP* sk_lo,
-                                            typename CF::OP* sv, int t0, int N) {
+                                            typename CF::OP* sv, int t0, int N, float lg = 0.f, int len = 0,
+                                            typename CF::OP* skw = nullptr) {
   using T = typename CF::IO;
   using OP = typename CF::OP;
   using TQ = Tile<OP, CF::R>;
@@ -168,6 +176,21 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typ
       unpack16<T>(cr.k[i], f);
 #pragma unroll
       for (int e = 0; e < CF::EPL; ++e) f[e] = phi_pointwise<CF::PHI>(f[e]);
+      u32x4 hw = u32x4{0u, 0u, 0u, 0u};  // weighted features for skw
+      if constexpr (DECAY) {
+        // (keys past len, beyond N, get a weight above one; they are
+        // zeroed below by selection, never by arithmetic)
+        const float wgt = __builtin_amdgcn_exp2f(lg * (float)(len - 1 - tok));
+        if (skw) {
+          float fw[CF::EPL];
+#pragma unroll
+          for (int e = 0; e < CF::EPL; ++e) fw[e] = f[e] * wgt;
+          hw = pack16<OP>(fw);
+        } else {
+#pragma unroll
+          for (int e = 0; e < CF::EPL; ++e) f[e] *= wgt;
+        }
+      }
       u32x4 hi = pack16<OP>(f);
       u32x4 lo = u32x4{0u, 0u, 0u, 0u};
       if constexpr (sizeof(OP) == 2) {
@@ -184,8 +207,12 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typ
         const bool valid = t0 + tok < N;
         hi = valid ? hi : u32x4{0u, 0u, 0u, 0u};
         lo = valid ? lo : u32x4{0u, 0u, 0u, 0u};
+        hw = valid ? hw : u32x4{0u, 0u, 0u, 0u};
       }
       *reinterpret_cast<u32x4*>(sk + TQ::off(tok, col)) = hi;
+      if constexpr (DECAY) {
+        if (skw) *reinterpret_cast<u32x4*>(skw + TQ::off(tok, col)) = hw;
+      }
       if constexpr (sizeof(OP) == 2) {
         if (sk_lo) *reinterpret_cast<u32x4*>(sk_lo + TQ::off(tok, col)) = lo;
       }
@@ -390,11 +417,17 @@ struct OutRegs {
 //    dacc[0] = z_hi.phi(q) + rowsum(A) and dacc[1] = z_lo.phi(q).
 //    fp32: in VALU.
 // The weights and phi(Q) enter both sums exactly as rounded for the MFMA.
-template <class CF, bool CAUSAL>
+// Decay (DECAY, lg = log2 gamma): for row i = 16 ib + li of the chunk the
+// carried state is i + 1 tokens old, so its read-out and its z term are
+// scaled by gamma^(i+1) (they are formed first), and weight (i, j) by
+// gamma^(i-j) before the diagonal mask.  normalize = 0 (DECAY only) skips
+// the division.
+template <class CF, bool CAUSAL, bool DECAY = false>
 __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&qf)[CF::RBW][CF::R / CF::KS],
                                               const typename CF::OP* sk, const typename CF::OP* sv,
                                               const typename CF::OP* ss, const typename CF::ZT* sz,
-                                              OutRegs<CF>& out, int w, int g, int li) {
+                                              OutRegs<CF>& out, int w, int g, int li, float lg = 0.f,
+                                              int normalize = 1) {
   using OP = typename CF::OP;
   using TQ = Tile<OP, CF::R>;
   using TV = Tile<OP, CF::DV>;
@@ -422,6 +455,33 @@ __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&q
     f32x4 o[CTW];
 #pragma unroll
     for (int c = 0; c < CTW; ++c) o[c] = zero4();
+    // read-out of the carried state: o += S^T phi(Q)^T
+    auto readout = [&]() {
+#pragma unroll
+      for (int cti = 0; cti < CTW; ++cti) {
+        const int ct = ct0 + cti;
+        if constexpr (PL == 8) {
+#pragma unroll
+          for (int ks = 0; ks < R / KS; ++ks)
+            o[cti] = mfma16(tr_frag<DV>(ss, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, 16 * ct, li), qf[rbi][ks], o[cti]);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < R / KS; ++ks)
+            o[cti] = mfma16(ss[TV::off(QRegs<CF>::feature(ks, g), 16 * ct + li)], qf[rbi][ks], o[cti]);
+        }
+      }
+    };
+    if constexpr (DECAY) {
+      const float rowdec = __builtin_amdgcn_exp2f(lg * (float)(16 * ib + li + 1));
+      readout();
+#pragma unroll
+      for (int cti = 0; cti < CTW; ++cti) o[cti] *= rowdec;
+      if constexpr (PL == 8) {
+        dacc *= rowdec;
+      } else {
+        den *= rowdec;
+      }
+    }
 
     if constexpr (CAUSAL) {
       // key blocks are taken in pairs (one K = 32 MFMA step for bf16); only
@@ -435,6 +495,12 @@ __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&q
           } else {
             t = mfma16(sk[TQ::off(16 * jb + li, QRegs<CF>::feature(ks, g))], qf[rbi][ks], t);
           }
+        }
+        if constexpr (DECAY) {
+          // gamma^(i-j); above the diagonal the factor exceeds one, and those
+          // entries are then replaced by zero (selection below)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) t[r] *= __builtin_amdgcn_exp2f(lg * (float)(16 * (ib - jb) + li - 4 * g - r));
         }
         if constexpr (PL == 8) {
           if (jb == ib) {  // wave-uniform: only the diagonal block is masked
@@ -489,21 +555,10 @@ __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&q
       den = xor_sum16_32(den);
     }
 
-#pragma unroll
-    for (int cti = 0; cti < CTW; ++cti) {
-      const int ct = ct0 + cti;
-      if constexpr (PL == 8) {
-#pragma unroll
-        for (int ks = 0; ks < R / KS; ++ks)
-          o[cti] = mfma16(tr_frag<DV>(ss, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, 16 * ct, li), qf[rbi][ks], o[cti]);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < R / KS; ++ks)
-          o[cti] = mfma16(ss[TV::off(QRegs<CF>::feature(ks, g), 16 * ct + li)], qf[rbi][ks], o[cti]);
-      }
-    }
+    if constexpr (!DECAY) readout();
 
-    const float rden = __builtin_amdgcn_rcpf(den);  // one reciprocal per row (<= 1 ulp)
+    // one reciprocal per row (<= 1 ulp)
+    const float rden = (DECAY && !normalize) ? 1.f : __builtin_amdgcn_rcpf(den);
 #pragma unroll
     for (int cti = 0; cti < CTW; ++cti) {
       if constexpr (sizeof(typename CF::IO) == 2) {
@@ -664,6 +719,16 @@ struct SmemOut {
   OP s[Tile<OP, CF::DV>::elems(CF::R)];
   alignas(16) typename CF::ZT z[CF::ZE];
   alignas(16) OP scr[Scratch<CF>::ELEMS];
+  __device__ OP* kw_tile() { return nullptr; }
+};
+// With a decay: also the keys' features weighted by their age at the end of
+// the chunk, gamma^(C - 1 - j), which the state carry contracts (the
+// weights use the plain features).
+template <class CF>
+struct SmemOutDecay : SmemOut<CF> {
+  using OP = typename CF::OP;
+  alignas(16) OP kw[Tile<OP, CF::R>::elems(CF::C)];
+  __device__ OP* kw_tile() { return kw; }
 };
 
 // LDS of the non-causal output kernel: the full-sequence sums only.
@@ -697,10 +762,15 @@ __device__ __forceinline__ HeadBufs head_bufs(const typename CF::IO* Q, const ty
 }
 
 // Per-span state: dS = phi(K_span)^T V_span, dz = sum phi(K_span) -> ws slot s.
-template <class CF>
+// With a decay (DECAY, gamma[head]), the span's sum is decayed to the span's
+// end: key t enters with gamma^(t_end - 1 - t).  Per chunk of len tokens the
+// running sum is multiplied by gamma^len before the chunk's keys, weighted
+// by gamma^(len - 1 - j), are added.
+template <class CF, bool DECAY = false>
 __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO* __restrict__ K,
                                                             const typename CF::IO* __restrict__ V,
-                                                            float* __restrict__ ws, int N, int n_span) {
+                                                            float* __restrict__ ws, int N, int n_span,
+                                                            const float* __restrict__ gamma, int H) {
   using OP = typename CF::OP;
   __shared__ SmemState<CF> sm;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
@@ -709,6 +779,7 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
   const int t_begin = span_begin<CF>(s, n_span, N);
   const int t_end = span_begin<CF>(s + 1, n_span, N);
   const HeadBufs hb = head_bufs<CF>(nullptr, K, V, nullptr, bh, N);
+  const float lg = DECAY ? __builtin_amdgcn_logf(gamma[bh % H]) : 0.f;  // log2(gamma)
 
   f32x4 acc[CF::TPW];
 #pragma unroll
@@ -716,6 +787,16 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
   f32x4 zt[CF::ZPW];
 #pragma unroll
   for (int k = 0; k < CF::ZPW; ++k) zt[k] = zero4();
+  // decay of the running sum over a chunk of len tokens
+  auto age = [&](int len) {
+    if constexpr (DECAY) {
+      const float dg = __builtin_amdgcn_exp2f(lg * (float)len);
+#pragma unroll
+      for (int i = 0; i < CF::TPW; ++i) acc[i] *= dg;
+#pragma unroll
+      for (int k = 0; k < CF::ZPW; ++k) zt[k] *= dg;
+    }
+  };
 
   // two chunks of loads in flight: chunk c+2 is requested as soon as chunk
   // c has been staged (LDS double buffering, one barrier per chunk).  Every
@@ -730,17 +811,21 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
   int buf = 0;
   for (int t0 = t_begin; t0 < t_end; t0 += 2 * CF::C) {
     OP* lo = sizeof(OP) == 2 ? sm.k_lo[buf] : nullptr;
-    stage_chunk<CF, false>(ca, nullptr, sm.k[buf], lo, sm.v[buf], t0, N);
+    const int len_a = min(CF::C, t_end - t0);
+    stage_chunk<CF, false, DECAY>(ca, nullptr, sm.k[buf], lo, sm.v[buf], t0, N, lg, len_a);
     load_chunk<CF, false>(ca, hb, min(t0 + 2 * CF::C, last));
     __syncthreads();
+    age(len_a);
     state_mfma<CF>(acc, zt, sm.k[buf], lo, sm.v[buf], w, g, li);
     buf ^= 1;
     const bool second = t0 + CF::C < t_end;  // workgroup-uniform
+    const int len_b = min(CF::C, t_end - t0 - CF::C);
     lo = sizeof(OP) == 2 ? sm.k_lo[buf] : nullptr;
-    if (second) stage_chunk<CF, false>(cb, nullptr, sm.k[buf], lo, sm.v[buf], t0 + CF::C, N);
+    if (second) stage_chunk<CF, false, DECAY>(cb, nullptr, sm.k[buf], lo, sm.v[buf], t0 + CF::C, N, lg, len_b);
     load_chunk<CF, false>(cb, hb, min(t0 + 3 * CF::C, last));
     if (second) {
       __syncthreads();
+      age(len_b);
       state_mfma<CF>(acc, zt, sm.k[buf], lo, sm.v[buf], w, g, li);
       buf ^= 1;
     }
@@ -763,12 +848,19 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
 // Exclusive fp32 prefix over spans, element-parallel: slot s becomes the
 // state before span s (starting from S0/z0 or zero); slot n_span receives
 // the total, which is also copied to S_out/z_out when given.  The summation
-// order is fixed, so results are reproducible.
+// order is fixed, so results are reproducible.  With a decay (DECAY) the
+// running state is multiplied by gamma^L before a span of L tokens is added
+// (each span's own sum is already decayed to the span's end); the span
+// lengths are walked with an incremental quotient and remainder of
+// s * n_chunks / n_span, the split span_begin uses.
+template <bool DECAY>
 __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ ws, int R, int DV, int n_span,
                                                            const float* __restrict__ S0,
                                                            const float* __restrict__ z0,
                                                            float* __restrict__ S_out,
-                                                           float* __restrict__ z_out) {
+                                                           float* __restrict__ z_out,
+                                                           const float* __restrict__ gamma, int H, int N,
+                                                           int chunk) {
   const int E = R * DV + R;
   const int e = blockIdx.x * kThreads + threadIdx.x;
   const int bh = blockIdx.y;
@@ -781,6 +873,15 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
     if (z0) acc = z0[(size_t)bh * R + (e - R * DV)];
   }
   float* p = ws + (size_t)bh * (n_span + 1) * E + e;
+  float lg = 0.f;                    // log2(gamma)
+  int q_ch = 0, r_ch = 0, rem = 0;   // n_chunks = q_ch n_span + r_ch; running remainder
+  long long c_beg = 0;               // first chunk of the current span
+  if constexpr (DECAY) {
+    lg = __builtin_amdgcn_logf(gamma[bh % H]);
+    const int n_chunks = (N + chunk - 1) / chunk;
+    q_ch = n_chunks / n_span;
+    r_ch = n_chunks % n_span;
+  }
   // all loads of a batch are issued before the dependent adds, so a span
   // scan costs ceil(n_span / 16) memory round trips instead of n_span
   constexpr int kBatch = 16;
@@ -790,7 +891,18 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
     for (int j = 0; j < kBatch; ++j) x[j] = s0 + j < n_span ? p[(size_t)(s0 + j) * E] : 0.f;
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      if (s0 + j < n_span) p[(size_t)(s0 + j) * E] = acc;
+      if (s0 + j < n_span) {
+        p[(size_t)(s0 + j) * E] = acc;
+        if constexpr (DECAY) {
+          rem += r_ch;
+          const int step = q_ch + (rem >= n_span ? 1 : 0);
+          rem -= rem >= n_span ? n_span : 0;
+          const long long c_end = c_beg + step;
+          const long long t_b = min((long long)N, c_beg * chunk), t_e = min((long long)N, c_end * chunk);
+          acc *= __builtin_amdgcn_exp2f(lg * (float)(t_e - t_b));
+          c_beg = c_end;
+        }
+      }
       acc += x[j];
     }
   }
@@ -807,13 +919,21 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
 // c+1 is loaded into registers while chunk c is computed; LDS holds one
 // chunk, with a barrier before it is overwritten and one after it is written;
 // chunk c's outputs are stored before the state update.
-template <class CF, bool CAUSAL>
-__global__ __launch_bounds__(CF::NT, CF::MINB) void la_output_kernel(const typename CF::IO* __restrict__ Q,
+// With a decay (DECAY, causal only): chunk_outputs applies gamma to the
+// weights and to the carried state's read-out, and the carry is
+// S <- gamma^C S + sum_j gamma^(C-1-j) phi(k_j) v_j^T (z likewise), from the
+// weighted feature tile.
+template <class CF, bool CAUSAL, bool DECAY = false>
+__global__ __launch_bounds__(CF::NT, DECAY ? CF::MINB_DECAY : CF::MINB) void la_output_kernel(const typename CF::IO* __restrict__ Q,
                                                                 const typename CF::IO* __restrict__ K,
                                                                 const typename CF::IO* __restrict__ V,
                                                                 typename CF::IO* __restrict__ O,
-                                                                const float* __restrict__ ws, int N, int n_span) {
-  __shared__ typename std::conditional<CAUSAL, SmemOut<CF>, SmemOutNC<CF>>::type sm;
+                                                                const float* __restrict__ ws, int N, int n_span,
+                                                                const float* __restrict__ gamma, int H,
+                                                                int normalize) {
+  static_assert(CAUSAL || !DECAY, "the decay is defined for the causal form");
+  __shared__ typename std::conditional<CAUSAL, typename std::conditional<DECAY, SmemOutDecay<CF>, SmemOut<CF>>::type,
+                                       SmemOutNC<CF>>::type sm;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
   // heads in the reverse order of la_state_kernel: the keys and values
   // that kernel read last are the likeliest to still sit in the
@@ -823,6 +943,7 @@ __global__ __launch_bounds__(CF::NT, CF::MINB) void la_output_kernel(const typen
   const int t_begin = span_begin<CF>(s, n_span, N);
   const int t_end = span_begin<CF>(s + 1, n_span, N);
   const HeadBufs hb = head_bufs<CF>(Q, K, V, O, bh, N);
+  const float lg = DECAY ? __builtin_amdgcn_logf(gamma[bh % H]) : 0.f;  // log2(gamma)
 
   // carried state: this wave's tiles of S (fp32) and its z tiles
   constexpr int E = CF::R * CF::DV + CF::R;
@@ -884,16 +1005,27 @@ __global__ __launch_bounds__(CF::NT, CF::MINB) void la_output_kernel(const typen
     do {
       __syncthreads();  // every wave is done with the previous chunk's S, z, phi(K), V
       publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
-      stage_chunk<CF, false>(cr, nullptr, sm.k, nullptr, sm.v, t0, N);
+      stage_chunk<CF, false, DECAY>(cr, nullptr, sm.k, nullptr, sm.v, t0, N, lg, CF::C, sm.kw_tile());
       typename QRegs<CF>::frag qf[CF::RBW][CF::R / CF::KS];
       qr.to_frags(qf, scr, g, li);
       const int tn = min(t0 + CF::C, last);
       load_chunk<CF, false>(cr, hb, tn);
       qr.load(hb.q, tn, w, g, li);
       __syncthreads();
-      chunk_outputs<CF, true>(qf, sm.k, sm.v, sm.s, sm.z, out, w, g, li);
+      chunk_outputs<CF, true, DECAY>(qf, sm.k, sm.v, sm.s, sm.z, out, w, g, li, lg, normalize);
       store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
-      state_mfma<CF>(sacc, zt, sm.k, nullptr, sm.v, w, g, li);
+      if constexpr (DECAY) {
+        // the carry past this chunk (unused after a span's last chunk, so a
+        // partial last chunk needs no other length)
+        const float dg = __builtin_amdgcn_exp2f(lg * (float)CF::C);
+#pragma unroll
+        for (int i = 0; i < CF::TPW; ++i) sacc[i] *= dg;
+#pragma unroll
+        for (int k = 0; k < CF::ZPW; ++k) zt[k] *= dg;
+        state_mfma<CF>(sacc, zt, sm.kw_tile(), nullptr, sm.v, w, g, li);
+      } else {
+        state_mfma<CF>(sacc, zt, sm.k, nullptr, sm.v, w, g, li);
+      }
       t0 += CF::C;
     } while (t0 < t_end);
   }
@@ -1177,23 +1309,33 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
   auto rec = [&](int i) {
     if (a.events && a.events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a.events[i]), st);
   };
+  const bool decay = a.gamma != nullptr && a.causal;
   rec(0);
   if (n_span > 0 && BH > 0) {
-    hipLaunchKernelGGL((la_state_kernel<CF>), dim3(BH * n_span), dim3(CF::NT), 0, st, K, V, ws, a.N, n_span);
+    if (decay)
+      hipLaunchKernelGGL((la_state_kernel<CF, true>), dim3(BH * n_span), dim3(CF::NT), 0, st, K, V, ws, a.N, n_span,
+                         a.gamma, a.H);
+    else
+      hipLaunchKernelGGL((la_state_kernel<CF, false>), dim3(BH * n_span), dim3(CF::NT), 0, st, K, V, ws, a.N, n_span,
+                         nullptr, 1);
   }
   rec(1);
   rec(2);
-  hipError_t e = scan_launch(ws, BH, CF::R, CF::DV, n_span, a.S0, a.z0, a.S_out, a.z_out, st);
+  hipError_t e = scan_launch(ws, BH, CF::R, CF::DV, n_span, a.S0, a.z0, a.S_out, a.z_out, st,
+                             decay ? a.gamma : nullptr, a.H, a.N, CF::C);
   if (e != hipSuccess) return e;
   rec(3);
   rec(4);
   if (n_span > 0 && BH > 0) {
-    if (a.causal)
+    if (decay)
+      hipLaunchKernelGGL((la_output_kernel<CF, true, true>), dim3(BH * n_span), dim3(CF::NT), 0, st, Q, K, V, O, ws,
+                         a.N, n_span, a.gamma, a.H, a.normalize);
+    else if (a.causal)
       hipLaunchKernelGGL((la_output_kernel<CF, true>), dim3(BH * n_span), dim3(CF::NT), 0, st, Q, K, V, O, ws,
-                         a.N, n_span);
+                         a.N, n_span, nullptr, 1, 1);
     else
       hipLaunchKernelGGL((la_output_kernel<CF, false>), dim3(BH * n_span), dim3(CF::NT), 0, st, Q, K, V, O, ws,
-                         a.N, n_span);
+                         a.N, n_span, nullptr, 1, 1);
   }
   rec(5);
   return hipGetLastError();
@@ -1216,11 +1358,17 @@ static hipError_t dispatch_chunk(const PrefillArgs& a) {
 }
 
 hipError_t scan_launch(float* ws, int BH, int R, int DV, int n_span, const float* S0, const float* z0,
-                       float* S_out, float* z_out, hipStream_t stream) {
+                       float* S_out, float* z_out, hipStream_t stream, const float* gamma, int H, int N, int chunk) {
   const int E = R * DV + R;
-  if (BH > 0)
-    hipLaunchKernelGGL(la_scan_kernel, dim3((E + kThreads - 1) / kThreads, BH), dim3(kThreads), 0, stream, ws, R,
-                       DV, n_span, S0, z0, S_out, z_out);
+  if (BH > 0) {
+    const dim3 grid((E + kThreads - 1) / kThreads, BH);
+    if (gamma)
+      hipLaunchKernelGGL(la_scan_kernel<true>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0, S_out,
+                         z_out, gamma, H > 0 ? H : 1, N, chunk > 0 ? chunk : 64);
+    else
+      hipLaunchKernelGGL(la_scan_kernel<false>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0, S_out,
+                         z_out, nullptr, 1, N, chunk > 0 ? chunk : 64);
+  }
   return hipGetLastError();
 }
 

@@ -109,6 +109,16 @@ def draw_decode_token(n_seq, H, d, dv, seed=DATA_SEED, io="bf16"):
     return round_to_io(q, io), round_to_io(k, io), round_to_io(v, io)
 
 
+def decay_gammas(H):
+    """Per-head decays for the decayed (RetNet-form) workloads, float32 [H]:
+    gamma_h = 1 - 2^-(5 + 7 h / (H - 1)), one time scale per head from
+    1 - 1/32 to 1 - 1/4096 (the pages give no values beyond gamma = 0.99; a
+    spread of fixed per-head rates is what they describe).  Deterministic."""
+    h = np.arange(H, dtype=np.float64)
+    e = 5.0 + 7.0 * h / max(H - 1, 1)
+    return (1.0 - 2.0 ** (-e)).astype(np.float32)
+
+
 @dataclass(frozen=True)
 class Workload:
     """Shapes of one named workload (no arithmetic)."""

@@ -144,6 +144,41 @@ def test_decode_argument_errors(lib):
     assert dec(B=0, S=None, z=None) == 0
 
 
+def test_decay_argument_errors(lib):
+    """la_forward_decay / la_decode_step_decay: every case returns before any
+    HIP call (the pointers are never dereferenced)."""
+    def fd(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, B=1, H=1, N=64, d=64, dv=64, io=1, phi=0, r=0, gamma=FAKE,
+           normalize=1, chunk=64, S0=None, z0=None, S_out=None, z_out=None, ws=FAKE, ws_bytes=1 << 30):
+        return lib.la_forward_decay(Q, K, V, O, B, H, N, d, dv, io, phi, r, gamma, normalize, chunk, S0, z0, S_out,
+                                    z_out, ws, ws_bytes, None)
+    assert fd(gamma=None) == 1                           # LA_ERR_NULL
+    assert fd(Q=None) == 1
+    assert fd(N=-1) == 2                                 # LA_ERR_SHAPE
+    assert fd(normalize=2) == 3                          # LA_ERR_UNSUPPORTED
+    assert fd(phi=1, r=256) == 3                         # no FAVOR+ with a decay
+    assert fd(d=96, dv=96) == 3
+    assert fd(gamma=MISALIGNED) == 4                     # LA_ERR_ALIGN
+    assert fd(ws=None) == 5                              # LA_ERR_WORKSPACE
+    assert fd(ws_bytes=16) == 5
+    assert fd(S0=FAKE, z0=None) == 1
+    assert fd(Q=None, K=None, V=None, O=None, B=0, ws=None) == 0
+
+    def dd(S=FAKE, z=FAKE, q=FAKE, k=FAKE, v=FAKE, o=FAKE, Sn=FAKE, zn=FAKE, B=1, H=1, d=64, dv=64, io=1,
+           phi=0, r=0, gamma=FAKE, normalize=1):
+        return lib.la_decode_step_decay(S, z, q, k, v, o, Sn, zn, B, H, d, dv, io, phi, r, gamma, normalize, None)
+    assert dd(gamma=None) == 1
+    assert dd(S=None) == 1
+    assert dd(normalize=-1) == 3
+    assert dd(phi=1, r=256) == 3
+    assert dd(d=32, dv=32) == 3
+    assert dd(gamma=MISALIGNED) == 4
+    assert dd(B=0, S=None, z=None) == 0
+    # spans: the decayed output kernel runs two workgroups per CU at d = 64
+    n = ctypes.c_int()
+    assert lib.la_forward_decay_config(1, 32, 32768, 64, 64, 1, 0, 0, 64, ctypes.byref(n)) == 0 and n.value == 16
+    assert lib.la_forward_decay_config(1, 32, 32768, 64, 64, 1, 1, 256, 64, ctypes.byref(n)) == 3
+
+
 def test_feature_map_argument_errors(lib):
     def fm(X=FAKE, Y=FAKE, rows=10, d=64, io=1, phi=0, r=0, omega=None):
         return lib.la_feature_map(X, Y, rows, d, io, phi, r, omega, None)
