@@ -109,6 +109,8 @@ def parse_args(argv=None):
     p.add_argument("--noncausal", action="store_true", help="non-causal prefill")
     p.add_argument("--decay", action="store_true",
                    help="causal prefill with a fixed per-head decay (RetNet form, la_forward_decay)")
+    p.add_argument("--gated", action="store_true",
+                   help="causal prefill with a per-token scalar gate (SSD scalar-decay form, la_forward_gated)")
     p.add_argument("--chunk", type=int, default=None,
                    help="chunk size (default: the workload's, 0 = the library's choice)")
     p.add_argument("--settle", type=float, default=SETTLE_S,
@@ -130,15 +132,19 @@ def cpu_info():
     return model
 
 
-def time_oracle_prefill(q, k, v, causal, max_heads, phi="elu1", omega=None, gamma=None):
-    """fp64 oracle (token recurrence, decayed when ``gamma`` is given, or the
-    reassociated non-causal form) on the first ``max_heads`` heads of batch 0;
-    returns (seconds, heads, cores)."""
+def time_oracle_prefill(q, k, v, causal, max_heads, phi="elu1", omega=None, gamma=None, log_a=None):
+    """fp64 oracle (token recurrence, decayed when ``gamma`` is given, gated
+    when ``log_a`` is, or the reassociated non-causal form) on the first
+    ``max_heads`` heads of batch 0; returns (seconds, heads, cores)."""
     from oracle import linear_attention as ora
     from oracle import decay as dec
+    from oracle import gated as gat
+    import numpy as np
     h = min(max_heads, q.shape[1])
     t0, c0 = time.perf_counter(), time.process_time()
-    if gamma is not None:
+    if log_a is not None:
+        gat.recurrent_gated(q[:1, :h], k[:1, :h], v[:1, :h], np.exp(log_a[:1, :h].astype("float64")), phi=phi)
+    elif gamma is not None:
         dec.recurrent_decay(q[:1, :h], k[:1, :h], v[:1, :h], gamma[:h].astype("float64"), phi=phi)
     elif causal:
         ora.recurrent_attention(q[:1, :h], k[:1, :h], v[:1, :h], phi=phi, omega=omega)
@@ -155,11 +161,14 @@ def bench_prefill(args, torch, la, synth):
     if args.chunk is not None:
         w = dataclasses.replace(w, chunk=args.chunk)
     causal = not args.noncausal
-    if args.decay and (not causal or w.phi == "favor"):
-        raise SystemExit("--decay: causal pointwise-feature workloads only")
+    if (args.decay or args.gated) and (not causal or w.phi == "favor"):
+        raise SystemExit("--decay / --gated: causal pointwise-feature workloads only")
+    if args.decay and args.gated:
+        raise SystemExit("--decay and --gated exclude each other")
     dev = torch.device("cuda:0")
     q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
     gamma = synth.decay_gammas(w.H) if args.decay else None
+    log_a = synth.draw_log_gates(w.B, w.H, w.N) if args.gated else None
 
     def to_dev(x):
         return hostio.upload_bf16_bits(synth.bf16_bits(x), dev)
@@ -173,14 +182,19 @@ def bench_prefill(args, torch, la, synth):
     omega = synth.draw_omega(w.r, w.d) if w.phi == "favor" else None
     om_dev = hostio.upload_f32(omega, dev) if omega is not None else None
     gamma_dev = hostio.upload_f32(gamma, dev) if gamma is not None else None
+    gates = None
+    if log_a is not None:
+        g0 = hostio.upload_f32(log_a, dev)
+        gates = [g0] + [g0.clone() for _ in range(ROTATE - 1)]
     ws = torch.empty(la.workspace_bytes(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
-                                        chunk=w.chunk),
+                                        chunk=w.chunk, gated=log_a is not None),
                      dtype=torch.uint8, device=dev)
 
     def step(i, events=None):
         Q, K, V = sets[i % ROTATE]
         la.forward(Q, K, V, phi=w.phi, omega=om_dev, causal=causal, chunk=w.chunk, out=outs[i % ROTATE],
-                   workspace=ws, events=events, gamma=gamma_dev)
+                   workspace=ws, events=events, gamma=gamma_dev,
+                   log_gate=gates[i % ROTATE] if gates is not None else None)
 
     for i in range(args.warmup):
         step(i)
@@ -216,13 +230,15 @@ def bench_prefill(args, torch, la, synth):
     ms = (t1 - t0) * 1e3 / args.steps
     token_heads = w.B * w.H * w.N
     alg_bytes = token_heads * (2 * w.d + 2 * w.dv) * 2          # read Q, K, V, write O (bf16)
+    if log_a is not None:
+        alg_bytes += token_heads * 4                             # read the fp32 log gates
     # features (FAVOR+: two d x r projections), state build + read-out
     # (4 r dv), intra-chunk products over full C x C tiles
     feat_flops = 2 * 2 * w.d * w.r if w.phi == "favor" else 0
     alg_flops = token_heads * (feat_flops + 4 * w.r * w.dv + (2 * w.chunk * (w.r + w.dv) if causal else 0))
     out_ms = out_live_ms
     n_span, single_pass = la.forward_config(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
-                                            chunk=w.chunk, decay=gamma is not None)
+                                            chunk=w.chunk, decay=gamma is not None, gated=log_a is not None)
     names = (FAVOR_KERNEL_NAMES if w.phi == "favor" else FUSED_KERNEL_NAMES if single_pass else KERNEL_NAMES)
     out_kernel = names[2]
     traffic = read_traffic(args.workload + ("" if causal else "_noncausal"), out_kernel)
@@ -237,7 +253,7 @@ def bench_prefill(args, torch, la, synth):
     else:
         # the output kernel reads Q, K, V and writes O (causal); non-causal it
         # reads Q and writes O only
-        out_bytes = alg_bytes if causal else token_heads * (w.d + w.dv) * 2
+        out_bytes = alg_bytes if causal else token_heads * (w.d + w.dv) * 2  # (gated: with the gates)
         achieved = out_bytes / (out_ms * 1e-3) / 1e9
         roof = {"kernel": out_kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
@@ -259,9 +275,11 @@ def bench_prefill(args, torch, la, synth):
             "workload": f"{w.name} prefill B{w.B} H{w.H} N{w.N} d{w.d} dv{w.dv} bf16 I/O, fp32 state, "
                         f"phi={'FAVOR+ r=%d' % w.r if w.phi == 'favor' else 'elu+1'}, "
                         f"{'causal' if causal else 'non-causal'}, chunk {w.chunk}"
-                        + (", per-head decay gamma_h = 1 - 2^-(5 + 7h/(H-1)) (RetNet form)" if gamma is not None else ""),
+                        + (", per-head decay gamma_h = 1 - 2^-(5 + 7h/(H-1)) (RetNet form)" if gamma is not None else "")
+                        + (", per-token gates log a = -dt A_h, dt log-uniform [1e-3, 1e-1], A_h = 1 + 15h/(H-1)"
+                           " (SSD scalar-decay form)" if log_a is not None else ""),
             "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv, "r": w.r, "chunk": w.chunk, "causal": causal,
-            "phi": w.phi, "accumulate": "fp32", "decay": gamma is not None,
+            "phi": w.phi, "accumulate": "fp32", "decay": gamma is not None, "gated": log_a is not None,
         },
         "roofline": roof,
         "path_roofline": {
@@ -278,7 +296,8 @@ def bench_prefill(args, torch, la, synth):
         "settle": {"seconds": args.settle, "untimed_steps": settled},
     }
     if not args.no_cpu_baseline:
-        wall, h, cores = time_oracle_prefill(q, k, v, causal, max_heads=w.H, phi=w.phi, omega=omega, gamma=gamma)
+        wall, h, cores = time_oracle_prefill(q, k, v, causal, max_heads=w.H, phi=w.phi, omega=omega, gamma=gamma,
+                                             log_a=log_a)
         # the sample covers h of the B*H heads at full length: scale to the job
         per_job = wall * (w.B * w.H) / h
         res["cpu_baseline"] = {
@@ -286,7 +305,7 @@ def bench_prefill(args, torch, la, synth):
             "unit": "tokens/s",
             "cores": cores,
             "kind": "oracle",
-            "sample": f"fp64 {('decayed token recurrence' if gamma is not None else 'token recurrence') if causal else 'reassociated form'} over {h} of "
+            "sample": f"fp64 {('gated token recurrence' if log_a is not None else 'decayed token recurrence' if gamma is not None else 'token recurrence') if causal else 'reassociated form'} over {h} of "
                       f"{w.B * w.H} heads x {w.N} tokens ({wall:.1f} s), scaled to the full job",
             "cpu": cpu_info(),
         }

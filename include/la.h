@@ -18,7 +18,12 @@
  *     attention variants" sec. 7.1): S_t = gamma S_{t-1} + phi(k_t) v_t^T,
  *     z_t = gamma z_{t-1} + phi(k_t), read out normalised as above or, with
  *     normalize = 0, as o_t = phi(q_t)^T S_t (the page's form with the
- *     identity map).
+ *     identity map);
+ *   - causal with a per-token scalar gate a_t (the scalar-decay form of
+ *     Mamba-2's SSD, "Linear attention and SSM", section on how SSD unifies
+ *     SSM and attention: A_t = a_t I, output ((Q K^T) o L) V with
+ *     L_ij = a_{j+1} ... a_i): S_t = a_t S_{t-1} + phi(k_t) v_t^T,
+ *     z_t = a_t z_{t-1} + phi(k_t), read out as the decay above.
  *
  * Conventions shared by every call
  *   - Tensors are contiguous row-major device buffers owned by the caller:
@@ -51,6 +56,7 @@
  *       la_forward_decay: as la_forward for ELU1/IDENTITY (no FAVOR+).
  *       la_decode_step: d = d_v in {64, 128}; FAVOR+ with r = 256.
  *       la_decode_step_decay: d = d_v in {64, 128}, ELU1/IDENTITY.
+ *       la_forward_gated, la_decode_step_gated: as the decay calls.
  *       la_feature_map: ELU1/IDENTITY with d % 8 == 0; FAVOR+ with d in {64, 128},
  *       r = 256.
  */
@@ -203,6 +209,66 @@ la_status la_forward_decay_timed(const void *Q, const void *K, const void *V, vo
 la_status la_decode_step_decay(const float *S, const float *z, const void *q, const void *k, const void *v,
                                void *o, float *S_new, float *z_new, int B, int H, int d, int d_v, int io_dtype,
                                int phi, int r, const float *gamma, int normalize, void *stream);
+
+/*
+ * Causal prefill with a per-token scalar gate ("Linear attention and SSM",
+ * Mamba-2 SSD section, eq. of M = (C B^T) o L with A_t = a_t I):
+ *   S_t = a_t S_{t-1} + phi(k_t) v_t^T,  z_t = a_t z_{t-1} + phi(k_t),
+ * so that token j enters o_t with weight (a_{j+1} ... a_t) phi(q_t).phi(k_j);
+ * o_t = phi(q_t)^T S_t / phi(q_t)^T z_t, or phi(q_t)^T S_t when
+ * normalize = 0 (the page's structured masked attention with the feature
+ * map applied to Q and K).  All gates one gives la_forward's causal result;
+ * a constant gate per head gives la_forward_decay's.  An initial state S0,
+ * z0 enters o_t (0-based) with a_0 ... a_t.
+ *   log_a     in: device fp32 [B][H][N], the natural log of each gate
+ *             (<= 0; Mamba-2 forms it as -Delta_t * A).  The kernels use
+ *             max(log2 a_t, -126): a gate below 2^-126, zero (-inf) included,
+ *             acts as 2^-126.  Positive values are not rejected (they are not
+ *             read on the host) and give gates above one.  Inside a chunk
+ *             the gate products are formed as 2^(c_i - c_j) from running
+ *             fp32 sums c of log2 gates, so a weight's relative error grows
+ *             with |c| (about |c| * 2^-23; with gates of Mamba-2's range
+ *             |c| stays below a few hundred).
+ *   normalize 1 (divide by phi(q)^T z) or 0.
+ *   workspace at least la_forward_gated_workspace_bytes(...) bytes (the span
+ *             states plus one fp32 total gate per (head, span)).
+ *   The other arguments are la_forward's with causal = 1 and no omega
+ *   (FAVOR+ returns LA_ERR_UNSUPPORTED).
+ * Errors: as la_forward; LA_ERR_NULL for a NULL log_a.
+ */
+la_status la_forward_gated(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int d,
+                           int d_v, int io_dtype, int phi, int r, const float *log_a, int normalize, int chunk,
+                           const float *S0, const float *z0, float *S_out, float *z_out, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Workspace bytes la_forward_gated needs (0 for invalid or unsupported
+ * arguments); LA_SPAN applies as for la_forward_workspace_bytes. */
+size_t la_forward_gated_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r,
+                                        int chunk);
+
+/* Spans per head la_forward_gated uses for this shape (*n_span; may be NULL);
+ * errors as its shape checks.  No device work. */
+la_status la_forward_gated_config(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk,
+                                  int *n_span);
+
+/* la_forward_gated plus timing events, as la_forward_timed. */
+la_status la_forward_gated_timed(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int d,
+                                 int d_v, int io_dtype, int phi, int r, const float *log_a, int normalize, int chunk,
+                                 const float *S0, const float *z0, float *S_out, float *z_out, void *workspace,
+                                 size_t workspace_bytes, void *stream, void *const *events);
+
+/*
+ * Decode step with a per-token scalar gate:
+ *   S_new = a S + phi(k) v^T, z_new = a z + phi(k),
+ *   o = phi(q)^T S_new / phi(q)^T z_new (normalize = 1) or phi(q)^T S_new.
+ * log_a: device fp32 [B][H], the natural log of this token's gate per
+ * sequence and head (clamped as in la_forward_gated); other arguments as
+ * la_decode_step (ELU1/IDENTITY only).
+ * Errors: as la_decode_step; LA_ERR_NULL for a NULL log_a.
+ */
+la_status la_decode_step_gated(const float *S, const float *z, const void *q, const void *k, const void *v,
+                               void *o, float *S_new, float *z_new, int B, int H, int d, int d_v, int io_dtype,
+                               int phi, int r, const float *log_a, int normalize, void *stream);
 
 /*
  * Standalone feature map: Y[i] = phi(X[i]) for rows i = 0..rows-1.

@@ -42,6 +42,11 @@ _SIGS = {
     "la_forward_decay": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
     "la_forward_decay_timed": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp, _vp]),
     "la_decode_step_decay": (_i, [_vp] * 8 + [_i] * 7 + [_vp, _i, _vp]),
+    "la_forward_gated_workspace_bytes": (ctypes.c_size_t, [_i] * 9),
+    "la_forward_gated_config": (_i, [_i] * 9 + [ctypes.POINTER(_i)]),
+    "la_forward_gated": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
+    "la_forward_gated_timed": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp, _vp]),
+    "la_decode_step_gated": (_i, [_vp] * 8 + [_i] * 7 + [_vp, _i, _vp]),
     "la_feature_map": (_i, [_vp, _vp, ctypes.c_longlong, _i, _i, _i, _i, _vp, _vp]),
     "la_status_string": (ctypes.c_char_p, [_i]),
     "la_version": (_i, []),
@@ -155,16 +160,24 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def workspace_bytes(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64):
+def workspace_bytes(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64, gated=False):
+    """Workspace bytes of la_forward (la_forward_gated with ``gated``; the
+    decay call needs no more than la_forward's causal size)."""
     io_code = LA_BF16 if io == "bf16" else LA_F32
+    if gated:
+        return int(load_library().la_forward_gated_workspace_bytes(B, H, N, d, dv, io_code, PHI[phi], r, chunk))
     return int(load_library().la_forward_workspace_bytes(B, H, N, d, dv, io_code, PHI[phi], r, int(causal), chunk))
 
 
-def forward_config(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64, decay=False):
+def forward_config(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64, decay=False, gated=False):
     """(n_span, single_pass) that la_forward (la_forward_decay with
-    ``decay``) uses for this shape."""
+    ``decay``, la_forward_gated with ``gated``) uses for this shape."""
     io_code = LA_BF16 if io == "bf16" else LA_F32
     n, sp = ctypes.c_int(), ctypes.c_int()
+    if gated:
+        _check(load_library().la_forward_gated_config(B, H, N, d, dv, io_code, PHI[phi], r, chunk, ctypes.byref(n)),
+               "la_forward_gated_config")
+        return n.value, False
     if decay:
         _check(load_library().la_forward_decay_config(B, H, N, d, dv, io_code, PHI[phi], r, chunk, ctypes.byref(n)),
                "la_forward_decay_config")
@@ -187,8 +200,22 @@ def _gamma_arg(gamma, H, dev, causal=True):
     return gamma
 
 
+def _log_gate_arg(log_gate, shape, dev, causal=True):
+    """Per-token gates: a fp32 device tensor of natural-log gates (or None)."""
+    if log_gate is None:
+        return None
+    torch = _torch()
+    if not causal:
+        raise ValueError("the gates are defined for the causal form only")
+    _require(log_gate, "log_gate", torch.float32, dev)
+    if tuple(log_gate.shape) != tuple(shape):
+        raise ValueError(f"log_gate must have shape {tuple(shape)}, got {tuple(log_gate.shape)}")
+    return log_gate
+
+
 def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, z0=None,
-            return_state=False, out=None, workspace=None, events=None, gamma=None, normalize=True):
+            return_state=False, out=None, workspace=None, events=None, gamma=None, normalize=True,
+            log_gate=None):
     """Causal (or non-causal) linear attention over Q, K [B,H,N,d], V [B,H,N,dv].
 
     Returns O [B,H,N,dv] (same dtype as Q); with ``return_state`` also the
@@ -197,7 +224,9 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
     handles from :func:`event_create` recorded around the library's kernels.
     ``gamma``: optional fp32 device tensor [H] of per-head decays in (0, 1]
     (causal only; la_forward_decay), with ``normalize=False`` for the
-    unnormalised read-out.
+    unnormalised read-out.  ``log_gate``: optional fp32 device tensor
+    [B,H,N] of per-token natural-log gates log a_t (causal only;
+    la_forward_gated), likewise with ``normalize``.
     """
     torch = _torch()
     lib = load_library()
@@ -229,20 +258,30 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
         S_out = torch.empty((B, H, r, dv), dtype=torch.float32, device=dev)
         z_out = torch.empty((B, H, r), dtype=torch.float32, device=dev)
     gamma = _gamma_arg(gamma, H, dev, causal)
-    if gamma is None and not normalize:
-        raise ValueError("normalize=False is available with a decay (gamma) only")
-    need = int(lib.la_forward_workspace_bytes(B, H, N, d, dv, io, PHI[phi], r, int(causal), chunk))
+    log_gate = _log_gate_arg(log_gate, (B, H, N), dev, causal)
+    if gamma is not None and log_gate is not None:
+        raise ValueError("give gamma or log_gate, not both")
+    if gamma is None and log_gate is None and not normalize:
+        raise ValueError("normalize=False is available with a decay (gamma or log_gate) only")
+    if (gamma is not None or log_gate is not None) and phi == "favor":
+        raise ValueError("the decay is available for the pointwise feature maps only")
+    if log_gate is not None:
+        need = int(lib.la_forward_gated_workspace_bytes(B, H, N, d, dv, io, PHI[phi], r, chunk))
+    else:
+        need = int(lib.la_forward_workspace_bytes(B, H, N, d, dv, io, PHI[phi], r, int(causal), chunk))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     tail = [chunk, _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(dev)]
     head = [_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, d, dv, io, PHI[phi], r]
-    if gamma is None:
+    if log_gate is not None:
+        args = head + [_ptr(log_gate), int(bool(normalize))] + tail
+        fn, name = ((lib.la_forward_gated, "la_forward_gated") if events is None
+                    else (lib.la_forward_gated_timed, "la_forward_gated_timed"))
+    elif gamma is None:
         args = head + [_ptr(omega), int(causal)] + tail
         fn, name = (lib.la_forward, "la_forward") if events is None else (lib.la_forward_timed, "la_forward_timed")
     else:
-        if phi == "favor":
-            raise ValueError("the decay is available for the pointwise feature maps only")
         args = head + [_ptr(gamma), int(bool(normalize))] + tail
         fn, name = ((lib.la_forward_decay, "la_forward_decay") if events is None
                     else (lib.la_forward_decay_timed, "la_forward_decay_timed"))
@@ -256,11 +295,14 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
     return out
 
 
-def decode_step(S, z, q, k, v, *, phi="elu1", omega=None, inplace=True, out=None, gamma=None, normalize=True):
+def decode_step(S, z, q, k, v, *, phi="elu1", omega=None, inplace=True, out=None, gamma=None, normalize=True,
+                log_gate=None):
     """One decode step for every (batch, head): S, z updated in place (or new
     tensors when ``inplace=False``).  Returns o, or (o, S_new, z_new).
     ``gamma``: optional fp32 device tensor [H] of per-head decays
-    (la_decode_step_decay), with ``normalize=False`` for o = phi(q)^T S'."""
+    (la_decode_step_decay), with ``normalize=False`` for o = phi(q)^T S'.
+    ``log_gate``: optional fp32 device tensor [B,H], this token's natural-log
+    gate per sequence and head (la_decode_step_gated)."""
     torch = _torch()
     lib = load_library()
     B, H, d = q.shape
@@ -283,10 +325,18 @@ def decode_step(S, z, q, k, v, *, phi="elu1", omega=None, inplace=True, out=None
     if tuple(out.shape) != (B, H, dv):
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, dv)}")
     gamma = _gamma_arg(gamma, H, dev)
-    if gamma is None and not normalize:
-        raise ValueError("normalize=False is available with a decay (gamma) only")
+    log_gate = _log_gate_arg(log_gate, (B, H), dev)
+    if gamma is not None and log_gate is not None:
+        raise ValueError("give gamma or log_gate, not both")
+    if gamma is None and log_gate is None and not normalize:
+        raise ValueError("normalize=False is available with a decay (gamma or log_gate) only")
     S_new, z_new = (S, z) if inplace else (torch.empty_like(S), torch.empty_like(z))
-    if gamma is None:
+    if log_gate is not None:
+        st = lib.la_decode_step_gated(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_new),
+                                      _ptr(z_new), B, H, d, dv, _io_code(q), PHI[phi], r, _ptr(log_gate),
+                                      int(bool(normalize)), _stream(dev))
+        _check(st, "la_decode_step_gated")
+    elif gamma is None:
         st = lib.la_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_new),
                                 _ptr(z_new), B, H, d, dv, _io_code(q), PHI[phi], r, _ptr(omega), _stream(dev))
         _check(st, "la_decode_step")

@@ -126,18 +126,19 @@ la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int p
   return LA_OK;
 }
 
-size_t workspace_for(const Shape& sh) {
+size_t workspace_for(const Shape& sh, bool gated = false) {
   if (sh.fused) return la::fused_workspace_bytes(sh.BH, sh.n_span, sh.r, sh.dv);
-  const size_t E = static_cast<size_t>(sh.r) * sh.dv + sh.r;
-  return static_cast<size_t>(sh.BH) * (static_cast<size_t>(sh.n_span) + 1) * E * sizeof(float);
+  return la::prefill_workspace_bytes(sh.BH, sh.n_span, sh.r, sh.dv, gated);
 }
 
+// gamma: fixed per-head decay; log_a: per-token gates (at most one of the two).
 la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
                        int d_v, int io, int phi, int r, const float* omega, int causal, int chunk, const float* S0,
                        const float* z0, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
-                       void* stream, void* const* events, const float* gamma = nullptr, int normalize = 1) {
+                       void* stream, void* const* events, const float* gamma = nullptr, int normalize = 1,
+                       const float* log_a = nullptr) {
   Shape sh;
-  const int decay = gamma != nullptr;
+  const int decay = gamma != nullptr || log_a != nullptr;
   la_status st = check_forward_shape(B, H, N, d, d_v, io, phi, r, causal, chunk, &sh, decay);
   if (st != LA_OK) return st;
   const bool have_tokens = sh.BH > 0 && N > 0;
@@ -145,10 +146,10 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
   if (phi == LA_PHI_FAVOR && !omega) return LA_ERR_NULL;
   if ((S0 == nullptr) != (z0 == nullptr)) return LA_ERR_NULL;
   if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_NULL;
-  const void* ptrs[] = {Q, K, V, O, omega, S0, z0, S_out, z_out, workspace, gamma};
+  const void* ptrs[] = {Q, K, V, O, omega, S0, z0, S_out, z_out, workspace, gamma, log_a};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return LA_ERR_ALIGN;
-  const size_t need = workspace_for(sh);
+  const size_t need = workspace_for(sh, log_a != nullptr);
   if (sh.BH > 0 && (!workspace || workspace_bytes < need)) return LA_ERR_WORKSPACE;
   if (sh.BH == 0) return LA_OK;
 
@@ -159,7 +160,7 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
   a.chunk = sh.chunk; a.n_span = sh.n_span; a.fused = sh.fused; a.group = fused_group();
   a.S0 = S0; a.z0 = z0; a.S_out = S_out; a.z_out = z_out;
   a.workspace = workspace; a.stream = stream; a.events = events;
-  a.gamma = gamma; a.normalize = normalize;
+  a.gamma = gamma; a.normalize = normalize; a.log_a = log_a;
   return hip_status(la::prefill_launch(a));
 }
 
@@ -213,7 +214,8 @@ namespace {
 
 la_status decode_impl(const float* S, const float* z, const void* q, const void* k, const void* v, void* o,
                       float* S_new, float* z_new, int B, int H, int d, int d_v, int io_dtype, int phi, int r,
-                      const float* omega, void* stream, const float* gamma, int normalize) {
+                      const float* omega, void* stream, const float* gamma, int normalize,
+                      const float* log_a = nullptr) {
   if (B < 0 || H < 0 || d <= 0 || d_v <= 0 || r < 0) return LA_ERR_SHAPE;
   if (static_cast<long long>(B) * H > 0x7fffffffLL) return LA_ERR_SHAPE;
   if (io_dtype != LA_F32 && io_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
@@ -223,14 +225,14 @@ la_status decode_impl(const float* S, const float* z, const void* q, const void*
   const long long BH = static_cast<long long>(B) * H;
   if (BH > 0 && (!S || !z || !q || !k || !v || !o || !S_new || !z_new)) return LA_ERR_NULL;
   if (phi == LA_PHI_FAVOR && !omega) return LA_ERR_NULL;
-  const void* ptrs[] = {S, z, q, k, v, o, S_new, z_new, omega, gamma};
+  const void* ptrs[] = {S, z, q, k, v, o, S_new, z_new, omega, gamma, log_a};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return LA_ERR_ALIGN;
   if (BH == 0) return LA_OK;
   la::DecodeArgs a;
   a.S = S; a.z = z; a.q = q; a.k = k; a.v = v; a.o = o; a.S_new = S_new; a.z_new = z_new;
   a.B = B; a.H = H; a.d = d; a.dv = d_v; a.r = rr; a.io = io_dtype; a.phi = phi; a.omega = omega;
-  a.stream = stream; a.gamma = gamma; a.normalize = normalize;
+  a.stream = stream; a.gamma = gamma; a.normalize = normalize; a.log_a = log_a;
   return hip_status(la::decode_launch(a));
 }
 
@@ -270,6 +272,48 @@ la_status la_decode_step_decay(const float* S, const float* z, const void* q, co
   if (phi == LA_PHI_FAVOR) return LA_ERR_UNSUPPORTED;
   return decode_impl(S, z, q, k, v, o, S_new, z_new, B, H, d, d_v, io_dtype, phi, r, nullptr, stream, gamma,
                      normalize);
+}
+
+size_t la_forward_gated_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r,
+                                        int chunk) {
+  Shape sh;
+  if (check_forward_shape(B, H, N, d, d_v, io_dtype, phi, r, 1, chunk, &sh, 1) != LA_OK) return 0;
+  return workspace_for(sh, true);
+}
+
+la_status la_forward_gated_config(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk,
+                                  int* n_span) {
+  return la_forward_decay_config(B, H, N, d, d_v, io_dtype, phi, r, chunk, n_span);
+}
+
+la_status la_forward_gated(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+                           int d_v, int io_dtype, int phi, int r, const float* log_a, int normalize, int chunk,
+                           const float* S0, const float* z0, float* S_out, float* z_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!log_a) return LA_ERR_NULL;
+  if (normalize != 0 && normalize != 1) return LA_ERR_UNSUPPORTED;
+  return forward_impl(Q, K, V, O, B, H, N, d, d_v, io_dtype, phi, r, nullptr, 1, chunk, S0, z0, S_out, z_out,
+                      workspace, workspace_bytes, stream, nullptr, nullptr, normalize, log_a);
+}
+
+la_status la_forward_gated_timed(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+                                 int d_v, int io_dtype, int phi, int r, const float* log_a, int normalize, int chunk,
+                                 const float* S0, const float* z0, float* S_out, float* z_out, void* workspace,
+                                 size_t workspace_bytes, void* stream, void* const* events) {
+  if (!log_a) return LA_ERR_NULL;
+  if (normalize != 0 && normalize != 1) return LA_ERR_UNSUPPORTED;
+  return forward_impl(Q, K, V, O, B, H, N, d, d_v, io_dtype, phi, r, nullptr, 1, chunk, S0, z0, S_out, z_out,
+                      workspace, workspace_bytes, stream, events, nullptr, normalize, log_a);
+}
+
+la_status la_decode_step_gated(const float* S, const float* z, const void* q, const void* k, const void* v,
+                               void* o, float* S_new, float* z_new, int B, int H, int d, int d_v, int io_dtype,
+                               int phi, int r, const float* log_a, int normalize, void* stream) {
+  if (!log_a) return LA_ERR_NULL;
+  if (normalize != 0 && normalize != 1) return LA_ERR_UNSUPPORTED;
+  if (phi == LA_PHI_FAVOR) return LA_ERR_UNSUPPORTED;
+  return decode_impl(S, z, q, k, v, o, S_new, z_new, B, H, d, d_v, io_dtype, phi, r, nullptr, stream, nullptr,
+                     normalize, log_a);
 }
 
 la_status la_feature_map(const void* X, float* Y, long long rows, int d, int io_dtype, int phi, int r,

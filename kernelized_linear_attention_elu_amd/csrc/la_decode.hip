@@ -8,7 +8,11 @@
 // With a fixed per-head decay gamma ("Efficient attention variants" sec. 7.1)
 // the old state is multiplied by gamma first: S' = gamma S + phi(k) v^T,
 // z' = gamma z + phi(k); without one gamma = 1, which changes no bit.  With
-// normalize = 0 the read-out is phi(q)^T S' (no division).
+// a per-token gate a ("Linear attention and SSM", Mamba-2 SSD section:
+// A_t = a_t I) the same with a in place of gamma, given as log a per
+// (batch, head); a gate under 2^-126 (zero included) acts as 2^-126, as in
+// the gated prefill.  With normalize = 0 the read-out is phi(q)^T S' (no
+// division).
 //
 // The step streams S once (read 4*R*DV bytes, write 4*R*DV bytes); its
 // arithmetic intensity is ~0.5 flop/byte, so it is HBM-bound and runs on the
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
                                                              float* S_new, float* z_new,
                                                              const float* __restrict__ omega,
                                                              const float* __restrict__ gamma, int H,
-                                                             int normalize) {
+                                                             int normalize, const float* __restrict__ log_a) {
   constexpr int TPR = DV / 4;          // threads per state row
   constexpr int RPP = kThreads / TPR;  // rows per pass
   static_assert(R % RPP == 0, "state rows must split evenly");
@@ -93,7 +97,8 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
   __shared__ float scratch[2][kWaves];
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
-  const float gm = gamma ? gamma[bh % H] : 1.f;
+  const float gm = log_a ? __builtin_amdgcn_exp2f(fmaxf(log_a[bh] * 1.4426950408889634f, -126.f))
+                        : gamma ? gamma[bh % H] : 1.f;
 
   features_to_lds<T, D, R, PHI>(q + (size_t)bh * D, omega, fq, xbuf, scratch[0]);
   features_to_lds<T, D, R, PHI>(k + (size_t)bh * D, omega, fk, xbuf, scratch[1]);
@@ -148,7 +153,7 @@ static hipError_t launch_decode(const DecodeArgs& a) {
   hipLaunchKernelGGL((la_decode_kernel<T, D, R, DV, PHI>), dim3(BH), dim3(kThreads), 0,
                      static_cast<hipStream_t>(a.stream), a.S, a.z, static_cast<const T*>(a.q),
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<T*>(a.o), a.S_new,
-                     a.z_new, a.omega, a.gamma, a.H > 0 ? a.H : 1, a.normalize);
+                     a.z_new, a.omega, a.gamma, a.H > 0 ? a.H : 1, a.normalize, a.log_a);
   return hipGetLastError();
 }
 

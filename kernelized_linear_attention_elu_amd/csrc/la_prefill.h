@@ -31,7 +31,19 @@ struct PrefillArgs {
   // pointwise maps only: S_t = gamma S_{t-1} + phi(k_t) v_t^T, z likewise
   const float* gamma = nullptr;
   int normalize = 1;    // 0: o_t = phi(q_t)^T S_t (no division by phi(q_t)^T z_t)
+  // per-token gate (device [B*H][N] fp32, natural log of a_t <= 0; null:
+  // none), causal pointwise maps only: S_t = a_t S_{t-1} + phi(k_t) v_t^T,
+  // z likewise; excludes gamma.  The workspace then also holds one fp32
+  // total log2 gate per (head, span) after the span states.
+  const float* log_a = nullptr;
 };
+
+// Workspace of the three-kernel path: fp32 span states [B*H][n_span+1][R*DV+R],
+// then (gated decay) the spans' total log2 gates [B*H][n_span].
+inline size_t prefill_workspace_bytes(long long BH, int n_span, int r, int dv, bool gated) {
+  const size_t E = (size_t)r * dv + r;
+  return (size_t)BH * ((size_t)n_span + 1) * E * sizeof(float) + (gated ? (size_t)BH * n_span * sizeof(float) : 0);
+}
 
 // Single-pass causal prefill (la_prefill.hip): tokens per workgroup and the
 // default number of spans per look-back block.
@@ -55,10 +67,12 @@ hipError_t favor_prefill_launch(const PrefillArgs& a);
 
 // Span scan over a workspace of R x DV states (la_prefill.hip).  With a decay
 // (gamma, H heads), a span of L tokens multiplies the running state by
-// gamma^L; span lengths follow from N, the chunk and n_span.
+// gamma^L; span lengths follow from N, the chunk and n_span.  With gates
+// (totals: [BH][n_span] total log2 gate of each span), span s multiplies it
+// by 2^totals[s].
 hipError_t scan_launch(float* ws, int BH, int R, int DV, int n_span, const float* S0, const float* z0,
                        float* S_out, float* z_out, hipStream_t stream, const float* gamma = nullptr, int H = 1,
-                       int N = 0, int chunk = 64);
+                       int N = 0, int chunk = 64, const float* totals = nullptr);
 
 struct DecodeArgs {
   const float* S;
@@ -76,6 +90,7 @@ struct DecodeArgs {
   void* stream;
   const float* gamma = nullptr;  // per-head decay (device [H]); null: none
   int normalize = 1;
+  const float* log_a = nullptr;  // this token's gate per (batch, head), natural log (device [B*H]); null: none
 };
 
 bool decode_supported(int io, int phi, int d, int dv, int r);

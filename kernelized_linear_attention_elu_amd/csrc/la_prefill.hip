@@ -99,6 +99,53 @@ __device__ __forceinline__ void state_tile(int w, int i, int& ct, int& ft) {
   ct = i;
 }
 
+// ------------------------------------------------------------------ decay kinds
+
+// How the state decays from one token to the next.
+constexpr int kNoDecay = 0;  // S_t = S_{t-1} + phi(k_t) v_t^T
+constexpr int kFixed = 1;    // S_t = gamma S_{t-1} + ..., one gamma per head (lg = log2 gamma)
+constexpr int kGated = 2;    // S_t = a_t S_{t-1} + ..., one gate per token (log a_t given)
+
+// A gate's log2 is clamped from below: a gate under 2^-126, zero included,
+// acts as 2^-126 (far below what an fp32 sum of the outputs resolves), and
+// differences of running sums stay finite (never -inf minus -inf).
+constexpr float kMinLog2Gate = -126.f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Inclusive prefix sum over the 64 lanes of a wave (six shuffle steps).
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off);
+    x = l >= off ? x + y : x;
+  }
+  return x;
+}
+
+// Running log2 gates of one chunk (kGated): lane l holds the sum of the
+// clamped log2 gates of the chunk's tokens 0..l (lo) and, for 128-token
+// chunks, 0..64+l (hi).  Gates past N load as log 0 (a gate of one), so the
+// sum stays flat there.  Every wave forms its own copy from its own loads.
+template <class CF>
+struct GateCum {
+  float lo = 0.f, hi = 0.f;
+  __device__ __forceinline__ void init(const float (&a)[CF::C > 64 ? 2 : 1]) {
+    lo = wave_prefix_sum(fmaxf(a[0] * kLog2e, kMinLog2Gate));
+    if constexpr (CF::C > 64) hi = wave_prefix_sum(fmaxf(a[1] * kLog2e, kMinLog2Gate)) + __shfl(lo, 63);
+  }
+  // the running sum through chunk token tok (0 <= tok < C; tok may differ
+  // between lanes)
+  __device__ __forceinline__ float at(int tok) const {
+    const float x = __shfl(lo, tok & 63);
+    if constexpr (CF::C > 64) {
+      const float y = __shfl(hi, tok & 63);
+      return tok < 64 ? x : y;
+    }
+    return x;
+  }
+};
+
 // ------------------------------------------------------------------ staging
 
 template <class CF, bool WITH_Q>
@@ -106,16 +153,24 @@ struct ChunkRegs {
   u32x4 q[WITH_Q ? CF::LQ : 1];
   u32x4 k[CF::LQ];
   u32x4 v[CF::LV];
+  float a[CF::C > 64 ? 2 : 1];  // natural log gates of tokens t0 + lane (+ 64) (kGated)
 };
 
 // Global -> registers for the chunk starting at token t0.  Rows beyond N
-// read as zero (buffer bounds); no load is predicated.
-template <class CF, bool WITH_Q>
+// read as zero (buffer bounds); no load is predicated.  GATED: the chunk's
+// log gates first (staging needs them before the keys), one per lane.
+template <class CF, bool WITH_Q, bool GATED = false>
 __device__ __forceinline__ void load_chunk(ChunkRegs<CF, WITH_Q>& cr, const HeadBufs& hb, int t0) {
   const int tid = threadIdx.x;
   using T = typename CF::IO;
   constexpr int QV = CF::D / CF::EPL;   // vectors per Q/K row
   constexpr int VVR = CF::DV / CF::EPL; // vectors per V row
+  if constexpr (GATED) {
+    const int lane = tid & 63;
+    cr.a[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(hb.a, (t0 + lane) * 4, 0, 0));
+    if constexpr (CF::C > 64)
+      cr.a[1] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(hb.a, (t0 + 64 + lane) * 4, 0, 0));
+  }
   // (a chunk smaller than one vector per thread, 16 tokens at d = 64, is
   // the only case that needs the vi guard; it folds away otherwise)
 #pragma unroll
@@ -142,15 +197,19 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<CF, WITH_Q>& cr, const Head
 // features so that they add nothing to the state.  With a non-null sk_lo the
 // rounding residual phi - round(phi) of the keys is stored too (a bf16 lo
 // word), so that hi + lo carries phi(K) to ~2^-16 relative.
-// Decay (DECAY, lg = log2 gamma): key j of the chunk (0-based) is weighted
-// by gamma^(len - 1 - j), its age at the end of the chunk's len tokens.  The
-// weighted features go to sk (and sk_lo) when skw is null, otherwise sk
-// keeps the plain features and skw receives the weighted ones.
-template <class CF, bool WITH_Q, bool DECAY = false>
-__device__ __forceinline__ void stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typename CF::OP* sq,
-                                            typename CF::OP* sk, typename CF::OP* sk_lo,
-                                            typename CF::OP* sv, int t0, int N, float lg = 0.f, int len = 0,
-                                            typename CF::OP* skw = nullptr) {
+// Decay (DK != kNoDecay): key j of the chunk (0-based) is weighted by its
+// decay at the end of the chunk's len tokens, gamma^(len - 1 - j) (kFixed,
+// lg = log2 gamma) or a_{j+1} ... a_{len-1} (kGated, from the running log2
+// gates, which wave 0 also writes to scum[0 .. max(C, 64)) when scum is
+// given).  The weighted features go to sk (and sk_lo) when skw is null,
+// otherwise sk keeps the plain features and skw receives the weighted ones.
+// Returns the log2 of the chunk's whole decay over its len tokens (what a
+// state carried across the chunk is multiplied by), 0 without a decay.
+template <class CF, bool WITH_Q, int DK = kNoDecay>
+__device__ __forceinline__ float stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typename CF::OP* sq,
+                                             typename CF::OP* sk, typename CF::OP* sk_lo,
+                                             typename CF::OP* sv, int t0, int N, float lg = 0.f, int len = 0,
+                                             typename CF::OP* skw = nullptr, float* scum = nullptr) {
   using T = typename CF::IO;
   using OP = typename CF::OP;
   using TQ = Tile<OP, CF::R>;
@@ -158,6 +217,19 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typ
   const int tid = threadIdx.x;
   constexpr int QV = CF::D / CF::EPL;
   constexpr int VVR = CF::DV / CF::EPL;
+  GateCum<CF> gc;
+  float total = 0.f;
+  if constexpr (DK == kGated) {
+    gc.init(cr.a);
+    total = gc.at(len - 1);
+    if (scum && wave_id() == 0) {
+      const int lane = tid & 63;
+      scum[lane] = gc.lo;
+      if constexpr (CF::C > 64) scum[64 + lane] = gc.hi;
+    }
+  } else if constexpr (DK == kFixed) {
+    total = lg * (float)len;
+  }
   // only a chunk that reaches past N has keys to mask (a uniform branch)
   auto keys = [&](auto tail) {
 #pragma unroll
@@ -177,10 +249,11 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typ
 #pragma unroll
       for (int e = 0; e < CF::EPL; ++e) f[e] = phi_pointwise<CF::PHI>(f[e]);
       u32x4 hw = u32x4{0u, 0u, 0u, 0u};  // weighted features for skw
-      if constexpr (DECAY) {
-        // (keys past len, beyond N, get a weight above one; they are
+      if constexpr (DK != kNoDecay) {
+        // (keys past len, beyond N, may get a weight above one; they are
         // zeroed below by selection, never by arithmetic)
-        const float wgt = __builtin_amdgcn_exp2f(lg * (float)(len - 1 - tok));
+        const float wgt =
+            __builtin_amdgcn_exp2f(DK == kFixed ? lg * (float)(len - 1 - tok) : total - gc.at(tok));
         if (skw) {
           float fw[CF::EPL];
 #pragma unroll
@@ -210,7 +283,7 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typ
         hw = valid ? hw : u32x4{0u, 0u, 0u, 0u};
       }
       *reinterpret_cast<u32x4*>(sk + TQ::off(tok, col)) = hi;
-      if constexpr (DECAY) {
+      if constexpr (DK != kNoDecay) {
         if (skw) *reinterpret_cast<u32x4*>(skw + TQ::off(tok, col)) = hw;
       }
       if constexpr (sizeof(OP) == 2) {
@@ -228,6 +301,7 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typ
     if (CF::VV % CF::NT == 0 || vi < CF::VV)
       *reinterpret_cast<u32x4*>(sv + TV::off(vi / VVR, (vi % VVR) * CF::EPL)) = cr.v[i];
   }
+  return total;
 }
 
 // ------------------------------------------------------------------ state update
@@ -417,17 +491,19 @@ struct OutRegs {
 //    dacc[0] = z_hi.phi(q) + rowsum(A) and dacc[1] = z_lo.phi(q).
 //    fp32: in VALU.
 // The weights and phi(Q) enter both sums exactly as rounded for the MFMA.
-// Decay (DECAY, lg = log2 gamma): for row i = 16 ib + li of the chunk the
-// carried state is i + 1 tokens old, so its read-out and its z term are
-// scaled by gamma^(i+1) (they are formed first), and weight (i, j) by
-// gamma^(i-j) before the diagonal mask.  normalize = 0 (DECAY only) skips
-// the division.
-template <class CF, bool CAUSAL, bool DECAY = false>
+// Decay (DK != kNoDecay): for row i = 16 ib + li of the chunk the carried
+// state's read-out and its z term are scaled by the decay over tokens
+// 0..i, gamma^(i+1) (kFixed, lg = log2 gamma) or 2^cum[i] (kGated; cum: the
+// chunk's running log2 gates in LDS), formed first; weight (i, j) by the
+// decay over tokens j+1..i, gamma^(i-j) or 2^(cum[i] - cum[j]), before the
+// diagonal mask.  normalize = 0 (with a decay only) skips the division.
+template <class CF, bool CAUSAL, int DK = kNoDecay>
 __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&qf)[CF::RBW][CF::R / CF::KS],
                                               const typename CF::OP* sk, const typename CF::OP* sv,
                                               const typename CF::OP* ss, const typename CF::ZT* sz,
                                               OutRegs<CF>& out, int w, int g, int li, float lg = 0.f,
-                                              int normalize = 1) {
+                                              int normalize = 1, const float* scum = nullptr) {
+  constexpr bool DECAY = DK != kNoDecay;
   using OP = typename CF::OP;
   using TQ = Tile<OP, CF::R>;
   using TV = Tile<OP, CF::DV>;
@@ -471,8 +547,10 @@ __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&q
         }
       }
     };
+    // running log2 decay through row i (kGated)
+    const float crow = DK == kGated ? scum[16 * ib + li] : 0.f;
     if constexpr (DECAY) {
-      const float rowdec = __builtin_amdgcn_exp2f(lg * (float)(16 * ib + li + 1));
+      const float rowdec = __builtin_amdgcn_exp2f(DK == kFixed ? lg * (float)(16 * ib + li + 1) : crow);
       readout();
 #pragma unroll
       for (int cti = 0; cti < CTW; ++cti) o[cti] *= rowdec;
@@ -496,11 +574,16 @@ __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&q
             t = mfma16(sk[TQ::off(16 * jb + li, QRegs<CF>::feature(ks, g))], qf[rbi][ks], t);
           }
         }
-        if constexpr (DECAY) {
+        if constexpr (DK == kFixed) {
           // gamma^(i-j); above the diagonal the factor exceeds one, and those
           // entries are then replaced by zero (selection below)
 #pragma unroll
           for (int r = 0; r < 4; ++r) t[r] *= __builtin_amdgcn_exp2f(lg * (float)(16 * (ib - jb) + li - 4 * g - r));
+        } else if constexpr (DK == kGated) {
+          // 2^(cum[i] - cum[j]) (above the diagonal: replaced by selection)
+          const f32x4 cj = *reinterpret_cast<const f32x4*>(scum + 16 * jb + 4 * g);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) t[r] *= __builtin_amdgcn_exp2f(crow - cj[r]);
         }
         if constexpr (PL == 8) {
           if (jb == ib) {  // wave-uniform: only the diagonal block is masked
@@ -720,15 +803,18 @@ struct SmemOut {
   alignas(16) typename CF::ZT z[CF::ZE];
   alignas(16) OP scr[Scratch<CF>::ELEMS];
   __device__ OP* kw_tile() { return nullptr; }
+  __device__ float* cum_tile() { return nullptr; }
 };
-// With a decay: also the keys' features weighted by their age at the end of
-// the chunk, gamma^(C - 1 - j), which the state carry contracts (the
-// weights use the plain features).
+// With a decay: also the keys' features weighted by their decay at the end
+// of the chunk, which the state carry contracts (the weights use the plain
+// features), and (gated) the chunk's running log2 gates.
 template <class CF>
 struct SmemOutDecay : SmemOut<CF> {
   using OP = typename CF::OP;
   alignas(16) OP kw[Tile<OP, CF::R>::elems(CF::C)];
+  alignas(16) float cum[CF::C > 64 ? CF::C : 64];
   __device__ OP* kw_tile() { return kw; }
+  __device__ float* cum_tile() { return cum; }
 };
 
 // LDS of the non-causal output kernel: the full-sequence sums only.
@@ -762,24 +848,31 @@ __device__ __forceinline__ HeadBufs head_bufs(const typename CF::IO* Q, const ty
 }
 
 // Per-span state: dS = phi(K_span)^T V_span, dz = sum phi(K_span) -> ws slot s.
-// With a decay (DECAY, gamma[head]), the span's sum is decayed to the span's
-// end: key t enters with gamma^(t_end - 1 - t).  Per chunk of len tokens the
-// running sum is multiplied by gamma^len before the chunk's keys, weighted
-// by gamma^(len - 1 - j), are added.
-template <class CF, bool DECAY = false>
+// With a decay (DK != kNoDecay: gamma[head], or the head's per-token log
+// gates log_a[bh][N]), the span's sum is decayed to the span's end: key t
+// enters with its decay over tokens t+1 .. t_end-1.  Per chunk the running
+// sum is multiplied by the chunk's whole decay before the chunk's keys,
+// weighted by their decay to the chunk's end, are added.  Gated: the span's
+// total log2 gate goes to totals[bh][s] for the span scan.
+template <class CF, int DK = kNoDecay>
 __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO* __restrict__ K,
                                                             const typename CF::IO* __restrict__ V,
                                                             float* __restrict__ ws, int N, int n_span,
-                                                            const float* __restrict__ gamma, int H) {
+                                                            const float* __restrict__ gamma, int H,
+                                                            const float* __restrict__ log_a,
+                                                            float* __restrict__ totals) {
   using OP = typename CF::OP;
+  constexpr bool DECAY = DK != kNoDecay, GATED = DK == kGated;
   __shared__ SmemState<CF> sm;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
   const int bh = blockIdx.x / n_span;
   const int s = blockIdx.x % n_span;
   const int t_begin = span_begin<CF>(s, n_span, N);
   const int t_end = span_begin<CF>(s + 1, n_span, N);
-  const HeadBufs hb = head_bufs<CF>(nullptr, K, V, nullptr, bh, N);
-  const float lg = DECAY ? __builtin_amdgcn_logf(gamma[bh % H]) : 0.f;  // log2(gamma)
+  HeadBufs hb = head_bufs<CF>(nullptr, K, V, nullptr, bh, N);
+  if constexpr (GATED) hb.a = make_rsrc(log_a + (size_t)bh * N, (unsigned)N * 4u);
+  const float lg = DK == kFixed ? __builtin_amdgcn_logf(gamma[bh % H]) : 0.f;  // log2(gamma)
+  float span_l2 = 0.f;  // gated: the span's total log2 gate so far
 
   f32x4 acc[CF::TPW];
 #pragma unroll
@@ -787,10 +880,11 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
   f32x4 zt[CF::ZPW];
 #pragma unroll
   for (int k = 0; k < CF::ZPW; ++k) zt[k] = zero4();
-  // decay of the running sum over a chunk of len tokens
-  auto age = [&](int len) {
+  // decay of the running sum over a chunk whose whole log2 decay is l2
+  auto age = [&](float l2) {
     if constexpr (DECAY) {
-      const float dg = __builtin_amdgcn_exp2f(lg * (float)len);
+      span_l2 += l2;
+      const float dg = __builtin_amdgcn_exp2f(l2);
 #pragma unroll
       for (int i = 0; i < CF::TPW; ++i) acc[i] *= dg;
 #pragma unroll
@@ -805,30 +899,34 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
   // memory operations and the counter waits stay exact.
   const int last = t_end > t_begin ? t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C : t_begin;
   ChunkRegs<CF, false> ca, cb;
-  load_chunk<CF, false>(ca, hb, t_begin);
+  load_chunk<CF, false, GATED>(ca, hb, t_begin);
   mem_order_fence();  // ca's loads first, as in the loop: exact counter waits
-  load_chunk<CF, false>(cb, hb, min(t_begin + CF::C, last));
+  load_chunk<CF, false, GATED>(cb, hb, min(t_begin + CF::C, last));
   int buf = 0;
   for (int t0 = t_begin; t0 < t_end; t0 += 2 * CF::C) {
     OP* lo = sizeof(OP) == 2 ? sm.k_lo[buf] : nullptr;
     const int len_a = min(CF::C, t_end - t0);
-    stage_chunk<CF, false, DECAY>(ca, nullptr, sm.k[buf], lo, sm.v[buf], t0, N, lg, len_a);
-    load_chunk<CF, false>(ca, hb, min(t0 + 2 * CF::C, last));
+    const float l2a = stage_chunk<CF, false, DK>(ca, nullptr, sm.k[buf], lo, sm.v[buf], t0, N, lg, len_a);
+    load_chunk<CF, false, GATED>(ca, hb, min(t0 + 2 * CF::C, last));
     __syncthreads();
-    age(len_a);
+    age(l2a);
     state_mfma<CF>(acc, zt, sm.k[buf], lo, sm.v[buf], w, g, li);
     buf ^= 1;
     const bool second = t0 + CF::C < t_end;  // workgroup-uniform
     const int len_b = min(CF::C, t_end - t0 - CF::C);
     lo = sizeof(OP) == 2 ? sm.k_lo[buf] : nullptr;
-    if (second) stage_chunk<CF, false, DECAY>(cb, nullptr, sm.k[buf], lo, sm.v[buf], t0 + CF::C, N, lg, len_b);
-    load_chunk<CF, false>(cb, hb, min(t0 + 3 * CF::C, last));
+    float l2b = 0.f;
+    if (second) l2b = stage_chunk<CF, false, DK>(cb, nullptr, sm.k[buf], lo, sm.v[buf], t0 + CF::C, N, lg, len_b);
+    load_chunk<CF, false, GATED>(cb, hb, min(t0 + 3 * CF::C, last));
     if (second) {
       __syncthreads();
-      age(len_b);
+      age(l2b);
       state_mfma<CF>(acc, zt, sm.k[buf], lo, sm.v[buf], w, g, li);
       buf ^= 1;
     }
+  }
+  if constexpr (GATED) {
+    if (tid == 0) totals[(size_t)bh * n_span + s] = span_l2;
   }
 
   constexpr int E = CF::R * CF::DV + CF::R;
@@ -852,15 +950,18 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
 // running state is multiplied by gamma^L before a span of L tokens is added
 // (each span's own sum is already decayed to the span's end); the span
 // lengths are walked with an incremental quotient and remainder of
-// s * n_chunks / n_span, the split span_begin uses.
-template <bool DECAY>
+// s * n_chunks / n_span, the split span_begin uses.  With gates (kGated)
+// the running state is multiplied by 2^totals[bh][s], the span's total log2
+// gate, instead.
+template <int DK>
 __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ ws, int R, int DV, int n_span,
                                                            const float* __restrict__ S0,
                                                            const float* __restrict__ z0,
                                                            float* __restrict__ S_out,
                                                            float* __restrict__ z_out,
                                                            const float* __restrict__ gamma, int H, int N,
-                                                           int chunk) {
+                                                           int chunk, const float* __restrict__ totals) {
+  constexpr bool DECAY = DK == kFixed;
   const int E = R * DV + R;
   const int e = blockIdx.x * kThreads + threadIdx.x;
   const int bh = blockIdx.y;
@@ -886,13 +987,18 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
   // scan costs ceil(n_span / 16) memory round trips instead of n_span
   constexpr int kBatch = 16;
   for (int s0 = 0; s0 < n_span; s0 += kBatch) {
-    float x[kBatch];
+    float x[kBatch], tl[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) x[j] = s0 + j < n_span ? p[(size_t)(s0 + j) * E] : 0.f;
+    if constexpr (DK == kGated) {
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) tl[j] = s0 + j < n_span ? totals[(size_t)bh * n_span + s0 + j] : 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (s0 + j < n_span) {
         p[(size_t)(s0 + j) * E] = acc;
+        if constexpr (DK == kGated) acc *= __builtin_amdgcn_exp2f(tl[j]);
         if constexpr (DECAY) {
           rem += r_ch;
           const int step = q_ch + (rem >= n_span ? 1 : 0);
@@ -919,18 +1025,17 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
 // c+1 is loaded into registers while chunk c is computed; LDS holds one
 // chunk, with a barrier before it is overwritten and one after it is written;
 // chunk c's outputs are stored before the state update.
-// With a decay (DECAY, causal only): chunk_outputs applies gamma to the
-// weights and to the carried state's read-out, and the carry is
-// S <- gamma^C S + sum_j gamma^(C-1-j) phi(k_j) v_j^T (z likewise), from the
-// weighted feature tile.
-template <class CF, bool CAUSAL, bool DECAY = false>
-__global__ __launch_bounds__(CF::NT, DECAY ? CF::MINB_DECAY : CF::MINB) void la_output_kernel(const typename CF::IO* __restrict__ Q,
-                                                                const typename CF::IO* __restrict__ K,
-                                                                const typename CF::IO* __restrict__ V,
-                                                                typename CF::IO* __restrict__ O,
-                                                                const float* __restrict__ ws, int N, int n_span,
-                                                                const float* __restrict__ gamma, int H,
-                                                                int normalize) {
+// With a decay (DK != kNoDecay, causal only): chunk_outputs applies it to
+// the weights and to the carried state's read-out, and the carry is
+// S <- D S + sum_j D_j phi(k_j) v_j^T (z likewise), from the weighted
+// feature tile, with D the chunk's whole decay and D_j key j's decay to the
+// chunk's end (gamma^C and gamma^(C-1-j), or products of the chunk's gates).
+template <class CF, bool CAUSAL, int DK = kNoDecay>
+__global__ __launch_bounds__(CF::NT, DK != kNoDecay ? CF::MINB_DECAY : CF::MINB) void la_output_kernel(
+    const typename CF::IO* __restrict__ Q, const typename CF::IO* __restrict__ K,
+    const typename CF::IO* __restrict__ V, typename CF::IO* __restrict__ O, const float* __restrict__ ws, int N,
+    int n_span, const float* __restrict__ gamma, int H, int normalize, const float* __restrict__ log_a) {
+  constexpr bool DECAY = DK != kNoDecay, GATED = DK == kGated;
   static_assert(CAUSAL || !DECAY, "the decay is defined for the causal form");
   __shared__ typename std::conditional<CAUSAL, typename std::conditional<DECAY, SmemOutDecay<CF>, SmemOut<CF>>::type,
                                        SmemOutNC<CF>>::type sm;
@@ -942,8 +1047,9 @@ __global__ __launch_bounds__(CF::NT, DECAY ? CF::MINB_DECAY : CF::MINB) void la_
   const int s = blockIdx.x % n_span;
   const int t_begin = span_begin<CF>(s, n_span, N);
   const int t_end = span_begin<CF>(s + 1, n_span, N);
-  const HeadBufs hb = head_bufs<CF>(Q, K, V, O, bh, N);
-  const float lg = DECAY ? __builtin_amdgcn_logf(gamma[bh % H]) : 0.f;  // log2(gamma)
+  HeadBufs hb = head_bufs<CF>(Q, K, V, O, bh, N);
+  if constexpr (GATED) hb.a = make_rsrc(log_a + (size_t)bh * N, (unsigned)N * 4u);
+  const float lg = DK == kFixed ? __builtin_amdgcn_logf(gamma[bh % H]) : 0.f;  // log2(gamma)
 
   // carried state: this wave's tiles of S (fp32) and its z tiles
   constexpr int E = CF::R * CF::DV + CF::R;
@@ -995,7 +1101,7 @@ __global__ __launch_bounds__(CF::NT, DECAY ? CF::MINB_DECAY : CF::MINB) void la_
     const int last = t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C;
     ChunkRegs<CF, false> cr;
     QRegs<CF> qr;
-    load_chunk<CF, false>(cr, hb, t_begin);
+    load_chunk<CF, false, GATED>(cr, hb, t_begin);
     mem_order_fence();
     qr.load(hb.q, t_begin, w, g, li);
     mem_order_fence();
@@ -1005,19 +1111,20 @@ __global__ __launch_bounds__(CF::NT, DECAY ? CF::MINB_DECAY : CF::MINB) void la_
     do {
       __syncthreads();  // every wave is done with the previous chunk's S, z, phi(K), V
       publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
-      stage_chunk<CF, false, DECAY>(cr, nullptr, sm.k, nullptr, sm.v, t0, N, lg, CF::C, sm.kw_tile());
+      const float l2 =
+          stage_chunk<CF, false, DK>(cr, nullptr, sm.k, nullptr, sm.v, t0, N, lg, CF::C, sm.kw_tile(), sm.cum_tile());
       typename QRegs<CF>::frag qf[CF::RBW][CF::R / CF::KS];
       qr.to_frags(qf, scr, g, li);
       const int tn = min(t0 + CF::C, last);
-      load_chunk<CF, false>(cr, hb, tn);
+      load_chunk<CF, false, GATED>(cr, hb, tn);
       qr.load(hb.q, tn, w, g, li);
       __syncthreads();
-      chunk_outputs<CF, true, DECAY>(qf, sm.k, sm.v, sm.s, sm.z, out, w, g, li, lg, normalize);
+      chunk_outputs<CF, true, DK>(qf, sm.k, sm.v, sm.s, sm.z, out, w, g, li, lg, normalize, sm.cum_tile());
       store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
       if constexpr (DECAY) {
         // the carry past this chunk (unused after a span's last chunk, so a
-        // partial last chunk needs no other length)
-        const float dg = __builtin_amdgcn_exp2f(lg * (float)CF::C);
+        // partial last chunk needs no other length; gates past N are one)
+        const float dg = __builtin_amdgcn_exp2f(l2);
 #pragma unroll
         for (int i = 0; i < CF::TPW; ++i) sacc[i] *= dg;
 #pragma unroll
@@ -1309,33 +1416,42 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
   auto rec = [&](int i) {
     if (a.events && a.events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a.events[i]), st);
   };
-  const bool decay = a.gamma != nullptr && a.causal;
+  const int dk = !a.causal ? kNoDecay : a.log_a ? kGated : a.gamma ? kFixed : kNoDecay;
+  // gated: the spans' total log2 gates follow the span states
+  float* totals = dk == kGated ? ws + (size_t)BH * (n_span + 1) * (CF::R * CF::DV + CF::R) : nullptr;
+  const dim3 grid(BH * n_span), block(CF::NT);
   rec(0);
   if (n_span > 0 && BH > 0) {
-    if (decay)
-      hipLaunchKernelGGL((la_state_kernel<CF, true>), dim3(BH * n_span), dim3(CF::NT), 0, st, K, V, ws, a.N, n_span,
-                         a.gamma, a.H);
+    if (dk == kGated)
+      hipLaunchKernelGGL((la_state_kernel<CF, kGated>), grid, block, 0, st, K, V, ws, a.N, n_span, nullptr, 1,
+                         a.log_a, totals);
+    else if (dk == kFixed)
+      hipLaunchKernelGGL((la_state_kernel<CF, kFixed>), grid, block, 0, st, K, V, ws, a.N, n_span, a.gamma, a.H,
+                         nullptr, nullptr);
     else
-      hipLaunchKernelGGL((la_state_kernel<CF, false>), dim3(BH * n_span), dim3(CF::NT), 0, st, K, V, ws, a.N, n_span,
-                         nullptr, 1);
+      hipLaunchKernelGGL((la_state_kernel<CF, kNoDecay>), grid, block, 0, st, K, V, ws, a.N, n_span, nullptr, 1,
+                         nullptr, nullptr);
   }
   rec(1);
   rec(2);
   hipError_t e = scan_launch(ws, BH, CF::R, CF::DV, n_span, a.S0, a.z0, a.S_out, a.z_out, st,
-                             decay ? a.gamma : nullptr, a.H, a.N, CF::C);
+                             dk == kFixed ? a.gamma : nullptr, a.H, a.N, CF::C, totals);
   if (e != hipSuccess) return e;
   rec(3);
   rec(4);
   if (n_span > 0 && BH > 0) {
-    if (decay)
-      hipLaunchKernelGGL((la_output_kernel<CF, true, true>), dim3(BH * n_span), dim3(CF::NT), 0, st, Q, K, V, O, ws,
-                         a.N, n_span, a.gamma, a.H, a.normalize);
+    if (dk == kGated)
+      hipLaunchKernelGGL((la_output_kernel<CF, true, kGated>), grid, block, 0, st, Q, K, V, O, ws, a.N, n_span,
+                         nullptr, 1, a.normalize, a.log_a);
+    else if (dk == kFixed)
+      hipLaunchKernelGGL((la_output_kernel<CF, true, kFixed>), grid, block, 0, st, Q, K, V, O, ws, a.N, n_span,
+                         a.gamma, a.H, a.normalize, nullptr);
     else if (a.causal)
-      hipLaunchKernelGGL((la_output_kernel<CF, true>), dim3(BH * n_span), dim3(CF::NT), 0, st, Q, K, V, O, ws,
-                         a.N, n_span, nullptr, 1, 1);
+      hipLaunchKernelGGL((la_output_kernel<CF, true>), grid, block, 0, st, Q, K, V, O, ws, a.N, n_span, nullptr, 1,
+                         1, nullptr);
     else
-      hipLaunchKernelGGL((la_output_kernel<CF, false>), dim3(BH * n_span), dim3(CF::NT), 0, st, Q, K, V, O, ws,
-                         a.N, n_span, nullptr, 1, 1);
+      hipLaunchKernelGGL((la_output_kernel<CF, false>), grid, block, 0, st, Q, K, V, O, ws, a.N, n_span, nullptr,
+                         1, 1, nullptr);
   }
   rec(5);
   return hipGetLastError();
@@ -1358,16 +1474,20 @@ static hipError_t dispatch_chunk(const PrefillArgs& a) {
 }
 
 hipError_t scan_launch(float* ws, int BH, int R, int DV, int n_span, const float* S0, const float* z0,
-                       float* S_out, float* z_out, hipStream_t stream, const float* gamma, int H, int N, int chunk) {
+                       float* S_out, float* z_out, hipStream_t stream, const float* gamma, int H, int N, int chunk,
+                       const float* totals) {
   const int E = R * DV + R;
   if (BH > 0) {
     const dim3 grid((E + kThreads - 1) / kThreads, BH);
-    if (gamma)
-      hipLaunchKernelGGL(la_scan_kernel<true>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0, S_out,
-                         z_out, gamma, H > 0 ? H : 1, N, chunk > 0 ? chunk : 64);
+    if (totals)
+      hipLaunchKernelGGL(la_scan_kernel<kGated>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0, S_out,
+                         z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, totals);
+    else if (gamma)
+      hipLaunchKernelGGL(la_scan_kernel<kFixed>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0, S_out,
+                         z_out, gamma, H > 0 ? H : 1, N, chunk > 0 ? chunk : 64, nullptr);
     else
-      hipLaunchKernelGGL(la_scan_kernel<false>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0, S_out,
-                         z_out, nullptr, 1, N, chunk > 0 ? chunk : 64);
+      hipLaunchKernelGGL(la_scan_kernel<kNoDecay>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0,
+                         S_out, z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, nullptr);
   }
   return hipGetLastError();
 }

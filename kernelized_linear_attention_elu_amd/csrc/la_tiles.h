@@ -102,6 +102,7 @@ __device__ __forceinline__ bf16x8 tr_frag_lo(const bf16* base, int ra, int col_b
 // Buffer resources of one head's Q, K (N x D) and V, O (N x DV).
 struct HeadBufs {
   __amdgpu_buffer_rsrc_t q, k, v, o;
+  __amdgpu_buffer_rsrc_t a;  // per-token log gates of the head (gated decay only)
 };
 
 }  // namespace la

@@ -119,6 +119,28 @@ def decay_gammas(H):
     return (1.0 - 2.0 ** (-e)).astype(np.float32)
 
 
+GATE_SEED = 20251203
+
+
+def draw_log_gates(B, H, N, seed=GATE_SEED, resets=0):
+    """Per-token natural-log gates for the gated (SSD-form) workloads, float32
+    [B, H, N]: log a_t = -dt_t * A_h with dt_t log-uniform in [1e-3, 1e-1]
+    and A_h = 1 + 15 h / (H - 1), the step and rate ranges Mamba-2 initialises
+    its selective step and scalar decay with (the pages give no values; they
+    describe a large step forgetting the history and a small one keeping it).
+    ``resets`` tokens per head, at seeded positions, get log a = -inf (a zero
+    gate).  Deterministic."""
+    rng = np.random.default_rng(seed)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=(B, H, N)))
+    A = 1.0 + 15.0 * np.arange(H, dtype=np.float64) / max(H - 1, 1)
+    out = (-dt * A[None, :, None]).astype(np.float32)
+    for b in range(B):
+        for h in range(H):
+            if resets and N:
+                out[b, h, rng.choice(N, size=min(resets, N), replace=False)] = -np.inf
+    return out
+
+
 @dataclass(frozen=True)
 class Workload:
     """Shapes of one named workload (no arithmetic)."""

@@ -179,6 +179,43 @@ def test_decay_argument_errors(lib):
     assert lib.la_forward_decay_config(1, 32, 32768, 64, 64, 1, 1, 256, 64, ctypes.byref(n)) == 3
 
 
+def test_gated_argument_errors(lib):
+    """la_forward_gated / la_decode_step_gated / the gated workspace query:
+    every case returns before any HIP call."""
+    def fg(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, B=1, H=1, N=64, d=64, dv=64, io=1, phi=0, r=0, log_a=FAKE,
+           normalize=1, chunk=64, S0=None, z0=None, S_out=None, z_out=None, ws=FAKE, ws_bytes=1 << 30):
+        return lib.la_forward_gated(Q, K, V, O, B, H, N, d, dv, io, phi, r, log_a, normalize, chunk, S0, z0, S_out,
+                                    z_out, ws, ws_bytes, None)
+    assert fg(log_a=None) == 1                           # LA_ERR_NULL
+    assert fg(V=None) == 1
+    assert fg(H=-1) == 2                                 # LA_ERR_SHAPE
+    assert fg(normalize=5) == 3                          # LA_ERR_UNSUPPORTED
+    assert fg(phi=1, r=256) == 3                         # no FAVOR+ with gates
+    assert fg(chunk=48) == 3
+    assert fg(log_a=MISALIGNED) == 4                     # LA_ERR_ALIGN
+    assert fg(ws=None) == 5                              # LA_ERR_WORKSPACE
+    assert fg(Q=None, K=None, V=None, O=None, H=0, ws=None) == 0
+    # the gated workspace adds one fp32 total per (head, span) to the states
+    B, H, N = 1, 32, 32768
+    n = ctypes.c_int()
+    assert lib.la_forward_gated_config(B, H, N, 64, 64, 1, 0, 0, 64, ctypes.byref(n)) == 0 and n.value == 16
+    need = lib.la_forward_gated_workspace_bytes(B, H, N, 64, 64, 1, 0, 0, 64)
+    assert need == B * H * ((n.value + 1) * (64 * 64 + 64) + n.value) * 4
+    assert fg(B=B, H=H, N=N, ws_bytes=need - 4) == 5
+    assert lib.la_forward_gated_workspace_bytes(B, H, N, 64, 64, 1, 1, 256, 64) == 0
+    assert lib.la_forward_gated_workspace_bytes(B, H, N, 96, 96, 1, 0, 0, 64) == 0
+
+    def dg(S=FAKE, z=FAKE, q=FAKE, k=FAKE, v=FAKE, o=FAKE, Sn=FAKE, zn=FAKE, B=1, H=1, d=64, dv=64, io=1,
+           phi=0, r=0, log_a=FAKE, normalize=1):
+        return lib.la_decode_step_gated(S, z, q, k, v, o, Sn, zn, B, H, d, dv, io, phi, r, log_a, normalize, None)
+    assert dg(log_a=None) == 1
+    assert dg(o=None) == 1
+    assert dg(normalize=2) == 3
+    assert dg(phi=1, r=256) == 3
+    assert dg(log_a=MISALIGNED) == 4
+    assert dg(H=0, S=None) == 0
+
+
 def test_feature_map_argument_errors(lib):
     def fm(X=FAKE, Y=FAKE, rows=10, d=64, io=1, phi=0, r=0, omega=None):
         return lib.la_feature_map(X, Y, rows, d, io, phi, r, omega, None)
