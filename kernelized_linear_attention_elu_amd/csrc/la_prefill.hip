@@ -112,14 +112,22 @@ constexpr int kGated = 2;    // S_t = a_t S_{t-1} + ..., one gate per token (log
 constexpr float kMinLog2Gate = -126.f;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Inclusive prefix sum over the 64 lanes of a wave (six shuffle steps).
+// Inclusive prefix sum over the 64 lanes of a wave, in VALU data-parallel
+// moves (DPP): shifts by 1, 2, 4 and 8 lanes inside each 16-lane row (lanes
+// shifted in from outside the row read zero), then lane 15 of rows 0 and 2
+// added into rows 1 and 3, then lane 31 into rows 2 and 3.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_add(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false);
+  return x + __int_as_float(y);
+}
 __device__ __forceinline__ float wave_prefix_sum(float x) {
-  const int l = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(x, off);
-    x = l >= off ? x + y : x;
-  }
+  x = dpp_add<0x111>(x);        // row_shr:1
+  x = dpp_add<0x112>(x);        // row_shr:2
+  x = dpp_add<0x114>(x);        // row_shr:4
+  x = dpp_add<0x118>(x);        // row_shr:8
+  x = dpp_add<0x142, 0xa>(x);   // row_bcast:15 into rows 1, 3
+  x = dpp_add<0x143, 0xc>(x);   // row_bcast:31 into rows 2, 3
   return x;
 }
 
@@ -132,7 +140,18 @@ struct GateCum {
   float lo = 0.f, hi = 0.f;
   __device__ __forceinline__ void init(const float (&a)[CF::C > 64 ? 2 : 1]) {
     lo = wave_prefix_sum(fmaxf(a[0] * kLog2e, kMinLog2Gate));
-    if constexpr (CF::C > 64) hi = wave_prefix_sum(fmaxf(a[1] * kLog2e, kMinLog2Gate)) + __shfl(lo, 63);
+    if constexpr (CF::C > 64) hi = wave_prefix_sum(fmaxf(a[1] * kLog2e, kMinLog2Gate)) + lane_value(lo, 63);
+  }
+  // the value lane 'lane' holds, for a wave-uniform lane (a scalar read)
+  __device__ static __forceinline__ float lane_value(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), __builtin_amdgcn_readfirstlane(lane)));
+  }
+  // the running sum through chunk token tok, for a wave-uniform tok
+  __device__ __forceinline__ float at_uniform(int tok) const {
+    if constexpr (CF::C > 64) {
+      if (tok >= 64) return lane_value(hi, tok - 64);
+    }
+    return lane_value(lo, tok);
   }
   // the running sum through chunk token tok (0 <= tok < C; tok may differ
   // between lanes)
@@ -221,7 +240,7 @@ __device__ __forceinline__ float stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, ty
   float total = 0.f;
   if constexpr (DK == kGated) {
     gc.init(cr.a);
-    total = gc.at(len - 1);
+    total = gc.at_uniform(len - 1);
     if (scum && wave_id() == 0) {
       const int lane = tid & 63;
       scum[lane] = gc.lo;
