@@ -111,6 +111,8 @@ def parse_args(argv=None):
                    help="causal prefill with a fixed per-head decay (RetNet form, la_forward_decay)")
     p.add_argument("--gated", action="store_true",
                    help="causal prefill with a per-token scalar gate (SSD scalar-decay form, la_forward_gated)")
+    p.add_argument("--gla", action="store_true",
+                   help="causal prefill with a per-token, per-key-channel gate (GLA form, la_forward_gla)")
     p.add_argument("--chunk", type=int, default=None,
                    help="chunk size (default: the workload's, 0 = the library's choice)")
     p.add_argument("--settle", type=float, default=SETTLE_S,
@@ -132,17 +134,21 @@ def cpu_info():
     return model
 
 
-def time_oracle_prefill(q, k, v, causal, max_heads, phi="elu1", omega=None, gamma=None, log_a=None):
+def time_oracle_prefill(q, k, v, causal, max_heads, phi="elu1", omega=None, gamma=None, log_a=None, log_a_ch=None):
     """fp64 oracle (token recurrence, decayed when ``gamma`` is given, gated
     when ``log_a`` is, or the reassociated non-causal form) on the first
     ``max_heads`` heads of batch 0; returns (seconds, heads, cores)."""
     from oracle import linear_attention as ora
     from oracle import decay as dec
     from oracle import gated as gat
+    from oracle import gla
     import numpy as np
     h = min(max_heads, q.shape[1])
     t0, c0 = time.perf_counter(), time.process_time()
-    if log_a is not None:
+    if log_a_ch is not None:
+        gla.recurrent_gla(q[:1, :h], k[:1, :h], v[:1, :h],
+                          np.maximum(np.exp(log_a_ch[:1, :h].astype("float64")), 2.0 ** -14), phi=phi)
+    elif log_a is not None:
         gat.recurrent_gated(q[:1, :h], k[:1, :h], v[:1, :h], np.exp(log_a[:1, :h].astype("float64")), phi=phi)
     elif gamma is not None:
         dec.recurrent_decay(q[:1, :h], k[:1, :h], v[:1, :h], gamma[:h].astype("float64"), phi=phi)
@@ -161,14 +167,17 @@ def bench_prefill(args, torch, la, synth):
     if args.chunk is not None:
         w = dataclasses.replace(w, chunk=args.chunk)
     causal = not args.noncausal
-    if (args.decay or args.gated) and (not causal or w.phi == "favor"):
-        raise SystemExit("--decay / --gated: causal pointwise-feature workloads only")
-    if args.decay and args.gated:
-        raise SystemExit("--decay and --gated exclude each other")
+    if (args.decay or args.gated or args.gla) and (not causal or w.phi == "favor"):
+        raise SystemExit("--decay / --gated / --gla: causal pointwise-feature workloads only")
+    if args.decay + args.gated + args.gla > 1:
+        raise SystemExit("--decay, --gated and --gla exclude each other")
+    if args.gla and w.d == 128 and args.chunk is None:
+        w = dataclasses.replace(w, chunk=32)   # the per-channel gated kernels take chunks up to 32 at d = 128
     dev = torch.device("cuda:0")
     q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
     gamma = synth.decay_gammas(w.H) if args.decay else None
     log_a = synth.draw_log_gates(w.B, w.H, w.N) if args.gated else None
+    log_a_ch = synth.draw_log_gates_ch(w.B, w.H, w.N, w.r) if args.gla else None
 
     def to_dev(x):
         return hostio.upload_bf16_bits(synth.bf16_bits(x), dev)
@@ -182,19 +191,23 @@ def bench_prefill(args, torch, la, synth):
     omega = synth.draw_omega(w.r, w.d) if w.phi == "favor" else None
     om_dev = hostio.upload_f32(omega, dev) if omega is not None else None
     gamma_dev = hostio.upload_f32(gamma, dev) if gamma is not None else None
-    gates = None
+    gates = gates_ch = None
     if log_a is not None:
         g0 = hostio.upload_f32(log_a, dev)
         gates = [g0] + [g0.clone() for _ in range(ROTATE - 1)]
+    if log_a_ch is not None:
+        g0 = hostio.upload_f32(log_a_ch, dev)
+        gates_ch = [g0] + [g0.clone() for _ in range(ROTATE - 1)]
     ws = torch.empty(la.workspace_bytes(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
-                                        chunk=w.chunk, gated=log_a is not None),
+                                        chunk=w.chunk, gated=log_a is not None, gla=log_a_ch is not None),
                      dtype=torch.uint8, device=dev)
 
     def step(i, events=None):
         Q, K, V = sets[i % ROTATE]
         la.forward(Q, K, V, phi=w.phi, omega=om_dev, causal=causal, chunk=w.chunk, out=outs[i % ROTATE],
                    workspace=ws, events=events, gamma=gamma_dev,
-                   log_gate=gates[i % ROTATE] if gates is not None else None)
+                   log_gate=gates[i % ROTATE] if gates is not None else None,
+                   log_gate_ch=gates_ch[i % ROTATE] if gates_ch is not None else None)
 
     for i in range(args.warmup):
         step(i)
@@ -232,13 +245,16 @@ def bench_prefill(args, torch, la, synth):
     alg_bytes = token_heads * (2 * w.d + 2 * w.dv) * 2          # read Q, K, V, write O (bf16)
     if log_a is not None:
         alg_bytes += token_heads * 4                             # read the fp32 log gates
+    if log_a_ch is not None:
+        alg_bytes += token_heads * 4 * w.r                       # read the fp32 per-channel log gates
     # features (FAVOR+: two d x r projections), state build + read-out
     # (4 r dv), intra-chunk products over full C x C tiles
     feat_flops = 2 * 2 * w.d * w.r if w.phi == "favor" else 0
     alg_flops = token_heads * (feat_flops + 4 * w.r * w.dv + (2 * w.chunk * (w.r + w.dv) if causal else 0))
     out_ms = out_live_ms
     n_span, single_pass = la.forward_config(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
-                                            chunk=w.chunk, decay=gamma is not None, gated=log_a is not None)
+                                            chunk=w.chunk, decay=gamma is not None, gated=log_a is not None,
+                                            gla=log_a_ch is not None)
     names = (FAVOR_KERNEL_NAMES if w.phi == "favor" else FUSED_KERNEL_NAMES if single_pass else KERNEL_NAMES)
     out_kernel = names[2]
     traffic = read_traffic(args.workload + ("" if causal else "_noncausal"), out_kernel)
@@ -277,9 +293,12 @@ def bench_prefill(args, torch, la, synth):
                         f"{'causal' if causal else 'non-causal'}, chunk {w.chunk}"
                         + (", per-head decay gamma_h = 1 - 2^-(5 + 7h/(H-1)) (RetNet form)" if gamma is not None else "")
                         + (", per-token gates log a = -dt A_h, dt log-uniform [1e-3, 1e-1], A_h = 1 + 15h/(H-1)"
-                           " (SSD scalar-decay form)" if log_a is not None else ""),
+                           " (SSD scalar-decay form)" if log_a is not None else "")
+                        + (", per-token per-key-channel gates sigmoid(x)^(1/16), x ~ N(0, 4) (GLA form)"
+                           if log_a_ch is not None else ""),
             "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv, "r": w.r, "chunk": w.chunk, "causal": causal,
             "phi": w.phi, "accumulate": "fp32", "decay": gamma is not None, "gated": log_a is not None,
+            "gla": log_a_ch is not None,
         },
         "roofline": roof,
         "path_roofline": {
@@ -297,7 +316,7 @@ def bench_prefill(args, torch, la, synth):
     }
     if not args.no_cpu_baseline:
         wall, h, cores = time_oracle_prefill(q, k, v, causal, max_heads=w.H, phi=w.phi, omega=omega, gamma=gamma,
-                                             log_a=log_a)
+                                             log_a=log_a, log_a_ch=log_a_ch)
         # the sample covers h of the B*H heads at full length: scale to the job
         per_job = wall * (w.B * w.H) / h
         res["cpu_baseline"] = {
@@ -305,7 +324,7 @@ def bench_prefill(args, torch, la, synth):
             "unit": "tokens/s",
             "cores": cores,
             "kind": "oracle",
-            "sample": f"fp64 {('gated token recurrence' if log_a is not None else 'decayed token recurrence' if gamma is not None else 'token recurrence') if causal else 'reassociated form'} over {h} of "
+            "sample": f"fp64 {('per-channel gated token recurrence' if log_a_ch is not None else 'gated token recurrence' if log_a is not None else 'decayed token recurrence' if gamma is not None else 'token recurrence') if causal else 'reassociated form'} over {h} of "
                       f"{w.B * w.H} heads x {w.N} tokens ({wall:.1f} s), scaled to the full job",
             "cpu": cpu_info(),
         }

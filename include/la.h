@@ -23,7 +23,11 @@
  *     Mamba-2's SSD, "Linear attention and SSM", section on how SSD unifies
  *     SSM and attention: A_t = a_t I, output ((Q K^T) o L) V with
  *     L_ij = a_{j+1} ... a_i): S_t = a_t S_{t-1} + phi(k_t) v_t^T,
- *     z_t = a_t z_{t-1} + phi(k_t), read out as the decay above.
+ *     z_t = a_t z_{t-1} + phi(k_t), read out as the decay above;
+ *   - causal with a gate per token and key channel (GLA form, "Efficient
+ *     attention variants" sec. 7.2): S_t = diag(a_t) S_{t-1} + phi(k_t) v_t^T,
+ *     z_t = a_t * z_{t-1} + phi(k_t) (elementwise), entry f of a_t keeping
+ *     row f of the state, read out as the decay above.
  *
  * Conventions shared by every call
  *   - Tensors are contiguous row-major device buffers owned by the caller:
@@ -57,6 +61,9 @@
  *       la_decode_step: d = d_v in {64, 128}; FAVOR+ with r = 256.
  *       la_decode_step_decay: d = d_v in {64, 128}, ELU1/IDENTITY.
  *       la_forward_gated, la_decode_step_gated: as the decay calls.
+ *       la_forward_gla: ELU1/IDENTITY, d = d_v = 64 (bf16: chunk 16..128;
+ *       fp32: 16..64) or d = d_v = 128 (bf16, chunk 16 or 32; chunk = 0
+ *       means 32 there); la_decode_step_gla: as the decay decode.
  *       la_feature_map: ELU1/IDENTITY with d % 8 == 0; FAVOR+ with d in {64, 128},
  *       r = 256.
  */
@@ -269,6 +276,65 @@ la_status la_forward_gated_timed(const void *Q, const void *K, const void *V, vo
 la_status la_decode_step_gated(const float *S, const float *z, const void *q, const void *k, const void *v,
                                void *o, float *S_new, float *z_new, int B, int H, int d, int d_v, int io_dtype,
                                int phi, int r, const float *log_a, int normalize, void *stream);
+
+/*
+ * Causal prefill with a gate per token and key channel ("Efficient attention
+ * variants" sec. 7.2, GLA; the RWKV-5/6 update of "Linear attention and SSM"
+ * has the same shape):
+ *   S_t = diag(a_t) S_{t-1} + phi(k_t) v_t^T,  z_t = a_t * z_{t-1} + phi(k_t),
+ * so that token j enters o_t with weight sum_f phi(q_t)_f phi(k_j)_f
+ * a_{j+1,f} ... a_{t,f}; o_t = phi(q_t)^T S_t / phi(q_t)^T z_t, or
+ * phi(q_t)^T S_t when normalize = 0.  All gates one gives la_forward's causal
+ * result; the same gate on every channel gives la_forward_gated's.  An
+ * initial state S0, z0 enters o_t through channel f with a_{0,f} ... a_{t,f}.
+ *   log_a     in: device fp32 [B][H][N][r], the natural log of each gate
+ *             (<= 0; GLA forms a_t = sigmoid(x_t)^(1/16) per channel).  The
+ *             kernels use max(log2 a, -14): a gate below 2^-14 (about 6.1e-5),
+ *             zero included, acts as 2^-14, so that the factors the
+ *             within-block weights are split into (16-token blocks, a
+ *             reference at each half block) stay finite for features below
+ *             2^16 in magnitude; GLA's gates stay far above the floor.
+ *             Positive values are not rejected and give gates above one.
+ *   normalize 1 (divide by phi(q)^T z) or 0.
+ *   chunk     see the supported shapes; 0 means 64 (32 at d = 128).
+ *   workspace at least la_forward_gla_workspace_bytes(...) bytes (the span
+ *             states plus r fp32 total gates per (head, span)).
+ *   The other arguments are la_forward's with causal = 1 and no omega.
+ *   Also N must satisfy (N + 128) * r * 4 < 2^31 (LA_ERR_SHAPE otherwise).
+ * Errors: as la_forward; LA_ERR_NULL for a NULL log_a.
+ */
+la_status la_forward_gla(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int d,
+                         int d_v, int io_dtype, int phi, int r, const float *log_a, int normalize, int chunk,
+                         const float *S0, const float *z0, float *S_out, float *z_out, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* Workspace bytes la_forward_gla needs (0 for invalid or unsupported
+ * arguments); LA_SPAN applies as for la_forward_workspace_bytes. */
+size_t la_forward_gla_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk);
+
+/* Spans per head (*n_span) and chunk (*chunk_used) la_forward_gla uses for
+ * this shape; either pointer may be NULL; errors as its shape checks.  No
+ * device work. */
+la_status la_forward_gla_config(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk,
+                                int *n_span, int *chunk_used);
+
+/* la_forward_gla plus timing events, as la_forward_timed. */
+la_status la_forward_gla_timed(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int d,
+                               int d_v, int io_dtype, int phi, int r, const float *log_a, int normalize, int chunk,
+                               const float *S0, const float *z0, float *S_out, float *z_out, void *workspace,
+                               size_t workspace_bytes, void *stream, void *const *events);
+
+/*
+ * Decode step with a gate per key channel:
+ *   S_new = diag(a) S + phi(k) v^T, z_new = a * z + phi(k),
+ *   o = phi(q)^T S_new / phi(q)^T z_new (normalize = 1) or phi(q)^T S_new.
+ * log_a: device fp32 [B][H][r], natural logs of this token's gates (clamped
+ * as in la_forward_gla); other arguments as la_decode_step (ELU1/IDENTITY).
+ * Errors: as la_decode_step; LA_ERR_NULL for a NULL log_a.
+ */
+la_status la_decode_step_gla(const float *S, const float *z, const void *q, const void *k, const void *v, void *o,
+                             float *S_new, float *z_new, int B, int H, int d, int d_v, int io_dtype, int phi, int r,
+                             const float *log_a, int normalize, void *stream);
 
 /*
  * Standalone feature map: Y[i] = phi(X[i]) for rows i = 0..rows-1.

@@ -47,6 +47,11 @@ _SIGS = {
     "la_forward_gated": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
     "la_forward_gated_timed": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp, _vp]),
     "la_decode_step_gated": (_i, [_vp] * 8 + [_i] * 7 + [_vp, _i, _vp]),
+    "la_forward_gla_workspace_bytes": (ctypes.c_size_t, [_i] * 9),
+    "la_forward_gla_config": (_i, [_i] * 9 + [ctypes.POINTER(_i), ctypes.POINTER(_i)]),
+    "la_forward_gla": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
+    "la_forward_gla_timed": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp, _vp]),
+    "la_decode_step_gla": (_i, [_vp] * 8 + [_i] * 7 + [_vp, _i, _vp]),
     "la_feature_map": (_i, [_vp, _vp, ctypes.c_longlong, _i, _i, _i, _i, _vp, _vp]),
     "la_status_string": (ctypes.c_char_p, [_i]),
     "la_version": (_i, []),
@@ -160,20 +165,29 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def workspace_bytes(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64, gated=False):
-    """Workspace bytes of la_forward (la_forward_gated with ``gated``; the
-    decay call needs no more than la_forward's causal size)."""
+def workspace_bytes(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64, gated=False, gla=False):
+    """Workspace bytes of la_forward (la_forward_gated with ``gated``,
+    la_forward_gla with ``gla``; the decay call needs no more than
+    la_forward's causal size)."""
     io_code = LA_BF16 if io == "bf16" else LA_F32
+    if gla:
+        return int(load_library().la_forward_gla_workspace_bytes(B, H, N, d, dv, io_code, PHI[phi], r, chunk))
     if gated:
         return int(load_library().la_forward_gated_workspace_bytes(B, H, N, d, dv, io_code, PHI[phi], r, chunk))
     return int(load_library().la_forward_workspace_bytes(B, H, N, d, dv, io_code, PHI[phi], r, int(causal), chunk))
 
 
-def forward_config(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64, decay=False, gated=False):
+def forward_config(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64, decay=False, gated=False,
+                   gla=False):
     """(n_span, single_pass) that la_forward (la_forward_decay with
-    ``decay``, la_forward_gated with ``gated``) uses for this shape."""
+    ``decay``, la_forward_gated with ``gated``, la_forward_gla with ``gla``)
+    uses for this shape."""
     io_code = LA_BF16 if io == "bf16" else LA_F32
     n, sp = ctypes.c_int(), ctypes.c_int()
+    if gla:
+        _check(load_library().la_forward_gla_config(B, H, N, d, dv, io_code, PHI[phi], r, chunk, ctypes.byref(n),
+                                                    ctypes.byref(sp)), "la_forward_gla_config")
+        return n.value, False
     if gated:
         _check(load_library().la_forward_gated_config(B, H, N, d, dv, io_code, PHI[phi], r, chunk, ctypes.byref(n)),
                "la_forward_gated_config")
@@ -215,7 +229,7 @@ def _log_gate_arg(log_gate, shape, dev, causal=True):
 
 def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, z0=None,
             return_state=False, out=None, workspace=None, events=None, gamma=None, normalize=True,
-            log_gate=None):
+            log_gate=None, log_gate_ch=None):
     """Causal (or non-causal) linear attention over Q, K [B,H,N,d], V [B,H,N,dv].
 
     Returns O [B,H,N,dv] (same dtype as Q); with ``return_state`` also the
@@ -226,7 +240,9 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
     (causal only; la_forward_decay), with ``normalize=False`` for the
     unnormalised read-out.  ``log_gate``: optional fp32 device tensor
     [B,H,N] of per-token natural-log gates log a_t (causal only;
-    la_forward_gated), likewise with ``normalize``.
+    la_forward_gated), likewise with ``normalize``.  ``log_gate_ch``:
+    optional fp32 device tensor [B,H,N,r] of per-token, per-key-channel
+    natural-log gates (causal only; la_forward_gla).
     """
     torch = _torch()
     lib = load_library()
@@ -259,13 +275,17 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
         z_out = torch.empty((B, H, r), dtype=torch.float32, device=dev)
     gamma = _gamma_arg(gamma, H, dev, causal)
     log_gate = _log_gate_arg(log_gate, (B, H, N), dev, causal)
-    if gamma is not None and log_gate is not None:
-        raise ValueError("give gamma or log_gate, not both")
-    if gamma is None and log_gate is None and not normalize:
-        raise ValueError("normalize=False is available with a decay (gamma or log_gate) only")
-    if (gamma is not None or log_gate is not None) and phi == "favor":
+    log_gate_ch = _log_gate_arg(log_gate_ch, (B, H, N, r), dev, causal)
+    n_decay = sum(x is not None for x in (gamma, log_gate, log_gate_ch))
+    if n_decay > 1:
+        raise ValueError("give at most one of gamma, log_gate, log_gate_ch")
+    if n_decay == 0 and not normalize:
+        raise ValueError("normalize=False is available with a decay (gamma, log_gate or log_gate_ch) only")
+    if n_decay and phi == "favor":
         raise ValueError("the decay is available for the pointwise feature maps only")
-    if log_gate is not None:
+    if log_gate_ch is not None:
+        need = int(lib.la_forward_gla_workspace_bytes(B, H, N, d, dv, io, PHI[phi], r, chunk))
+    elif log_gate is not None:
         need = int(lib.la_forward_gated_workspace_bytes(B, H, N, d, dv, io, PHI[phi], r, chunk))
     else:
         need = int(lib.la_forward_workspace_bytes(B, H, N, d, dv, io, PHI[phi], r, int(causal), chunk))
@@ -274,7 +294,11 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
     tail = [chunk, _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(dev)]
     head = [_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, d, dv, io, PHI[phi], r]
-    if log_gate is not None:
+    if log_gate_ch is not None:
+        args = head + [_ptr(log_gate_ch), int(bool(normalize))] + tail
+        fn, name = ((lib.la_forward_gla, "la_forward_gla") if events is None
+                    else (lib.la_forward_gla_timed, "la_forward_gla_timed"))
+    elif log_gate is not None:
         args = head + [_ptr(log_gate), int(bool(normalize))] + tail
         fn, name = ((lib.la_forward_gated, "la_forward_gated") if events is None
                     else (lib.la_forward_gated_timed, "la_forward_gated_timed"))
@@ -296,13 +320,15 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
 
 
 def decode_step(S, z, q, k, v, *, phi="elu1", omega=None, inplace=True, out=None, gamma=None, normalize=True,
-                log_gate=None):
+                log_gate=None, log_gate_ch=None):
     """One decode step for every (batch, head): S, z updated in place (or new
     tensors when ``inplace=False``).  Returns o, or (o, S_new, z_new).
     ``gamma``: optional fp32 device tensor [H] of per-head decays
     (la_decode_step_decay), with ``normalize=False`` for o = phi(q)^T S'.
     ``log_gate``: optional fp32 device tensor [B,H], this token's natural-log
-    gate per sequence and head (la_decode_step_gated)."""
+    gate per sequence and head (la_decode_step_gated).  ``log_gate_ch``:
+    optional fp32 device tensor [B,H,r], this token's natural-log gates per
+    key channel (la_decode_step_gla)."""
     torch = _torch()
     lib = load_library()
     B, H, d = q.shape
@@ -326,12 +352,19 @@ def decode_step(S, z, q, k, v, *, phi="elu1", omega=None, inplace=True, out=None
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, dv)}")
     gamma = _gamma_arg(gamma, H, dev)
     log_gate = _log_gate_arg(log_gate, (B, H), dev)
-    if gamma is not None and log_gate is not None:
-        raise ValueError("give gamma or log_gate, not both")
-    if gamma is None and log_gate is None and not normalize:
-        raise ValueError("normalize=False is available with a decay (gamma or log_gate) only")
+    log_gate_ch = _log_gate_arg(log_gate_ch, (B, H, r), dev)
+    n_decay = sum(x is not None for x in (gamma, log_gate, log_gate_ch))
+    if n_decay > 1:
+        raise ValueError("give at most one of gamma, log_gate, log_gate_ch")
+    if n_decay == 0 and not normalize:
+        raise ValueError("normalize=False is available with a decay (gamma, log_gate or log_gate_ch) only")
     S_new, z_new = (S, z) if inplace else (torch.empty_like(S), torch.empty_like(z))
-    if log_gate is not None:
+    if log_gate_ch is not None:
+        st = lib.la_decode_step_gla(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_new),
+                                    _ptr(z_new), B, H, d, dv, _io_code(q), PHI[phi], r, _ptr(log_gate_ch),
+                                    int(bool(normalize)), _stream(dev))
+        _check(st, "la_decode_step_gla")
+    elif log_gate is not None:
         st = lib.la_decode_step_gated(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_new),
                                       _ptr(z_new), B, H, d, dv, _io_code(q), PHI[phi], r, _ptr(log_gate),
                                       int(bool(normalize)), _stream(dev))

@@ -44,6 +44,8 @@ constexpr int kCUs = 256;
 
 int output_occupancy(int io, int phi, int d, int chunk, int causal, int decay) {
   if (phi == LA_PHI_FAVOR) return 1;
+  // per-channel gates: three weighted key tiles and the gate tile in LDS
+  if (decay == 2) return (io == LA_BF16 && d == 64 && chunk <= 64) ? 2 : 1;
   // with a decay the output kernel runs two workgroups per CU at d = 64
   if (decay) return (d == 64 && chunk <= 64) ? 2 : 1;
   // the non-causal output kernel holds only Q chunks and the shared sums
@@ -98,7 +100,8 @@ bool use_fused(int io, int phi, int d, int d_v, int r, int causal, int chunk, in
   return env && env[0] == '1';
 }
 
-// decay: a fixed per-head decay is requested (causal, pointwise maps only).
+// decay: 1 for a fixed per-head decay or per-token gates, 2 for per-channel
+// gates (causal, pointwise maps only).
 la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int phi, int r, int causal, int chunk,
                               Shape* sh, int decay = 0) {
   if (B < 0 || H < 0 || N < 0 || d <= 0 || d_v <= 0 || r < 0 || chunk < 0) return LA_ERR_SHAPE;
@@ -108,8 +111,9 @@ la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int p
   if (causal != 0 && causal != 1) return LA_ERR_UNSUPPORTED;
   if (decay && (phi == LA_PHI_FAVOR || !causal)) return LA_ERR_UNSUPPORTED;
   const int rr = norm_r(phi, d, r);
-  const int ch = norm_chunk(chunk);
+  const int ch = decay == 2 && chunk == 0 && d == 128 ? 32 : norm_chunk(chunk);
   if (!la::prefill_supported(io, phi, d, d_v, rr, ch)) return LA_ERR_UNSUPPORTED;
+  if (decay == 2 && !la::gla_supported(io, d, d_v, rr, ch)) return LA_ERR_UNSUPPORTED;
   const long long BH = static_cast<long long>(B) * H;
   if (BH > (1LL << 30)) return LA_ERR_SHAPE;
   // a head's Q/K/V/O must fit a 32-bit buffer range (the kernels address
@@ -117,6 +121,8 @@ la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int p
   // workgroups) must fit a 32-bit launch
   const long long row = static_cast<long long>(d > d_v ? d : d_v) * (io == LA_BF16 ? 2 : 4);
   if (static_cast<long long>(N) * row >= (1LL << 31)) return LA_ERR_SHAPE;
+  // per-channel gates: a head's [N][r] fp32 gates, one chunk past N included
+  if (decay == 2 && (static_cast<long long>(N) + 128) * rr * 4 >= (1LL << 31)) return LA_ERR_SHAPE;
   const int fused = !decay && use_fused(io, phi, d, d_v, rr, causal, ch, N) ? 1 : 0;
   const int n_span =
       fused ? (N + la::kFusedSpan - 1) / la::kFusedSpan : choose_n_span(BH, N, ch, d, io, phi, causal, decay);
@@ -126,19 +132,20 @@ la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int p
   return LA_OK;
 }
 
-size_t workspace_for(const Shape& sh, bool gated = false) {
+size_t workspace_for(const Shape& sh, bool gated = false, bool per_channel = false) {
   if (sh.fused) return la::fused_workspace_bytes(sh.BH, sh.n_span, sh.r, sh.dv);
-  return la::prefill_workspace_bytes(sh.BH, sh.n_span, sh.r, sh.dv, gated);
+  return la::prefill_workspace_bytes(sh.BH, sh.n_span, sh.r, sh.dv, gated, per_channel);
 }
 
-// gamma: fixed per-head decay; log_a: per-token gates (at most one of the two).
+// gamma: fixed per-head decay; log_a: per-token gates; log_a_ch: per-token,
+// per-channel gates (at most one of the three).
 la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
                        int d_v, int io, int phi, int r, const float* omega, int causal, int chunk, const float* S0,
                        const float* z0, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
                        void* stream, void* const* events, const float* gamma = nullptr, int normalize = 1,
-                       const float* log_a = nullptr) {
+                       const float* log_a = nullptr, const float* log_a_ch = nullptr) {
   Shape sh;
-  const int decay = gamma != nullptr || log_a != nullptr;
+  const int decay = log_a_ch != nullptr ? 2 : (gamma != nullptr || log_a != nullptr) ? 1 : 0;
   la_status st = check_forward_shape(B, H, N, d, d_v, io, phi, r, causal, chunk, &sh, decay);
   if (st != LA_OK) return st;
   const bool have_tokens = sh.BH > 0 && N > 0;
@@ -146,10 +153,10 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
   if (phi == LA_PHI_FAVOR && !omega) return LA_ERR_NULL;
   if ((S0 == nullptr) != (z0 == nullptr)) return LA_ERR_NULL;
   if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_NULL;
-  const void* ptrs[] = {Q, K, V, O, omega, S0, z0, S_out, z_out, workspace, gamma, log_a};
+  const void* ptrs[] = {Q, K, V, O, omega, S0, z0, S_out, z_out, workspace, gamma, log_a, log_a_ch};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return LA_ERR_ALIGN;
-  const size_t need = workspace_for(sh, log_a != nullptr);
+  const size_t need = workspace_for(sh, log_a != nullptr, log_a_ch != nullptr);
   if (sh.BH > 0 && (!workspace || workspace_bytes < need)) return LA_ERR_WORKSPACE;
   if (sh.BH == 0) return LA_OK;
 
@@ -160,7 +167,7 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
   a.chunk = sh.chunk; a.n_span = sh.n_span; a.fused = sh.fused; a.group = fused_group();
   a.S0 = S0; a.z0 = z0; a.S_out = S_out; a.z_out = z_out;
   a.workspace = workspace; a.stream = stream; a.events = events;
-  a.gamma = gamma; a.normalize = normalize; a.log_a = log_a;
+  a.gamma = gamma; a.normalize = normalize; a.log_a = log_a; a.log_a_ch = log_a_ch;
   return hip_status(la::prefill_launch(a));
 }
 
@@ -215,7 +222,7 @@ namespace {
 la_status decode_impl(const float* S, const float* z, const void* q, const void* k, const void* v, void* o,
                       float* S_new, float* z_new, int B, int H, int d, int d_v, int io_dtype, int phi, int r,
                       const float* omega, void* stream, const float* gamma, int normalize,
-                      const float* log_a = nullptr) {
+                      const float* log_a = nullptr, const float* log_a_ch = nullptr) {
   if (B < 0 || H < 0 || d <= 0 || d_v <= 0 || r < 0) return LA_ERR_SHAPE;
   if (static_cast<long long>(B) * H > 0x7fffffffLL) return LA_ERR_SHAPE;
   if (io_dtype != LA_F32 && io_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
@@ -225,14 +232,14 @@ la_status decode_impl(const float* S, const float* z, const void* q, const void*
   const long long BH = static_cast<long long>(B) * H;
   if (BH > 0 && (!S || !z || !q || !k || !v || !o || !S_new || !z_new)) return LA_ERR_NULL;
   if (phi == LA_PHI_FAVOR && !omega) return LA_ERR_NULL;
-  const void* ptrs[] = {S, z, q, k, v, o, S_new, z_new, omega, gamma, log_a};
+  const void* ptrs[] = {S, z, q, k, v, o, S_new, z_new, omega, gamma, log_a, log_a_ch};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return LA_ERR_ALIGN;
   if (BH == 0) return LA_OK;
   la::DecodeArgs a;
   a.S = S; a.z = z; a.q = q; a.k = k; a.v = v; a.o = o; a.S_new = S_new; a.z_new = z_new;
   a.B = B; a.H = H; a.d = d; a.dv = d_v; a.r = rr; a.io = io_dtype; a.phi = phi; a.omega = omega;
-  a.stream = stream; a.gamma = gamma; a.normalize = normalize; a.log_a = log_a;
+  a.stream = stream; a.gamma = gamma; a.normalize = normalize; a.log_a = log_a; a.log_a_ch = log_a_ch;
   return hip_status(la::decode_launch(a));
 }
 
@@ -314,6 +321,53 @@ la_status la_decode_step_gated(const float* S, const float* z, const void* q, co
   if (phi == LA_PHI_FAVOR) return LA_ERR_UNSUPPORTED;
   return decode_impl(S, z, q, k, v, o, S_new, z_new, B, H, d, d_v, io_dtype, phi, r, nullptr, stream, nullptr,
                      normalize, log_a);
+}
+
+size_t la_forward_gla_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r,
+                                      int chunk) {
+  Shape sh;
+  if (check_forward_shape(B, H, N, d, d_v, io_dtype, phi, r, 1, chunk, &sh, 2) != LA_OK) return 0;
+  return workspace_for(sh, false, true);
+}
+
+la_status la_forward_gla_config(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk,
+                                int* n_span, int* chunk_used) {
+  Shape sh;
+  const la_status st = check_forward_shape(B, H, N, d, d_v, io_dtype, phi, r, 1, chunk, &sh, 2);
+  if (st != LA_OK) return st;
+  if (n_span) *n_span = sh.n_span;
+  if (chunk_used) *chunk_used = sh.chunk;
+  return LA_OK;
+}
+
+la_status la_forward_gla(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+                         int d_v, int io_dtype, int phi, int r, const float* log_a, int normalize, int chunk,
+                         const float* S0, const float* z0, float* S_out, float* z_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!log_a) return LA_ERR_NULL;
+  if (normalize != 0 && normalize != 1) return LA_ERR_UNSUPPORTED;
+  return forward_impl(Q, K, V, O, B, H, N, d, d_v, io_dtype, phi, r, nullptr, 1, chunk, S0, z0, S_out, z_out,
+                      workspace, workspace_bytes, stream, nullptr, nullptr, normalize, nullptr, log_a);
+}
+
+la_status la_forward_gla_timed(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+                               int d_v, int io_dtype, int phi, int r, const float* log_a, int normalize, int chunk,
+                               const float* S0, const float* z0, float* S_out, float* z_out, void* workspace,
+                               size_t workspace_bytes, void* stream, void* const* events) {
+  if (!log_a) return LA_ERR_NULL;
+  if (normalize != 0 && normalize != 1) return LA_ERR_UNSUPPORTED;
+  return forward_impl(Q, K, V, O, B, H, N, d, d_v, io_dtype, phi, r, nullptr, 1, chunk, S0, z0, S_out, z_out,
+                      workspace, workspace_bytes, stream, events, nullptr, normalize, nullptr, log_a);
+}
+
+la_status la_decode_step_gla(const float* S, const float* z, const void* q, const void* k, const void* v, void* o,
+                             float* S_new, float* z_new, int B, int H, int d, int d_v, int io_dtype, int phi, int r,
+                             const float* log_a, int normalize, void* stream) {
+  if (!log_a) return LA_ERR_NULL;
+  if (normalize != 0 && normalize != 1) return LA_ERR_UNSUPPORTED;
+  if (phi == LA_PHI_FAVOR) return LA_ERR_UNSUPPORTED;
+  return decode_impl(S, z, q, k, v, o, S_new, z_new, B, H, d, d_v, io_dtype, phi, r, nullptr, stream, nullptr,
+                     normalize, nullptr, log_a);
 }
 
 la_status la_feature_map(const void* X, float* Y, long long rows, int d, int io_dtype, int phi, int r,

@@ -88,11 +88,12 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
                                                              float* S_new, float* z_new,
                                                              const float* __restrict__ omega,
                                                              const float* __restrict__ gamma, int H,
-                                                             int normalize, const float* __restrict__ log_a) {
+                                                             int normalize, const float* __restrict__ log_a,
+                                                             const float* __restrict__ log_a_ch) {
   constexpr int TPR = DV / 4;          // threads per state row
   constexpr int RPP = kThreads / TPR;  // rows per pass
   static_assert(R % RPP == 0, "state rows must split evenly");
-  __shared__ float fq[R], fk[R], vv[DV], xbuf[D];
+  __shared__ float fq[R], fk[R], vv[DV], xbuf[D], gch[R];
   __shared__ float red[RPP * DV];
   __shared__ float scratch[2][kWaves];
   const int bh = blockIdx.x;
@@ -103,6 +104,11 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
   features_to_lds<T, D, R, PHI>(q + (size_t)bh * D, omega, fq, xbuf, scratch[0]);
   features_to_lds<T, D, R, PHI>(k + (size_t)bh * D, omega, fk, xbuf, scratch[1]);
   for (int c = tid; c < DV; c += kThreads) vv[c] = load_io<T>(v + (size_t)bh * DV + c);
+  // per-channel gates (state row f keeps a_f of itself; the floor of the
+  // per-channel gated prefill, log2 a >= -14)
+  for (int f = tid; f < R; f += kThreads)
+    gch[f] = log_a_ch ? __builtin_amdgcn_exp2f(fmaxf(log_a_ch[(size_t)bh * R + f] * 1.4426950408889634f, -14.f))
+                      : gm;
   __syncthreads();
 
   const int c4 = tid % TPR;
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
 #pragma unroll
   for (int it = 0; it < R / RPP; ++it) {
     const int f = r0 + it * RPP;
-    s[it] = s[it] * gm + fk[f] * v4;
+    s[it] = s[it] * gch[f] + fk[f] * v4;
     __builtin_nontemporal_store(s[it], reinterpret_cast<f32x4*>(Sn + (size_t)f * DV));
     num += fq[f] * s[it];
   }
@@ -131,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
 
   float dpart = 0.f;
   for (int f = tid; f < R; f += kThreads) {
-    const float zn = z[(size_t)bh * R + f] * gm + fk[f];
+    const float zn = z[(size_t)bh * R + f] * gch[f] + fk[f];
     z_new[(size_t)bh * R + f] = zn;
     dpart += fq[f] * zn;
   }
@@ -153,7 +159,7 @@ static hipError_t launch_decode(const DecodeArgs& a) {
   hipLaunchKernelGGL((la_decode_kernel<T, D, R, DV, PHI>), dim3(BH), dim3(kThreads), 0,
                      static_cast<hipStream_t>(a.stream), a.S, a.z, static_cast<const T*>(a.q),
                      static_cast<const T*>(a.k), static_cast<const T*>(a.v), static_cast<T*>(a.o), a.S_new,
-                     a.z_new, a.omega, a.gamma, a.H > 0 ? a.H : 1, a.normalize, a.log_a);
+                     a.z_new, a.omega, a.gamma, a.H > 0 ? a.H : 1, a.normalize, a.log_a, a.log_a_ch);
   return hipGetLastError();
 }
 

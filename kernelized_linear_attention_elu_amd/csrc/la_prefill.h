@@ -36,14 +36,22 @@ struct PrefillArgs {
   // z likewise; excludes gamma.  The workspace then also holds one fp32
   // total log2 gate per (head, span) after the span states.
   const float* log_a = nullptr;
+  // per-token, per-key-channel gate (device [B*H][N][r] fp32, natural logs;
+  // null: none), causal pointwise maps only: S_t = diag(a_t) S_{t-1} +
+  // phi(k_t) v_t^T; excludes gamma and log_a.  The workspace then also holds
+  // r fp32 total log2 gates per (head, span) after the span states.
+  const float* log_a_ch = nullptr;
 };
 
 // Workspace of the three-kernel path: fp32 span states [B*H][n_span+1][R*DV+R],
 // then (gated decay) the spans' total log2 gates [B*H][n_span].
-inline size_t prefill_workspace_bytes(long long BH, int n_span, int r, int dv, bool gated) {
+inline size_t prefill_workspace_bytes(long long BH, int n_span, int r, int dv, bool gated, bool per_channel = false) {
   const size_t E = (size_t)r * dv + r;
-  return (size_t)BH * ((size_t)n_span + 1) * E * sizeof(float) + (gated ? (size_t)BH * n_span * sizeof(float) : 0);
+  const size_t tot = per_channel ? (size_t)BH * n_span * r : gated ? (size_t)BH * n_span : 0;
+  return (size_t)BH * ((size_t)n_span + 1) * E * sizeof(float) + tot * sizeof(float);
 }
+// Shapes the per-channel gated prefill supports (causal, ELU+1 / identity).
+bool gla_supported(int io, int d, int dv, int r, int chunk);
 
 // Single-pass causal prefill (la_prefill.hip): tokens per workgroup and the
 // default number of spans per look-back block.
@@ -72,7 +80,7 @@ hipError_t favor_prefill_launch(const PrefillArgs& a);
 // by 2^totals[s].
 hipError_t scan_launch(float* ws, int BH, int R, int DV, int n_span, const float* S0, const float* z0,
                        float* S_out, float* z_out, hipStream_t stream, const float* gamma = nullptr, int H = 1,
-                       int N = 0, int chunk = 64, const float* totals = nullptr);
+                       int N = 0, int chunk = 64, const float* totals = nullptr, int per_channel = 0);
 
 struct DecodeArgs {
   const float* S;
@@ -91,6 +99,7 @@ struct DecodeArgs {
   const float* gamma = nullptr;  // per-head decay (device [H]); null: none
   int normalize = 1;
   const float* log_a = nullptr;  // this token's gate per (batch, head), natural log (device [B*H]); null: none
+  const float* log_a_ch = nullptr;  // this token's per-channel gates, natural logs (device [B*H][r]); null: none
 };
 
 bool decode_supported(int io, int phi, int d, int dv, int r);

@@ -105,6 +105,7 @@ __device__ __forceinline__ void state_tile(int w, int i, int& ct, int& ft) {
 constexpr int kNoDecay = 0;  // S_t = S_{t-1} + phi(k_t) v_t^T
 constexpr int kFixed = 1;    // S_t = gamma S_{t-1} + ..., one gamma per head (lg = log2 gamma)
 constexpr int kGated = 2;    // S_t = a_t S_{t-1} + ..., one gate per token (log a_t given)
+constexpr int kChannel = 3;  // S_t = diag(a_t) S_{t-1} + ..., one gate per token and key channel
 
 // A gate's log2 is clamped from below: a gate under 2^-126, zero included,
 // acts as 2^-126 (far below what an fp32 sum of the outputs resolves), and
@@ -429,6 +430,44 @@ struct QRegs {
           col = CF::PL == 8 ? 32 * v + 8 * g : 16 * g + 4 * v;
         }
         raw[rbi][v] = __builtin_amdgcn_raw_buffer_load_b128(q, (row * CF::D + col) * (int)sizeof(T), 0, kStreamLoad);
+      }
+    }
+  }
+  // phi in fp32, kept in fp32 (the per-channel gated path scales it before
+  // rounding): value n of a lane is feature 32 (n / 8) + 8 g + n % 8 (bf16)
+  // or 16 g + n (fp32), the k-slot order of to_frags
+  __device__ __forceinline__ void to_f32(float (&fq)[CF::RBW][CF::R / 4], OP* scr, int g, int li) const {
+    using T = typename CF::IO;
+    if constexpr (kRows) {
+      using TS = Tile<OP, CF::D>;
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int rbi = 0; rbi < CF::RBW; ++rbi)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const int qi = v * 64 + lane;
+          *reinterpret_cast<u32x4*>(scr + TS::off(16 * rbi + qi / UPR, 8 * (qi % UPR))) = raw[rbi][v];
+        }
+#pragma unroll
+      for (int rbi = 0; rbi < CF::RBW; ++rbi)
+#pragma unroll
+        for (int ks = 0; ks < NV; ++ks) {
+          float f[8];
+          unpack16<bf16>(*reinterpret_cast<const u32x4*>(scr + TS::off(16 * rbi + li, 32 * ks + 8 * g)), f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) fq[rbi][8 * ks + e] = phi_pointwise<CF::PHI>(f[e]);
+        }
+    } else {
+      static_assert(CF::PL == 1, "fp32 operands read their fragments directly");
+#pragma unroll
+      for (int rbi = 0; rbi < CF::RBW; ++rbi) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          float f[CF::EPL];
+          unpack16<T>(raw[rbi][v], f);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fq[rbi][4 * v + e] = phi_pointwise<CF::PHI>(f[e]);
+        }
       }
     }
   }
@@ -971,7 +1010,8 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
 // lengths are walked with an incremental quotient and remainder of
 // s * n_chunks / n_span, the split span_begin uses.  With gates (kGated)
 // the running state is multiplied by 2^totals[bh][s], the span's total log2
-// gate, instead.
+// gate, instead; with per-channel gates (kChannel) by 2^totals[bh][s][f]
+// for state row f.
 template <int DK>
 __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ ws, int R, int DV, int n_span,
                                                            const float* __restrict__ S0,
@@ -1012,12 +1052,18 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
     if constexpr (DK == kGated) {
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) tl[j] = s0 + j < n_span ? totals[(size_t)bh * n_span + s0 + j] : 0.f;
+    } else if constexpr (DK == kChannel) {
+      // this element's state row (or z entry)
+      const int f = is_s ? e / DV : e - R * DV;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        tl[j] = s0 + j < n_span ? totals[((size_t)bh * n_span + s0 + j) * R + f] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (s0 + j < n_span) {
         p[(size_t)(s0 + j) * E] = acc;
-        if constexpr (DK == kGated) acc *= __builtin_amdgcn_exp2f(tl[j]);
+        if constexpr (DK == kGated || DK == kChannel) acc *= __builtin_amdgcn_exp2f(tl[j]);
         if constexpr (DECAY) {
           rem += r_ch;
           const int step = q_ch + (rem >= n_span ? 1 : 0);
@@ -1155,6 +1201,573 @@ __global__ __launch_bounds__(CF::NT, DK != kNoDecay ? CF::MINB_DECAY : CF::MINB)
       t0 += CF::C;
     } while (t0 < t_end);
   }
+}
+
+
+// ------------------------------------------------------------------ per-channel gates
+
+// Causal prefill with a gate per key channel (the GLA form):
+//   S_t = diag(a_t) S_{t-1} + phi(k_t) v_t^T,  z_t = a_t z_{t-1} + phi(k_t),
+// a_t in (0, 1]^R given as natural logs [B*H][N][R].  Per chunk and channel,
+// with lg = max(log2 a, kGlaMinLog2):
+//   P_i  the sum of lg over the tokens of i's 16-token block up to i
+//        (block-local running sums, an fp32 [C][R] LDS tile);
+//   M_b  P at token 7 of block b, T_b P at its token 15 (the block's total).
+// Every gate product of the chunk is 2^x with x a short sum of these, and
+// each factor goes on one MFMA operand:
+//   weight (i, j), j in an earlier block jb:
+//       2^(P_i + sum_{jb<b<ib} T_b) on phi(q_i), 2^(T_jb - P_j) on phi(k_j);
+//   weight (i, j), same block b, row i among the block's tokens 0..7:
+//       2^(P_i) on phi(q_i), 2^(-P_j) on phi(k_j);
+//   ... row i among tokens 8..15:  2^(P_i - M_b) on phi(q_i), 2^(M_b - P_j) on phi(k_j);
+//   read-out of the carried state, row i:  2^(P_i + sum_{b<ib} T_b);
+//   key j's decay to the chunk's end:  2^(T_jb - P_j + sum_{b>jb} T_b);
+//   the carried state over the chunk:  2^(sum_b T_b) per state row.
+// Row i's factors use gates of tokens up to i only, so no later token can
+// change an earlier output, not even in rounding.  Every query factor is at
+// most one, and so is every key factor except the same-block ones, which
+// lie below 2^(8 |kGlaMinLog2|) = 2^112 on the entries that are kept (at
+// most 8 tokens between j and the reference): with features below 2^16 in
+// magnitude they stay finite in fp32 and bf16 (largest 2^128), which is
+// what the floor is for.  The entries above the diagonal, whose factors may
+// overflow, are replaced by selection.
+constexpr float kGlaMinLog2 = -14.f;
+
+template <class CF>
+struct GlaCfg {
+  static constexpr int GV = CF::C * CF::R / 4;   // fp32 gate vectors (4 channels) per chunk
+  static constexpr int NU = GV / 64;             // units of 64 vectors: one block x 16 channels
+  static constexpr int GPW = NU / CF::NW;        // units per wave
+  static constexpr int NQ = CF::R / 4;           // phi(q) values per lane and row block
+  static_assert(CF::R % 16 == 0 && NU % CF::NW == 0, "gate units must split evenly over waves");
+};
+
+template <class CF>
+struct GateRegsGla {
+  f32x4 g[GlaCfg<CF>::GPW];
+};
+
+// Unit k of the calling wave: block b = u % RB and channels 16 (u / RB) ..
+// +15 with u = wave + NW k; lane l holds token 16 b + l % 16 and channels
+// 4 (4 (u / RB) + l / 16) .. +3, so each 16-lane row of the wave holds one
+// block's tokens of 4 channels, in token order.
+template <class CF>
+__device__ __forceinline__ void gla_unit(int k, int w, int lane, int& tok, int& ch) {
+  const int u = w + CF::NW * k;
+  tok = 16 * (u % CF::RB) + (lane & 15);
+  ch = 4 * (4 * (u / CF::RB) + (lane >> 4));
+}
+
+template <class CF>
+__device__ __forceinline__ void load_gates_gla(GateRegsGla<CF>& gr, __amdgpu_buffer_rsrc_t a, int t0) {
+  const int w = wave_id(), lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < GlaCfg<CF>::GPW; ++k) {
+    int tok, ch;
+    gla_unit<CF>(k, w, lane, tok, ch);
+    gr.g[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(a, ((t0 + tok) * CF::R + ch) * 4, 0, 0));
+  }
+}
+
+// Clamped log2 gates -> block-local running sums (a prefix over each 16-lane
+// row, in DPP moves) -> the P tile.
+template <class CF>
+__device__ __forceinline__ void gla_prefix_to_lds(const GateRegsGla<CF>& gr, float* sp) {
+  using TP = Tile<float, CF::R>;
+  const int w = wave_id(), lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < GlaCfg<CF>::GPW; ++k) {
+    f32x4 x = gr.g[k];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float y = fmaxf(x[e] * kLog2e, kGlaMinLog2);
+      y = dpp_add<0x111>(y);  // row_shr:1
+      y = dpp_add<0x112>(y);  // row_shr:2
+      y = dpp_add<0x114>(y);  // row_shr:4
+      y = dpp_add<0x118>(y);  // row_shr:8
+      x[e] = y;
+    }
+    int tok, ch;
+    gla_unit<CF>(k, w, lane, tok, ch);
+    *reinterpret_cast<f32x4*>(sp + TP::off(tok, ch)) = x;
+  }
+}
+
+// V rows of the chunk -> LDS (the value half of stage_chunk).
+template <class CF>
+__device__ __forceinline__ void stage_values(const ChunkRegs<CF, false>& cr, typename CF::OP* sv) {
+  using TV = Tile<typename CF::OP, CF::DV>;
+  constexpr int VVR = CF::DV / CF::EPL;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < CF::LV; ++i) {
+    const int vi = tid + i * CF::NT;
+    if (CF::VV % CF::NT == 0 || vi < CF::VV)
+      *reinterpret_cast<u32x4*>(sv + TV::off(vi / VVR, (vi % VVR) * CF::EPL)) = cr.v[i];
+  }
+}
+
+// phi(K) of the chunk, weighted, -> LDS (reads the P tile):
+//   skw   phi(k_j) 2^(T_jb - P_j + sum_{b>jb} T_b)  (decay to the chunk's end;
+//         with skw_lo its bf16 rounding residual too)
+//   OUT:  skd0 phi(k_j) 2^(-P_j), skd1 phi(k_j) 2^(M_jb - P_j) (same-block
+//         weights of rows 0..7 and 8..15), skb phi(k_j) 2^(T_jb - P_j).
+// Keys at or beyond N get zero features.
+template <class CF, bool OUT>
+__device__ __forceinline__ void gla_stage_keys(const ChunkRegs<CF, false>& cr, const float* sp,
+                                               typename CF::OP* skd0, typename CF::OP* skd1, typename CF::OP* skb,
+                                               typename CF::OP* skw, typename CF::OP* skw_lo, int t0, int N) {
+  using T = typename CF::IO;
+  using OP = typename CF::OP;
+  using TQ = Tile<OP, CF::R>;
+  using TP = Tile<float, CF::R>;
+  constexpr int QV = CF::D / CF::EPL, EPL = CF::EPL, RB = CF::RB;
+  const int tid = threadIdx.x;
+  auto row = [&](int r, int col, float* x) {
+#pragma unroll
+    for (int e4 = 0; e4 < EPL / 4; ++e4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(sp + TP::off(r, col + 4 * e4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * e4 + e] = v[e];
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < CF::LQ; ++i) {
+    const int vi = tid + i * CF::NT;
+    if (!(CF::VQ % CF::NT == 0 || vi < CF::VQ)) continue;
+    const int tok = vi / QV;
+    const int col = (vi % QV) * EPL;
+    const int jb = tok >> 4;
+    float f[EPL], pj[EPL], tj[EPL], after[EPL];
+    unpack16<T>(cr.k[i], f);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) f[e] = phi_pointwise<CF::PHI>(f[e]);
+    row(tok, col, pj);
+    row(16 * jb + 15, col, tj);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) after[e] = 0.f;
+#pragma unroll
+    for (int b = 1; b < RB; ++b) {
+      if (b > jb) {
+        float tb[EPL];
+        row(16 * b + 15, col, tb);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) after[e] += tb[e];
+      }
+    }
+    const bool valid = t0 + tok < N;
+    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+    float kw[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) kw[e] = f[e] * __builtin_amdgcn_exp2f(tj[e] - pj[e] + after[e]);
+    const u32x4 hw = pack16<OP>(kw);
+    *reinterpret_cast<u32x4*>(skw + TQ::off(tok, col)) = valid ? hw : zero;
+    if constexpr (sizeof(OP) == 2) {
+      if (skw_lo) {
+        float h[EPL], r[EPL];
+        unpack16<bf16>(hw, h);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) r[e] = kw[e] - h[e];
+        const u32x4 lo = pack16<OP>(r);
+        *reinterpret_cast<u32x4*>(skw_lo + TQ::off(tok, col)) = valid ? lo : zero;
+      }
+    }
+    if constexpr (OUT) {
+      float mj[EPL], kd0[EPL], kd1[EPL], kb[EPL];
+      row(16 * jb + 7, col, mj);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        kd0[e] = f[e] * __builtin_amdgcn_exp2f(-pj[e]);
+        kd1[e] = f[e] * __builtin_amdgcn_exp2f(mj[e] - pj[e]);
+        kb[e] = f[e] * __builtin_amdgcn_exp2f(tj[e] - pj[e]);
+      }
+      const u32x4 x0 = pack16<OP>(kd0), x1 = pack16<OP>(kd1), xb = pack16<OP>(kb);
+      *reinterpret_cast<u32x4*>(skd0 + TQ::off(tok, col)) = valid ? x0 : zero;
+      *reinterpret_cast<u32x4*>(skd1 + TQ::off(tok, col)) = valid ? x1 : zero;
+      *reinterpret_cast<u32x4*>(skb + TQ::off(tok, col)) = valid ? xb : zero;
+    }
+  }
+}
+
+// Output rows of one chunk with per-channel gates: chunk_outputs' causal
+// product with the operand scalings listed above.  fq: this wave's phi(q)
+// values in fp32 (QRegs::to_f32 order).  Key blocks are taken from the
+// diagonal down, so that the query scaling for block jb is the one for jb+1
+// plus T_{jb+1}.
+template <class CF>
+__device__ __forceinline__ void chunk_outputs_gla(const float (&fq)[CF::RBW][CF::R / 4], const typename CF::OP* skd0,
+                                                  const typename CF::OP* skd1, const typename CF::OP* skb,
+                                                  const typename CF::OP* sv,
+                                                  const typename CF::OP* ss, const typename CF::ZT* sz,
+                                                  const float* sp, OutRegs<CF>& out, int w, int g, int li,
+                                                  int normalize) {
+  using OP = typename CF::OP;
+  using frag = typename Op<OP>::frag;
+  using TQ = Tile<OP, CF::R>;
+  using TV = Tile<OP, CF::DV>;
+  using TP = Tile<float, CF::R>;
+  constexpr int KS = CF::KS, PL = CF::PL, RB = CF::RB, CTW = CF::CTW, R = CF::R, DV = CF::DV;
+  constexpr int NQ = GlaCfg<CF>::NQ;
+  const bf16 one = static_cast<bf16>(1.0f), zero = static_cast<bf16>(0.0f);
+  const bf16 o1 = (li & 3) == 0 ? one : zero;
+  const bf16x8 ones_rows = bf16x8{o1, o1, o1, o1, o1, o1, o1, o1};
+  const int zrow = min(li & 3, 2);
+  // feature of value n of this lane (QRegs::to_f32 order); groups of 4
+  // consecutive n are consecutive features
+  auto chan = [&](int n) { return PL == 8 ? 32 * (n >> 3) + 8 * g + (n & 7) : 16 * g + n; };
+  auto row_vals = [&](int r, float (&x)[NQ]) {
+#pragma unroll
+    for (int n4 = 0; n4 < NQ / 4; ++n4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(sp + TP::off(r, chan(4 * n4)));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * n4 + e] = v[e];
+    }
+  };
+#pragma unroll
+  for (int rbi = 0; rbi < CF::RBW; ++rbi) {
+    const int ib = (RB >= CF::NW) ? (w + CF::NW * rbi) : (w % RB);
+    const int ct0 = (RB >= CF::NW) ? 0 : (w / RB) * CTW;
+    // phi(q_i) scaled by 2^x, rounded to MFMA operands
+    auto scaled = [&](const float (&x)[NQ], frag (&qs)[R / KS]) {
+      if constexpr (PL == 8) {
+#pragma unroll
+        for (int ks = 0; ks < R / KS; ++ks) {
+          float f8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f8[e] = fq[rbi][8 * ks + e] * __builtin_amdgcn_exp2f(x[8 * ks + e]);
+          qs[ks] = cvt_bf16x8(f8);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < R / KS; ++ks) qs[ks] = fq[rbi][ks] * __builtin_amdgcn_exp2f(x[ks]);
+      }
+    };
+    // x = P_i + sum_{x_at < b < ib} T_b: the query scaling for key block
+    // x_at (the diagonal block, taken first, reads x while it is still P_i)
+    float x[NQ];
+    row_vals(16 * ib + li, x);
+    int x_at = ib - 1;
+    auto advance = [&](int jb) {
+      while (x_at > jb) {
+        float tb[NQ];
+        row_vals(16 * x_at + 15, tb);
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) x[n] += tb[n];
+        --x_at;
+      }
+    };
+
+    float den = 0.f;
+    f32x4 dacc = zero4();
+    f32x4 o[CTW];
+#pragma unroll
+    for (int c = 0; c < CTW; ++c) o[c] = zero4();
+
+    auto contract = [&](const OP* kt, int jb, const frag (&qs)[R / KS]) {
+      f32x4 t = zero4();
+#pragma unroll
+      for (int ks = 0; ks < R / KS; ++ks) {
+        if constexpr (PL == 8) {
+          t = mfma16(load_frag(kt + TQ::off(16 * jb + li, ks * KS + g * PL)), qs[ks], t);
+        } else {
+          t = mfma16(kt[TQ::off(16 * jb + li, QRegs<CF>::feature(ks, g))], qs[ks], t);
+        }
+      }
+      return t;
+    };
+    auto weights = [&](int jb) {
+      frag qs[R / KS];
+      f32x4 t;
+      if (jb == ib) {
+        // rows 0..7 of the block: reference at the block's start; rows
+        // 8..15: at its token 7.  Each lane scales its own row's phi(q);
+        // both contractions cover all 16 rows and each lane keeps its own.
+        float xd[NQ];
+        row_vals(16 * ib + 7, xd);
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) xd[n] = li < 8 ? x[n] : x[n] - xd[n];
+        scaled(xd, qs);
+        const f32x4 t0 = contract(skd0, jb, qs);
+        const f32x4 t1 = contract(skd1, jb, qs);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = li < 8 ? t0[r] : t1[r];
+      } else {
+        advance(jb);
+        scaled(x, qs);
+        t = contract(skb, jb, qs);
+      }
+      if constexpr (PL == 8) {
+        if (jb == ib) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) t[r] = 4 * g + r > li ? 0.f : t[r];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float xv = (jb == ib && 4 * g + r > li) ? 0.f : t[r];
+          t[r] = xv;
+          den += xv;
+        }
+      }
+      return t;
+    };
+#pragma unroll
+    for (int jp = (RB + 1) / 2 - 1; jp >= 0; --jp) {
+      const int jb0 = 2 * jp, jb1 = 2 * jp + 1;
+      if (jb0 > ib) continue;
+      const bool two = jb1 < RB && jb1 <= ib;
+      const f32x4 a1 = two ? weights(jb1) : zero4();
+      const f32x4 a0 = weights(jb0);
+      if constexpr (PL == 8) {
+        const float w8[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        const bf16x8 bv = cvt_bf16x8(w8);
+        dacc = mfma16(ones_rows, bv, dacc);
+#pragma unroll
+        for (int cti = 0; cti < CTW; ++cti) {
+          const int ct = ct0 + cti;
+          const bf16x8 av = two ? tr_frag<DV>(sv, 16 * jb0 + 4 * g, 16 * jb1 + 4 * g, 16 * ct, li)
+                                : tr_frag_lo<DV>(sv, 16 * jb0 + 4 * g, 16 * ct, li);
+          o[cti] = mfma16(av, bv, o[cti]);
+        }
+      } else {
+#pragma unroll
+        for (int cti = 0; cti < CTW; ++cti) {
+          const int ct = ct0 + cti;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            o[cti] = mfma16(sv[TV::off(16 * jb0 + 4 * g + r, 16 * ct + li)], a0[r], o[cti]);
+            if (two) o[cti] = mfma16(sv[TV::off(16 * jb1 + 4 * g + r, 16 * ct + li)], a1[r], o[cti]);
+          }
+        }
+      }
+    }
+
+    // read-out of the carried state and its z term: phi(q_i) 2^(P_i + sum_{b<ib} T_b)
+    advance(-1);
+    {
+      frag qs[R / KS];
+      scaled(x, qs);
+#pragma unroll
+      for (int ks = 0; ks < R / KS; ++ks) {
+        if constexpr (PL == 1) {
+          den += qs[ks] * sz[QRegs<CF>::feature(ks, g)];
+        } else {
+          dacc = mfma16(load_frag(sz + zrow * R + ks * KS + g * PL), qs[ks], dacc);
+        }
+      }
+#pragma unroll
+      for (int cti = 0; cti < CTW; ++cti) {
+        const int ct = ct0 + cti;
+#pragma unroll
+        for (int ks = 0; ks < R / KS; ++ks) {
+          if constexpr (PL == 8) {
+            o[cti] = mfma16(tr_frag<DV>(ss, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, 16 * ct, li), qs[ks], o[cti]);
+          } else {
+            o[cti] = mfma16(ss[TV::off(QRegs<CF>::feature(ks, g), 16 * ct + li)], qs[ks], o[cti]);
+          }
+        }
+      }
+    }
+
+    if constexpr (PL == 8) {
+      den = dacc[0] + dacc[1];
+    } else {
+      den = xor_sum16_32(den);
+    }
+    const float rden = normalize ? __builtin_amdgcn_rcpf(den) : 1.f;
+#pragma unroll
+    for (int cti = 0; cti < CTW; ++cti) {
+      if constexpr (sizeof(typename CF::IO) == 2) {
+        out.v[rbi][cti] = cvt_bf16x4(o[cti] * rden);
+      } else {
+        out.v[rbi][cti] = o[cti] * rden;
+      }
+    }
+  }
+}
+
+// This lane's state row f = 16 w + li: the log2 of its decay over the chunk,
+// sum_b T_b.
+template <class CF>
+__device__ __forceinline__ float gla_chunk_l2(const float* sp, int w, int li) {
+  using TP = Tile<float, CF::R>;
+  float c = 0.f;
+#pragma unroll
+  for (int b = 0; b < CF::RB; ++b) c += sp[TP::off(16 * b + 15, 16 * w + li)];
+  return c;
+}
+
+template <class CF>
+struct SmemStateGla {
+  using OP = typename CF::OP;
+  OP kw[Tile<OP, CF::R>::elems(CF::C)];
+  OP kw_lo[sizeof(OP) == 2 ? Tile<OP, CF::R>::elems(CF::C) : 1];
+  OP v[Tile<OP, CF::DV>::elems(CF::C)];
+  alignas(16) float p[Tile<float, CF::R>::elems(CF::C)];
+};
+
+template <class CF>
+struct SmemOutGla {
+  using OP = typename CF::OP;
+  OP kd0[Tile<OP, CF::R>::elems(CF::C)];
+  OP kd1[Tile<OP, CF::R>::elems(CF::C)];
+  OP kb[Tile<OP, CF::R>::elems(CF::C)];
+  OP kw[Tile<OP, CF::R>::elems(CF::C)];
+  OP v[Tile<OP, CF::DV>::elems(CF::C)];
+  OP s[Tile<OP, CF::DV>::elems(CF::R)];
+  alignas(16) typename CF::ZT z[CF::ZE];
+  alignas(16) OP scr[Scratch<CF>::ELEMS];
+  alignas(16) float p[Tile<float, CF::R>::elems(CF::C)];
+};
+
+// Whether the per-channel gated kernels of this configuration fit the LDS.
+template <class CF>
+constexpr bool gla_fits() {
+  return sizeof(SmemOutGla<CF>) <= 160 * 1024 && sizeof(SmemStateGla<CF>) <= 160 * 1024;
+}
+
+// Per-span state with per-channel gates: the span's sum decayed to its end
+// (key j of a chunk weighted to the chunk's end, the running sum's row f
+// multiplied by the chunk's decay 2^(sum_b T_b)); the span's total log2 gate
+// per channel goes to totals[bh][s][R].  One LDS buffer, three barriers per
+// chunk (the P tile is complete before the keys are weighted).
+template <class CF>
+__global__ __launch_bounds__(CF::NT) void la_state_kernel_gla(const typename CF::IO* __restrict__ K,
+                                                                const typename CF::IO* __restrict__ V,
+                                                                float* __restrict__ ws, int N, int n_span,
+                                                                const float* __restrict__ log_a,
+                                                                float* __restrict__ totals) {
+  using OP = typename CF::OP;
+  __shared__ SmemStateGla<CF> sm;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
+  const int bh = blockIdx.x / n_span;
+  const int s = blockIdx.x % n_span;
+  const int t_begin = span_begin<CF>(s, n_span, N);
+  const int t_end = span_begin<CF>(s + 1, n_span, N);
+  HeadBufs hb = head_bufs<CF>(nullptr, K, V, nullptr, bh, N);
+  hb.a = make_rsrc(log_a + (size_t)bh * N * CF::R, (unsigned)N * CF::R * 4u);
+
+  f32x4 acc[CF::TPW];
+#pragma unroll
+  for (int i = 0; i < CF::TPW; ++i) acc[i] = zero4();
+  f32x4 zt[CF::ZPW];
+#pragma unroll
+  for (int k = 0; k < CF::ZPW; ++k) zt[k] = zero4();
+  float span_l2 = 0.f;  // row 16 w + li: the span's total log2 gate so far
+
+  const int last = t_end > t_begin ? t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C : t_begin;
+  ChunkRegs<CF, false> cr;
+  GateRegsGla<CF> gr;
+  load_gates_gla<CF>(gr, hb.a, t_begin);
+  load_chunk<CF, false>(cr, hb, t_begin);
+  OP* lo = sizeof(OP) == 2 ? sm.kw_lo : nullptr;
+  for (int t0 = t_begin; t0 < t_end; t0 += CF::C) {
+    __syncthreads();  // the previous chunk's MFMA work is done with kw, v
+    gla_prefix_to_lds<CF>(gr, sm.p);
+    stage_values<CF>(cr, sm.v);
+    __syncthreads();
+    gla_stage_keys<CF, false>(cr, sm.p, nullptr, nullptr, nullptr, sm.kw, lo, t0, N);
+    const float l2 = gla_chunk_l2<CF>(sm.p, w, li);
+    const int tn = min(t0 + CF::C, last);
+    load_gates_gla<CF>(gr, hb.a, tn);
+    load_chunk<CF, false>(cr, hb, tn);
+    __syncthreads();
+    span_l2 += l2;
+    const float dg = __builtin_amdgcn_exp2f(l2);
+#pragma unroll
+    for (int i = 0; i < CF::TPW; ++i) acc[i] *= dg;
+#pragma unroll
+    for (int k = 0; k < CF::ZPW; ++k) zt[k] *= dg;
+    state_mfma<CF>(acc, zt, sm.kw, lo, sm.v, w, g, li);
+  }
+
+  constexpr int E = CF::R * CF::DV + CF::R;
+  float* slot = ws + ((size_t)bh * (n_span + 1) + s) * E;
+#pragma unroll
+  for (int i = 0; i < CF::TPW; ++i) {
+    int ct, ft;
+    state_tile<CF>(w, i, ct, ft);
+    *reinterpret_cast<f32x4*>(slot + (16 * ft + li) * CF::DV + 16 * ct + 4 * g) = acc[i];
+  }
+  if (g == 0) {
+    slot[CF::R * CF::DV + 16 * w + li] = zt[0][0];
+    totals[((size_t)bh * n_span + s) * CF::R + 16 * w + li] = span_l2;
+  }
+}
+
+// Outputs of one span with per-channel gates (causal): la_output_kernel's
+// chunk walk with the P tile, four weighted key tiles and one more barrier
+// per chunk (the keys are weighted once the P tile is complete).
+template <class CF>
+__global__ __launch_bounds__(CF::NT, CF::MINB_DECAY) void la_output_kernel_gla(
+    const typename CF::IO* __restrict__ Q, const typename CF::IO* __restrict__ K,
+    const typename CF::IO* __restrict__ V, typename CF::IO* __restrict__ O, const float* __restrict__ ws, int N,
+    int n_span, const float* __restrict__ log_a, int normalize) {
+  __shared__ SmemOutGla<CF> sm;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
+  const int bh = (int)(gridDim.x / n_span) - 1 - (int)(blockIdx.x / n_span);
+  const int s = blockIdx.x % n_span;
+  const int t_begin = span_begin<CF>(s, n_span, N);
+  const int t_end = span_begin<CF>(s + 1, n_span, N);
+  HeadBufs hb = head_bufs<CF>(Q, K, V, O, bh, N);
+  hb.a = make_rsrc(log_a + (size_t)bh * N * CF::R, (unsigned)N * CF::R * 4u);
+
+  constexpr int E = CF::R * CF::DV + CF::R;
+  const float* pre = ws + ((size_t)bh * (n_span + 1) + s) * E;
+  f32x4 sacc[CF::TPW];
+#pragma unroll
+  for (int i = 0; i < CF::TPW; ++i) {
+    int ct, ft;
+    state_tile<CF>(w, i, ct, ft);
+    sacc[i] = *reinterpret_cast<const f32x4*>(pre + (16 * ft + li) * CF::DV + 16 * ct + 4 * g);
+  }
+  f32x4 zt[CF::ZPW];
+  {
+    const float zv = pre[CF::R * CF::DV + 16 * w + li];
+    zt[0] = f32x4{zv, zv, zv, zv};
+  }
+
+  // the same exact counter waits as la_output_kernel: the prologue issues
+  // the loop's memory operations in the loop's order (gates, K and V, Q,
+  // then the stores, dropped)
+  if (t_begin >= t_end) return;
+  const int last = t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C;
+  ChunkRegs<CF, false> cr;
+  GateRegsGla<CF> gr;
+  QRegs<CF> qr;
+  load_gates_gla<CF>(gr, hb.a, t_begin);
+  load_chunk<CF, false>(cr, hb, t_begin);
+  mem_order_fence();
+  qr.load(hb.q, t_begin, w, g, li);
+  mem_order_fence();
+  dummy_stores<CF>(hb.o);
+  typename CF::OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
+  OutRegs<CF> out;
+  int t0 = t_begin;
+  do {
+    __syncthreads();  // every wave is done with the previous chunk's tiles
+    publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
+    gla_prefix_to_lds<CF>(gr, sm.p);
+    stage_values<CF>(cr, sm.v);
+    float fq[CF::RBW][GlaCfg<CF>::NQ];
+    qr.to_f32(fq, scr, g, li);
+    __syncthreads();  // the P tile is complete
+    gla_stage_keys<CF, true>(cr, sm.p, sm.kd0, sm.kd1, sm.kb, sm.kw, nullptr, t0, N);
+    const int tn = min(t0 + CF::C, last);
+    load_gates_gla<CF>(gr, hb.a, tn);
+    load_chunk<CF, false>(cr, hb, tn);
+    qr.load(hb.q, tn, w, g, li);
+    __syncthreads();
+    chunk_outputs_gla<CF>(fq, sm.kd0, sm.kd1, sm.kb, sm.v, sm.s, sm.z, sm.p, out, w, g, li, normalize);
+    store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
+    // the carry past this chunk (gates past N are one)
+    const float dg = __builtin_amdgcn_exp2f(gla_chunk_l2<CF>(sm.p, w, li));
+#pragma unroll
+    for (int i = 0; i < CF::TPW; ++i) sacc[i] *= dg;
+    zt[0] *= dg;
+    state_mfma<CF>(sacc, zt, sm.kw, nullptr, sm.v, w, g, li);
+    t0 += CF::C;
+  } while (t0 < t_end);
 }
 
 // ------------------------------------------------------------------ single pass
@@ -1435,6 +2048,30 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
   auto rec = [&](int i) {
     if (a.events && a.events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a.events[i]), st);
   };
+  if (a.log_a_ch) {
+    if constexpr (gla_fits<CF>()) {
+      if (!a.causal) return hipErrorInvalidValue;
+      float* tot = ws + (size_t)BH * (n_span + 1) * (CF::R * CF::DV + CF::R);
+      const dim3 grid(BH * n_span), block(CF::NT);
+      rec(0);
+      if (n_span > 0 && BH > 0)
+        hipLaunchKernelGGL((la_state_kernel_gla<CF>), grid, block, 0, st, K, V, ws, a.N, n_span, a.log_a_ch, tot);
+      rec(1);
+      rec(2);
+      hipError_t e = scan_launch(ws, BH, CF::R, CF::DV, n_span, a.S0, a.z0, a.S_out, a.z_out, st, nullptr, a.H,
+                                 a.N, CF::C, tot, 1);
+      if (e != hipSuccess) return e;
+      rec(3);
+      rec(4);
+      if (n_span > 0 && BH > 0)
+        hipLaunchKernelGGL((la_output_kernel_gla<CF>), grid, block, 0, st, Q, K, V, O, ws, a.N, n_span,
+                           a.log_a_ch, a.normalize);
+      rec(5);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   const int dk = !a.causal ? kNoDecay : a.log_a ? kGated : a.gamma ? kFixed : kNoDecay;
   // gated: the spans' total log2 gates follow the span states
   float* totals = dk == kGated ? ws + (size_t)BH * (n_span + 1) * (CF::R * CF::DV + CF::R) : nullptr;
@@ -1494,11 +2131,14 @@ static hipError_t dispatch_chunk(const PrefillArgs& a) {
 
 hipError_t scan_launch(float* ws, int BH, int R, int DV, int n_span, const float* S0, const float* z0,
                        float* S_out, float* z_out, hipStream_t stream, const float* gamma, int H, int N, int chunk,
-                       const float* totals) {
+                       const float* totals, int per_channel) {
   const int E = R * DV + R;
   if (BH > 0) {
     const dim3 grid((E + kThreads - 1) / kThreads, BH);
-    if (totals)
+    if (totals && per_channel)
+      hipLaunchKernelGGL(la_scan_kernel<kChannel>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0,
+                         S_out, z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, totals);
+    else if (totals)
       hipLaunchKernelGGL(la_scan_kernel<kGated>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0, S_out,
                          z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, totals);
     else if (gamma)
@@ -1522,6 +2162,14 @@ bool prefill_supported(int io, int phi, int d, int dv, int r, int chunk) {
     return false;
   }
   if (io == 0) return d == 64 && chunk <= 64;  // fp32
+  return false;
+}
+
+bool gla_supported(int io, int d, int dv, int r, int chunk) {
+  if (r != d || dv != d) return false;
+  if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128) return false;
+  if (io == 1) return d == 64 || (d == 128 && chunk <= 32);  // (d = 128, chunk 64: the tiles exceed the LDS)
+  if (io == 0) return d == 64 && chunk <= 64;
   return false;
 }
 

@@ -141,6 +141,24 @@ def draw_log_gates(B, H, N, seed=GATE_SEED, resets=0):
     return out
 
 
+def draw_log_gates_ch(B, H, N, r, seed=GATE_SEED + 1, resets=0):
+    """Per-token, per-key-channel natural-log gates for the GLA-form
+    workloads, float32 [B, H, N, r]: log a = log(sigmoid(x)) / 16 with
+    x ~ N(0, 2^2), GLA's sigmoid(x)^(1/16) gate form (the pages give no
+    values).  ``resets`` (token, channel) entries per head, at seeded
+    positions, get log a = -inf (a zero gate).  Deterministic."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, H, N, r), dtype=np.float32) * np.float32(2.0)
+    out = (-np.logaddexp(np.float32(0.0), -x) / np.float32(16.0)).astype(np.float32)
+    for b in range(B):
+        for h in range(H):
+            if resets and N:
+                t = rng.integers(0, N, size=resets)
+                f = rng.integers(0, r, size=resets)
+                out[b, h, t, f] = -np.inf
+    return out
+
+
 @dataclass(frozen=True)
 class Workload:
     """Shapes of one named workload (no arithmetic)."""

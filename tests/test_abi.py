@@ -216,6 +216,47 @@ def test_gated_argument_errors(lib):
     assert dg(H=0, S=None) == 0
 
 
+def test_gla_argument_errors(lib):
+    """la_forward_gla / la_decode_step_gla / the GLA workspace and config
+    queries: every case returns before any HIP call."""
+    def fg(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, B=1, H=1, N=64, d=64, dv=64, io=1, phi=0, r=0, log_a=FAKE,
+           normalize=1, chunk=64, S0=None, z0=None, S_out=None, z_out=None, ws=FAKE, ws_bytes=1 << 30):
+        return lib.la_forward_gla(Q, K, V, O, B, H, N, d, dv, io, phi, r, log_a, normalize, chunk, S0, z0, S_out,
+                                  z_out, ws, ws_bytes, None)
+    assert fg(log_a=None) == 1                           # LA_ERR_NULL
+    assert fg(K=None) == 1
+    assert fg(N=-3) == 2                                 # LA_ERR_SHAPE
+    assert fg(N=(1 << 23)) == 2                          # the head's [N][r] fp32 gates pass 2^31 bytes
+    assert fg(normalize=-1) == 3                         # LA_ERR_UNSUPPORTED
+    assert fg(phi=1, r=256) == 3                         # no FAVOR+
+    assert fg(d=128, dv=128, chunk=64) == 3              # d = 128: chunk 16 or 32 only
+    assert fg(io=0, chunk=128) == 3
+    assert fg(log_a=MISALIGNED) == 4                     # LA_ERR_ALIGN
+    assert fg(ws=None) == 5                              # LA_ERR_WORKSPACE
+    assert fg(Q=None, K=None, V=None, O=None, B=0, ws=None) == 0
+    # r total gates per (head, span) follow the span states
+    B, H, N = 1, 32, 32768
+    n, c = ctypes.c_int(), ctypes.c_int()
+    assert lib.la_forward_gla_config(B, H, N, 64, 64, 1, 0, 0, 64, ctypes.byref(n), ctypes.byref(c)) == 0
+    assert n.value == 16 and c.value == 64
+    need = lib.la_forward_gla_workspace_bytes(B, H, N, 64, 64, 1, 0, 0, 64)
+    assert need == B * H * ((n.value + 1) * (64 * 64 + 64) + n.value * 64) * 4
+    assert fg(B=B, H=H, N=N, ws_bytes=need - 4) == 5
+    # chunk 0 at d = 128 means 32
+    assert lib.la_forward_gla_config(2, 16, 65536, 128, 128, 1, 0, 0, 0, ctypes.byref(n), ctypes.byref(c)) == 0
+    assert c.value == 32
+
+    def dg(S=FAKE, z=FAKE, q=FAKE, k=FAKE, v=FAKE, o=FAKE, Sn=FAKE, zn=FAKE, B=1, H=1, d=64, dv=64, io=1,
+           phi=0, r=0, log_a=FAKE, normalize=1):
+        return lib.la_decode_step_gla(S, z, q, k, v, o, Sn, zn, B, H, d, dv, io, phi, r, log_a, normalize, None)
+    assert dg(log_a=None) == 1
+    assert dg(q=None) == 1
+    assert dg(normalize=3) == 3
+    assert dg(phi=1, r=256) == 3
+    assert dg(log_a=MISALIGNED) == 4
+    assert dg(B=0, S=None) == 0
+
+
 def test_feature_map_argument_errors(lib):
     def fm(X=FAKE, Y=FAKE, rows=10, d=64, io=1, phi=0, r=0, omega=None):
         return lib.la_feature_map(X, Y, rows, d, io, phi, r, omega, None)
