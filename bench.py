@@ -48,6 +48,8 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 KERNEL_NAMES = ("la_state_kernel", "la_scan_kernel", "la_output_kernel")
 FAVOR_KERNEL_NAMES = ("la_state_favor_kernel", "la_scan_kernel", "la_output_favor_kernel")
 FUSED_KERNEL_NAMES = ("la_fused_reset_kernel", None, "la_fused_kernel")
+BACKWARD_KERNEL_NAMES = ("la_state_kernel", "la_scan_kernel", "la_bwd_dq_kernel", "la_suffix_scan_kernel",
+                         "la_bwd_dkv_kernel")
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "kernelized_linear_attention_elu_amd", "csrc")
 ROTATE = 3                     # input/output copies used in turn by the prefill bench
@@ -111,6 +113,8 @@ def parse_args(argv=None):
                    help="causal prefill with a fixed per-head decay (RetNet form, la_forward_decay)")
     p.add_argument("--gated", action="store_true",
                    help="causal prefill with a per-token scalar gate (SSD scalar-decay form, la_forward_gated)")
+    p.add_argument("--backward", action="store_true",
+                   help="the backward pass of the causal prefill (la_backward: dQ, dK, dV for an upstream dO)")
     p.add_argument("--gla", action="store_true",
                    help="causal prefill with a per-token, per-key-channel gate (GLA form, la_forward_gla)")
     p.add_argument("--chunk", type=int, default=None,
@@ -331,6 +335,126 @@ def bench_prefill(args, torch, la, synth):
     return res
 
 
+def bench_backward(args, torch, la, synth):
+    """One step = la_backward over the workload: the forward span states and
+    their scan, the dQ pass, the reverse scan, the dK/dV pass, with Q, K, V,
+    O (the library's forward output) and dO resident in HBM."""
+    from kernelized_linear_attention_elu_amd import hostio
+    import numpy as np
+    w = synth.WORKLOADS[args.workload]
+    if w.phi == "favor" or w.d != 64 or args.noncausal:
+        raise SystemExit("--backward: causal, d = 64, pointwise feature maps")
+    dev = torch.device("cuda:0")
+    q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
+    rng = np.random.default_rng(91)
+    dO = synth.round_to_io(rng.standard_normal((w.B, w.H, w.N, w.dv), dtype=np.float32), "bf16")
+
+    def to_dev(x):
+        return hostio.upload_bf16_bits(synth.bf16_bits(x), dev)
+
+    Q0, K0, V0, G0 = to_dev(q), to_dev(k), to_dev(v), to_dev(dO)
+    O0 = la.forward(Q0, K0, V0, phi=w.phi)
+    sets = [(Q0, K0, V0, O0, G0)] + [tuple(t.clone() for t in (Q0, K0, V0, O0, G0)) for _ in range(ROTATE - 1)]
+    outs = [(torch.empty_like(Q0), torch.empty_like(K0), torch.empty_like(V0)) for _ in range(ROTATE)]
+    ws = torch.empty(int(la.load_library().la_backward_workspace_bytes(w.B, w.H, w.N, w.d, w.dv, la.LA_BF16,
+                                                                        la.PHI[w.phi], 0, 64)),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i, events=None):
+        Q, K, V, O, G = sets[i % ROTATE]
+        la.backward(Q, K, V, O, G, phi=w.phi, out=outs[i % ROTATE], workspace=ws, events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    settled = settle(torch, step, args.settle)
+    nk = la.LA_BACKWARD_KERNELS
+    evs = [[la.event_create() for _ in range(2 * nk)] for _ in range(args.steps)]
+    live = [[None] * (2 * nk - 2) + e[2 * nk - 2:] for e in evs]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, live[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    last_live_ms = sum(la.event_elapsed_ms(e[2 * nk - 2], e[2 * nk - 1]) for e in evs) / args.steps
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    kern_ms = [0.0] * nk
+    for e in evs:
+        for j in range(nk):
+            kern_ms[j] += la.event_elapsed_ms(e[2 * j], e[2 * j + 1]) / args.steps
+    for e in evs:
+        for x in e:
+            la.event_destroy(x)
+    ms = (t1 - t0) * 1e3 / args.steps
+    token_heads = w.B * w.H * w.N
+    # the dK/dV pass (timed live, the last kernel of the step) reads Q, K, V,
+    # dO and (D_i, h_i), writes dK, dV
+    pass_b_bytes = token_heads * ((3 * w.d + w.dv) * 2 + 8 + (w.d + w.dv) * 2)
+    achieved = pass_b_bytes / (last_live_ms * 1e-3) / 1e9
+    n_span = int(ctypes_config(la, w))
+    step_bytes = token_heads * ((w.d + w.dv) * 2                     # forward span states read K, V (+ scan)
+                                + ((2 * w.d + 3 * w.dv) * 2 + w.d * 2 + 8)   # dQ pass
+                                + ((2 * w.d + 2 * w.dv) * 2 + 8 + (w.d + w.dv) * 2))  # dK/dV pass
+    res = {
+        "metric": "causal LA backward tokens/s at N=32k,d=64 bf16 (dQ, dK, dV)",
+        "value": w.B * w.N / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name} backward B{w.B} H{w.H} N{w.N} d{w.d} dv{w.dv} bf16 I/O, fp32 states, "
+                        f"phi=elu+1, causal, chunk 64, dO ~ N(0, 1)",
+            "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv, "chunk": 64, "phi": w.phi, "backward": True,
+        },
+        "roofline": {"kernel": "la_bwd_dkv_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "path_roofline": {"bound": "hbm", "alg_bytes": step_bytes,
+                          "achieved_gbs": step_bytes / (ms * 1e-3) / 1e9,
+                          "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "kernels_us": {n: t * 1e3 for n, t in zip(BACKWARD_KERNEL_NAMES, kern_ms)},
+        "dominant_kernel_us_live": last_live_ms * 1e3,
+        "path": {"spans_per_head": n_span},
+        "settle": {"seconds": args.settle, "untimed_steps": settled},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import backward as bwd
+        # a bounded sample: the sampled-row gradient oracle (two fp64 token
+        # loops over every token of the sampled heads) for one row per head
+        h = min(2, w.H)
+        t_a = time.perf_counter()
+        c_a = time.process_time()
+        bwd.grad_rows(q[:1, :h], k[:1, :h], v[:1, :h], dO[:1, :h], [w.N - 1])
+        wall = time.perf_counter() - t_a
+        cpu = time.process_time() - c_a
+        per_job = wall * (w.B * w.H) / h
+        res["cpu_baseline"] = {
+            "value": w.B * w.N / per_job, "unit": "tokens/s", "cores": max(1, round(cpu / max(wall, 1e-9))),
+            "kind": "oracle",
+            "sample": f"fp64 prefix/suffix-state gradient loops over {h} of {w.B * w.H} heads x {w.N} tokens "
+                      f"({wall:.1f} s), scaled to the full job",
+            "cpu": cpu_info(),
+        }
+    return res
+
+
+def ctypes_config(la, w):
+    import ctypes
+    n = ctypes.c_int()
+    la.load_library().la_backward_config(w.B, w.H, w.N, w.d, w.dv, la.LA_BF16, la.PHI[w.phi], 0, 64,
+                                         ctypes.byref(n))
+    return n.value
+
+
 def bench_decode(args, torch, la, synth):
     from kernelized_linear_attention_elu_amd import hostio
     import numpy as np
@@ -456,6 +580,8 @@ def main(argv=None):
             res = bench_decode(args, torch, la, synth)
         elif args.workload == "feature":
             res = bench_feature(args, torch, la, synth)
+        elif args.backward:
+            res = bench_backward(args, torch, la, synth)
         else:
             res = bench_prefill(args, torch, la, synth)
     print(json.dumps(res), flush=True)

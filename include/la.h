@@ -61,6 +61,7 @@
  *       la_decode_step: d = d_v in {64, 128}; FAVOR+ with r = 256.
  *       la_decode_step_decay: d = d_v in {64, 128}, ELU1/IDENTITY.
  *       la_forward_gated, la_decode_step_gated: as the decay calls.
+ *       la_backward: bf16, ELU1/IDENTITY, d = d_v = 64, chunk 64 (0 means 64).
  *       la_forward_gla: ELU1/IDENTITY, d = d_v = 64 (bf16: chunk 16..128;
  *       fp32: 16..64) or d = d_v = 128 (bf16, chunk 16 or 32; chunk = 0
  *       means 32 there); la_decode_step_gla: as the decay decode.
@@ -335,6 +336,53 @@ la_status la_forward_gla_timed(const void *Q, const void *K, const void *V, void
 la_status la_decode_step_gla(const float *S, const float *z, const void *q, const void *k, const void *v, void *o,
                              float *S_new, float *z_new, int B, int H, int d, int d_v, int io_dtype, int phi, int r,
                              const float *log_a, int normalize, void *stream);
+
+/* Number of kernels la_backward enqueues (forward span states, their scan,
+ * the dQ pass, the reverse scan, the dK/dV pass). */
+#define LA_BACKWARD_KERNELS 5
+
+/*
+ * Backward pass of the causal normalised output (no initial state): for an
+ * upstream gradient dO, the gradients of sum(dO * O) with respect to Q, K
+ * and V.  The pages define the forward ("Efficient attention variants"
+ * sec. 5) and name the backward among the costs that decide speed (sec. 8)
+ * without deriving it; what is computed is the chain rule on that forward:
+ * with D_i = phi(q_i).z_i, g_i = dO_i / D_i, h_i = -(dO_i . O_i) / D_i,
+ *   dphi(q_i) = sum_{j<=i} (v_j.g_i + h_i) phi(k_j),
+ *   dphi(k_j) = sum_{i>=j} (v_j.g_i + h_i) phi(q_i),
+ *   dv_j      = sum_{i>=j} (phi(q_i).phi(k_j)) g_i,
+ * and dq = dphi(q) * phi'(q), dk = dphi(k) * phi'(k) (phi' of ELU+1 with
+ * alpha = 1: 1 for x > 0, e^x otherwise; 1 for the identity).  Evaluated
+ * chunkwise: a forward-direction pass for dQ (with the forward's span
+ * prefix states) and a reverse-direction pass for dK, dV (with suffix states
+ * of phi(q) g^T and phi(q) h), bf16 operands and fp32 accumulation.
+ *   Q, K, V, O, dO in:  device bf16, O the forward output of la_forward
+ *                  (causal, same phi) for these Q, K, V; layouts as la_forward.
+ *   dQ, dK, dV     out: device bf16, the shapes of Q, K, V; may not alias the
+ *                  inputs.
+ *   workspace      device scratch of at least la_backward_workspace_bytes(...).
+ * Supported: bf16, ELU1/IDENTITY, d = d_v = 64, chunk 64 (0 means 64); others
+ * return LA_ERR_UNSUPPORTED.
+ * Errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_UNSUPPORTED, LA_ERR_ALIGN,
+ * LA_ERR_WORKSPACE (nothing enqueued), LA_ERR_HIP.
+ */
+la_status la_backward(const void *Q, const void *K, const void *V, const void *O, const void *dO, void *dQ, void *dK,
+                      void *dV, int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes la_backward needs (0 for invalid or unsupported arguments):
+ * two sets of fp32 span states and (D_i, h_i) per token. */
+size_t la_backward_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk);
+
+/* Spans per head la_backward uses (*n_span; may be NULL); no device work. */
+la_status la_backward_config(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk,
+                             int *n_span);
+
+/* la_backward plus timing: events NULL or 2*LA_BACKWARD_KERNELS hipEvent_t,
+ * events[2i] recorded before kernel i and events[2i+1] after it. */
+la_status la_backward_timed(const void *Q, const void *K, const void *V, const void *O, const void *dO, void *dQ,
+                            void *dK, void *dV, int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r,
+                            int chunk, void *workspace, size_t workspace_bytes, void *stream, void *const *events);
 
 /*
  * Standalone feature map: Y[i] = phi(X[i]) for rows i = 0..rows-1.

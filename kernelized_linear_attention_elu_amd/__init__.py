@@ -25,6 +25,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "la.h")
 LA_F32, LA_BF16 = 0, 1
 PHI = {"elu1": 0, "favor": 1, "identity": 2}
 LA_FORWARD_KERNELS = 3
+LA_BACKWARD_KERNELS = 5
 STATUS = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_UNSUPPORTED",
           4: "LA_ERR_ALIGN", 5: "LA_ERR_WORKSPACE", 6: "LA_ERR_HIP"}
 
@@ -47,6 +48,10 @@ _SIGS = {
     "la_forward_gated": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
     "la_forward_gated_timed": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp, _vp]),
     "la_decode_step_gated": (_i, [_vp] * 8 + [_i] * 7 + [_vp, _i, _vp]),
+    "la_backward_workspace_bytes": (ctypes.c_size_t, [_i] * 9),
+    "la_backward_config": (_i, [_i] * 9 + [ctypes.POINTER(_i)]),
+    "la_backward": (_i, [_vp] * 8 + [_i] * 9 + [_vp, ctypes.c_size_t, _vp]),
+    "la_backward_timed": (_i, [_vp] * 8 + [_i] * 9 + [_vp, ctypes.c_size_t, _vp, _vp]),
     "la_forward_gla_workspace_bytes": (ctypes.c_size_t, [_i] * 9),
     "la_forward_gla_config": (_i, [_i] * 9 + [ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "la_forward_gla": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
@@ -317,6 +322,43 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
     if return_state:
         return out, S_out, z_out
     return out
+
+
+def backward(Q, K, V, O, dO, *, phi="elu1", chunk=64, out=None, workspace=None, events=None):
+    """Gradients (dQ, dK, dV) of sum(dO * O) for the causal normalised output
+    O = forward(Q, K, V, phi=phi) (la_backward; bf16, d = d_v = 64).  ``out``:
+    optional (dQ, dK, dV) tensors to fill.  ``events``: optional list of
+    2*LA_BACKWARD_KERNELS event handles."""
+    torch = _torch()
+    lib = load_library()
+    if Q.dim() != 4:
+        raise ValueError("Q, K, V, O, dO must be [B, H, N, d]")
+    B, H, N, d = Q.shape
+    dv = V.shape[-1]
+    dev = Q.device
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("O", O), ("dO", dO)):
+        _require(t, name, Q.dtype, dev)
+    if K.shape != Q.shape or V.shape[:3] != Q.shape[:3] or O.shape != V.shape or dO.shape != V.shape:
+        raise ValueError("shape mismatch between Q, K, V, O, dO")
+    io = _io_code(Q)
+    if out is None:
+        out = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+    dQ, dK, dV = out
+    for name, t, ref in (("dQ", dQ, Q), ("dK", dK, K), ("dV", dV, V)):
+        _require(t, name, Q.dtype, dev)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
+    need = int(lib.la_backward_workspace_bytes(B, H, N, d, dv, io, PHI[phi], 0, chunk))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    args = [_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), B, H, N, d, dv, io,
+            PHI[phi], 0, chunk, _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)]
+    if events is None:
+        _check(lib.la_backward(*args), "la_backward")
+    else:
+        arr = (ctypes.c_void_p * (2 * LA_BACKWARD_KERNELS))(*events)
+        _check(lib.la_backward_timed(*args, arr), "la_backward_timed")
+    return dQ, dK, dV
 
 
 def decode_step(S, z, q, k, v, *, phi="elu1", omega=None, inplace=True, out=None, gamma=None, normalize=True,

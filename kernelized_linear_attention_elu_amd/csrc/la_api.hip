@@ -370,6 +370,71 @@ la_status la_decode_step_gla(const float* S, const float* z, const void* q, cons
                      normalize, nullptr, log_a);
 }
 
+namespace {
+
+la_status backward_shape(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk, Shape* sh) {
+  if (B < 0 || H < 0 || N < 0 || d <= 0 || d_v <= 0 || r < 0 || chunk < 0) return LA_ERR_SHAPE;
+  if (io_dtype != LA_F32 && io_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  if (phi != LA_PHI_ELU1 && phi != LA_PHI_FAVOR && phi != LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;
+  const int rr = norm_r(phi, d, r);
+  const int ch = norm_chunk(chunk);
+  if (!la::backward_supported(io_dtype, phi, d, d_v, rr, ch)) return LA_ERR_UNSUPPORTED;
+  return check_forward_shape(B, H, N, d, d_v, io_dtype, phi, r, 1, chunk, sh, 1);
+}
+
+la_status backward_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO, void* dQ,
+                        void* dK, void* dV, int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r,
+                        int chunk, void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  Shape sh;
+  const la_status st = backward_shape(B, H, N, d, d_v, io_dtype, phi, r, chunk, &sh);
+  if (st != LA_OK) return st;
+  const bool have_tokens = sh.BH > 0 && N > 0;
+  if (have_tokens && (!Q || !K || !V || !O || !dO || !dQ || !dK || !dV)) return LA_ERR_NULL;
+  const void* ptrs[] = {Q, K, V, O, dO, dQ, dK, dV, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return LA_ERR_ALIGN;
+  const size_t need = la::backward_workspace_bytes(sh.BH, sh.n_span, N, sh.r, sh.dv);
+  if (have_tokens && (!workspace || workspace_bytes < need)) return LA_ERR_WORKSPACE;
+  if (!have_tokens) return LA_OK;
+  la::BackwardArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.dQ = dQ; a.dK = dK; a.dV = dV;
+  a.B = B; a.H = H; a.N = N; a.d = d; a.dv = d_v; a.r = sh.r;
+  a.io = io_dtype; a.phi = phi; a.chunk = sh.chunk; a.n_span = sh.n_span;
+  a.workspace = workspace; a.stream = stream; a.events = events;
+  return hip_status(la::backward_launch(a));
+}
+
+}  // namespace
+
+size_t la_backward_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk) {
+  Shape sh;
+  if (backward_shape(B, H, N, d, d_v, io_dtype, phi, r, chunk, &sh) != LA_OK) return 0;
+  return la::backward_workspace_bytes(sh.BH, sh.n_span, N, sh.r, sh.dv);
+}
+
+la_status la_backward_config(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk,
+                             int* n_span) {
+  Shape sh;
+  const la_status st = backward_shape(B, H, N, d, d_v, io_dtype, phi, r, chunk, &sh);
+  if (st != LA_OK) return st;
+  if (n_span) *n_span = sh.n_span;
+  return LA_OK;
+}
+
+la_status la_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO, void* dQ, void* dK,
+                      void* dV, int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(Q, K, V, O, dO, dQ, dK, dV, B, H, N, d, d_v, io_dtype, phi, r, chunk, workspace,
+                       workspace_bytes, stream, nullptr);
+}
+
+la_status la_backward_timed(const void* Q, const void* K, const void* V, const void* O, const void* dO, void* dQ,
+                            void* dK, void* dV, int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r,
+                            int chunk, void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  return backward_impl(Q, K, V, O, dO, dQ, dK, dV, B, H, N, d, d_v, io_dtype, phi, r, chunk, workspace,
+                       workspace_bytes, stream, events);
+}
+
 la_status la_feature_map(const void* X, float* Y, long long rows, int d, int io_dtype, int phi, int r,
                          const float* omega, void* stream) {
   if (rows < 0 || d <= 0 || r < 0 || d > kMaxDim) return LA_ERR_SHAPE;

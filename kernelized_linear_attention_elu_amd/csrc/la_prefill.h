@@ -82,6 +82,31 @@ hipError_t scan_launch(float* ws, int BH, int R, int DV, int n_span, const float
                        float* S_out, float* z_out, hipStream_t stream, const float* gamma = nullptr, int H = 1,
                        int N = 0, int chunk = 64, const float* totals = nullptr, int per_channel = 0);
 
+// Gradients of the causal normalised output (la_prefill.hip).
+struct BackwardArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  void* dQ;
+  void* dK;
+  void* dV;
+  int B, H, N, d, dv, r;
+  int io, phi, chunk, n_span;
+  void* workspace;
+  void* stream;
+  void* const* events;  // optional: 10 hipEvent_t around the five kernels
+};
+// Workspace: forward span states, reverse span sums (both [B*H][n_span+1]
+// [r*d_v + r] fp32), then (D_i, h_i) per token ([B*H][N][2] fp32).
+inline size_t backward_workspace_bytes(long long BH, int n_span, int N, int r, int dv) {
+  const size_t E = (size_t)r * dv + r;
+  return (2 * (size_t)BH * ((size_t)n_span + 1) * E + (size_t)BH * N * 2) * sizeof(float);
+}
+bool backward_supported(int io, int phi, int d, int dv, int r, int chunk);
+hipError_t backward_launch(const BackwardArgs& a);
+
 struct DecodeArgs {
   const float* S;
   const float* z;

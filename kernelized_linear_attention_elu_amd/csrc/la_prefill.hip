@@ -471,6 +471,24 @@ struct QRegs {
       }
     }
   }
+  // the rows as loaded, in fragment layout (no phi; bf16 rows only)
+  __device__ __forceinline__ void to_raw(bf16x8 (&fr)[CF::RBW][CF::R / CF::KS], OP* scr, int g, int li) const {
+    static_assert(kRows, "raw fragments of bf16 rows");
+    using TS = Tile<OP, CF::D>;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int rbi = 0; rbi < CF::RBW; ++rbi)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int qi = v * 64 + lane;
+        *reinterpret_cast<u32x4*>(scr + TS::off(16 * rbi + qi / UPR, 8 * (qi % UPR))) = raw[rbi][v];
+      }
+#pragma unroll
+    for (int rbi = 0; rbi < CF::RBW; ++rbi)
+#pragma unroll
+      for (int ks = 0; ks < NV; ++ks)
+        fr[rbi][ks] = *reinterpret_cast<const bf16x8*>(scr + TS::off(16 * rbi + li, 32 * ks + 8 * g));
+  }
   // apply phi in fp32 and round to the operand type (scr: this wave's LDS
   // scratch of RBW x 16 rows, used when kRows)
   __device__ __forceinline__ void to_frags(frag (&qf)[CF::RBW][CF::R / CF::KS], OP* scr, int g, int li) const {
@@ -1770,6 +1788,474 @@ __global__ __launch_bounds__(CF::NT, CF::MINB_DECAY) void la_output_kernel_gla(
   } while (t0 < t_end);
 }
 
+
+// ------------------------------------------------------------------ backward
+
+// Gradients of the causal, normalised output (no initial state) for an
+// upstream gradient dO.  With A_ij = phi(q_i).phi(k_j) (j <= i), D_i =
+// sum_j A_ij, O_i = sum_j A_ij v_j / D_i, g_i = dO_i / D_i and h_i =
+// -(dO_i . O_i) / D_i:
+//   dphi(q_i) = sum_{j<=i} (v_j.g_i + h_i) phi(k_j) = S_i g_i + h_i z_i
+//   dphi(k_j) = sum_{i>=j} (v_j.g_i + h_i) phi(q_i) = R_j v_j + u_j
+//   dv_j      = sum_{i>=j} A_ij g_i                  = R_j^T phi(k_j)
+// with the prefix state S_i, z_i of the forward and the suffix state
+// R_j = sum_{i>=j} phi(q_i) g_i^T, u_j = sum_{i>=j} phi(q_i) h_i; then
+// dq = dphi(q) * phi'(q), and phi' = min(1, phi) for ELU+1 (1 for x > 0,
+// e^x = phi(x) otherwise), 1 for the identity.  Chunkwise like the forward:
+//   pass A (la_bwd_dq_kernel), spans walked forward from the forward's span
+//     prefix: per chunk the masked weights give D_i (as the forward does),
+//     then g, h, W_ij = v_j.g_i + h_i (MFMA, masked) and dphi(q) = W phi(K)
+//     + S g + h z; D_i and h_i go to the workspace, and the span's own
+//     reverse sums dR = phi(Q)^T G, du = sum phi(q) h to a second set of
+//     span slots;
+//   a reverse scan of those slots gives each span the suffix (R, u) of the
+//     later spans;
+//   pass B (la_bwd_dkv_kernel), spans walked backward: per chunk
+//     A^T, W^T (MFMA, masked i >= j), dv = A^T G + R^T phi(K), dphi(k) =
+//     W^T phi(Q) + R v + u, then R += phi(Q)^T G, u += sum phi(q) h.
+// Arithmetic as in the forward: bf16 operands (phi, V, g, the weights), fp32
+// accumulation and states.
+
+// phi'(x) from phi(x) for the pointwise maps.
+template <int PHI>
+__device__ __forceinline__ float phi_deriv_from_phi(float p) {
+  if constexpr (PHI == PHI_ELU1) return fminf(p, 1.f);
+  return 1.f;
+}
+
+// acc += X^T Y over the chunk's tokens, as state_mfma but with the tiles
+// named (sx: the row operand, [C][R] phi(Q) or phi(K); sy: [C][DV] G or V),
+// and the z-like row weighted per token by sw[token] (fp32, or all ones
+// when sw is null).
+template <class CF>
+__device__ __forceinline__ void state_mfma_w(f32x4 (&acc)[CF::TPW], f32x4 (&zt)[CF::ZPW], const bf16* sx,
+                                             const bf16* sy, const float* sw, int w, int g, int li) {
+  constexpr int R = CF::R, DV = CF::DV;
+  static_assert(CF::C >= 32, "k-steps of 32 tokens");
+  const bf16 one = static_cast<bf16>(1.0f);
+#pragma unroll
+  for (int ks = 0; ks < CF::C / 32; ++ks) {
+    const int ra = ks * 32 + 8 * g;
+    const bf16x8 kh = tr_frag<R>(sx, ra, ra + 4, 16 * w, li);
+#pragma unroll
+    for (int i = 0; i < CF::TPW; ++i) {
+      const bf16x8 a = tr_frag<DV>(sy, ra, ra + 4, 16 * i, li);
+      acc[i] = mfma16(a, kh, acc[i]);
+    }
+    bf16x8 wv;
+    if (sw) {
+      // k-slots of this lane: tokens ra .. ra + 3, ra + 4 .. ra + 7
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(sw + ra);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(sw + ra + 4);
+      const float w8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      wv = cvt_bf16x8(w8);
+    } else {
+      wv = bf16x8{one, one, one, one, one, one, one, one};
+    }
+    zt[0] = mfma16(wv, kh, zt[0]);
+  }
+}
+
+template <class CF>
+struct SmemBwdA {
+  using OP = typename CF::OP;
+  OP k[Tile<OP, CF::R>::elems(CF::C)];
+  OP v[Tile<OP, CF::DV>::elems(CF::C)];
+  OP s[Tile<OP, CF::DV>::elems(CF::R)];
+  OP q[Tile<OP, CF::R>::elems(CF::C)];     // phi(Q) rows of the chunk
+  OP gt[Tile<OP, CF::DV>::elems(CF::C)];   // g rows of the chunk
+  alignas(16) float h[CF::C];
+  alignas(16) typename CF::ZT z[CF::ZE];
+  alignas(16) OP scr[Scratch<CF>::ELEMS];
+};
+
+// Pass A: dQ, and per token (D_i, h_i) -> dh[bh][N][2]; per span the reverse
+// sums -> wsb slot s.  O and dO are read in the layout of Q.
+template <class CF>
+__global__ __launch_bounds__(CF::NT, 2) void la_bwd_dq_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, const bf16* __restrict__ O,
+    const bf16* __restrict__ dO, bf16* __restrict__ dQ, const float* __restrict__ ws, float* __restrict__ wsb,
+    float* __restrict__ dh, int N, int n_span) {
+  using OP = typename CF::OP;
+  static_assert(sizeof(OP) == 2 && CF::RB == CF::NW && CF::RBW == 1 && CF::CTW == CF::CT && CF::R == CF::DV,
+                "one 16-row block per wave, d = d_v");
+  constexpr int R = CF::R, DV = CF::DV, KS = CF::KS, RB = CF::RB, FT = CF::FT;
+  using TQ = Tile<OP, R>;
+  using TV = Tile<OP, DV>;
+  __shared__ SmemBwdA<CF> sm;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
+  const int bh = blockIdx.x / n_span;
+  const int s = blockIdx.x % n_span;
+  const int t_begin = span_begin<CF>(s, n_span, N);
+  const int t_end = span_begin<CF>(s + 1, n_span, N);
+  const HeadBufs hb = head_bufs<CF>(Q, K, V, dQ, bh, N);
+  const size_t qk = (size_t)N * CF::D;
+  const __amdgpu_buffer_rsrc_t r_o = make_rsrc(O + bh * qk, (unsigned)(qk * 2));
+  const __amdgpu_buffer_rsrc_t r_do = make_rsrc(dO + bh * qk, (unsigned)(qk * 2));
+  const __amdgpu_buffer_rsrc_t r_dh = make_rsrc(dh + (size_t)bh * N * 2, (unsigned)N * 8u);
+
+  constexpr int E = R * DV + R;
+  const float* pre = ws + ((size_t)bh * (n_span + 1) + s) * E;
+  f32x4 sacc[CF::TPW], racc[CF::TPW];
+#pragma unroll
+  for (int i = 0; i < CF::TPW; ++i) {
+    int ct, ft;
+    state_tile<CF>(w, i, ct, ft);
+    sacc[i] = *reinterpret_cast<const f32x4*>(pre + (16 * ft + li) * DV + 16 * ct + 4 * g);
+    racc[i] = zero4();
+  }
+  f32x4 zt[1], ut[1];
+  {
+    const float zv = pre[R * DV + 16 * w + li];
+    zt[0] = f32x4{zv, zv, zv, zv};
+    ut[0] = zero4();
+  }
+  const bf16 one = static_cast<bf16>(1.0f), zero = static_cast<bf16>(0.0f);
+  const bf16 o1 = (li & 3) == 0 ? one : zero;
+  const bf16x8 ones_rows = bf16x8{o1, o1, o1, o1, o1, o1, o1, o1};
+  const int zrow = min(li & 3, 2);
+  const int ib = w;
+  OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
+
+  for (int t0 = t_begin; t0 < t_end; t0 += CF::C) {
+    ChunkRegs<CF, false> cr;
+    QRegs<CF> qr, orr, dor;
+    load_chunk<CF, false>(cr, hb, t0);
+    qr.load(hb.q, t0, w, g, li);
+    orr.load(r_o, t0, w, g, li);
+    dor.load(r_do, t0, w, g, li);
+    __syncthreads();  // every wave is done with the previous chunk's tiles
+    publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
+    stage_chunk<CF, false>(cr, nullptr, sm.k, nullptr, sm.v, t0, N);
+    typename QRegs<CF>::frag qf[1][R / KS];
+    qr.to_frags(qf, scr, g, li);
+    bf16x8 of[1][R / KS], df[1][R / KS];
+    orr.to_raw(of, scr, g, li);
+    dor.to_raw(df, scr, g, li);
+    // phi(q) rows of this wave's block -> the chunk's phi(Q) tile
+#pragma unroll
+    for (int ks = 0; ks < R / KS; ++ks) *reinterpret_cast<bf16x8*>(sm.q + TQ::off(16 * ib + li, 32 * ks + 8 * g)) = qf[0][ks];
+    __syncthreads();
+
+    // 1. D_i: the masked weights' row sums (bf16 weights, as the forward)
+    //    plus phi(q_i).z
+    f32x4 dacc = zero4();
+#pragma unroll
+    for (int ks = 0; ks < R / KS; ++ks) dacc = mfma16(load_frag(sm.z + zrow * R + ks * KS + g * 8), qf[0][ks], dacc);
+    auto masked = [&](f32x4 t, int jb) {
+      if (jb == ib) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = 4 * g + r > li ? 0.f : t[r];
+      }
+      return t;
+    };
+#pragma unroll
+    for (int jp = 0; jp < (RB + 1) / 2; ++jp) {
+      const int jb0 = 2 * jp, jb1 = 2 * jp + 1;
+      if (jb0 > ib) continue;
+      const bool two = jb1 < RB && jb1 <= ib;
+      f32x4 a0 = zero4(), a1 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < R / KS; ++ks) {
+        a0 = mfma16(load_frag(sm.k + TQ::off(16 * jb0 + li, ks * KS + g * 8)), qf[0][ks], a0);
+        if (two) a1 = mfma16(load_frag(sm.k + TQ::off(16 * jb1 + li, ks * KS + g * 8)), qf[0][ks], a1);
+      }
+      a0 = masked(a0, jb0);
+      a1 = two ? masked(a1, jb1) : zero4();
+      const float w8[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      dacc = mfma16(ones_rows, cvt_bf16x8(w8), dacc);
+    }
+    const float den = dacc[0] + dacc[1];
+    // rows beyond N get g = 0, h = 0 (their denominator may be zero, and
+    // their g enters the span's reverse sums)
+    const float rden = t0 + 16 * ib + li < N ? __builtin_amdgcn_rcpf(den) : 0.f;
+
+    // 2. g_i = dO_i / D_i (operand), h_i = -(dO_i . O_i) / D_i
+    bf16x8 gf[R / KS];
+    float dot = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < R / KS; ++ks) {
+      float fd[8], fo[8], fg[8];
+      unpack16<bf16>(__builtin_bit_cast(u32x4, df[0][ks]), fd);
+      unpack16<bf16>(__builtin_bit_cast(u32x4, of[0][ks]), fo);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dot += fd[e] * fo[e];
+        fg[e] = fd[e] * rden;
+      }
+      gf[ks] = cvt_bf16x8(fg);
+    }
+    const float hv = -xor_sum16_32(dot) * rden;
+    // g rows and h -> LDS for the reverse sums; (D_i, h_i) -> dh
+#pragma unroll
+    for (int ks = 0; ks < R / KS; ++ks) *reinterpret_cast<bf16x8*>(sm.gt + TV::off(16 * ib + li, 32 * ks + 8 * g)) = gf[ks];
+    if (g == 0) {
+      sm.h[16 * ib + li] = hv;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(den), __float_as_uint(hv)}, r_dh,
+                                            (t0 + 16 * ib + li) * 8, 0, 0);
+    }
+
+    // 3. W_ij = v_j.g_i + h_i (masked), and dphi(q_i) = sum_j W_ij phi(k_j)
+    f32x4 dq[FT];
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) dq[ft] = zero4();
+#pragma unroll
+    for (int jp = 0; jp < (RB + 1) / 2; ++jp) {
+      const int jb0 = 2 * jp, jb1 = 2 * jp + 1;
+      if (jb0 > ib) continue;
+      const bool two = jb1 < RB && jb1 <= ib;
+      f32x4 w0 = zero4(), w1 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DV / KS; ++ks) {
+        w0 = mfma16(load_frag(sm.v + TV::off(16 * jb0 + li, ks * KS + g * 8)), gf[ks], w0);
+        if (two) w1 = mfma16(load_frag(sm.v + TV::off(16 * jb1 + li, ks * KS + g * 8)), gf[ks], w1);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        w0[r] += hv;
+        w1[r] += hv;
+      }
+      w0 = masked(w0, jb0);
+      w1 = two ? masked(w1, jb1) : zero4();
+      const float w8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      const bf16x8 bv = cvt_bf16x8(w8);
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        const bf16x8 av = two ? tr_frag<R>(sm.k, 16 * jb0 + 4 * g, 16 * jb1 + 4 * g, 16 * ft, li)
+                              : tr_frag_lo<R>(sm.k, 16 * jb0 + 4 * g, 16 * ft, li);
+        dq[ft] = mfma16(av, bv, dq[ft]);
+      }
+    }
+    // 4. + S g_i + h_i z, then phi'(q)
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+#pragma unroll
+      for (int ks = 0; ks < DV / KS; ++ks)
+        dq[ft] = mfma16(load_frag(sm.s + TV::off(16 * ft + li, ks * KS + g * 8)), gf[ks], dq[ft]);
+      const bf16x4 fq4 = *reinterpret_cast<const bf16x4*>(sm.q + TQ::off(16 * ib + li, 16 * ft + 4 * g));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int f = 16 * ft + 4 * g + r;
+        const float zf = static_cast<float>(sm.z[f]) + static_cast<float>(sm.z[R + f]);
+        dq[ft][r] = (dq[ft][r] + hv * zf) * phi_deriv_from_phi<CF::PHI>(static_cast<float>(fq4[r]));
+      }
+    }
+    OutRegs<CF> out;
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) out.v[0][ft] = cvt_bf16x4(dq[ft]);
+    store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
+    __syncthreads();  // the chunk's phi(Q), G and h tiles are complete
+
+    // 5. reverse sums of the span and the forward carry
+    state_mfma_w<CF>(racc, ut, sm.q, sm.gt, sm.h, w, g, li);
+    state_mfma<CF>(sacc, zt, sm.k, nullptr, sm.v, w, g, li);
+  }
+
+  float* slot = wsb + ((size_t)bh * (n_span + 1) + s) * E;
+#pragma unroll
+  for (int i = 0; i < CF::TPW; ++i) {
+    int ct, ft;
+    state_tile<CF>(w, i, ct, ft);
+    *reinterpret_cast<f32x4*>(slot + (16 * ft + li) * DV + 16 * ct + 4 * g) = racc[i];
+  }
+  if (g == 0) slot[R * DV + 16 * w + li] = ut[0][0];
+}
+
+// Exclusive suffix over spans: slot s becomes the sum of the slots after it.
+__global__ __launch_bounds__(kThreads) void la_suffix_scan_kernel(float* __restrict__ ws, int E, int n_span) {
+  const int e = blockIdx.x * kThreads + threadIdx.x;
+  const int bh = blockIdx.y;
+  if (e >= E) return;
+  float* p = ws + (size_t)bh * (n_span + 1) * E + e;
+  float acc = 0.f;
+  for (int s = n_span - 1; s >= 0; --s) {
+    const float x = p[(size_t)s * E];
+    p[(size_t)s * E] = acc;
+    acc += x;
+  }
+  p[(size_t)n_span * E] = acc;
+}
+
+template <class CF>
+struct SmemBwdB {
+  using OP = typename CF::OP;
+  OP q[Tile<OP, CF::R>::elems(CF::C)];
+  OP k[Tile<OP, CF::R>::elems(CF::C)];
+  OP v[Tile<OP, CF::DV>::elems(CF::C)];
+  OP gt[Tile<OP, CF::DV>::elems(CF::C)];
+  OP rs[Tile<OP, CF::DV>::elems(CF::R)];   // the carried R, bf16
+  alignas(16) float h[CF::C];
+  alignas(16) float u[CF::R];
+  alignas(16) OP scr[Scratch<CF>::ELEMS];
+};
+
+// Pass B: dK, dV, spans walked backward from the suffix (R, u) of the
+// later spans (wsb slot s after the suffix scan).
+template <class CF>
+__global__ __launch_bounds__(CF::NT, 2) void la_bwd_dkv_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ dh, bf16* __restrict__ dK, bf16* __restrict__ dV,
+    const float* __restrict__ wsb, int N, int n_span) {
+  using OP = typename CF::OP;
+  static_assert(sizeof(OP) == 2 && CF::RB == CF::NW && CF::RBW == 1 && CF::CTW == CF::CT && CF::R == CF::DV,
+                "one 16-row block per wave, d = d_v");
+  constexpr int R = CF::R, DV = CF::DV, KS = CF::KS, RB = CF::RB, FT = CF::FT, CT = CF::CT;
+  using TQ = Tile<OP, R>;
+  using TV = Tile<OP, DV>;
+  __shared__ SmemBwdB<CF> sm;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
+  const int bh = blockIdx.x / n_span;
+  const int s = blockIdx.x % n_span;
+  const int t_begin = span_begin<CF>(s, n_span, N);
+  const int t_end = span_begin<CF>(s + 1, n_span, N);
+  const HeadBufs hb = head_bufs<CF>(Q, K, V, dK, bh, N);
+  const size_t qk = (size_t)N * CF::D;
+  const __amdgpu_buffer_rsrc_t r_do = make_rsrc(dO + bh * qk, (unsigned)(qk * 2));
+  const __amdgpu_buffer_rsrc_t r_dv = make_rsrc(dV + bh * qk, (unsigned)(qk * 2));
+  const __amdgpu_buffer_rsrc_t r_dh = make_rsrc(dh + (size_t)bh * N * 2, (unsigned)N * 8u);
+
+  constexpr int E = R * DV + R;
+  const float* suf = wsb + ((size_t)bh * (n_span + 1) + s) * E;
+  f32x4 racc[CF::TPW];
+#pragma unroll
+  for (int i = 0; i < CF::TPW; ++i) {
+    int ct, ft;
+    state_tile<CF>(w, i, ct, ft);
+    racc[i] = *reinterpret_cast<const f32x4*>(suf + (16 * ft + li) * DV + 16 * ct + 4 * g);
+  }
+  f32x4 ut[1];
+  {
+    const float uv = suf[R * DV + 16 * w + li];
+    ut[0] = f32x4{uv, uv, uv, uv};
+  }
+  const int jb = w;
+  OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
+  constexpr int VVR = DV / 8;
+  if (t_begin >= t_end) return;
+  const int last = t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C;
+
+  for (int t0 = last; t0 >= t_begin; t0 -= CF::C) {
+    ChunkRegs<CF, true> cr;
+    load_chunk<CF, true>(cr, hb, t0);
+    // dO rows (V's layout) and each row's 1 / D
+    u32x4 dov[CF::LV];
+    float rd[CF::LV];
+#pragma unroll
+    for (int i = 0; i < CF::LV; ++i) {
+      const int vi = tid + i * CF::NT;
+      const int tok = vi / VVR;
+      dov[i] = __builtin_amdgcn_raw_buffer_load_b128(r_do, ((t0 + tok) * DV + (vi % VVR) * 8) * 2, 0, 0);
+      rd[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dh, (t0 + tok) * 8, 0, 0));
+    }
+    const float hl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dh, (t0 + (tid & 63)) * 8 + 4, 0, 0));
+    __syncthreads();  // every wave is done with the previous chunk's tiles
+    // the carried R (bf16) and u
+#pragma unroll
+    for (int i = 0; i < CF::TPW; ++i) {
+      int ct, ft;
+      state_tile<CF>(w, i, ct, ft);
+      *reinterpret_cast<bf16x4*>(sm.rs + TV::off(16 * ft + li, 16 * ct + 4 * g)) = cvt_bf16x4(racc[i]);
+    }
+    if (g == 0) sm.u[16 * w + li] = ut[0][0];
+    stage_chunk<CF, true>(cr, sm.q, sm.k, nullptr, sm.v, t0, N);
+#pragma unroll
+    for (int i = 0; i < CF::LV; ++i) {
+      const int vi = tid + i * CF::NT;
+      const int tok = vi / VVR;
+      float f[8];
+      unpack16<bf16>(dov[i], f);
+      const float r = t0 + tok < N ? __builtin_amdgcn_rcpf(rd[i]) : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] *= r;
+      *reinterpret_cast<u32x4*>(sm.gt + TV::off(tok, (vi % VVR) * 8)) = pack16<bf16>(f);
+    }
+    if (w == 0 && (tid & 63) < CF::C) sm.h[tid & 63] = t0 + (tid & 63) < N ? hl : 0.f;
+    __syncthreads();
+
+    // this wave's key rows j = 16 jb + li: phi(k_j), v_j as B operands
+    bf16x8 kf[R / KS], vf[DV / KS];
+#pragma unroll
+    for (int ks = 0; ks < R / KS; ++ks) kf[ks] = load_frag(sm.k + TQ::off(16 * jb + li, ks * KS + g * 8));
+#pragma unroll
+    for (int ks = 0; ks < DV / KS; ++ks) vf[ks] = load_frag(sm.v + TV::off(16 * jb + li, ks * KS + g * 8));
+    auto masked = [&](f32x4 t, int ib) {
+      if (ib == jb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = 4 * g + r < li ? 0.f : t[r];
+      }
+      return t;
+    };
+    f32x4 dv[CT], dk[FT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) dv[c] = zero4();
+#pragma unroll
+    for (int f = 0; f < FT; ++f) dk[f] = zero4();
+    // query blocks ib >= jb, in pairs (one 32-token MFMA step)
+#pragma unroll
+    for (int ip = 0; ip < (RB + 1) / 2; ++ip) {
+      const int ib0 = 2 * ip, ib1 = 2 * ip + 1;
+      if (ib1 < jb || (ib1 >= RB && ib0 < jb)) continue;
+      const bool has0 = ib0 >= jb, has1 = ib1 < RB && ib1 >= jb;
+      f32x4 a0 = zero4(), a1 = zero4(), w0 = zero4(), w1 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < R / KS; ++ks) {
+        if (has0) a0 = mfma16(load_frag(sm.q + TQ::off(16 * ib0 + li, ks * KS + g * 8)), kf[ks], a0);
+        if (has1) a1 = mfma16(load_frag(sm.q + TQ::off(16 * ib1 + li, ks * KS + g * 8)), kf[ks], a1);
+      }
+#pragma unroll
+      for (int ks = 0; ks < DV / KS; ++ks) {
+        if (has0) w0 = mfma16(load_frag(sm.gt + TV::off(16 * ib0 + li, ks * KS + g * 8)), vf[ks], w0);
+        if (has1) w1 = mfma16(load_frag(sm.gt + TV::off(16 * ib1 + li, ks * KS + g * 8)), vf[ks], w1);
+      }
+      // lane (g, li): entry [i = 16 ib + 4 g + r][j = 16 jb + li]; W^T adds h_i
+      const f32x4 h0 = *reinterpret_cast<const f32x4*>(sm.h + 16 * ib0 + 4 * g);
+      const f32x4 h1 = has1 ? *reinterpret_cast<const f32x4*>(sm.h + 16 * ib1 + 4 * g) : zero4();
+      w0 += h0;
+      w1 += h1;
+      a0 = has0 ? masked(a0, ib0) : zero4();
+      a1 = has1 ? masked(a1, ib1) : zero4();
+      w0 = has0 ? masked(w0, ib0) : zero4();
+      w1 = has1 ? masked(w1, ib1) : zero4();
+      const float a8[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      const float w8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      const bf16x8 ab = cvt_bf16x8(a8), wb = cvt_bf16x8(w8);
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+        dv[c] = mfma16(tr_frag<DV>(sm.gt, 16 * ib0 + 4 * g, 16 * ib1 + 4 * g, 16 * c, li), ab, dv[c]);
+#pragma unroll
+      for (int f = 0; f < FT; ++f)
+        dk[f] = mfma16(tr_frag<R>(sm.q, 16 * ib0 + 4 * g, 16 * ib1 + 4 * g, 16 * f, li), wb, dk[f]);
+    }
+    // + the later chunks: dv_j += R^T phi(k_j), dphi(k_j) += R v_j + u
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int ks = 0; ks < R / KS; ++ks)
+        dv[c] = mfma16(tr_frag<DV>(sm.rs, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, 16 * c, li), kf[ks], dv[c]);
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+#pragma unroll
+      for (int ks = 0; ks < DV / KS; ++ks)
+        dk[f] = mfma16(load_frag(sm.rs + TV::off(16 * f + li, ks * KS + g * 8)), vf[ks], dk[f]);
+      const f32x4 uf = *reinterpret_cast<const f32x4*>(sm.u + 16 * f + 4 * g);
+      const bf16x4 fk4 = *reinterpret_cast<const bf16x4*>(sm.k + TQ::off(16 * jb + li, 16 * f + 4 * g));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dk[f][r] = (dk[f][r] + uf[r]) * phi_deriv_from_phi<CF::PHI>(static_cast<float>(fk4[r]));
+    }
+    OutRegs<CF> ok, ov;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      ov.v[0][c] = cvt_bf16x4(dv[c]);
+      ok.v[0][c] = cvt_bf16x4(dk[c]);
+    }
+    store_outputs<CF>(ok, hb.o, t0, w, g, li, false, scr);
+    store_outputs<CF>(ov, r_dv, t0, w, g, li, false, scr);
+    // the carry toward earlier chunks
+    state_mfma_w<CF>(racc, ut, sm.q, sm.gt, sm.h, w, g, li);
+  }
+}
+
 // ------------------------------------------------------------------ single pass
 
 // One kernel per causal prefill: each workgroup takes one span of
@@ -2163,6 +2649,56 @@ bool prefill_supported(int io, int phi, int d, int dv, int r, int chunk) {
   }
   if (io == 0) return d == 64 && chunk <= 64;  // fp32
   return false;
+}
+
+template <class CF>
+static hipError_t launch_backward(const BackwardArgs& a) {
+  const int BH = a.B * a.H, n_span = a.n_span;
+  hipStream_t st = static_cast<hipStream_t>(a.stream);
+  constexpr int E = CF::R * CF::DV + CF::R;
+  float* wsf = static_cast<float*>(a.workspace);
+  float* wsb = wsf + (size_t)BH * (n_span + 1) * E;
+  float* dh = wsb + (size_t)BH * (n_span + 1) * E;
+  const bf16* Q = static_cast<const bf16*>(a.Q);
+  const bf16* K = static_cast<const bf16*>(a.K);
+  const bf16* V = static_cast<const bf16*>(a.V);
+  (void)hipGetLastError();
+  auto rec = [&](int i) {
+    if (a.events && a.events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a.events[i]), st);
+  };
+  const dim3 grid(BH * n_span), block(CF::NT);
+  rec(0);
+  hipLaunchKernelGGL((la_state_kernel<CF, kNoDecay>), grid, block, 0, st, K, V, wsf, a.N, n_span, nullptr, 1, nullptr,
+                     nullptr);
+  rec(1);
+  rec(2);
+  hipError_t e = scan_launch(wsf, BH, CF::R, CF::DV, n_span, nullptr, nullptr, nullptr, nullptr, st);
+  if (e != hipSuccess) return e;
+  rec(3);
+  rec(4);
+  hipLaunchKernelGGL((la_bwd_dq_kernel<CF>), grid, block, 0, st, Q, K, V, static_cast<const bf16*>(a.O),
+                     static_cast<const bf16*>(a.dO), static_cast<bf16*>(a.dQ), wsf, wsb, dh, a.N, n_span);
+  rec(5);
+  rec(6);
+  hipLaunchKernelGGL(la_suffix_scan_kernel, dim3((E + kThreads - 1) / kThreads, BH), dim3(kThreads), 0, st, wsb, E,
+                     n_span);
+  rec(7);
+  rec(8);
+  hipLaunchKernelGGL((la_bwd_dkv_kernel<CF>), grid, block, 0, st, Q, K, V, static_cast<const bf16*>(a.dO), dh,
+                     static_cast<bf16*>(a.dK), static_cast<bf16*>(a.dV), wsb, a.N, n_span);
+  rec(9);
+  return hipGetLastError();
+}
+
+bool backward_supported(int io, int phi, int d, int dv, int r, int chunk) {
+  return io == 1 && (phi == PHI_ELU1 || phi == PHI_IDENTITY) && d == 64 && dv == 64 && r == 64 && chunk == 64;
+}
+
+hipError_t backward_launch(const BackwardArgs& a) {
+  if (!backward_supported(a.io, a.phi, a.d, a.dv, a.r, a.chunk)) return hipErrorInvalidValue;
+  if (a.B * a.H == 0 || a.N == 0) return hipSuccess;
+  return a.phi == PHI_ELU1 ? launch_backward<Cfg<bf16, 64, 64, 64, 64, PHI_ELU1>>(a)
+                           : launch_backward<Cfg<bf16, 64, 64, 64, 64, PHI_IDENTITY>>(a);
 }
 
 bool gla_supported(int io, int d, int dv, int r, int chunk) {

@@ -33,7 +33,7 @@ import numpy as np
 
 from oracle.linear_attention import feature_map
 
-__all__ = ["phi_prime", "grad_causal"]
+__all__ = ["phi_prime", "grad_causal", "grad_rows"]
 
 
 def phi_prime(phi, x):
@@ -67,3 +67,53 @@ def grad_causal(q, k, v, dO, phi="elu1"):
     dfk = np.swapaxes(dA, -1, -2) @ fq
     dv = np.swapaxes(A / D[..., None], -1, -2) @ dO
     return dfq * phi_prime(phi, q), dfk * phi_prime(phi, k), dv
+
+
+def grad_rows(q, k, v, dO, rows, phi="elu1"):
+    """The same gradients at selected token rows, for long sequences: one
+    forward token loop (prefix sums S_t, z_t of the recurrence, then D_t,
+    O_t, g_t = dO_t / D_t, h_t = -(dO_t . O_t) / D_t) and one reverse loop
+    (suffix sums R_t = sum_{i>=t} phi(q_i) g_i^T, u_t = sum_{i>=t} phi(q_i)
+    h_i), from which
+        dphi(q_t) = S_t g_t + h_t z_t,  dphi(k_t) = R_t v_t + u_t,
+        dv_t = R_t^T phi(k_t),
+    i.e. the sums of grad_causal regrouped by the associativity the
+    recurrent form rests on.  Vectorised over the leading dimensions; returns
+    (dQ, dK, dV) at ``rows`` ([..., len(rows), d] etc.).  Pinned against
+    grad_causal in tests/test_oracle_backward_pins.py."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    fq = feature_map(phi, q)
+    fk = feature_map(phi, k)
+    lead = fq.shape[:-2]
+    n, r = fq.shape[-2], fq.shape[-1]
+    dv_ = v.shape[-1]
+    want = {t: i for i, t in enumerate(rows)}
+    gq = np.empty(lead + (len(rows), r))
+    gk = np.empty(lead + (len(rows), r))
+    gv = np.empty(lead + (len(rows), dv_))
+    g = np.empty(lead + (n, dv_))
+    h = np.empty(lead + (n,))
+    S = np.zeros(lead + (r, dv_))
+    z = np.zeros(lead + (r,))
+    for t in range(n):
+        S = S + fk[..., t, :, None] * v[..., t, None, :]
+        z = z + fk[..., t, :]
+        D = np.einsum("...r,...r->...", fq[..., t, :], z)
+        O = np.einsum("...r,...rc->...c", fq[..., t, :], S) / D[..., None]
+        g[..., t, :] = dO[..., t, :] / D[..., None]
+        h[..., t] = -np.einsum("...c,...c->...", dO[..., t, :], O) / D
+        if t in want:
+            gq[..., want[t], :] = np.einsum("...rc,...c->...r", S, g[..., t, :]) + h[..., t, None] * z
+    R = np.zeros(lead + (r, dv_))
+    u = np.zeros(lead + (r,))
+    for t in range(n - 1, -1, -1):
+        R = R + fq[..., t, :, None] * g[..., t, None, :]
+        u = u + fq[..., t, :] * h[..., t, None]
+        if t in want:
+            gk[..., want[t], :] = np.einsum("...rc,...c->...r", R, v[..., t, :]) + u
+            gv[..., want[t], :] = np.einsum("...rc,...r->...c", R, fk[..., t, :])
+    sel = list(rows)
+    return gq * phi_prime(phi, q[..., sel, :]), gk * phi_prime(phi, k[..., sel, :]), gv

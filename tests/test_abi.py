@@ -257,6 +257,30 @@ def test_gla_argument_errors(lib):
     assert dg(B=0, S=None) == 0
 
 
+def test_backward_argument_errors(lib):
+    """la_backward and its queries: every case returns before any HIP call."""
+    def fb(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, dQ=FAKE, dK=FAKE, dV=FAKE, B=1, H=1, N=64, d=64, dv=64, io=1,
+           phi=0, r=0, chunk=64, ws=FAKE, ws_bytes=1 << 30):
+        return lib.la_backward(Q, K, V, O, dO, dQ, dK, dV, B, H, N, d, dv, io, phi, r, chunk, ws, ws_bytes, None)
+    assert fb(dO=None) == 1                              # LA_ERR_NULL
+    assert fb(dV=None) == 1
+    assert fb(N=-1) == 2                                 # LA_ERR_SHAPE
+    assert fb(io=0) == 3                                 # bf16 only
+    assert fb(d=128, dv=128) == 3
+    assert fb(chunk=32) == 3
+    assert fb(phi=1, r=256) == 3
+    assert fb(O=MISALIGNED) == 4                         # LA_ERR_ALIGN
+    assert fb(ws=None) == 5                              # LA_ERR_WORKSPACE
+    assert fb(Q=None, K=None, V=None, O=None, dO=None, dQ=None, dK=None, dV=None, N=0, ws=None) == 0
+    B, H, N = 1, 32, 32768
+    n = ctypes.c_int()
+    assert lib.la_backward_config(B, H, N, 64, 64, 1, 0, 0, 0, ctypes.byref(n)) == 0 and n.value == 16
+    need = lib.la_backward_workspace_bytes(B, H, N, 64, 64, 1, 0, 0, 64)
+    assert need == (2 * B * H * (n.value + 1) * (64 * 64 + 64) + B * H * N * 2) * 4
+    assert fb(B=B, H=H, N=N, ws_bytes=need - 4) == 5
+    assert lib.la_backward_workspace_bytes(B, H, N, 64, 64, 0, 0, 0, 64) == 0
+
+
 def test_feature_map_argument_errors(lib):
     def fm(X=FAKE, Y=FAKE, rows=10, d=64, io=1, phi=0, r=0, omega=None):
         return lib.la_feature_map(X, Y, rows, d, io, phi, r, omega, None)

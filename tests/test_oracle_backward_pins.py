@@ -10,7 +10,9 @@ gradients independently of its code:
   dQ = dK = 0; with dO = 1 everywhere, dV_j is the column sum of the
   normalised causal attention, sum_{i>=j} A_ij / D_i; for one token,
   dV = dO and dQ = dK = 0;
-* the identity map's gradient is the ELU+1 one with phi' = 1.
+* the identity map's gradient is the ELU+1 one with phi' = 1;
+* the sampled-row form (prefix and suffix states, for long sequences)
+  equals the explicit form at every sampled row.
 
 Planted mistakes (the rowsum(dO*O) term dropped, the mask transposed, phi'
 left out, dV from the unnormalised weights) each fail a pin
@@ -107,6 +109,20 @@ def test_identity_is_elu_path_with_unit_derivative():
     g_id = bwd.grad_causal(q + 1.0, k + 1.0, v, dO, phi="identity")
     for a, b in zip(g_elu, g_id):
         np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("phi", ["elu1", "identity"])
+def test_sampled_rows_equal_the_explicit_form(phi):
+    shape_qk, shape_v = (2, 2, 45, 5), (2, 2, 45, 3)
+    q, k, v = _rand(shape_qk, 19, 0.6), _rand(shape_qk, 20, 0.6), _rand(shape_v, 21)
+    if phi == "identity":
+        q, k = np.abs(q) + 0.1, np.abs(k) + 0.1
+    dO = _rand(shape_v, 22)
+    full = bwd.grad_causal(q, k, v, dO, phi=phi)
+    rows = [0, 1, 17, 30, 44]
+    part = bwd.grad_rows(q, k, v, dO, rows, phi=phi)
+    for a, b in zip(part, full):
+        np.testing.assert_allclose(a, b[..., rows, :], rtol=1e-11, atol=1e-12)
 
 
 def _mutant(kind):
