@@ -48,6 +48,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 KERNEL_NAMES = ("la_state_kernel", "la_scan_kernel", "la_output_kernel")
 FAVOR_KERNEL_NAMES = ("la_state_favor_kernel", "la_scan_kernel", "la_output_favor_kernel")
 FUSED_KERNEL_NAMES = ("la_fused_reset_kernel", None, "la_fused_kernel")
+GLA_KERNEL_NAMES = ("la_state_kernel_gla", "la_scan_kernel", "la_output_kernel_gla")
 BACKWARD_KERNEL_NAMES = ("la_state_kernel", "la_scan_kernel", "la_bwd_dq_kernel", "la_suffix_scan_kernel",
                          "la_bwd_dkv_kernel")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -259,9 +260,13 @@ def bench_prefill(args, torch, la, synth):
     n_span, single_pass = la.forward_config(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
                                             chunk=w.chunk, decay=gamma is not None, gated=log_a is not None,
                                             gla=log_a_ch is not None)
-    names = (FAVOR_KERNEL_NAMES if w.phi == "favor" else FUSED_KERNEL_NAMES if single_pass else KERNEL_NAMES)
+    names = (FAVOR_KERNEL_NAMES if w.phi == "favor" else FUSED_KERNEL_NAMES if single_pass
+             else GLA_KERNEL_NAMES if log_a_ch is not None else KERNEL_NAMES)
     out_kernel = names[2]
-    traffic = read_traffic(args.workload + ("" if causal else "_noncausal"), out_kernel)
+    # the decayed and gated variants of la_output_kernel are other kernels:
+    # their counter figures are kept under their own workload tag
+    mode = "_decay" if gamma is not None else "_gated" if log_a is not None else ""
+    traffic = read_traffic(args.workload + ("" if causal else "_noncausal") + mode, out_kernel)
     if w.phi == "favor":
         # the output kernel's own work: phi(Q) and phi(K) projections, the
         # read-out and the state carry (2 r dv each), the intra-chunk products
@@ -417,7 +422,8 @@ def bench_backward(args, torch, la, synth):
             "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv, "chunk": 64, "phi": w.phi, "backward": True,
         },
         "roofline": {"kernel": "la_bwd_dkv_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": read_traffic(args.workload + "_backward", "la_bwd_dkv_kernel")},
         "path_roofline": {"bound": "hbm", "alg_bytes": step_bytes,
                           "achieved_gbs": step_bytes / (ms * 1e-3) / 1e9,
                           "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},

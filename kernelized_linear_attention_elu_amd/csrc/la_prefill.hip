@@ -1917,13 +1917,15 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dq_kernel(
   const int ib = w;
   OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
 
+  // chunk c+1 is loaded into registers while chunk c is computed
+  const int last = t_end > t_begin ? t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C : t_begin;
+  ChunkRegs<CF, false> cr;
+  QRegs<CF> qr, orr, dor;
+  load_chunk<CF, false>(cr, hb, t_begin);
+  qr.load(hb.q, t_begin, w, g, li);
+  orr.load(r_o, t_begin, w, g, li);
+  dor.load(r_do, t_begin, w, g, li);
   for (int t0 = t_begin; t0 < t_end; t0 += CF::C) {
-    ChunkRegs<CF, false> cr;
-    QRegs<CF> qr, orr, dor;
-    load_chunk<CF, false>(cr, hb, t0);
-    qr.load(hb.q, t0, w, g, li);
-    orr.load(r_o, t0, w, g, li);
-    dor.load(r_do, t0, w, g, li);
     __syncthreads();  // every wave is done with the previous chunk's tiles
     publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
     stage_chunk<CF, false>(cr, nullptr, sm.k, nullptr, sm.v, t0, N);
@@ -1935,6 +1937,13 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dq_kernel(
     // phi(q) rows of this wave's block -> the chunk's phi(Q) tile
 #pragma unroll
     for (int ks = 0; ks < R / KS; ++ks) *reinterpret_cast<bf16x8*>(sm.q + TQ::off(16 * ib + li, 32 * ks + 8 * g)) = qf[0][ks];
+    {
+      const int tn = min(t0 + CF::C, last);  // (past the span's last chunk: re-read, unused)
+      load_chunk<CF, false>(cr, hb, tn);
+      qr.load(hb.q, tn, w, g, li);
+      orr.load(r_o, tn, w, g, li);
+      dor.load(r_do, tn, w, g, li);
+    }
     __syncthreads();
 
     // 1. D_i: the masked weights' row sums (bf16 weights, as the forward)
@@ -2135,20 +2144,25 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dkv_kernel(
   if (t_begin >= t_end) return;
   const int last = t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C;
 
-  for (int t0 = last; t0 >= t_begin; t0 -= CF::C) {
-    ChunkRegs<CF, true> cr;
-    load_chunk<CF, true>(cr, hb, t0);
-    // dO rows (V's layout) and each row's 1 / D
-    u32x4 dov[CF::LV];
-    float rd[CF::LV];
+  // chunk c-1 is loaded into registers while chunk c is computed: Q, K, V,
+  // the dO rows (V's layout), each row's D and the chunk's h
+  ChunkRegs<CF, true> cr;
+  u32x4 dov[CF::LV];
+  float rd[CF::LV];
+  float hl;
+  auto load_all = [&](int tc) {
+    load_chunk<CF, true>(cr, hb, tc);
 #pragma unroll
     for (int i = 0; i < CF::LV; ++i) {
       const int vi = tid + i * CF::NT;
       const int tok = vi / VVR;
-      dov[i] = __builtin_amdgcn_raw_buffer_load_b128(r_do, ((t0 + tok) * DV + (vi % VVR) * 8) * 2, 0, 0);
-      rd[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dh, (t0 + tok) * 8, 0, 0));
+      dov[i] = __builtin_amdgcn_raw_buffer_load_b128(r_do, ((tc + tok) * DV + (vi % VVR) * 8) * 2, 0, 0);
+      rd[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dh, (tc + tok) * 8, 0, 0));
     }
-    const float hl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dh, (t0 + (tid & 63)) * 8 + 4, 0, 0));
+    hl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dh, (tc + (tid & 63)) * 8 + 4, 0, 0));
+  };
+  load_all(last);
+  for (int t0 = last; t0 >= t_begin; t0 -= CF::C) {
     __syncthreads();  // every wave is done with the previous chunk's tiles
     // the carried R (bf16) and u
 #pragma unroll
@@ -2171,6 +2185,7 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dkv_kernel(
       *reinterpret_cast<u32x4*>(sm.gt + TV::off(tok, (vi % VVR) * 8)) = pack16<bf16>(f);
     }
     if (w == 0 && (tid & 63) < CF::C) sm.h[tid & 63] = t0 + (tid & 63) < N ? hl : 0.f;
+    load_all(max(t0 - CF::C, t_begin));  // (before the span's first chunk: re-read, unused)
     __syncthreads();
 
     // this wave's key rows j = 16 jb + li: phi(k_j), v_j as B operands
