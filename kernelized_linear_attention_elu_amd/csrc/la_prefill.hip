@@ -2078,10 +2078,19 @@ __global__ __launch_bounds__(kThreads) void la_suffix_scan_kernel(float* __restr
   if (e >= E) return;
   float* p = ws + (size_t)bh * (n_span + 1) * E + e;
   float acc = 0.f;
-  for (int s = n_span - 1; s >= 0; --s) {
-    const float x = p[(size_t)s * E];
-    p[(size_t)s * E] = acc;
-    acc += x;
+  // a batch's loads are issued before its dependent adds (as la_scan_kernel)
+  constexpr int kBatch = 16;
+  for (int s1 = n_span; s1 > 0; s1 -= kBatch) {   // spans s1 - kBatch .. s1 - 1, from the top
+    float x[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) x[j] = s1 - 1 - j >= 0 ? p[(size_t)(s1 - 1 - j) * E] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (s1 - 1 - j >= 0) {
+        p[(size_t)(s1 - 1 - j) * E] = acc;
+        acc += x[j];
+      }
+    }
   }
   p[(size_t)n_span * E] = acc;
 }
