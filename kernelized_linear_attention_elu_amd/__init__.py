@@ -219,16 +219,16 @@ def _gamma_arg(gamma, H, dev, causal=True):
     return gamma
 
 
-def _log_gate_arg(log_gate, shape, dev, causal=True):
+def _log_gate_arg(log_gate, shape, dev, causal=True, name="log_gate"):
     """Per-token gates: a fp32 device tensor of natural-log gates (or None)."""
     if log_gate is None:
         return None
     torch = _torch()
     if not causal:
         raise ValueError("the gates are defined for the causal form only")
-    _require(log_gate, "log_gate", torch.float32, dev)
+    _require(log_gate, name, torch.float32, dev)
     if tuple(log_gate.shape) != tuple(shape):
-        raise ValueError(f"log_gate must have shape {tuple(shape)}, got {tuple(log_gate.shape)}")
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(log_gate.shape)}")
     return log_gate
 
 
@@ -280,7 +280,7 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
         z_out = torch.empty((B, H, r), dtype=torch.float32, device=dev)
     gamma = _gamma_arg(gamma, H, dev, causal)
     log_gate = _log_gate_arg(log_gate, (B, H, N), dev, causal)
-    log_gate_ch = _log_gate_arg(log_gate_ch, (B, H, N, r), dev, causal)
+    log_gate_ch = _log_gate_arg(log_gate_ch, (B, H, N, r), dev, causal, name="log_gate_ch")
     n_decay = sum(x is not None for x in (gamma, log_gate, log_gate_ch))
     if n_decay > 1:
         raise ValueError("give at most one of gamma, log_gate, log_gate_ch")
@@ -394,7 +394,7 @@ def decode_step(S, z, q, k, v, *, phi="elu1", omega=None, inplace=True, out=None
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, dv)}")
     gamma = _gamma_arg(gamma, H, dev)
     log_gate = _log_gate_arg(log_gate, (B, H), dev)
-    log_gate_ch = _log_gate_arg(log_gate_ch, (B, H, r), dev)
+    log_gate_ch = _log_gate_arg(log_gate_ch, (B, H, r), dev, name="log_gate_ch")
     n_decay = sum(x is not None for x in (gamma, log_gate, log_gate_ch))
     if n_decay > 1:
         raise ValueError("give at most one of gamma, log_gate, log_gate_ch")
