@@ -216,3 +216,19 @@ def test_decay_long_workload_sampled(lib):
         z_ref[0, h] = fk.sum(axis=0)
     check_close(S, S_ref, "bf16", "S_N")
     check_close(z, z_ref, "bf16", "z_N")
+
+
+def test_decay_wide_workload_sampled(lib):
+    """The wide workload (B2 H16 N65536 d128 bf16) with the per-head decays of
+    synth.decay_gammas, in the bench's launch configuration: sampled rows of
+    every (batch, head) from the definition."""
+    w = synth.WORKLOADS["wide"]
+    q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
+    g = synth.decay_gammas(w.H)
+    O = to_host(_run(lib, q, k, v, g))
+    rng = np.random.default_rng(39)
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = sorted({0, 63, 64, 8191, 8192, w.N - 1, int(rng.integers(0, w.N))})   # 8192-token spans
+            ref = dec.causal_rows_decay(q[b, h], k[b, h], v[b, h], rows, float(g[h]))
+            check_close(O[b, h, rows], ref, "bf16", f"b{b} h{h}")

@@ -269,3 +269,20 @@ def test_gated_long_workload_sampled(lib):
         z_ref[0, h] = fk.sum(axis=0)
     check_close(S, S_ref, "bf16", "S_N")
     check_close(z, z_ref, "bf16", "z_N")
+
+
+def test_gated_wide_workload_sampled(lib):
+    """The wide workload (B2 H16 N65536 d128 bf16) with the seeded per-token
+    gates, in the bench's launch configuration: sampled rows of every
+    (batch, head) from the definition."""
+    w = synth.WORKLOADS["wide"]
+    q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
+    log_a = synth.draw_log_gates(w.B, w.H, w.N)
+    O = to_host(_run(lib, q, k, v, log_a))
+    a = _gates(log_a)
+    rng = np.random.default_rng(56)
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = sorted({0, 63, 64, 8191, 8192, w.N - 1, int(rng.integers(0, w.N))})   # 8192-token spans
+            ref = gat.causal_rows_gated(q[b, h], k[b, h], v[b, h], a[b, h], rows)
+            check_close(O[b, h, rows], ref, "bf16", f"b{b} h{h}")

@@ -270,3 +270,20 @@ def test_gla_long_workload_sampled(lib):
         z_ref[0, h] = fk.sum(axis=0)
     check_close(S, S_ref, "bf16", "S_N")
     check_close(z, z_ref, "bf16", "z_N")
+
+
+def test_gla_wide_workload_sampled(lib):
+    """The wide workload (B2 H16 N65536 d128 bf16) with the seeded GLA gates,
+    in the bench's launch configuration (chunk 32 at d = 128): sampled rows of
+    every (batch, head) from the definition."""
+    w = synth.WORKLOADS["wide"]
+    q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
+    log_a = synth.draw_log_gates_ch(w.B, w.H, w.N, w.d)
+    O = to_host(_run(lib, q, k, v, log_a, chunk=32))
+    rng = np.random.default_rng(78)
+    for b in range(w.B):
+        for h in range(w.H):
+            al = _gates(log_a[b, h])
+            rows = sorted({0, 31, 32, 8191, 8192, w.N - 1, int(rng.integers(0, w.N))})   # 8192-token spans
+            ref = gla.causal_rows_gla(q[b, h], k[b, h], v[b, h], al, rows)
+            check_close(O[b, h, rows], ref, "bf16", f"b{b} h{h}")
