@@ -61,7 +61,7 @@
  *       la_decode_step: d = d_v in {64, 128}; FAVOR+ with r = 256.
  *       la_decode_step_decay: d = d_v in {64, 128}, ELU1/IDENTITY.
  *       la_forward_gated, la_decode_step_gated: as the decay calls.
- *       la_backward: bf16, ELU1/IDENTITY, d = d_v = 64, chunk 64 (0 means 64).
+ *       la_backward: bf16, ELU1/IDENTITY, d = d_v in {64, 128}, chunk 64 (0 means 64).
  *       la_forward_gla: ELU1/IDENTITY, d = d_v = 64 (bf16: chunk 16..128;
  *       fp32: 16..64) or d = d_v = 128 (bf16, chunk 16 or 32; chunk = 0
  *       means 32 there); la_decode_step_gla: as the decay decode.
@@ -361,8 +361,8 @@ la_status la_decode_step_gla(const float *S, const float *z, const void *q, cons
  *   dQ, dK, dV     out: device bf16, the shapes of Q, K, V; may not alias the
  *                  inputs.
  *   workspace      device scratch of at least la_backward_workspace_bytes(...).
- * Supported: bf16, ELU1/IDENTITY, d = d_v = 64, chunk 64 (0 means 64); others
- * return LA_ERR_UNSUPPORTED.
+ * Supported: bf16, ELU1/IDENTITY, d = d_v in {64, 128}, chunk 64 (0 means 64);
+ * others return LA_ERR_UNSUPPORTED.
  * Errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_UNSUPPORTED, LA_ERR_ALIGN,
  * LA_ERR_WORKSPACE (nothing enqueued), LA_ERR_HIP.
  */

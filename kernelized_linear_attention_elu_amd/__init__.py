@@ -326,7 +326,7 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
 
 def backward(Q, K, V, O, dO, *, phi="elu1", chunk=64, out=None, workspace=None, events=None):
     """Gradients (dQ, dK, dV) of sum(dO * O) for the causal normalised output
-    O = forward(Q, K, V, phi=phi) (la_backward; bf16, d = d_v = 64).  ``out``:
+    O = forward(Q, K, V, phi=phi) (la_backward; bf16, d = d_v in {64, 128}).  ``out``:
     optional (dQ, dK, dV) tensors to fill.  ``events``: optional list of
     2*LA_BACKWARD_KERNELS event handles."""
     torch = _torch()

@@ -1872,13 +1872,13 @@ struct SmemBwdA {
 // Pass A: dQ, and per token (D_i, h_i) -> dh[bh][N][2]; per span the reverse
 // sums -> wsb slot s.  O and dO are read in the layout of Q.
 template <class CF>
-__global__ __launch_bounds__(CF::NT, 2) void la_bwd_dq_kernel(
+__global__ __launch_bounds__(CF::NT, CF::NW == 8 ? 1 : 2) void la_bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, const bf16* __restrict__ O,
     const bf16* __restrict__ dO, bf16* __restrict__ dQ, const float* __restrict__ ws, float* __restrict__ wsb,
     float* __restrict__ dh, int N, int n_span) {
   using OP = typename CF::OP;
-  static_assert(sizeof(OP) == 2 && CF::RB == CF::NW && CF::RBW == 1 && CF::CTW == CF::CT && CF::R == CF::DV,
-                "one 16-row block per wave, d = d_v");
+  static_assert(sizeof(OP) == 2 && CF::RBW == 1 && CF::R == CF::DV && CF::CTW * CF::WPR == CF::CT,
+                "one 16-row block per wave (WPR waves share it, each with its share of the column tiles), d = d_v");
   constexpr int R = CF::R, DV = CF::DV, KS = CF::KS, RB = CF::RB, FT = CF::FT;
   using TQ = Tile<OP, R>;
   using TV = Tile<OP, DV>;
@@ -1914,18 +1914,28 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dq_kernel(
   const bf16 o1 = (li & 3) == 0 ? one : zero;
   const bf16x8 ones_rows = bf16x8{o1, o1, o1, o1, o1, o1, o1, o1};
   const int zrow = min(li & 3, 2);
-  const int ib = w;
+  // this wave's row block; with eight waves two share a block and each
+  // takes half of the feature tiles of dQ
+  constexpr int FTW = FT / CF::WPR;
+  const int ib = w % RB, half = w / RB, ft0 = half * FTW;
   OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
 
-  // chunk c+1 is loaded into registers while chunk c is computed
+  // four waves: chunk c+1 is loaded into registers while chunk c is
+  // computed; eight (d = 128) have no registers to spare for it and load
+  // each chunk at the top of its iteration
+  constexpr bool PREFETCH = CF::NW == 4;
   const int last = t_end > t_begin ? t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C : t_begin;
   ChunkRegs<CF, false> cr;
   QRegs<CF> qr, orr, dor;
-  load_chunk<CF, false>(cr, hb, t_begin);
-  qr.load(hb.q, t_begin, w, g, li);
-  orr.load(r_o, t_begin, w, g, li);
-  dor.load(r_do, t_begin, w, g, li);
+  auto load_all = [&](int tc) {
+    load_chunk<CF, false>(cr, hb, tc);
+    qr.load(hb.q, tc, w, g, li);
+    orr.load(r_o, tc, w, g, li);
+    dor.load(r_do, tc, w, g, li);
+  };
+  if constexpr (PREFETCH) load_all(t_begin);
   for (int t0 = t_begin; t0 < t_end; t0 += CF::C) {
+    if constexpr (!PREFETCH) load_all(t0);
     __syncthreads();  // every wave is done with the previous chunk's tiles
     publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
     stage_chunk<CF, false>(cr, nullptr, sm.k, nullptr, sm.v, t0, N);
@@ -1935,15 +1945,12 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dq_kernel(
     orr.to_raw(of, scr, g, li);
     dor.to_raw(df, scr, g, li);
     // phi(q) rows of this wave's block -> the chunk's phi(Q) tile
+    if (half == 0) {
 #pragma unroll
-    for (int ks = 0; ks < R / KS; ++ks) *reinterpret_cast<bf16x8*>(sm.q + TQ::off(16 * ib + li, 32 * ks + 8 * g)) = qf[0][ks];
-    {
-      const int tn = min(t0 + CF::C, last);  // (past the span's last chunk: re-read, unused)
-      load_chunk<CF, false>(cr, hb, tn);
-      qr.load(hb.q, tn, w, g, li);
-      orr.load(r_o, tn, w, g, li);
-      dor.load(r_do, tn, w, g, li);
+      for (int ks = 0; ks < R / KS; ++ks)
+        *reinterpret_cast<bf16x8*>(sm.q + TQ::off(16 * ib + li, 32 * ks + 8 * g)) = qf[0][ks];
     }
+    if constexpr (PREFETCH) load_all(min(t0 + CF::C, last));  // (past the span's last chunk: re-read, unused)
     __syncthreads();
 
     // 1. D_i: the masked weights' row sums (bf16 weights, as the forward)
@@ -1996,9 +2003,12 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dq_kernel(
     }
     const float hv = -xor_sum16_32(dot) * rden;
     // g rows and h -> LDS for the reverse sums; (D_i, h_i) -> dh
+    if (half == 0) {
 #pragma unroll
-    for (int ks = 0; ks < R / KS; ++ks) *reinterpret_cast<bf16x8*>(sm.gt + TV::off(16 * ib + li, 32 * ks + 8 * g)) = gf[ks];
-    if (g == 0) {
+      for (int ks = 0; ks < R / KS; ++ks)
+        *reinterpret_cast<bf16x8*>(sm.gt + TV::off(16 * ib + li, 32 * ks + 8 * g)) = gf[ks];
+    }
+    if (half == 0 && g == 0) {
       sm.h[16 * ib + li] = hv;
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(den), __float_as_uint(hv)}, r_dh,
@@ -2006,9 +2016,9 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dq_kernel(
     }
 
     // 3. W_ij = v_j.g_i + h_i (masked), and dphi(q_i) = sum_j W_ij phi(k_j)
-    f32x4 dq[FT];
+    f32x4 dq[FTW];
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) dq[ft] = zero4();
+    for (int fi = 0; fi < FTW; ++fi) dq[fi] = zero4();
 #pragma unroll
     for (int jp = 0; jp < (RB + 1) / 2; ++jp) {
       const int jb0 = 2 * jp, jb1 = 2 * jp + 1;
@@ -2030,29 +2040,31 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dq_kernel(
       const float w8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
       const bf16x8 bv = cvt_bf16x8(w8);
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) {
+      for (int fi = 0; fi < FTW; ++fi) {
+        const int ft = ft0 + fi;
         const bf16x8 av = two ? tr_frag<R>(sm.k, 16 * jb0 + 4 * g, 16 * jb1 + 4 * g, 16 * ft, li)
                               : tr_frag_lo<R>(sm.k, 16 * jb0 + 4 * g, 16 * ft, li);
-        dq[ft] = mfma16(av, bv, dq[ft]);
+        dq[fi] = mfma16(av, bv, dq[fi]);
       }
     }
     // 4. + S g_i + h_i z, then phi'(q)
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
+    for (int fi = 0; fi < FTW; ++fi) {
+      const int ft = ft0 + fi;
 #pragma unroll
       for (int ks = 0; ks < DV / KS; ++ks)
-        dq[ft] = mfma16(load_frag(sm.s + TV::off(16 * ft + li, ks * KS + g * 8)), gf[ks], dq[ft]);
+        dq[fi] = mfma16(load_frag(sm.s + TV::off(16 * ft + li, ks * KS + g * 8)), gf[ks], dq[fi]);
       const bf16x4 fq4 = *reinterpret_cast<const bf16x4*>(sm.q + TQ::off(16 * ib + li, 16 * ft + 4 * g));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int f = 16 * ft + 4 * g + r;
         const float zf = static_cast<float>(sm.z[f]) + static_cast<float>(sm.z[R + f]);
-        dq[ft][r] = (dq[ft][r] + hv * zf) * phi_deriv_from_phi<CF::PHI>(static_cast<float>(fq4[r]));
+        dq[fi][r] = (dq[fi][r] + hv * zf) * phi_deriv_from_phi<CF::PHI>(static_cast<float>(fq4[r]));
       }
     }
     OutRegs<CF> out;
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) out.v[0][ft] = cvt_bf16x4(dq[ft]);
+    for (int fi = 0; fi < FTW; ++fi) out.v[0][fi] = cvt_bf16x4(dq[fi]);
     store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
     __syncthreads();  // the chunk's phi(Q), G and h tiles are complete
 
@@ -2111,13 +2123,13 @@ struct SmemBwdB {
 // Pass B: dK, dV, spans walked backward from the suffix (R, u) of the
 // later spans (wsb slot s after the suffix scan).
 template <class CF>
-__global__ __launch_bounds__(CF::NT, 2) void la_bwd_dkv_kernel(
+__global__ __launch_bounds__(CF::NT, CF::NW == 8 ? 1 : 2) void la_bwd_dkv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ dh, bf16* __restrict__ dK, bf16* __restrict__ dV,
     const float* __restrict__ wsb, int N, int n_span) {
   using OP = typename CF::OP;
-  static_assert(sizeof(OP) == 2 && CF::RB == CF::NW && CF::RBW == 1 && CF::CTW == CF::CT && CF::R == CF::DV,
-                "one 16-row block per wave, d = d_v");
+  static_assert(sizeof(OP) == 2 && CF::RBW == 1 && CF::R == CF::DV && CF::CTW * CF::WPR == CF::CT,
+                "one 16-row block per wave (WPR waves share it, each with its share of the column tiles), d = d_v");
   constexpr int R = CF::R, DV = CF::DV, KS = CF::KS, RB = CF::RB, FT = CF::FT, CT = CF::CT;
   using TQ = Tile<OP, R>;
   using TV = Tile<OP, DV>;
@@ -2147,14 +2159,19 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dkv_kernel(
     const float uv = suf[R * DV + 16 * w + li];
     ut[0] = f32x4{uv, uv, uv, uv};
   }
-  const int jb = w;
+  // this wave's key block; with eight waves two share a block and each
+  // takes half of the value tiles of dV and half of the feature tiles of dK
+  constexpr int FTW = FT / CF::WPR, CTW = CT / CF::WPR;
+  const int jb = w % RB, half = w / RB, ft0 = half * FTW, ct0 = half * CTW;
   OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
   constexpr int VVR = DV / 8;
   if (t_begin >= t_end) return;
   const int last = t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C;
 
-  // chunk c-1 is loaded into registers while chunk c is computed: Q, K, V,
-  // the dO rows (V's layout), each row's D and the chunk's h
+  // chunk c-1 is loaded into registers while chunk c is computed (four
+  // waves; eight load each chunk at the top of its iteration): Q, K, V, the
+  // dO rows (V's layout), each row's D and the chunk's h
+  constexpr bool PREFETCH = CF::NW == 4;
   ChunkRegs<CF, true> cr;
   u32x4 dov[CF::LV];
   float rd[CF::LV];
@@ -2170,8 +2187,9 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dkv_kernel(
     }
     hl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dh, (tc + (tid & 63)) * 8 + 4, 0, 0));
   };
-  load_all(last);
+  if constexpr (PREFETCH) load_all(last);
   for (int t0 = last; t0 >= t_begin; t0 -= CF::C) {
+    if constexpr (!PREFETCH) load_all(t0);
     __syncthreads();  // every wave is done with the previous chunk's tiles
     // the carried R (bf16) and u
 #pragma unroll
@@ -2194,7 +2212,7 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dkv_kernel(
       *reinterpret_cast<u32x4*>(sm.gt + TV::off(tok, (vi % VVR) * 8)) = pack16<bf16>(f);
     }
     if (w == 0 && (tid & 63) < CF::C) sm.h[tid & 63] = t0 + (tid & 63) < N ? hl : 0.f;
-    load_all(max(t0 - CF::C, t_begin));  // (before the span's first chunk: re-read, unused)
+    if constexpr (PREFETCH) load_all(max(t0 - CF::C, t_begin));  // (before the span's first chunk: re-read, unused)
     __syncthreads();
 
     // this wave's key rows j = 16 jb + li: phi(k_j), v_j as B operands
@@ -2210,11 +2228,11 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dkv_kernel(
       }
       return t;
     };
-    f32x4 dv[CT], dk[FT];
+    f32x4 dv[CTW], dk[FTW];
 #pragma unroll
-    for (int c = 0; c < CT; ++c) dv[c] = zero4();
+    for (int ci = 0; ci < CTW; ++ci) dv[ci] = zero4();
 #pragma unroll
-    for (int f = 0; f < FT; ++f) dk[f] = zero4();
+    for (int fi = 0; fi < FTW; ++fi) dk[fi] = zero4();
     // query blocks ib >= jb, in pairs (one 32-token MFMA step)
 #pragma unroll
     for (int ip = 0; ip < (RB + 1) / 2; ++ip) {
@@ -2245,33 +2263,34 @@ __global__ __launch_bounds__(CF::NT, 2) void la_bwd_dkv_kernel(
       const float w8[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
       const bf16x8 ab = cvt_bf16x8(a8), wb = cvt_bf16x8(w8);
 #pragma unroll
-      for (int c = 0; c < CT; ++c)
-        dv[c] = mfma16(tr_frag<DV>(sm.gt, 16 * ib0 + 4 * g, 16 * ib1 + 4 * g, 16 * c, li), ab, dv[c]);
+      for (int ci = 0; ci < CTW; ++ci)
+        dv[ci] = mfma16(tr_frag<DV>(sm.gt, 16 * ib0 + 4 * g, 16 * ib1 + 4 * g, 16 * (ct0 + ci), li), ab, dv[ci]);
 #pragma unroll
-      for (int f = 0; f < FT; ++f)
-        dk[f] = mfma16(tr_frag<R>(sm.q, 16 * ib0 + 4 * g, 16 * ib1 + 4 * g, 16 * f, li), wb, dk[f]);
+      for (int fi = 0; fi < FTW; ++fi)
+        dk[fi] = mfma16(tr_frag<R>(sm.q, 16 * ib0 + 4 * g, 16 * ib1 + 4 * g, 16 * (ft0 + fi), li), wb, dk[fi]);
     }
     // + the later chunks: dv_j += R^T phi(k_j), dphi(k_j) += R v_j + u
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
+    for (int ci = 0; ci < CTW; ++ci)
 #pragma unroll
       for (int ks = 0; ks < R / KS; ++ks)
-        dv[c] = mfma16(tr_frag<DV>(sm.rs, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, 16 * c, li), kf[ks], dv[c]);
+        dv[ci] = mfma16(tr_frag<DV>(sm.rs, ks * 32 + 8 * g, ks * 32 + 8 * g + 4, 16 * (ct0 + ci), li), kf[ks], dv[ci]);
 #pragma unroll
-    for (int f = 0; f < FT; ++f) {
+    for (int fi = 0; fi < FTW; ++fi) {
+      const int f = ft0 + fi;
 #pragma unroll
       for (int ks = 0; ks < DV / KS; ++ks)
-        dk[f] = mfma16(load_frag(sm.rs + TV::off(16 * f + li, ks * KS + g * 8)), vf[ks], dk[f]);
+        dk[fi] = mfma16(load_frag(sm.rs + TV::off(16 * f + li, ks * KS + g * 8)), vf[ks], dk[fi]);
       const f32x4 uf = *reinterpret_cast<const f32x4*>(sm.u + 16 * f + 4 * g);
       const bf16x4 fk4 = *reinterpret_cast<const bf16x4*>(sm.k + TQ::off(16 * jb + li, 16 * f + 4 * g));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dk[f][r] = (dk[f][r] + uf[r]) * phi_deriv_from_phi<CF::PHI>(static_cast<float>(fk4[r]));
+      for (int r = 0; r < 4; ++r) dk[fi][r] = (dk[fi][r] + uf[r]) * phi_deriv_from_phi<CF::PHI>(static_cast<float>(fk4[r]));
     }
     OutRegs<CF> ok, ov;
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      ov.v[0][c] = cvt_bf16x4(dv[c]);
-      ok.v[0][c] = cvt_bf16x4(dk[c]);
+    for (int ci = 0; ci < CTW; ++ci) {
+      ov.v[0][ci] = cvt_bf16x4(dv[ci]);
+      ok.v[0][ci] = cvt_bf16x4(dk[ci]);
     }
     store_outputs<CF>(ok, hb.o, t0, w, g, li, false, scr);
     store_outputs<CF>(ov, r_dv, t0, w, g, li, false, scr);
@@ -2715,12 +2734,16 @@ static hipError_t launch_backward(const BackwardArgs& a) {
 }
 
 bool backward_supported(int io, int phi, int d, int dv, int r, int chunk) {
-  return io == 1 && (phi == PHI_ELU1 || phi == PHI_IDENTITY) && d == 64 && dv == 64 && r == 64 && chunk == 64;
+  return io == 1 && (phi == PHI_ELU1 || phi == PHI_IDENTITY) && (d == 64 || d == 128) && dv == d && r == d &&
+         chunk == 64;
 }
 
 hipError_t backward_launch(const BackwardArgs& a) {
   if (!backward_supported(a.io, a.phi, a.d, a.dv, a.r, a.chunk)) return hipErrorInvalidValue;
   if (a.B * a.H == 0 || a.N == 0) return hipSuccess;
+  if (a.d == 128)
+    return a.phi == PHI_ELU1 ? launch_backward<Cfg<bf16, 128, 128, 128, 64, PHI_ELU1, 8>>(a)
+                             : launch_backward<Cfg<bf16, 128, 128, 128, 64, PHI_IDENTITY, 8>>(a);
   return a.phi == PHI_ELU1 ? launch_backward<Cfg<bf16, 64, 64, 64, 64, PHI_ELU1>>(a)
                            : launch_backward<Cfg<bf16, 64, 64, 64, 64, PHI_IDENTITY>>(a);
 }

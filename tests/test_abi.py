@@ -266,7 +266,7 @@ def test_backward_argument_errors(lib):
     assert fb(dV=None) == 1
     assert fb(N=-1) == 2                                 # LA_ERR_SHAPE
     assert fb(io=0) == 3                                 # bf16 only
-    assert fb(d=128, dv=128) == 3
+    assert fb(d=96, dv=96) == 3
     assert fb(chunk=32) == 3
     assert fb(phi=1, r=256) == 3
     assert fb(O=MISALIGNED) == 4                         # LA_ERR_ALIGN

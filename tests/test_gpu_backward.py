@@ -37,13 +37,13 @@ def span(monkeypatch):
     return _set
 
 
-def _draw(B, H, N, seed, phi="elu1"):
-    q, k, v = synth.draw_qkv(B, H, N, 64, 64, seed=seed)
+def _draw(B, H, N, seed, phi="elu1", d=64):
+    q, k, v = synth.draw_qkv(B, H, N, d, d, seed=seed)
     if phi == "identity":  # positive features keep the denominators positive
         q = synth.round_to_io(np.abs(q) + 0.25, "bf16")
         k = synth.round_to_io(np.abs(k) + 0.25, "bf16")
     rng = np.random.default_rng(seed + 1000)
-    dO = synth.round_to_io(rng.standard_normal((B, H, N, 64), dtype=np.float32), "bf16")
+    dO = synth.round_to_io(rng.standard_normal((B, H, N, d), dtype=np.float32), "bf16")
     return q, k, v, dO
 
 
@@ -94,6 +94,21 @@ def test_backward_small(lib, span, B, H, N, tokens, phi):
     in-span carries are exercised."""
     span(tokens)
     q, k, v, dO = _draw(B, H, N, 81 + N, phi)
+    dq, dk, dv = _run(lib, q, k, v, dO, phi)
+    rq, rk, rv = bwd.grad_causal(q, k, v, dO, phi=phi)
+    sq, sk, sv = _scales(q, k, v, dO, phi)
+    _check(dq, rq, sq, "dQ")
+    _check(dk, rk, sk, "dK")
+    _check(dv, rv, sv, "dV")
+
+
+@pytest.mark.parametrize("phi", ["elu1", "identity"])
+@pytest.mark.parametrize("N,tokens", [(17, None), (300, None), (333, 128)])
+def test_backward_wide_heads(lib, span, N, tokens, phi):
+    """d = d_v = 128: eight waves, two per 16-row block, each with half of the
+    feature and value tiles."""
+    span(tokens)
+    q, k, v, dO = _draw(2, 2, N, 95 + N, phi, d=128)
     dq, dk, dv = _run(lib, q, k, v, dO, phi)
     rq, rk, rv = bwd.grad_causal(q, k, v, dO, phi=phi)
     sq, sk, sv = _scales(q, k, v, dO, phi)
