@@ -1917,6 +1917,9 @@ __global__ __launch_bounds__(CF::NT, CF::NW == 8 ? 1 : 2) void la_bwd_dq_kernel(
   // this wave's row block; with eight waves two share a block and each
   // takes half of the feature tiles of dQ
   constexpr int FTW = FT / CF::WPR;
+  // four waves form the span's reverse sums here; eight (d = 128) leave
+  // them to la_bwd_rsum_kernel (no registers for a second 128 x 128 state)
+  constexpr bool RSUM = CF::NW == 4;
   const int ib = w % RB, half = w / RB, ft0 = half * FTW;
   OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
 
@@ -2003,13 +2006,13 @@ __global__ __launch_bounds__(CF::NT, CF::NW == 8 ? 1 : 2) void la_bwd_dq_kernel(
     }
     const float hv = -xor_sum16_32(dot) * rden;
     // g rows and h -> LDS for the reverse sums; (D_i, h_i) -> dh
-    if (half == 0) {
+    if (RSUM && half == 0) {
 #pragma unroll
       for (int ks = 0; ks < R / KS; ++ks)
         *reinterpret_cast<bf16x8*>(sm.gt + TV::off(16 * ib + li, 32 * ks + 8 * g)) = gf[ks];
     }
     if (half == 0 && g == 0) {
-      sm.h[16 * ib + li] = hv;
+      if constexpr (RSUM) sm.h[16 * ib + li] = hv;
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(den), __float_as_uint(hv)}, r_dh,
                                             (t0 + 16 * ib + li) * 8, 0, 0);
@@ -2066,13 +2069,87 @@ __global__ __launch_bounds__(CF::NT, CF::NW == 8 ? 1 : 2) void la_bwd_dq_kernel(
 #pragma unroll
     for (int fi = 0; fi < FTW; ++fi) out.v[0][fi] = cvt_bf16x4(dq[fi]);
     store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
-    __syncthreads();  // the chunk's phi(Q), G and h tiles are complete
-
-    // 5. reverse sums of the span and the forward carry
-    state_mfma_w<CF>(racc, ut, sm.q, sm.gt, sm.h, w, g, li);
+    if constexpr (RSUM) {
+      __syncthreads();  // the chunk's phi(Q), G and h tiles are complete
+      // 5. reverse sums of the span
+      state_mfma_w<CF>(racc, ut, sm.q, sm.gt, sm.h, w, g, li);
+    }
+    // the forward carry
     state_mfma<CF>(sacc, zt, sm.k, nullptr, sm.v, w, g, li);
   }
 
+  if constexpr (!RSUM) return;
+  float* slot = wsb + ((size_t)bh * (n_span + 1) + s) * E;
+#pragma unroll
+  for (int i = 0; i < CF::TPW; ++i) {
+    int ct, ft;
+    state_tile<CF>(w, i, ct, ft);
+    *reinterpret_cast<f32x4*>(slot + (16 * ft + li) * DV + 16 * ct + 4 * g) = racc[i];
+  }
+  if (g == 0) slot[R * DV + 16 * w + li] = ut[0][0];
+}
+
+
+// The span's reverse sums dR = phi(Q)^T G, du = sum phi(q) h -> wsb slot s,
+// for the eight-wave (d = 128) backward, whose dQ pass has no registers for
+// them: per chunk phi(Q) and G = dO / D (from the (D, h) the dQ pass wrote)
+// staged in LDS, then state_mfma_w.
+template <class CF>
+__global__ __launch_bounds__(CF::NT) void la_bwd_rsum_kernel(const bf16* __restrict__ Q,
+                                                            const bf16* __restrict__ dO,
+                                                            const float* __restrict__ dh,
+                                                            float* __restrict__ wsb, int N, int n_span) {
+  using OP = typename CF::OP;
+  constexpr int R = CF::R, DV = CF::DV, E = R * DV + R, VVR = DV / 8;
+  using TV = Tile<OP, DV>;
+  struct Smem {
+    OP q[Tile<OP, R>::elems(CF::C)];
+    OP gt[Tile<OP, DV>::elems(CF::C)];
+    alignas(16) float h[CF::C];
+  };
+  __shared__ Smem sm;
+  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
+  const int bh = blockIdx.x / n_span;
+  const int s = blockIdx.x % n_span;
+  const int t_begin = span_begin<CF>(s, n_span, N);
+  const int t_end = span_begin<CF>(s + 1, n_span, N);
+  const size_t qk = (size_t)N * CF::D;
+  HeadBufs hb;
+  hb.k = make_rsrc(Q + bh * qk, (unsigned)(qk * 2));      // Q rows staged as keys are
+  hb.v = make_rsrc(dO + bh * qk, (unsigned)(qk * 2));     // dO rows staged as values are
+  const __amdgpu_buffer_rsrc_t r_dh = make_rsrc(dh + (size_t)bh * N * 2, (unsigned)N * 8u);
+  f32x4 racc[CF::TPW];
+#pragma unroll
+  for (int i = 0; i < CF::TPW; ++i) racc[i] = zero4();
+  f32x4 ut[1] = {zero4()};
+  for (int t0 = t_begin; t0 < t_end; t0 += CF::C) {
+    ChunkRegs<CF, false> cr;
+    load_chunk<CF, false>(cr, hb, t0);
+    float rd[CF::LV];
+#pragma unroll
+    for (int i = 0; i < CF::LV; ++i) {
+      const int tok = (tid + i * CF::NT) / VVR;
+      rd[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dh, (t0 + tok) * 8, 0, 0));
+    }
+    const float hl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dh, (t0 + l) * 8 + 4, 0, 0));
+    __syncthreads();  // the previous chunk's MFMA work is done with the tiles
+    // phi(Q) (zero beyond N, as keys are) and G = dO / D
+    stage_chunk<CF, false>(cr, nullptr, sm.q, nullptr, sm.gt, t0, N);
+#pragma unroll
+    for (int i = 0; i < CF::LV; ++i) {
+      const int vi = tid + i * CF::NT;
+      const int tok = vi / VVR;
+      float f[8];
+      unpack16<bf16>(cr.v[i], f);
+      const float r = t0 + tok < N ? __builtin_amdgcn_rcpf(rd[i]) : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] *= r;
+      *reinterpret_cast<u32x4*>(sm.gt + TV::off(tok, (vi % VVR) * 8)) = pack16<bf16>(f);
+    }
+    if (w == 0 && l < CF::C) sm.h[l] = t0 + l < N ? hl : 0.f;
+    __syncthreads();
+    state_mfma_w<CF>(racc, ut, sm.q, sm.gt, sm.h, w, g, li);
+  }
   float* slot = wsb + ((size_t)bh * (n_span + 1) + s) * E;
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) {
@@ -2721,6 +2798,9 @@ static hipError_t launch_backward(const BackwardArgs& a) {
   rec(4);
   hipLaunchKernelGGL((la_bwd_dq_kernel<CF>), grid, block, 0, st, Q, K, V, static_cast<const bf16*>(a.O),
                      static_cast<const bf16*>(a.dO), static_cast<bf16*>(a.dQ), wsf, wsb, dh, a.N, n_span);
+  if constexpr (CF::NW != 4)  // (inside the dQ pass's event interval)
+    hipLaunchKernelGGL((la_bwd_rsum_kernel<CF>), grid, block, 0, st, Q, static_cast<const bf16*>(a.dO), dh, wsb,
+                       a.N, n_span);
   rec(5);
   rec(6);
   hipLaunchKernelGGL(la_suffix_scan_kernel, dim3((E + kThreads - 1) / kThreads, BH), dim3(kThreads), 0, st, wsb, E,
