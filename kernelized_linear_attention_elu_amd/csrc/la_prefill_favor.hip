@@ -71,7 +71,8 @@ __device__ __forceinline__ FavorConsts favor_consts() {
 // Per-token part of the exponent, formed once per token when its squared
 // norm is summed: -(|u|^2 log2(e) / (2 sqrt(d)) + log2(sqrt(r))).
 __device__ __forceinline__ float favor_bias(const FavorConsts& c, float norm2) { return -(norm2 * c.a2 + c.a3); }
-// phi for one feature: exp2(proj log2(e) d^(-1/4) + bias) - one FMA and one exp2.
+// phi for one feature: exp2(proj log2(e) d^(-1/4) + bias) - one FMA and one exp2
+// (0 for the bias -inf of a masked token, whose projection is 0).
 __device__ __forceinline__ float favor_phi(const FavorConsts& c, float proj, float bias) {
   return __builtin_amdgcn_exp2f(__builtin_fmaf(proj, c.a1, bias));
 }
@@ -127,10 +128,12 @@ __device__ __forceinline__ void load_raw(RawRegs<NS>& rr, const __amdgpu_buffer_
 // Registers -> LDS (row-major swizzled 64 x 64 tiles).  For the streams
 // flagged in `norms`, the squared norm of each token row is summed in fp32
 // (8 threads hold one row: a 3-step butterfly) and its exponent bias is
-// written to nrm.
+// written to nrm.  For the streams flagged in `masked`, rows at or beyond
+// `live` (tokens past the end of the sequence; their raw rows read as zero)
+// get the bias -inf instead, so that every feature of theirs is exp2(-inf) = 0.
 template <int NS>
 __device__ __forceinline__ void stage_raw(const RawRegs<NS>& rr, bf16* const (&dst)[NS], float* const (&nrm)[NS],
-                                          int norms) {
+                                          int norms, int masked, int live) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < FLQ; ++i) {
@@ -148,7 +151,8 @@ __device__ __forceinline__ void stage_raw(const RawRegs<NS>& rr, bf16* const (&d
         n2 += __shfl_xor(n2, 1);
         n2 += __shfl_xor(n2, 2);
         n2 += __shfl_xor(n2, 4);
-        if ((tid & 7) == 0) nrm[s][tok] = favor_bias(favor_consts(), n2);
+        if ((tid & 7) == 0)
+          nrm[s][tok] = (masked & (1 << s)) && tok >= live ? -__builtin_inff() : favor_bias(favor_consts(), n2);
       }
     }
   }
@@ -224,7 +228,7 @@ __global__ __launch_bounds__(FNT, 1) void la_state_favor_kernel(const bf16* __re
     {
       bf16* const dst[2] = {kraw[buf], vt[buf]};
       float* const nrm[2] = {kn[buf], nullptr};
-      stage_raw<2>(rr, dst, nrm, 1);
+      stage_raw<2>(rr, dst, nrm, 1, 1, N - t0);
     }
     if (t0 + FC < t_end) load_raw<2>(rr, src, t0 + FC);
     __syncthreads();
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(FNT, 1) void la_state_favor_kernel(const bf16* __re
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int tok = 16 * tb + 4 * g + r;
-          const float f = t0 + tok < N ? favor_phi(fc, p[r], kn[buf][tok]) : 0.f;
+          const float f = favor_phi(fc, p[r], kn[buf][tok]);  // 0 past the end (bias -inf)
           const bf16 h = static_cast<bf16>(f);
           ph[tb][r] = h;
           pl[tb][r] = static_cast<bf16>(f - static_cast<float>(h));
@@ -280,32 +284,59 @@ __global__ __launch_bounds__(FNT, 1) void la_state_favor_kernel(const bf16* __re
 
 // ------------------------------------------------------------------ outputs
 
+// The phi(Q)/phi(K) tiles ([token][feature], 256 features) and the carried
+// state tile ([feature][value]) of the output pass are only ever accessed in
+// 8-byte pieces (4 bf16 starting at a multiple of 4), so their rows are
+// swizzled at that granularity: piece p of row r is stored at p ^ hash(r mod 16).
+// gfx950 serves 8-byte LDS reads (plain and transposing) 32 lanes at a time
+// from 64 four-byte banks, and 8-byte writes 16 lanes at a time from a
+// 128-byte window (measured with the bank-conflict counter).  With
+//   phi tiles:  hash bits (0..4) = (r3, r2, r0, r1, r3),
+//   state tile: hash bits (0..3) = (r0, r3, r1, r2),
+// every access pattern of the pass is conflict-free:
+//   phi writes (16 consecutive rows, one piece): hash bits 0-3 are a
+//     bijection of r, so the rows hit 16 distinct pieces of the window;
+//   phi row reads (16 rows x pieces p, p + 1, p even): bits 1-4 are a
+//     bijection of r, so the 16 pairs are distinct;
+//   phi transposing reads (rows {b..b+3, b+8..b+11} x 4 pieces): bits 2-4
+//     are a bijection of (r0, r1, r3), so the 8 aligned groups are distinct;
+//   state writes (16 rows, one piece; a row is 128 bytes): the hash is a
+//     bijection of r;
+//   state transposing reads (8 consecutive rows x 4 pieces): r0 picks the
+//     half of the 256-byte bank space, bits 2-3 are a bijection of (r1, r2).
+__device__ __forceinline__ int phi_hash(int r) {
+  return ((r >> 3) & 1) | (((r >> 2) & 1) << 1) | ((r & 1) << 2) | (((r >> 1) & 1) << 3) | (((r >> 3) & 1) << 4);
+}
+__device__ __forceinline__ int phi_off(int row, int col) {
+  return row * FR + ((((col >> 2) ^ phi_hash(row & 15)) << 2) | (col & 3));
+}
+__device__ __forceinline__ int st_hash(int r) {
+  return (r & 1) | (((r >> 3) & 1) << 1) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 3);
+}
+__device__ __forceinline__ int st_off(int row, int col) {
+  return row * FDV + ((((col >> 2) ^ st_hash(row & 15)) << 2) | (col & 3));
+}
+
+constexpr int FZS = FR + 8;  // z row stride: the three rows start 16 bytes apart in bank space
+
 struct SmemOutFavor {
   bf16 qraw[2][FC * FD];
   bf16 kraw[2][FC * FD];
   bf16 v[2][FC * FDV];
   float qn[2][FC];
   float kn[2][FC];
-  bf16 sq[FC * FR];   // phi(Q) of the chunk, [token][feature]
+  bf16 sq[FC * FR];   // phi(Q) of the chunk, [token][feature] (phi_off)
   bf16 sk[FC * FR];   // phi(K) of the chunk
-  bf16 ss[FR * FDV];  // carried S, [feature][value]
-  bf16 sz[3 * FR];    // carried z as rows: bf16 hi, lo = z - hi, zeros
+  bf16 ss[FR * FDV];  // carried S, [feature][value] (st_off)
+  bf16 sz[3 * FZS];   // carried z as rows: bf16 hi, lo = z - hi, zeros
 };
 
-// Operand fragment of one row of a [token][feature] phi tile in the permuted
-// feature order (two 8-byte LDS reads).
-__device__ __forceinline__ bf16x8 prow_frag(const bf16* t, int row, int ks, int g) {
-  const bf16x4 a = *reinterpret_cast<const bf16x4*>(t + T256::off(row, 32 * ks + 4 * g));
-  const bf16x4 b = *reinterpret_cast<const bf16x4*>(t + T256::off(row, 32 * ks + 16 + 4 * g));
-  return cat4(a, b);
-}
-
-// The same for one of the three (unswizzled) z rows.
-__device__ __forceinline__ bf16x8 zrow_frag(const bf16* z, int row, int ks, int g) {
-  const bf16x4 a = *reinterpret_cast<const bf16x4*>(z + row * FR + 32 * ks + 4 * g);
-  const bf16x4 b = *reinterpret_cast<const bf16x4*>(z + row * FR + 32 * ks + 16 + 4 * g);
-  return cat4(a, b);
-}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x4 lds4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+// 8-byte LDS store as one ds_write_b64 (a bf16x4 store is split in two dword writes)
+__device__ __forceinline__ void sts4(bf16* p, bf16x4 v) { *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v); }
+// Transposing operand fragment from two 4-row groups (k-slots 0-3 at p0, 4-7 at p1).
+__device__ __forceinline__ bf16x8 tr2(const bf16* p0, const bf16* p1) { return cat4(ds_read_tr4(p0), ds_read_tr4(p1)); }
 
 // Outputs of one span (carried state from the scanned slot when causal, the
 // full-sequence sums otherwise).  Per chunk: stage raw Q, K, V (double
@@ -326,7 +357,7 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
                                                                  int n_span) {
   __shared__ SmemOutFavor sm;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63;
-  int g = l >> 4, li = l & 15;
+  const int g = l >> 4, li = l & 15, q4 = li >> 2, r4 = li & 3;
   const int bh = blockIdx.x / n_span;
   const int s = blockIdx.x % n_span;
   const int t_begin = span_begin64(s, n_span, N);
@@ -347,6 +378,41 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
   const int sft0 = TPW * (w / FCT);     // first feature tile of them
   const int ib = w % 4;                 // output row block
   const int oct0 = OCT * (w / 4);       // first output value tile
+
+  // Lane offsets (elements) into the LDS tiles, formed once.  Rows 16 apart
+  // share a hash, so every access of the chunk loop is one of these plus a
+  // compile-time constant - except the transposing phi(K) reads of the state
+  // carry, where feature tile sft0 + i is the offset XOR 16 i (the hash acts
+  // on the 32 pieces of a half row; see phi_off).
+  int o_raw[2];      // raw Q/K rows (projection operands): row li, columns 32 ks + 8 g
+  int o_phw[FPW];    // phi writes: row li, features 16 (FPW w + j) + 4 g
+  int o_prow[4][2];  // phi row reads: row li, features 32 kq + 16 h + 4 g (k-step kq + 4: + 128)
+  int o_vo[OCT];     // V transposing reads (outputs): row 4 g + li / 4, values 16 (oct0 + c) + 4 (li % 4)
+  int o_so[OCT];     // S transposing reads: the same rows and columns of the state tile
+  int o_vc[2];       // V transposing reads (state carry): row 8 g + 4 h + li / 4, values 16 sct + 4 (li % 4)
+  int o_kc[2];       // phi(K) transposing reads: the same rows, features 16 sft0 + 4 (li % 4)
+  int o_kz[2];       // ... features 16 w + 4 (li % 4) (z tile w; tile w + 8: + 128)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    o_raw[h] = T64::off(li, 32 * h + 8 * g);
+    o_phw[h] = phi_off(li, 16 * (FPW * w + h) + 4 * g);
+    o_vc[h] = T64::off(8 * g + 4 * h + q4, 16 * sct + 4 * r4);
+    o_kc[h] = phi_off(8 * g + 4 * h + q4, 16 * sft0 + 4 * r4);
+    o_kz[h] = phi_off(8 * g + 4 * h + q4, 16 * w + 4 * r4);
+    o_vo[h] = T64::off(4 * g + q4, 16 * (oct0 + h) + 4 * r4);
+    o_so[h] = st_off(4 * g + q4, 16 * (oct0 + h) + 4 * r4);
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) o_prow[kq][h] = phi_off(li, 32 * kq + 16 * h + 4 * g);
+  }
+  const int o_sw = st_off(16 * sft0 + li, 16 * sct + 4 * g);  // S writes (tile sft0 + i: + 16 i rows)
+  const int zrow = min(r4, 2);                                 // z_hi, z_lo or zeros
+  const int o_z = zrow * FZS + 4 * g;                          // z row reads (+ 32 ks, + 16)
+  // phi operand fragment of row `row` (a multiple of 16 plus li) at k-step ks
+  auto prow = [&](const bf16* t, int ks) {
+    const bf16* p = t + 128 * (ks >> 2);
+    return cat4(lds4(p + o_prow[ks & 3][0]), lds4(p + o_prow[ks & 3][1]));
+  };
+
   const float* pre = ws + ((size_t)bh * (n_span + 1) + (CAUSAL ? s : n_span)) * FE;
   f32x4 sacc[TPW];
 #pragma unroll
@@ -360,30 +426,26 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
   }
   const bf16 one = static_cast<bf16>(1.0f), zero = static_cast<bf16>(0.0f);
   const bf16x8 ones = bf16x8{one, one, one, one, one, one, one, one};
-  const bf16 o1 = (li & 3) == 0 ? one : zero;
+  const bf16 o1 = r4 == 0 ? one : zero;
   const bf16x8 ones_rows = bf16x8{o1, o1, o1, o1, o1, o1, o1, o1};  // rows 4m of the ones operand
-  const int zrow = min(li & 3, 2);                                    // z_hi, z_lo or zeros
 
   RawRegs<3> rr;
   load_raw<3>(rr, src, t_begin);
   bf16x4 out[OCT];
   int buf = 0;
   for (int t0 = t_begin; t0 < t_end; t0 += FC, buf ^= 1) {
-    // the lane coordinates are made opaque to the compiler once per chunk,
-    // so that the many per-lane LDS addresses derived from them are formed
-    // where they are used instead of being hoisted out of the loop and
-    // spilled (registers are tight at two waves per SIMD)
-    asm volatile("" : "+v"(g), "+v"(li));
+    // the 16 XORed offsets of the state carry are formed in the loop rather
+    // than kept live across it (registers are tight at two waves per SIMD)
+    asm volatile("" : "+v"(o_kc[0]), "+v"(o_kc[1]));
     {
       bf16* const dst[3] = {sm.qraw[buf], sm.kraw[buf], sm.v[buf]};
       float* const nrm[3] = {sm.qn[buf], sm.kn[buf], nullptr};
-      stage_raw<3>(rr, dst, nrm, CAUSAL ? 3 : 1);
+      stage_raw<3>(rr, dst, nrm, CAUSAL ? 3 : 1, 2, N - t0);
     }
     if (t0 != t_begin) {
       const int row = t0 - FC + 16 * ib + li;
 #pragma unroll
       for (int c = 0; c < OCT; ++c) {
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out[c]), orsrc,
                                               (row * FDV + 16 * (oct0 + c) + 4 * g) * 2, 0, kStreamStore);
       }
@@ -392,33 +454,37 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
     __syncthreads();
 
     // feature tiles: lane (g, li) gets features 16 ft + 4 g + r of token 16 tb + li
+    // (features of tokens past the end are 0 through their -inf bias)
+    const bf16* qraw = sm.qraw[buf];
+    const bf16* kraw = sm.kraw[buf];
 #pragma unroll
     for (int j = 0; j < FPW; ++j) {
-      const int ft = FPW * w + j;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const int tok = 16 * tb + li;
-        const f32x4 pq = project<false, false>(sm.qraw[buf], om, j, tb, g, li);
-        const float nq = sm.qn[buf][tok];
+        f32x4 pq = zero4(), pk = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          pq = mfma16(om.hi[j][ks], load_frag(qraw + 16 * tb * FD + o_raw[ks]), pq);
+          if constexpr (CAUSAL) pk = mfma16(om.hi[j][ks], load_frag(kraw + 16 * tb * FD + o_raw[ks]), pk);
+        }
+        const float nq = sm.qn[buf][16 * tb + li];
         bf16x4 hq;
 #pragma unroll
         for (int r = 0; r < 4; ++r) hq[r] = static_cast<bf16>(favor_phi(fc, pq[r], nq));
-        *reinterpret_cast<bf16x4*>(sm.sq + T256::off(tok, 16 * ft + 4 * g)) = hq;
+        sts4(sm.sq + 16 * tb * FR + o_phw[j], hq);
         if constexpr (CAUSAL) {
-          const f32x4 pk = project<false, false>(sm.kraw[buf], om, j, tb, g, li);
-          const float nk = sm.kn[buf][tok];
-          const bool valid = t0 + tok < N;
+          const float nk = sm.kn[buf][16 * tb + li];
           bf16x4 hk;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) hk[r] = static_cast<bf16>(valid ? favor_phi(fc, pk[r], nk) : 0.f);
-          *reinterpret_cast<bf16x4*>(sm.sk + T256::off(tok, 16 * ft + 4 * g)) = hk;
+          for (int r = 0; r < 4; ++r) hk[r] = static_cast<bf16>(favor_phi(fc, pk[r], nk));
+          sts4(sm.sk + 16 * tb * FR + o_phw[j], hk);
         }
       }
     }
     if (CAUSAL || t0 == t_begin) {
 #pragma unroll
       for (int i = 0; i < TPW; ++i)
-        *reinterpret_cast<bf16x4*>(sm.ss + T64::off(16 * (sft0 + i) + li, 16 * sct + 4 * g)) = cvt_bf16x4(sacc[i]);
+        sts4(sm.ss + 16 * i * FDV + o_sw, cvt_bf16x4(sacc[i]));
       // lane group 0 writes z_hi, group 1 z_lo, group 2 the zero row
       if (g < 3) {
 #pragma unroll
@@ -426,19 +492,22 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
           const float z = zt[k][0];
           const bf16 h = static_cast<bf16>(z);
           const bf16 v = g == 0 ? h : g == 1 ? static_cast<bf16>(z - static_cast<float>(h)) : zero;
-          sm.sz[g * FR + 16 * (w + FNW * k) + li] = v;
+          sm.sz[g * FZS + 16 * (w + FNW * k) + li] = v;
         }
       }
     }
     __syncthreads();
 
     // ---- outputs of row block ib, value tiles oct0, oct0 + 1
+    const bf16* vb = sm.v[buf];
+    const bf16* sq_ib = sm.sq + 16 * ib * FR;
     bf16x8 qf[FR / 32];
     f32x4 dacc = zero4();  // [0] = z_hi . phi(q) + rowsum(weights), [1] = z_lo . phi(q)
 #pragma unroll
     for (int ks = 0; ks < FR / 32; ++ks) {
-      qf[ks] = prow_frag(sm.sq, 16 * ib + li, ks, g);
-      dacc = mfma16(zrow_frag(sm.sz, zrow, ks, g), qf[ks], dacc);
+      qf[ks] = prow(sq_ib, ks);
+      const bf16* zp = sm.sz + o_z + 32 * ks;
+      dacc = mfma16(cat4(lds4(zp), lds4(zp + 16)), qf[ks], dacc);
     }
     f32x4 o[OCT];
 #pragma unroll
@@ -449,7 +518,7 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
       auto weights = [&](int jb) {
         f32x4 t = zero4();
 #pragma unroll
-        for (int ks = 0; ks < FR / 32; ++ks) t = mfma16(prow_frag(sm.sk, 16 * jb + li, ks, g), qf[ks], t);
+        for (int ks = 0; ks < FR / 32; ++ks) t = mfma16(prow(sm.sk + 16 * jb * FR, ks), qf[ks], t);
         if (jb == ib) {  // wave-uniform: only the diagonal block is masked
 #pragma unroll
           for (int r = 0; r < 4; ++r) t[r] = 4 * g + r > li ? 0.f : t[r];
@@ -468,9 +537,8 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
         dacc = mfma16(ones_rows, bv, dacc);
 #pragma unroll
         for (int c = 0; c < OCT; ++c) {
-          const int ct = oct0 + c;
-          const bf16x8 av = two ? tr_frag<64>(sm.v[buf], 16 * jb0 + 4 * g, 16 * jb1 + 4 * g, 16 * ct, li)
-                                : tr_frag_lo<64>(sm.v[buf], 16 * jb0 + 4 * g, 16 * ct, li);
+          const bf16* p0 = vb + o_vo[c] + 16 * jb0 * FDV;
+          const bf16x8 av = two ? tr2(p0, p0 + 16 * FDV) : cat4(ds_read_tr4(p0), bf16x4{0, 0, 0, 0});
           o[c] = mfma16(av, bv, o[c]);
         }
       }
@@ -478,8 +546,10 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
 #pragma unroll
     for (int c = 0; c < OCT; ++c)
 #pragma unroll
-      for (int ks = 0; ks < FR / 32; ++ks)
-        o[c] = mfma16(tr_frag<64>(sm.ss, 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * (oct0 + c), li), qf[ks], o[c]);
+      for (int ks = 0; ks < FR / 32; ++ks) {
+        const bf16* p0 = sm.ss + o_so[c] + 32 * ks * FDV;
+        o[c] = mfma16(tr2(p0, p0 + 16 * FDV), qf[ks], o[c]);
+      }
     const float rden = __builtin_amdgcn_rcpf(dacc[0] + dacc[1]);
 #pragma unroll
     for (int c = 0; c < OCT; ++c) out[c] = cvt_bf16x4(o[c] * rden);
@@ -488,14 +558,14 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
     if constexpr (CAUSAL) {
 #pragma unroll
       for (int ks = 0; ks < FC / 32; ++ks) {
-        const int ra = 32 * ks + 8 * g;
-        const bf16x8 a = tr_frag<64>(sm.v[buf], ra, ra + 4, 16 * sct, li);
+        const bf16* kb = sm.sk + 32 * ks * FR;
+        const bf16x8 a = tr2(vb + o_vc[0] + 32 * ks * FDV, vb + o_vc[1] + 32 * ks * FDV);
 #pragma unroll
         for (int i = 0; i < TPW; ++i)
-          sacc[i] = mfma16(a, tr_frag<256>(sm.sk, ra, ra + 4, 16 * (sft0 + i), li), sacc[i]);
+          sacc[i] = mfma16(a, tr2(kb + (o_kc[0] ^ (16 * i)), kb + (o_kc[1] ^ (16 * i))), sacc[i]);
 #pragma unroll
         for (int k = 0; k < ZPW; ++k)
-          zt[k] = mfma16(ones, tr_frag<256>(sm.sk, ra, ra + 4, 16 * (w + FNW * k), li), zt[k]);
+          zt[k] = mfma16(ones, tr2(kb + o_kz[0] + 128 * k, kb + o_kz[1] + 128 * k), zt[k]);
       }
     }
   }
@@ -504,7 +574,6 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
     const int row = last + 16 * ib + li;
 #pragma unroll
     for (int c = 0; c < OCT; ++c) {
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out[c]), orsrc,
                                             (row * FDV + 16 * (oct0 + c) + 4 * g) * 2, 0, kStreamStore);
     }
