@@ -342,8 +342,8 @@ __device__ __forceinline__ bf16x8 tr2(const bf16* p0, const bf16* p1) { return c
 // full-sequence sums otherwise).  Per chunk: stage raw Q, K, V (double
 // buffered) -> barrier -> feature tiles of phi(Q), phi(K) (wave w: features
 // 32 w .. +31 of every token) and the carried state -> LDS -> barrier ->
-// outputs, then the state carry.  Outputs: the two waves w and w + 4 share
-// row block ib = w mod 4 (query tokens 16 ib + li); each forms the row
+// outputs, then the state carry.  Outputs: the two waves w and 7 - w share
+// row block ib = min(w, 7 - w) (query tokens 16 ib + li); each forms the row
 // block's weights and denominator and produces value tiles 2 (w / 4) and
 // 2 (w / 4) + 1.  Carried state: wave w owns value tile w mod 4 and feature
 // tiles 8 (w / 4) .. +7, and z tiles w and w + 8.
@@ -376,7 +376,9 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
   constexpr int OCT = FCT / 2;          // value tiles per wave in the outputs (2)
   const int sct = w % FCT;              // value tile of this wave's carried state tiles
   const int sft0 = TPW * (w / FCT);     // first feature tile of them
-  const int ib = w % 4;                 // output row block
+  // output row block: waves w and w + 4 run on one SIMD, so they take row
+  // blocks b and 3 - b, which balances the causal weight tiles per SIMD
+  const int ib = w < 4 ? w : 7 - w;
   const int oct0 = OCT * (w / 4);       // first output value tile
 
   // Lane offsets (elements) into the LDS tiles, formed once.  Rows 16 apart
@@ -454,31 +456,48 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
     __syncthreads();
 
     // feature tiles: lane (g, li) gets features 16 ft + 4 g + r of token 16 tb + li
-    // (features of tokens past the end are 0 through their -inf bias)
-    const bf16* qraw = sm.qraw[buf];
-    const bf16* kraw = sm.kraw[buf];
+    // (features of tokens past the end are 0 through their -inf bias).  Token
+    // block by token block, both feature tiles of the wave from one read of
+    // the raw rows; the raw rows of block tb + 1 are read before the tiles of
+    // block tb are written, so that the reads do not wait behind the writes.
+    {
+      constexpr int NST = CAUSAL ? 2 : 1;  // streams with features: Q, and K when causal
+      const bf16* const raw[2] = {sm.qraw[buf], sm.kraw[buf]};
+      const float* const nrm[2] = {sm.qn[buf], sm.kn[buf]};
+      bf16* const phi[2] = {sm.sq, sm.sk};
+      bf16x8 xf[2][NST][2];  // [token block parity][stream][k-step]
+      float nb[2][NST];
+      auto read_block = [&](int tb, int p) {
 #pragma unroll
-    for (int j = 0; j < FPW; ++j) {
+        for (int st = 0; st < NST; ++st) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) xf[p][st][ks] = load_frag(raw[st] + 16 * tb * FD + o_raw[ks]);
+          nb[p][st] = nrm[st][16 * tb + li];
+        }
+      };
+      read_block(0, 0);
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        f32x4 pq = zero4(), pk = zero4();
+        const int p = tb & 1;
+        if (tb < 3) read_block(tb + 1, p ^ 1);
+        f32x4 pr[NST][FPW];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          pq = mfma16(om.hi[j][ks], load_frag(qraw + 16 * tb * FD + o_raw[ks]), pq);
-          if constexpr (CAUSAL) pk = mfma16(om.hi[j][ks], load_frag(kraw + 16 * tb * FD + o_raw[ks]), pk);
-        }
-        const float nq = sm.qn[buf][16 * tb + li];
-        bf16x4 hq;
+        for (int st = 0; st < NST; ++st)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hq[r] = static_cast<bf16>(favor_phi(fc, pq[r], nq));
-        sts4(sm.sq + 16 * tb * FR + o_phw[j], hq);
-        if constexpr (CAUSAL) {
-          const float nk = sm.kn[buf][16 * tb + li];
-          bf16x4 hk;
+          for (int j = 0; j < FPW; ++j) {
+            pr[st][j] = zero4();
 #pragma unroll
-          for (int r = 0; r < 4; ++r) hk[r] = static_cast<bf16>(favor_phi(fc, pk[r], nk));
-          sts4(sm.sk + 16 * tb * FR + o_phw[j], hk);
-        }
+            for (int ks = 0; ks < 2; ++ks) pr[st][j] = mfma16(om.hi[j][ks], xf[p][st][ks], pr[st][j]);
+          }
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+          for (int j = 0; j < FPW; ++j) {
+            bf16x4 h;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) h[r] = static_cast<bf16>(favor_phi(fc, pr[st][j][r], nb[p][st]));
+            sts4(phi[st] + 16 * tb * FR + o_phw[j], h);
+          }
       }
     }
     if (CAUSAL || t0 == t_begin) {
