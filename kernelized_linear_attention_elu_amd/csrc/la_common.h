@@ -121,11 +121,16 @@ __device__ __forceinline__ u32x4 pack16<float>(const float* f) {
 // ------------------------------------------------------------------ feature maps
 
 // Pointwise feature maps.  ELU(x)+1 with alpha = 1 is x + 1 for x > 0 and
-// e^x otherwise; the exponential only ever sees non-positive arguments.
+// e^x otherwise, evaluated as max(x + 1, e^-|x|): for x <= 0, e^x >= 1 + x
+// (convexity), so the max is e^x; for x > 0, e^-x < 1 < x + 1.  Four VALU
+// operations (scale with the -|.| input modifiers, exp2, add, max) instead
+// of a compare and a select around both branches, and the exponential only
+// ever sees non-positive arguments.  Near x = 0 the two sides agree to
+// within the exp2's rounding, below the bf16 operands' resolution.
 template <int PHI>
 __device__ __forceinline__ float phi_pointwise(float x) {
   if constexpr (PHI == PHI_ELU1) {
-    return x > 0.f ? x + 1.f : __expf(x);
+    return __builtin_fmaxf(x + 1.f, __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * 1.4426950408889634f));
   } else {
     return x;
   }
