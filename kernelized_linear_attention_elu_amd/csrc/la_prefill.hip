@@ -1460,18 +1460,29 @@ __device__ __forceinline__ void chunk_outputs_gla(const float (&fq)[CF::RBW][CF:
         for (int ks = 0; ks < R / KS; ++ks) qs[ks] = fq[rbi][ks] * __builtin_amdgcn_exp2f(x[ks]);
       }
     };
-    // x = P_i + sum_{x_at < b < ib} T_b: the query scaling for key block
-    // x_at (the diagonal block, taken first, reads x while it is still P_i)
+    // x = P_i + sum_{jb < b < ib} T_b: the query scaling for key block jb.
+    // The key blocks are visited in descending order (the diagonal first,
+    // which reads x while it is still P_i); advance(jb) adds the block totals
+    // T_b for jb < b < ib not yet in x, advance(-1) those for b < ib.
     float x[NQ];
     row_vals(16 * ib + li, x);
-    int x_at = ib - 1;
-    auto advance = [&](int jb) {
-      while (x_at > jb) {
-        float tb[NQ];
-        row_vals(16 * x_at + 15, tb);
+    auto add_block = [&](int b) {
+      float tb[NQ];
+      row_vals(16 * b + 15, tb);
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) x[n] += tb[n];
-        --x_at;
+      for (int n = 0; n < NQ; ++n) x[n] += tb[n];
+    };
+    int x_at = ib - 1;  // loop form: x holds the totals of the blocks above x_at
+    auto advance = [&](int jb) {
+      if constexpr (NQ <= 16) {
+        // each descending step adds exactly one block, T_{jb+1}: a
+        // wave-uniform branch and no loop, so x stays in its registers
+        // (the loop form's merges copied it: 2 % slower at d = 64)
+        if (jb + 1 < RB && jb + 1 < ib) add_block(jb + 1);
+      } else {
+        // at d = 128 the unrolled steps need more registers than the kernel
+        // has (it spilled and ran 1.5x slower); the loop form stays
+        while (x_at > jb) add_block(x_at--);
       }
     };
 
