@@ -402,7 +402,12 @@ const char *la_hip_error_string(void);
 /* Library ABI version (major * 100 + minor). */
 int la_version(void);
 
-/* Event helpers for la_forward_timed (thin wrappers over hipEvent*). */
+/* Event helpers for la_forward_timed (thin wrappers over hipEvent*).  The
+ * events are for timing only: they are created with
+ * hipEventDisableSystemFence, so recording one performs no system-scope
+ * fence (cache write-back and invalidate) and does not slow the kernels that
+ * follow.  Read elapsed times after synchronising the device (or the
+ * stream); the events do not order host-visible memory. */
 la_status la_event_create(void **event);
 la_status la_event_destroy(void *event);
 la_status la_event_elapsed_ms(void *start, void *end, float *ms);

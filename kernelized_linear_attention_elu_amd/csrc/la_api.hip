@@ -475,7 +475,10 @@ const char* la_hip_error_string(void) { return t_last_hip_error; }
 la_status la_event_create(void** event) {
   if (!event) return LA_ERR_NULL;
   hipEvent_t e;
-  if (hipEventCreate(&e) != hipSuccess) return hip_status(hipErrorUnknown);
+  // timing only: no system-scope fence (cache write-back and invalidate)
+  // when the event is recorded, so that recording it does not slow the
+  // kernels that follow; elapsed times stay valid after a device sync
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return hip_status(hipErrorUnknown);
   *event = e;
   return LA_OK;
 }
