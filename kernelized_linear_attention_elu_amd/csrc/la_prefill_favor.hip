@@ -56,7 +56,6 @@ constexpr int FLQ = FVQ / FNT;            // ... per thread
 static_assert(FVQ % FNT == 0 && FDV == FD, "raw chunk tiles are 64 x 64 bf16");
 
 using T64 = Tile<bf16, 64>;
-using T256 = Tile<bf16, 256>;
 
 // exp2 argument constants of phi: log2(e) d^(-1/4), log2(e) / (2 sqrt(d)),
 // and log2(sqrt(r)).
