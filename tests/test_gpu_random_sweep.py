@@ -1,7 +1,8 @@
 """Seeded random sweep over the prefill and backward entry points against
 the fp64 oracle: plain causal and non-causal (bf16 and fp32), fixed decay,
 per-token gates, per-channel gates, FAVOR+ and the backward, each at a
-random size (B <= 2, H <= 3, N < 700), dimension, chunk and span split.
+random size (B <= 2, H <= 3, N < 700), dimension, chunk and span split;
+and single decode steps of every kind from random states.
 Outputs use the tolerance rule of the other parity tests; final states
 (fp32 sums over up to 700 tokens) are bounded as in the fp32 tiny test,
 rtol 1e-5 + atol 1e-4, and by the bf16 rule for bf16 I/O."""
@@ -21,7 +22,7 @@ from tests.test_gpu_gla import FLOOR
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ["plain", "plain", "noncausal", "decay", "gated", "gla", "favor", "backward"]
+KINDS = ["plain", "plain", "noncausal", "decay", "gated", "gla", "favor", "backward", "decode"]
 
 
 def _check_state(got, ref, io, what):
@@ -35,6 +36,8 @@ def _case(lib, rng, om, monkeypatch):
     import torch
     pick = lambda xs: xs[int(rng.integers(0, len(xs)))]
     kind = pick(KINDS)
+    if kind == "decode":
+        return _decode_case(lib, rng, pick)
     B, H, N = int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 700))
     io, d, chunk = "bf16", 64, 64
     if kind in ("plain", "noncausal", "decay", "gated"):
@@ -93,6 +96,45 @@ def _case(lib, rng, om, monkeypatch):
         torch.cuda.synchronize()
         for nm, gt, rf, sc in zip(("dQ", "dK", "dV"), grads, bwd.grad_causal(q, k, v, dO), tb._scales(q, k, v, dO)):
             tb._check(to_host(gt), rf, sc, f"{what} {nm}")
+
+
+def _decode_case(lib, rng, pick):
+    """One decode step (plain, FAVOR+, decay, gated, per-channel gated) from
+    a random state: o, S', z' against the oracle's step."""
+    import torch
+    sub = pick(["plain", "plain", "favor", "decay", "gated", "gla"])
+    B, H = int(rng.integers(1, 65)), int(rng.integers(1, 9))
+    d = pick([64, 128])
+    io = pick(["bf16", "f32"]) if sub == "plain" else "bf16"
+    seed = int(rng.integers(0, 2**31))
+    what = f"decode {sub} B{B} H{H} d{d} {io} seed {seed}"
+    phi, om = ("favor", synth.draw_omega(256, d)) if sub == "favor" else ("elu1", None)
+    r = 256 if sub == "favor" else d
+    g = np.random.default_rng(seed)
+    S = g.standard_normal((B, H, r, d)).astype(np.float32)
+    z = g.uniform(1.0, 100.0, (B, H, r)).astype(np.float32)
+    q, k, v = (np.ascontiguousarray(x[:, :, 0]) for x in synth.draw_qkv(B, H, 1, d, d, seed=seed + 1, io=io))
+    kw = {}
+    if sub == "decay":
+        gam = (np.float32(1.0) - np.float32(2.0) ** (-g.uniform(3, 10, size=H)).astype(np.float32)).astype(np.float32)
+        kw["gamma"] = f32_dev(gam)
+        ref = dec.decode_step_decay(S, z, q, k, v, gam.astype(np.float64))
+    elif sub == "gated":
+        log_a = synth.draw_log_gates(B, H, 1, seed=seed + 2)[:, :, 0]
+        kw["log_gate"] = f32_dev(np.ascontiguousarray(log_a))
+        ref = gat.decode_step_gated(S, z, q, k, v, np.exp(log_a.astype(np.float64)))
+    elif sub == "gla":
+        log_a = synth.draw_log_gates_ch(B, H, 1, d, seed=seed + 3)[:, :, 0]
+        kw["log_gate_ch"] = f32_dev(np.ascontiguousarray(log_a))
+        ref = glo.decode_step_gla(S, z, q, k, v, np.maximum(np.exp(log_a.astype(np.float64)), FLOOR))
+    else:
+        ref = ora.decode_step(S, z, q, k, v, phi=phi, omega=om)
+    o, S1, z1 = lib.decode_step(f32_dev(S), f32_dev(z), to_dev(q, io), to_dev(k, io), to_dev(v, io), phi=phi,
+                                omega=f32_dev(om) if om is not None else None, inplace=False, **kw)
+    torch.cuda.synchronize()
+    check_close(to_host(o), ref[0], io, what + " o")
+    _check_state(to_host(S1), ref[1], "f32", what + " S'")
+    _check_state(to_host(z1), ref[2], "f32", what + " z'")
 
 
 @pytest.mark.parametrize("seed", [101, 202, 303])
