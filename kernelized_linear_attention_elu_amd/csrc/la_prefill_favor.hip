@@ -328,6 +328,7 @@ struct SmemOutFavor {
   bf16 sk[FC * FR];   // phi(K) of the chunk
   bf16 ss[FR * FDV];  // carried S, [feature][value] (st_off)
   bf16 sz[3 * FZS];   // carried z as rows: bf16 hi, lo = z - hi, zeros
+  bf16 so[FC * FDV];  // the chunk's outputs, [token][value] (T64), for whole-row stores
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -430,29 +431,39 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
   const bf16 o1 = r4 == 0 ? one : zero;
   const bf16x8 ones_rows = bf16x8{o1, o1, o1, o1, o1, o1, o1, o1};  // rows 4m of the ones operand
 
+  // A chunk's outputs go through the LDS tile so and leave, after the next
+  // chunk's first barrier, as whole rows: thread t stores 16 bytes of row
+  // t / 8 (two waves produce each row).  One store per thread and iteration
+  // (the first one, and one in the prologue, aimed past the buffer, where the
+  // hardware drops them), issued after the prefetch, so that at the loop
+  // head the memory operations outstanding are the same on every path and
+  // the staging's counter wait covers the prefetched loads only.
+  const int srow = tid >> 3, scol = 8 * (tid & 7);
+  int o_or = T64::off(srow, scol);                             // row reads of so
+  int o_ow = T64::off(16 * ib + li, 16 * oct0 + 4 * g);         // writes of so (value tile oct0 + c: XOR 16 c)
+  auto store_rows = [&](int t, bool real) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(sm.so + o_or);
+    __builtin_amdgcn_raw_buffer_store_b128(x, orsrc, real ? ((t + srow) * FDV + scol) * 2 : kDropOffset, 0,
+                                           kStreamStore);
+  };
   RawRegs<3> rr;
   load_raw<3>(rr, src, t_begin);
-  bf16x4 out[OCT];
+  mem_order_fence();
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, orsrc, kDropOffset, 0, kStreamStore);
   int buf = 0;
   for (int t0 = t_begin; t0 < t_end; t0 += FC, buf ^= 1) {
-    // the 16 XORed offsets of the state carry are formed in the loop rather
-    // than kept live across it (registers are tight at two waves per SIMD)
-    asm volatile("" : "+v"(o_kc[0]), "+v"(o_kc[1]));
+    // the XORed offsets of the state carry and the output tile are formed in
+    // the loop rather than kept live across it (registers are tight at two
+    // waves per SIMD)
+    asm volatile("" : "+v"(o_kc[0]), "+v"(o_kc[1]), "+v"(o_or), "+v"(o_ow));
     {
       bf16* const dst[3] = {sm.qraw[buf], sm.kraw[buf], sm.v[buf]};
       float* const nrm[3] = {sm.qn[buf], sm.kn[buf], nullptr};
       stage_raw<3>(rr, dst, nrm, CAUSAL ? 3 : 1, 2, N - t0);
     }
-    if (t0 != t_begin) {
-      const int row = t0 - FC + 16 * ib + li;
-#pragma unroll
-      for (int c = 0; c < OCT; ++c) {
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out[c]), orsrc,
-                                              (row * FDV + 16 * (oct0 + c) + 4 * g) * 2, 0, kStreamStore);
-      }
-    }
     if (t0 + FC < t_end) load_raw<3>(rr, src, t0 + FC);
     __syncthreads();
+    store_rows(t0 - FC, t0 != t_begin);  // the previous chunk's outputs (rows past N are dropped)
 
     // feature tiles: lane (g, li) gets features 16 ft + 4 g + r of token 16 tb + li
     // (features of tokens past the end are 0 through their -inf bias).  Token
@@ -570,7 +581,7 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
       }
     const float rden = __builtin_amdgcn_rcpf(dacc[0] + dacc[1]);
 #pragma unroll
-    for (int c = 0; c < OCT; ++c) out[c] = cvt_bf16x4(o[c] * rden);
+    for (int c = 0; c < OCT; ++c) sts4(sm.so + (o_ow ^ (16 * c)), cvt_bf16x4(o[c] * rden));
 
     // ---- state carry: S += phi(K_c)^T V_c, z += phi(K_c)^T 1 (bf16 features)
     if constexpr (CAUSAL) {
@@ -588,13 +599,8 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
     }
   }
   if (t_end > t_begin) {
-    const int last = t_begin + ((t_end - t_begin - 1) / FC) * FC;
-    const int row = last + 16 * ib + li;
-#pragma unroll
-    for (int c = 0; c < OCT; ++c) {
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out[c]), orsrc,
-                                            (row * FDV + 16 * (oct0 + c) + 4 * g) * 2, 0, kStreamStore);
-    }
+    __syncthreads();
+    store_rows(t_begin + ((t_end - t_begin - 1) / FC) * FC, true);
   }
 }
 
