@@ -22,8 +22,8 @@
 //                            The projection tiles come out of the MFMA with
 //                            tokens along the k-slot direction, so they feed
 //                            the state MFMA directly as bf16 hi + lo
-//                            operands (no LDS round trip); dz is summed from
-//                            the fp32 features.
+//                            operands (no LDS round trip); dz comes from a
+//                            ones operand against the same fragments.
 //   la_output_favor_kernel - per span, chunk by chunk: phi(Q), phi(K) tiles
 //                            -> LDS, then the masked intra-chunk product,
 //                            read-out of the carried state and divide, and
@@ -211,14 +211,18 @@ __global__ __launch_bounds__(FNT, 1) void la_state_favor_kernel(const bf16* __re
   OmegaFrags<true> om;
   om.load(omega, w, g, li);
 
-  f32x4 acc[FPW][FCT];
-  float zacc[FPW];
+  // dz on the MFMA as well (a ones operand against the same hi + lo feature
+  // fragments), off the VALU, which the features keep busy: lane (g, li) of
+  // zt[j] ends with the sum over the span of feature 16 (FPW w + j) + li
+  f32x4 acc[FPW][FCT], zt[FPW];
 #pragma unroll
   for (int j = 0; j < FPW; ++j) {
-    zacc[j] = 0.f;
+    zt[j] = zero4();
 #pragma unroll
     for (int ct = 0; ct < FCT; ++ct) acc[j][ct] = zero4();
   }
+  const bf16 one = static_cast<bf16>(1.0f);
+  const bf16x8 ones = bf16x8{one, one, one, one, one, one, one, one};
 
   RawRegs<2> rr;
   load_raw<2>(rr, src, t_begin);
@@ -254,7 +258,6 @@ __global__ __launch_bounds__(FNT, 1) void la_state_favor_kernel(const bf16* __re
           const bf16 h = static_cast<bf16>(f);
           ph[tb][r] = h;
           pl[tb][r] = static_cast<bf16>(f - static_cast<float>(h));
-          zacc[j] += f;
         }
       }
 #pragma unroll
@@ -266,6 +269,8 @@ __global__ __launch_bounds__(FNT, 1) void la_state_favor_kernel(const bf16* __re
           acc[j][ct] = mfma16(va[kp][ct], bh8, acc[j][ct]);
           acc[j][ct] = mfma16(va[kp][ct], bl8, acc[j][ct]);
         }
+        zt[j] = mfma16(ones, bh8, zt[j]);
+        zt[j] = mfma16(ones, bl8, zt[j]);
       }
     }
   }
@@ -276,8 +281,7 @@ __global__ __launch_bounds__(FNT, 1) void la_state_favor_kernel(const bf16* __re
     const int f = 16 * (FPW * w + j) + li;
 #pragma unroll
     for (int ct = 0; ct < FCT; ++ct) *reinterpret_cast<f32x4*>(slot + f * FDV + 16 * ct + 4 * g) = acc[j][ct];
-    const float zs = xor_sum16_32(zacc[j]);
-    if (g == 0) slot[FR * FDV + f] = zs;
+    if (g == 0) slot[FR * FDV + f] = zt[j][0];
   }
 }
 
