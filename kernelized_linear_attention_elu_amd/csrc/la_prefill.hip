@@ -970,30 +970,40 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
 
   // two chunks of loads in flight: chunk c+2 is requested as soon as chunk
   // c has been staged (LDS double buffering, one barrier per chunk).  Every
-  // load is issued unconditionally (past the span's last chunk it re-reads
-  // that chunk, from L2), so that no loop path differs in the number of
-  // memory operations and the counter waits stay exact.
-  const int last = t_end > t_begin ? t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C : t_begin;
+  // load is issued unconditionally (past the span's end it re-reads the
+  // chunk read last, from L2), so that no loop path differs in the number
+  // of memory operations and the counter waits stay exact.
+  // Order: with a decay the running sum is aged chunk by chunk, so the
+  // chunks go first to last.  Without one the order is free and they go
+  // last to first: the chunks this kernel reads last are then each span's
+  // first ones, which la_output_kernel, walking its spans forward, reads
+  // first, while they are the likeliest to still sit in the memory-side
+  // cache.
+  const int nch = (t_end - t_begin + CF::C - 1) / CF::C;
+  auto chunk_t0 = [&](int k) {
+    k = min(k, max(nch - 1, 0));
+    return t_begin + (DECAY ? k : max(nch - 1 - k, 0)) * CF::C;
+  };
   ChunkRegs<CF, false> ca, cb;
-  load_chunk<CF, false, GATED>(ca, hb, t_begin);
+  load_chunk<CF, false, GATED>(ca, hb, chunk_t0(0));
   mem_order_fence();  // ca's loads first, as in the loop: exact counter waits
-  load_chunk<CF, false, GATED>(cb, hb, min(t_begin + CF::C, last));
+  load_chunk<CF, false, GATED>(cb, hb, chunk_t0(1));
   int buf = 0;
-  for (int t0 = t_begin; t0 < t_end; t0 += 2 * CF::C) {
+  for (int k = 0; k < nch; k += 2) {
     OP* lo = sizeof(OP) == 2 ? sm.k_lo[buf] : nullptr;
-    const int len_a = min(CF::C, t_end - t0);
-    const float l2a = stage_chunk<CF, false, DK>(ca, nullptr, sm.k[buf], lo, sm.v[buf], t0, N, lg, len_a);
-    load_chunk<CF, false, GATED>(ca, hb, min(t0 + 2 * CF::C, last));
+    const int ta = chunk_t0(k);
+    const float l2a = stage_chunk<CF, false, DK>(ca, nullptr, sm.k[buf], lo, sm.v[buf], ta, N, lg, min(CF::C, t_end - ta));
+    load_chunk<CF, false, GATED>(ca, hb, chunk_t0(k + 2));
     __syncthreads();
     age(l2a);
     state_mfma<CF>(acc, zt, sm.k[buf], lo, sm.v[buf], w, g, li);
     buf ^= 1;
-    const bool second = t0 + CF::C < t_end;  // workgroup-uniform
-    const int len_b = min(CF::C, t_end - t0 - CF::C);
+    const bool second = k + 1 < nch;  // workgroup-uniform
+    const int tb = chunk_t0(k + 1);
     lo = sizeof(OP) == 2 ? sm.k_lo[buf] : nullptr;
     float l2b = 0.f;
-    if (second) l2b = stage_chunk<CF, false, DK>(cb, nullptr, sm.k[buf], lo, sm.v[buf], t0 + CF::C, N, lg, len_b);
-    load_chunk<CF, false, GATED>(cb, hb, min(t0 + 3 * CF::C, last));
+    if (second) l2b = stage_chunk<CF, false, DK>(cb, nullptr, sm.k[buf], lo, sm.v[buf], tb, N, lg, min(CF::C, t_end - tb));
+    load_chunk<CF, false, GATED>(cb, hb, chunk_t0(k + 3));
     if (second) {
       __syncthreads();
       age(l2b);
