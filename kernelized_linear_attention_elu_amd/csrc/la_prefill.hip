@@ -223,13 +223,16 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<CF, WITH_Q>& cr, const Head
 // gates, which wave 0 also writes to scum[0 .. max(C, 64)) when scum is
 // given).  The weighted features go to sk (and sk_lo) when skw is null,
 // otherwise sk keeps the plain features and skw receives the weighted ones.
+// A non-zero after (log2, at most 0) multiplies every key weight by 2^after:
+// the decay from the chunk's end to a later reference token.
 // Returns the log2 of the chunk's whole decay over its len tokens (what a
 // state carried across the chunk is multiplied by), 0 without a decay.
 template <class CF, bool WITH_Q, int DK = kNoDecay>
 __device__ __forceinline__ float stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typename CF::OP* sq,
                                              typename CF::OP* sk, typename CF::OP* sk_lo,
                                              typename CF::OP* sv, int t0, int N, float lg = 0.f, int len = 0,
-                                             typename CF::OP* skw = nullptr, float* scum = nullptr) {
+                                             typename CF::OP* skw = nullptr, float* scum = nullptr,
+                                             float after = 0.f) {
   using T = typename CF::IO;
   using OP = typename CF::OP;
   using TQ = Tile<OP, CF::R>;
@@ -273,7 +276,7 @@ __device__ __forceinline__ float stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, ty
         // (keys past len, beyond N, may get a weight above one; they are
         // zeroed below by selection, never by arithmetic)
         const float wgt =
-            __builtin_amdgcn_exp2f(DK == kFixed ? lg * (float)(len - 1 - tok) : total - gc.at(tok));
+            __builtin_amdgcn_exp2f((DK == kFixed ? lg * (float)(len - 1 - tok) : total - gc.at(tok)) + after);
         if (skw) {
           float fw[CF::EPL];
 #pragma unroll
@@ -938,7 +941,7 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
                                                             const float* __restrict__ log_a,
                                                             float* __restrict__ totals) {
   using OP = typename CF::OP;
-  constexpr bool DECAY = DK != kNoDecay, GATED = DK == kGated;
+  constexpr bool GATED = DK == kGated;
   __shared__ SmemState<CF> sm;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
   const int bh = blockIdx.x / n_span;
@@ -948,7 +951,10 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
   HeadBufs hb = head_bufs<CF>(nullptr, K, V, nullptr, bh, N);
   if constexpr (GATED) hb.a = make_rsrc(log_a + (size_t)bh * N, (unsigned)N * 4u);
   const float lg = DK == kFixed ? __builtin_amdgcn_logf(gamma[bh % H]) : 0.f;  // log2(gamma)
-  float span_l2 = 0.f;  // gated: the span's total log2 gate so far
+  // with a decay: the log2 decay from the end of the chunk being staged to
+  // the span's end (the chunks already summed lie after it); at the loop's
+  // end, the span's whole log2 decay
+  float after = 0.f;
 
   f32x4 acc[CF::TPW];
 #pragma unroll
@@ -956,34 +962,19 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
   f32x4 zt[CF::ZPW];
 #pragma unroll
   for (int k = 0; k < CF::ZPW; ++k) zt[k] = zero4();
-  // decay of the running sum over a chunk whose whole log2 decay is l2
-  auto age = [&](float l2) {
-    if constexpr (DECAY) {
-      span_l2 += l2;
-      const float dg = __builtin_amdgcn_exp2f(l2);
-#pragma unroll
-      for (int i = 0; i < CF::TPW; ++i) acc[i] *= dg;
-#pragma unroll
-      for (int k = 0; k < CF::ZPW; ++k) zt[k] *= dg;
-    }
-  };
 
   // two chunks of loads in flight: chunk c+2 is requested as soon as chunk
   // c has been staged (LDS double buffering, one barrier per chunk).  Every
   // load is issued unconditionally (past the span's end it re-reads the
   // chunk read last, from L2), so that no loop path differs in the number
   // of memory operations and the counter waits stay exact.
-  // Order: with a decay the running sum is aged chunk by chunk, so the
-  // chunks go first to last.  Without one the order is free and they go
-  // last to first: the chunks this kernel reads last are then each span's
-  // first ones, which la_output_kernel, walking its spans forward, reads
-  // first, while they are the likeliest to still sit in the memory-side
-  // cache.
+  // Order: last chunk to first.  The chunks this kernel reads last are then
+  // each span's first ones, which la_output_kernel, walking its spans
+  // forward, reads first, while they are the likeliest to still sit in the
+  // memory-side cache.  A decay is applied to each chunk's key weights (its
+  // decay to the span's end, after), so no running sum is rescaled.
   const int nch = (t_end - t_begin + CF::C - 1) / CF::C;
-  auto chunk_t0 = [&](int k) {
-    k = min(k, max(nch - 1, 0));
-    return t_begin + (DECAY ? k : max(nch - 1 - k, 0)) * CF::C;
-  };
+  auto chunk_t0 = [&](int k) { return t_begin + max(nch - 1 - k, 0) * CF::C; };
   ChunkRegs<CF, false> ca, cb;
   load_chunk<CF, false, GATED>(ca, hb, chunk_t0(0));
   mem_order_fence();  // ca's loads first, as in the loop: exact counter waits
@@ -992,27 +983,27 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
   for (int k = 0; k < nch; k += 2) {
     OP* lo = sizeof(OP) == 2 ? sm.k_lo[buf] : nullptr;
     const int ta = chunk_t0(k);
-    const float l2a = stage_chunk<CF, false, DK>(ca, nullptr, sm.k[buf], lo, sm.v[buf], ta, N, lg, min(CF::C, t_end - ta));
+    after += stage_chunk<CF, false, DK>(ca, nullptr, sm.k[buf], lo, sm.v[buf], ta, N, lg, min(CF::C, t_end - ta),
+                                        nullptr, nullptr, after);
     load_chunk<CF, false, GATED>(ca, hb, chunk_t0(k + 2));
     __syncthreads();
-    age(l2a);
     state_mfma<CF>(acc, zt, sm.k[buf], lo, sm.v[buf], w, g, li);
     buf ^= 1;
     const bool second = k + 1 < nch;  // workgroup-uniform
     const int tb = chunk_t0(k + 1);
     lo = sizeof(OP) == 2 ? sm.k_lo[buf] : nullptr;
-    float l2b = 0.f;
-    if (second) l2b = stage_chunk<CF, false, DK>(cb, nullptr, sm.k[buf], lo, sm.v[buf], tb, N, lg, min(CF::C, t_end - tb));
+    if (second)
+      after += stage_chunk<CF, false, DK>(cb, nullptr, sm.k[buf], lo, sm.v[buf], tb, N, lg, min(CF::C, t_end - tb),
+                                          nullptr, nullptr, after);
     load_chunk<CF, false, GATED>(cb, hb, chunk_t0(k + 3));
     if (second) {
       __syncthreads();
-      age(l2b);
       state_mfma<CF>(acc, zt, sm.k[buf], lo, sm.v[buf], w, g, li);
       buf ^= 1;
     }
   }
   if constexpr (GATED) {
-    if (tid == 0) totals[(size_t)bh * n_span + s] = span_l2;
+    if (tid == 0) totals[(size_t)bh * n_span + s] = after;
   }
 
   constexpr int E = CF::R * CF::DV + CF::R;
