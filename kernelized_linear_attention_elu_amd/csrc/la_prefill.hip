@@ -1331,11 +1331,15 @@ __device__ __forceinline__ void stage_values(const ChunkRegs<CF, false>& cr, typ
 //         with skw_lo its bf16 rounding residual too)
 //   OUT:  skd0 phi(k_j) 2^(-P_j), skd1 phi(k_j) 2^(M_jb - P_j) (same-block
 //         weights of rows 0..7 and 8..15), skb phi(k_j) 2^(T_jb - P_j).
+// With base given, skw's weights also carry 2^base[e] for this thread's
+// channels col + e (its channels are the same for every unit it stages): a
+// decay from the chunk's end to a later reference token, per channel.
 // Keys at or beyond N get zero features.
 template <class CF, bool OUT>
 __device__ __forceinline__ void gla_stage_keys(const ChunkRegs<CF, false>& cr, const float* sp,
                                                typename CF::OP* skd0, typename CF::OP* skd1, typename CF::OP* skb,
-                                               typename CF::OP* skw, typename CF::OP* skw_lo, int t0, int N) {
+                                               typename CF::OP* skw, typename CF::OP* skw_lo, int t0, int N,
+                                               const float* base = nullptr) {
   using T = typename CF::IO;
   using OP = typename CF::OP;
   using TQ = Tile<OP, CF::R>;
@@ -1364,7 +1368,7 @@ __device__ __forceinline__ void gla_stage_keys(const ChunkRegs<CF, false>& cr, c
     row(tok, col, pj);
     row(16 * jb + 15, col, tj);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) after[e] = 0.f;
+    for (int e = 0; e < EPL; ++e) after[e] = base ? base[e] : 0.f;
 #pragma unroll
     for (int b = 1; b < RB; ++b) {
       if (b > jb) {
@@ -1656,11 +1660,13 @@ constexpr bool gla_fits() {
   return sizeof(SmemOutGla<CF>) <= 160 * 1024 && sizeof(SmemStateGla<CF>) <= 160 * 1024;
 }
 
-// Per-span state with per-channel gates: the span's sum decayed to its end
-// (key j of a chunk weighted to the chunk's end, the running sum's row f
-// multiplied by the chunk's decay 2^(sum_b T_b)); the span's total log2 gate
-// per channel goes to totals[bh][s][R].  One LDS buffer, three barriers per
-// chunk (the P tile is complete before the keys are weighted).
+// Per-span state with per-channel gates: the span's sum decayed to its end.
+// The chunks go last to first (as in la_state_kernel), and key j of a chunk
+// is weighted by its decay to the span's end: to the chunk's end, times the
+// decay of the chunks already summed, per channel (the thread's running sum
+// of their totals sum_b T_b).  The span's total log2 gate per channel goes
+// to totals[bh][s][R].  One LDS buffer, three barriers per chunk (the P tile
+// is complete before the keys are weighted).
 template <class CF>
 __global__ __launch_bounds__(CF::NT) void la_state_kernel_gla(const typename CF::IO* __restrict__ K,
                                                                 const typename CF::IO* __restrict__ V,
@@ -1684,30 +1690,44 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel_gla(const typename CF:
 #pragma unroll
   for (int k = 0; k < CF::ZPW; ++k) zt[k] = zero4();
   float span_l2 = 0.f;  // row 16 w + li: the span's total log2 gate so far
+  // this thread's staging channels col .. col + EPL - 1: the log2 decay of
+  // the chunks already summed (the decay from the next chunk's end to the
+  // span's end)
+  using TP = Tile<float, CF::R>;
+  static_assert(CF::NT % (CF::D / CF::EPL) == 0, "a thread stages the same channels in every unit");
+  const int col = (tid % (CF::D / CF::EPL)) * CF::EPL;
+  float base[CF::EPL];
+#pragma unroll
+  for (int e = 0; e < CF::EPL; ++e) base[e] = 0.f;
 
-  const int last = t_end > t_begin ? t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C : t_begin;
+  const int nch = (t_end - t_begin + CF::C - 1) / CF::C;
+  auto chunk_t0 = [&](int k) { return t_begin + max(nch - 1 - k, 0) * CF::C; };
   ChunkRegs<CF, false> cr;
   GateRegsGla<CF> gr;
-  load_gates_gla<CF>(gr, hb.a, t_begin);
-  load_chunk<CF, false>(cr, hb, t_begin);
+  load_gates_gla<CF>(gr, hb.a, chunk_t0(0));
+  load_chunk<CF, false>(cr, hb, chunk_t0(0));
   OP* lo = sizeof(OP) == 2 ? sm.kw_lo : nullptr;
-  for (int t0 = t_begin; t0 < t_end; t0 += CF::C) {
+  for (int k = 0; k < nch; ++k) {
+    const int t0 = chunk_t0(k);
     __syncthreads();  // the previous chunk's MFMA work is done with kw, v
     gla_prefix_to_lds<CF>(gr, sm.p);
     stage_values<CF>(cr, sm.v);
     __syncthreads();
-    gla_stage_keys<CF, false>(cr, sm.p, nullptr, nullptr, nullptr, sm.kw, lo, t0, N);
-    const float l2 = gla_chunk_l2<CF>(sm.p, w, li);
-    const int tn = min(t0 + CF::C, last);
+    gla_stage_keys<CF, false>(cr, sm.p, nullptr, nullptr, nullptr, sm.kw, lo, t0, N, base);
+    span_l2 += gla_chunk_l2<CF>(sm.p, w, li);
+#pragma unroll
+    for (int b = 0; b < CF::RB; ++b) {
+#pragma unroll
+      for (int e4 = 0; e4 < CF::EPL / 4; ++e4) {
+        const f32x4 tb = *reinterpret_cast<const f32x4*>(sm.p + TP::off(16 * b + 15, col + 4 * e4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) base[4 * e4 + e] += tb[e];
+      }
+    }
+    const int tn = chunk_t0(k + 1);
     load_gates_gla<CF>(gr, hb.a, tn);
     load_chunk<CF, false>(cr, hb, tn);
     __syncthreads();
-    span_l2 += l2;
-    const float dg = __builtin_amdgcn_exp2f(l2);
-#pragma unroll
-    for (int i = 0; i < CF::TPW; ++i) acc[i] *= dg;
-#pragma unroll
-    for (int k = 0; k < CF::ZPW; ++k) zt[k] *= dg;
     state_mfma<CF>(acc, zt, sm.kw, lo, sm.v, w, g, li);
   }
 
