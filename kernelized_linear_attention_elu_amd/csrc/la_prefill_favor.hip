@@ -224,16 +224,21 @@ __global__ __launch_bounds__(FNT, 1) void la_state_favor_kernel(const bf16* __re
   const bf16 one = static_cast<bf16>(1.0f);
   const bf16x8 ones = bf16x8{one, one, one, one, one, one, one, one};
 
+  // the span's chunks last to first: the output pass, walking its spans
+  // forward, then starts on the chunks read last, the likeliest to still
+  // sit in the memory-side cache
+  const int nch = (t_end - t_begin + FC - 1) / FC;
   RawRegs<2> rr;
-  load_raw<2>(rr, src, t_begin);
+  load_raw<2>(rr, src, t_begin + max(nch - 1, 0) * FC);
   int buf = 0;
-  for (int t0 = t_begin; t0 < t_end; t0 += FC, buf ^= 1) {
+  for (int k = 0; k < nch; ++k, buf ^= 1) {
+    const int t0 = t_begin + (nch - 1 - k) * FC;
     {
       bf16* const dst[2] = {kraw[buf], vt[buf]};
       float* const nrm[2] = {kn[buf], nullptr};
       stage_raw<2>(rr, dst, nrm, 1, 1, N - t0);
     }
-    if (t0 + FC < t_end) load_raw<2>(rr, src, t0 + FC);
+    if (k + 1 < nch) load_raw<2>(rr, src, t0 - FC);
     __syncthreads();
 
     // V^T fragments (A operands): k-slots 0-3 = tokens 32 kp + 4 g + r,
