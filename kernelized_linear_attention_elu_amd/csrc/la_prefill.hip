@@ -2154,16 +2154,24 @@ __global__ __launch_bounds__(CF::NT) void la_bwd_rsum_kernel(const bf16* __restr
 #pragma unroll
   for (int i = 0; i < CF::TPW; ++i) racc[i] = zero4();
   f32x4 ut[1] = {zero4()};
-  for (int t0 = t_begin; t0 < t_end; t0 += CF::C) {
-    ChunkRegs<CF, false> cr;
+  // one chunk ahead: chunk c+1's Q, dO and (D, h) loads are issued once
+  // chunk c is staged and run under its MFMA work
+  const int nch = (t_end - t_begin + CF::C - 1) / CF::C;
+  auto chunk_t0 = [&](int k) { return t_begin + k * CF::C; };
+  ChunkRegs<CF, false> cr;
+  float rd[CF::LV], hl = 0.f;
+  auto load = [&](int t0) {
     load_chunk<CF, false>(cr, hb, t0);
-    float rd[CF::LV];
 #pragma unroll
     for (int i = 0; i < CF::LV; ++i) {
       const int tok = (tid + i * CF::NT) / VVR;
       rd[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dh, (t0 + tok) * 8, 0, 0));
     }
-    const float hl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dh, (t0 + l) * 8 + 4, 0, 0));
+    hl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_dh, (t0 + l) * 8 + 4, 0, 0));
+  };
+  if (nch > 0) load(chunk_t0(0));
+  for (int k = 0; k < nch; ++k) {
+    const int t0 = chunk_t0(k);
     __syncthreads();  // the previous chunk's MFMA work is done with the tiles
     // phi(Q) (zero beyond N, as keys are) and G = dO / D
     stage_chunk<CF, false>(cr, nullptr, sm.q, nullptr, sm.gt, t0, N);
@@ -2179,6 +2187,7 @@ __global__ __launch_bounds__(CF::NT) void la_bwd_rsum_kernel(const bf16* __restr
       *reinterpret_cast<u32x4*>(sm.gt + TV::off(tok, (vi % VVR) * 8)) = pack16<bf16>(f);
     }
     if (w == 0 && l < CF::C) sm.h[l] = t0 + l < N ? hl : 0.f;
+    if (k + 1 < nch) load(chunk_t0(k + 1));
     __syncthreads();
     state_mfma_w<CF>(racc, ut, sm.q, sm.gt, sm.h, w, g, li);
   }
