@@ -1956,21 +1956,27 @@ __global__ __launch_bounds__(CF::NT, CF::NW == 8 ? 1 : 2) void la_bwd_dq_kernel(
   OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
 
   // four waves: chunk c+1 is loaded into registers while chunk c is
-  // computed; eight (d = 128) have no registers to spare for it and load
-  // each chunk at the top of its iteration
+  // computed; eight (d = 128) have registers to spare for chunk c+1's K and
+  // V only, and load its Q, O and dO rows at the top of its iteration
   constexpr bool PREFETCH = CF::NW == 4;
   const int last = t_end > t_begin ? t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C : t_begin;
   ChunkRegs<CF, false> cr;
   QRegs<CF> qr, orr, dor;
-  auto load_all = [&](int tc) {
-    load_chunk<CF, false>(cr, hb, tc);
+  auto load_rows = [&](int tc) {
     qr.load(hb.q, tc, w, g, li);
     orr.load(r_o, tc, w, g, li);
     dor.load(r_do, tc, w, g, li);
   };
-  if constexpr (PREFETCH) load_all(t_begin);
+  auto load_all = [&](int tc) {
+    load_chunk<CF, false>(cr, hb, tc);
+    load_rows(tc);
+  };
+  if constexpr (PREFETCH)
+    load_all(t_begin);
+  else
+    load_chunk<CF, false>(cr, hb, t_begin);
   for (int t0 = t_begin; t0 < t_end; t0 += CF::C) {
-    if constexpr (!PREFETCH) load_all(t0);
+    if constexpr (!PREFETCH) load_rows(t0);
     __syncthreads();  // every wave is done with the previous chunk's tiles
     publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
     stage_chunk<CF, false>(cr, nullptr, sm.k, nullptr, sm.v, t0, N);
@@ -1985,7 +1991,11 @@ __global__ __launch_bounds__(CF::NT, CF::NW == 8 ? 1 : 2) void la_bwd_dq_kernel(
       for (int ks = 0; ks < R / KS; ++ks)
         *reinterpret_cast<bf16x8*>(sm.q + TQ::off(16 * ib + li, 32 * ks + 8 * g)) = qf[0][ks];
     }
-    if constexpr (PREFETCH) load_all(min(t0 + CF::C, last));  // (past the span's last chunk: re-read, unused)
+    // (past the span's last chunk: re-read, unused)
+    if constexpr (PREFETCH)
+      load_all(min(t0 + CF::C, last));
+    else
+      load_chunk<CF, false>(cr, hb, min(t0 + CF::C, last));
     __syncthreads();
 
     // 1. D_i: the masked weights' row sums (bf16 weights, as the forward)
