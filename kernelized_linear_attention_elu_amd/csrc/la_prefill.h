@@ -77,10 +77,12 @@ hipError_t favor_prefill_launch(const PrefillArgs& a);
 // (gamma, H heads), a span of L tokens multiplies the running state by
 // gamma^L; span lengths follow from N, the chunk and n_span.  With gates
 // (totals: [BH][n_span] total log2 gate of each span), span s multiplies it
-// by 2^totals[s].
+// by 2^totals[s].  total_only (no decay or gates): only the total, slot
+// n_span, is written (what the non-causal form reads).
 hipError_t scan_launch(float* ws, int BH, int R, int DV, int n_span, const float* S0, const float* z0,
                        float* S_out, float* z_out, hipStream_t stream, const float* gamma = nullptr, int H = 1,
-                       int N = 0, int chunk = 64, const float* totals = nullptr, int per_channel = 0);
+                       int N = 0, int chunk = 64, const float* totals = nullptr, int per_channel = 0,
+                       int total_only = 0);
 
 // Gradients of the causal normalised output (la_prefill.hip).
 struct BackwardArgs {

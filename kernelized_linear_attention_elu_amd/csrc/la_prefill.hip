@@ -1030,8 +1030,10 @@ __global__ __launch_bounds__(CF::NT) void la_state_kernel(const typename CF::IO*
 // s * n_chunks / n_span, the split span_begin uses.  With gates (kGated)
 // the running state is multiplied by 2^totals[bh][s], the span's total log2
 // gate, instead; with per-channel gates (kChannel) by 2^totals[bh][s][f]
-// for state row f.
-template <int DK>
+// for state row f.  TOTAL (the non-causal form, which reads only the
+// total): slot n_span alone is written; slots 0 .. n_span - 1 keep the span
+// sums.
+template <int DK, bool TOTAL = false>
 __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ ws, int R, int DV, int n_span,
                                                            const float* __restrict__ S0,
                                                            const float* __restrict__ z0,
@@ -1081,7 +1083,7 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (s0 + j < n_span) {
-        p[(size_t)(s0 + j) * E] = acc;
+        if constexpr (!TOTAL) p[(size_t)(s0 + j) * E] = acc;
         if constexpr (DK == kGated || DK == kChannel) acc *= __builtin_amdgcn_exp2f(tl[j]);
         if constexpr (DECAY) {
           rem += r_ch;
@@ -2748,7 +2750,7 @@ static hipError_t launch_prefill(const PrefillArgs& a) {
   rec(1);
   rec(2);
   hipError_t e = scan_launch(ws, BH, CF::R, CF::DV, n_span, a.S0, a.z0, a.S_out, a.z_out, st,
-                             dk == kFixed ? a.gamma : nullptr, a.H, a.N, CF::C, totals);
+                             dk == kFixed ? a.gamma : nullptr, a.H, a.N, CF::C, totals, 0, !a.causal);
   if (e != hipSuccess) return e;
   rec(3);
   rec(4);
@@ -2788,7 +2790,7 @@ static hipError_t dispatch_chunk(const PrefillArgs& a) {
 
 hipError_t scan_launch(float* ws, int BH, int R, int DV, int n_span, const float* S0, const float* z0,
                        float* S_out, float* z_out, hipStream_t stream, const float* gamma, int H, int N, int chunk,
-                       const float* totals, int per_channel) {
+                       const float* totals, int per_channel, int total_only) {
   const int E = R * DV + R;
   if (BH > 0) {
     const dim3 grid((E + kThreads - 1) / kThreads, BH);
@@ -2801,6 +2803,9 @@ hipError_t scan_launch(float* ws, int BH, int R, int DV, int n_span, const float
     else if (gamma)
       hipLaunchKernelGGL(la_scan_kernel<kFixed>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0, S_out,
                          z_out, gamma, H > 0 ? H : 1, N, chunk > 0 ? chunk : 64, nullptr);
+    else if (total_only)
+      hipLaunchKernelGGL((la_scan_kernel<kNoDecay, true>), grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0,
+                         z0, S_out, z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, nullptr);
     else
       hipLaunchKernelGGL(la_scan_kernel<kNoDecay>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0,
                          S_out, z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, nullptr);

@@ -638,7 +638,8 @@ hipError_t favor_prefill_launch(const PrefillArgs& a) {
                        n_span);
   rec(1);
   rec(2);
-  hipError_t e = scan_launch(ws, BH, FR, FDV, n_span, a.S0, a.z0, a.S_out, a.z_out, st);
+  hipError_t e = scan_launch(ws, BH, FR, FDV, n_span, a.S0, a.z0, a.S_out, a.z_out, st, nullptr, 1, 0, 64, nullptr,
+                             0, !a.causal);
   if (e != hipSuccess) return e;
   rec(3);
   rec(4);
