@@ -1056,7 +1056,7 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
   float* p = ws + (size_t)bh * (n_span + 1) * E + e;
   float lg = 0.f;                    // log2(gamma)
   int q_ch = 0, r_ch = 0, rem = 0;   // n_chunks = q_ch n_span + r_ch; running remainder
-  long long c_beg = 0;               // first chunk of the current span
+  int t_beg = 0;                     // first token of the current span
   if constexpr (DECAY) {
     lg = __builtin_amdgcn_logf(gamma[bh % H]);
     const int n_chunks = (N + chunk - 1) / chunk;
@@ -1089,10 +1089,10 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
           rem += r_ch;
           const int step = q_ch + (rem >= n_span ? 1 : 0);
           rem -= rem >= n_span ? n_span : 0;
-          const long long c_end = c_beg + step;
-          const long long t_b = min((long long)N, c_beg * chunk), t_e = min((long long)N, c_end * chunk);
-          acc *= __builtin_amdgcn_exp2f(lg * (float)(t_e - t_b));
-          c_beg = c_end;
+          // (32-bit: N < 2^24, as a head's rows fit a 32-bit byte range)
+          const int t_e = min(N, t_beg + step * chunk);
+          acc *= __builtin_amdgcn_exp2f(lg * (float)(t_e - t_beg));
+          t_beg = t_e;
         }
       }
       acc += x[j];
