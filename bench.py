@@ -19,7 +19,8 @@ timed before that runs up to 25 % slower.
 
 One JSON line is printed with the metric, the roofline of the dominant kernel
 (the output kernel) and of the whole step, and the fp64 CPU oracle timed on
-this host (single process) on a bounded sample of the same workload.
+this host's cores (one worker process per core, up to 16, each running the
+oracle on whole (batch, head) pairs) on the same workload.
 
 Workloads (names from kernelized_linear_attention_elu_amd.synth.WORKLOADS):
 long (default: B1 H32 N32768 d64 bf16 causal), prefill, wide, plus
@@ -47,7 +48,6 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 KERNEL_NAMES = ("la_state_kernel", "la_scan_kernel", "la_output_kernel")
 FAVOR_KERNEL_NAMES = ("la_state_favor_kernel", "la_scan_kernel", "la_output_favor_kernel")
-FUSED_KERNEL_NAMES = ("la_fused_reset_kernel", None, "la_fused_kernel")
 GLA_KERNEL_NAMES = ("la_state_kernel_gla", "la_scan_kernel", "la_output_kernel_gla")
 BACKWARD_KERNEL_NAMES = ("la_state_kernel", "la_scan_kernel", "la_bwd_dq_kernel", "la_suffix_scan_kernel",
                          "la_bwd_dkv_kernel")
@@ -139,31 +139,37 @@ def cpu_info():
     return model
 
 
-def time_oracle_prefill(q, k, v, causal, max_heads, phi="elu1", omega=None, gamma=None, log_a=None, log_a_ch=None):
-    """fp64 oracle (token recurrence, decayed when ``gamma`` is given, gated
-    when ``log_a`` is, or the reassociated non-causal form) on the first
-    ``max_heads`` heads of batch 0; returns (seconds, heads, cores)."""
+def _oracle_head(q, k, v, a, alpha, causal=True, phi="elu1", omega=None, gamma=None):
+    """The fp64 oracle on one (batch, head): the token recurrence (decayed,
+    gated or per-channel gated when given), or the reassociated non-causal
+    form."""
     from oracle import linear_attention as ora
     from oracle import decay as dec
     from oracle import gated as gat
     from oracle import gla
+    if alpha is not None:
+        return gla.recurrent_gla(q, k, v, alpha, phi=phi)[0]
+    if a is not None:
+        return gat.recurrent_gated(q, k, v, a, phi=phi)[0]
+    if gamma is not None:
+        return dec.recurrent_decay(q, k, v, gamma, phi=phi)[0]
+    if causal:
+        return ora.recurrent_attention(q, k, v, phi=phi, omega=omega)[0]
+    return ora.noncausal_attention(q, k, v, phi=phi, omega=omega)[0]
+
+
+def time_oracle_prefill(q, k, v, causal, phi="elu1", omega=None, gamma=None, log_a=None, log_a_ch=None):
+    """fp64 oracle over every (batch, head) of the workload in the worker pool
+    (oracle/heads.py); returns (seconds, heads, workers)."""
+    from oracle import heads
     import numpy as np
-    h = min(max_heads, q.shape[1])
-    t0, c0 = time.perf_counter(), time.process_time()
-    if log_a_ch is not None:
-        gla.recurrent_gla(q[:1, :h], k[:1, :h], v[:1, :h],
-                          np.maximum(np.exp(log_a_ch[:1, :h].astype("float64")), 2.0 ** -14), phi=phi)
-    elif log_a is not None:
-        gat.recurrent_gated(q[:1, :h], k[:1, :h], v[:1, :h], np.exp(log_a[:1, :h].astype("float64")), phi=phi)
-    elif gamma is not None:
-        dec.recurrent_decay(q[:1, :h], k[:1, :h], v[:1, :h], gamma[:h].astype("float64"), phi=phi)
-    elif causal:
-        ora.recurrent_attention(q[:1, :h], k[:1, :h], v[:1, :h], phi=phi, omega=omega)
-    else:
-        ora.noncausal_attention(q[:1, :h], k[:1, :h], v[:1, :h], phi=phi, omega=omega)
+    a = np.exp(log_a.astype("float64")) if log_a is not None else None
+    alpha = np.maximum(np.exp(log_a_ch.astype("float64")), 2.0 ** -14) if log_a_ch is not None else None
+    t0 = time.perf_counter()
+    heads.map_heads(_oracle_head, q, k, v, a, alpha, causal=causal, phi=phi, omega=omega,
+                    head_kw=lambda b, h: {"gamma": float(gamma[h]) if gamma is not None else None})
     wall = time.perf_counter() - t0
-    cpu = time.process_time() - c0
-    return wall, h, max(1, round(cpu / max(wall, 1e-9)))
+    return wall, q.shape[0] * q.shape[1], heads.processes()
 
 
 def bench_prefill(args, torch, la, synth):
@@ -260,8 +266,8 @@ def bench_prefill(args, torch, la, synth):
     n_span, single_pass = la.forward_config(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
                                             chunk=w.chunk, decay=gamma is not None, gated=log_a is not None,
                                             gla=log_a_ch is not None)
-    names = (FAVOR_KERNEL_NAMES if w.phi == "favor" else FUSED_KERNEL_NAMES if single_pass
-             else GLA_KERNEL_NAMES if log_a_ch is not None else KERNEL_NAMES)
+    names = (FAVOR_KERNEL_NAMES if w.phi == "favor" else GLA_KERNEL_NAMES if log_a_ch is not None
+             else KERNEL_NAMES)
     out_kernel = names[2]
     # the decayed and gated variants of la_output_kernel are other kernels:
     # their counter figures are kept under their own workload tag
@@ -324,17 +330,18 @@ def bench_prefill(args, torch, la, synth):
         "settle": {"seconds": args.settle, "untimed_steps": settled},
     }
     if not args.no_cpu_baseline:
-        wall, h, cores = time_oracle_prefill(q, k, v, causal, max_heads=w.H, phi=w.phi, omega=omega, gamma=gamma,
+        wall, h, cores = time_oracle_prefill(q, k, v, causal, phi=w.phi, omega=omega, gamma=gamma,
                                              log_a=log_a, log_a_ch=log_a_ch)
-        # the sample covers h of the B*H heads at full length: scale to the job
-        per_job = wall * (w.B * w.H) / h
+        form = (('per-channel gated token recurrence' if log_a_ch is not None else 'gated token recurrence'
+                 if log_a is not None else 'decayed token recurrence' if gamma is not None else 'token recurrence')
+                if causal else 'reassociated form')
         res["cpu_baseline"] = {
-            "value": w.B * w.N / per_job,
+            "value": w.B * w.N / wall,
             "unit": "tokens/s",
             "cores": cores,
             "kind": "oracle",
-            "sample": f"fp64 {('per-channel gated token recurrence' if log_a_ch is not None else 'gated token recurrence' if log_a is not None else 'decayed token recurrence' if gamma is not None else 'token recurrence') if causal else 'reassociated form'} over {h} of "
-                      f"{w.B * w.H} heads x {w.N} tokens ({wall:.1f} s), scaled to the full job",
+            "sample": f"the whole job: fp64 {form} over all {h} heads x {w.N} tokens ({wall:.1f} s), "
+                      f"one (batch, head) at a time per worker process",
             "cpu": cpu_info(),
         }
     return res
@@ -433,24 +440,24 @@ def bench_backward(args, torch, la, synth):
         "settle": {"seconds": args.settle, "untimed_steps": settled},
     }
     if not args.no_cpu_baseline:
-        from oracle import backward as bwd
-        # a bounded sample: the sampled-row gradient oracle (two fp64 token
-        # loops over every token of the sampled heads) for one row per head
-        h = min(2, w.H)
+        from oracle import heads
         t_a = time.perf_counter()
-        c_a = time.process_time()
-        bwd.grad_rows(q[:1, :h], k[:1, :h], v[:1, :h], dO[:1, :h], [w.N - 1])
+        heads.map_heads(_grad_head, q, k, v, dO)
         wall = time.perf_counter() - t_a
-        cpu = time.process_time() - c_a
-        per_job = wall * (w.B * w.H) / h
         res["cpu_baseline"] = {
-            "value": w.B * w.N / per_job, "unit": "tokens/s", "cores": max(1, round(cpu / max(wall, 1e-9))),
+            "value": w.B * w.N / wall, "unit": "tokens/s", "cores": heads.processes(),
             "kind": "oracle",
-            "sample": f"fp64 prefix/suffix-state gradient loops over {h} of {w.B * w.H} heads x {w.N} tokens "
-                      f"({wall:.1f} s), scaled to the full job",
+            "sample": f"the whole job: fp64 prefix/suffix-state gradient loops over all {w.B * w.H} heads x {w.N} "
+                      f"tokens ({wall:.1f} s), one (batch, head) at a time per worker process",
             "cpu": cpu_info(),
         }
     return res
+
+
+def _grad_head(q, k, v, dO):
+    """dQ, dK, dV of one (batch, head) from the fp64 gradient oracle."""
+    from oracle import backward as bwd
+    return bwd.grad_rows(q, k, v, dO, range(q.shape[-2]))
 
 
 def ctypes_config(la, w):
@@ -572,6 +579,11 @@ def main(argv=None):
               "with no exchange; the sequence would shard with one exchange of span states); "
               "run with --gpus 1", file=sys.stderr)
         return 2
+    if not args.no_cpu_baseline and args.workload not in ("copy", "decode", "feature"):
+        # the oracle's worker processes are forked before anything touches
+        # the GPU, so that none of them inherits GPU state
+        from oracle import heads
+        heads.start()
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

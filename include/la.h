@@ -99,24 +99,34 @@ typedef enum la_phi_kind { LA_PHI_ELU1 = 0, LA_PHI_FAVOR = 1, LA_PHI_IDENTITY = 
  * B*H*(n_span+1)*(r*d_v + r)*4).  A head's chunks are split as evenly as
  * possible over n_span spans (one workgroup each); n_span is chosen by the
  * library from B*H, N, d, chunk and the I/O type so that the workgroups fill
- * the GPU in one round.  The environment variable LA_SPAN (tokens, a multiple
- * of chunk) overrides the span length and must not change between this query
- * and the la_forward call.  Returns 0 for invalid or unsupported arguments.
+ * the GPU in one round (the current device's compute units times the
+ * workgroups per CU of the output kernel).  A span length set with
+ * la_set_span_tokens replaces that choice; la_forward refuses a workspace
+ * smaller than what its own call needs (LA_ERR_WORKSPACE), so a change in
+ * between cannot go unnoticed.  Returns 0 for invalid or unsupported
+ * arguments.
  */
 size_t la_forward_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int causal,
                                   int chunk);
 
 /*
+ * Process-wide span length for the chunkwise prefill entry points, in tokens
+ * (a multiple of 16; a value that is not a multiple of a call's chunk is
+ * ignored by that call); 0 restores the library's own choice.  For tests and
+ * tuning: it forces several spans per head (and with them the span scan) at
+ * small N.  Thread-safe; affects calls made after it returns.
+ * Errors: LA_ERR_SHAPE for a negative value, one above 2^24 or one that is
+ * not a multiple of 16.
+ */
+la_status la_set_span_tokens(int tokens);
+int la_get_span_tokens(void);
+
+/*
  * How la_forward will run this shape (no device work): *n_span receives the
- * number of spans per head (workgroups per head), *single_pass 1 when the
- * single-pass kernel serves it (if selected; causal, bf16, d = d_v = 64,
- * chunk 64, N >= 1:
- * each workgroup keeps its 256-token span of phi(K), V in LDS and takes the
- * prefix of the earlier spans from their published sums), 0 for the
- * three-kernel path (span states, span scan, outputs).  The three-kernel
- * path is the default; LA_FUSED=1 in the environment selects the single
- * pass where it applies.  Either pointer may be NULL.  Errors as
- * la_forward's shape checks.
+ * number of spans per head (workgroups per head), *single_pass 1 when a
+ * single-pass kernel serves it, 0 for the three-kernel path (span states,
+ * span scan, outputs).  Either pointer may be NULL.  Errors as la_forward's
+ * shape checks.
  */
 la_status la_forward_config(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int causal, int chunk,
                             int *n_span, int *single_pass);
@@ -250,7 +260,7 @@ la_status la_forward_gated(const void *Q, const void *K, const void *V, void *O,
                            size_t workspace_bytes, void *stream);
 
 /* Workspace bytes la_forward_gated needs (0 for invalid or unsupported
- * arguments); LA_SPAN applies as for la_forward_workspace_bytes. */
+ * arguments); the span length is chosen as for la_forward_workspace_bytes. */
 size_t la_forward_gated_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r,
                                         int chunk);
 
@@ -310,7 +320,7 @@ la_status la_forward_gla(const void *Q, const void *K, const void *V, void *O, i
                          size_t workspace_bytes, void *stream);
 
 /* Workspace bytes la_forward_gla needs (0 for invalid or unsupported
- * arguments); LA_SPAN applies as for la_forward_workspace_bytes. */
+ * arguments); the span length is chosen as for la_forward_workspace_bytes. */
 size_t la_forward_gla_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int chunk);
 
 /* Spans per head (*n_span) and chunk (*chunk_used) la_forward_gla uses for

@@ -34,6 +34,8 @@ _lib = None
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _SIGS = {
+    "la_set_span_tokens": (_i, [_i]),
+    "la_get_span_tokens": (_i, []),
     "la_forward_workspace_bytes": (ctypes.c_size_t, [_i] * 10),
     "la_forward_config": (_i, [_i] * 10 + [ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "la_forward": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
@@ -168,6 +170,12 @@ def _omega_rows(omega, phi, d):
 def _stream(device):
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def set_span_tokens(tokens):
+    """Process-wide span length of the chunkwise prefill (tokens, a multiple of
+    16; 0 restores the library's own choice): la_set_span_tokens."""
+    _check(load_library().la_set_span_tokens(int(tokens or 0)), "la_set_span_tokens")
 
 
 def workspace_bytes(B, H, N, d, dv, io="bf16", phi="elu1", r=0, causal=True, chunk=64, gated=False, gla=False):

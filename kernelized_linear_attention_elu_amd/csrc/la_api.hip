@@ -1,8 +1,11 @@
 // C-ABI layer: argument validation, span choice, workspace sizing, dispatch.
-// Validation never touches the HIP runtime, so every error path can be
-// exercised on a machine without a GPU.
+// Validation makes no device calls, so every error path can be exercised on
+// a machine without a GPU (the span choice asks the runtime for the current
+// device's compute-unit count and falls back to 256 when there is none).
 #include <stdint.h>
 #include <stdlib.h>
+
+#include <atomic>
 
 #include <hip/hip_runtime.h>
 
@@ -34,13 +37,38 @@ int norm_chunk(int chunk) { return chunk == 0 ? 64 : chunk; }
 // Spans per head.  Both prefill kernels run one workgroup per (head, span)
 // and a span's chunks are contiguous; spans of a head differ by at most one
 // chunk.  The default fills one round of workgroup slots of the output
-// kernel (256 CUs x workgroups per CU at its occupancy for this
-// configuration) so that no CU runs a partial second round, but keeps at
-// least 4 chunks per span so that the per-span state traffic (r*d_v*4 bytes
-// written, scanned and read back) stays small next to the span's data.  The
-// environment variable LA_SPAN (tokens, a multiple of the chunk) overrides
-// the span length.
-constexpr int kCUs = 256;
+// kernel (the device's compute units x workgroups per CU at its occupancy
+// for this configuration) so that no CU runs a partial second round, but
+// keeps at least 4 chunks per span so that the per-span state traffic
+// (r*d_v*4 bytes written, scanned and read back) stays small next to the
+// span's data.  la_set_span_tokens sets a process-wide span length instead
+// (tests use it to force several spans per head).
+
+// Span length set by la_set_span_tokens (0: the default choice).
+std::atomic<int> g_span_tokens{0};
+
+// Compute units of the calling thread's current device, queried once per
+// device (256 on MI355X; also the answer when no device can be queried, so
+// that shape queries work on a host without a GPU).
+constexpr int kDefaultCUs = 256;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  int n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = kDefaultCUs;
+  }
+  g_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 int output_occupancy(int io, int phi, int d, int chunk, int causal, int decay) {
   if (phi == LA_PHI_FAVOR) return 1;
@@ -60,12 +88,9 @@ int output_occupancy(int io, int phi, int d, int chunk, int causal, int decay) {
 int choose_n_span(long long BH, int N, int chunk, int d, int io, int phi, int causal, int decay) {
   if (N <= 0) return 0;
   const long long n_chunks = (static_cast<long long>(N) + chunk - 1) / chunk;
-  const char* env = getenv("LA_SPAN");
-  if (env && *env) {
-    const long v = strtol(env, nullptr, 10);
-    if (v >= chunk && v % chunk == 0 && v <= (1 << 24)) return static_cast<int>((N + v - 1) / v);
-  }
-  const long long slots = static_cast<long long>(kCUs) * output_occupancy(io, phi, d, chunk, causal, decay);
+  const int v = g_span_tokens.load(std::memory_order_relaxed);
+  if (v >= chunk && v % chunk == 0) return static_cast<int>((static_cast<long long>(N) + v - 1) / v);
+  const long long slots = static_cast<long long>(device_cus()) * output_occupancy(io, phi, d, chunk, causal, decay);
   long long n = (slots + BH - 1) / (BH > 0 ? BH : 1);
   const long long cap = n_chunks / 4 > 0 ? n_chunks / 4 : 1;
   if (n > cap) n = cap;
@@ -74,31 +99,9 @@ int choose_n_span(long long BH, int N, int chunk, int d, int io, int phi, int ca
 }
 
 struct Shape {
-  int B, H, N, d, dv, r, phi, causal, chunk, n_span, fused;
+  int B, H, N, d, dv, r, phi, causal, chunk, n_span;
   long long BH;
 };
-
-// Spans per look-back block of the single-pass kernel (LA_FUSED_GROUP
-// overrides the default; 1 .. 64).
-int fused_group() {
-  const char* env = getenv("LA_FUSED_GROUP");
-  if (env && *env) {
-    const long v = strtol(env, nullptr, 10);
-    if (v >= 1 && v <= 64) return static_cast<int>(v);
-  }
-  return la::kFusedGroup;
-}
-
-// The single-pass kernel can serve causal bf16 prefill at d = d_v = 64,
-// chunk 64, for any N >= 1.  It is selected with LA_FUSED=1 in the
-// environment; the three-kernel path is the default (on MI355X it is the
-// faster of the two at the long-sequence shapes: both are bound by per-chunk
-// work on the CUs, and the single pass adds the exchange of span states).
-bool use_fused(int io, int phi, int d, int d_v, int r, int causal, int chunk, int N) {
-  if (N <= 0 || !la::fused_supported(io, phi, d, d_v, r, chunk, causal)) return false;
-  const char* env = getenv("LA_FUSED");
-  return env && env[0] == '1';
-}
 
 // decay: 1 for a fixed per-head decay or per-token gates, 2 for per-channel
 // gates (causal, pointwise maps only).
@@ -123,17 +126,14 @@ la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int p
   if (static_cast<long long>(N) * row >= (1LL << 31)) return LA_ERR_SHAPE;
   // per-channel gates: a head's [N][r] fp32 gates, one chunk past N included
   if (decay == 2 && (static_cast<long long>(N) + 128) * rr * 4 >= (1LL << 31)) return LA_ERR_SHAPE;
-  const int fused = !decay && use_fused(io, phi, d, d_v, rr, causal, ch, N) ? 1 : 0;
-  const int n_span =
-      fused ? (N + la::kFusedSpan - 1) / la::kFusedSpan : choose_n_span(BH, N, ch, d, io, phi, causal, decay);
+  const int n_span = choose_n_span(BH, N, ch, d, io, phi, causal, decay);
   if (BH * n_span > 0x7fffffffLL) return LA_ERR_SHAPE;
   sh->B = B; sh->H = H; sh->N = N; sh->d = d; sh->dv = d_v; sh->r = rr; sh->phi = phi;
-  sh->causal = causal; sh->chunk = ch; sh->n_span = n_span; sh->fused = fused; sh->BH = BH;
+  sh->causal = causal; sh->chunk = ch; sh->n_span = n_span; sh->BH = BH;
   return LA_OK;
 }
 
 size_t workspace_for(const Shape& sh, bool gated = false, bool per_channel = false) {
-  if (sh.fused) return la::fused_workspace_bytes(sh.BH, sh.n_span, sh.r, sh.dv);
   return la::prefill_workspace_bytes(sh.BH, sh.n_span, sh.r, sh.dv, gated, per_channel);
 }
 
@@ -164,7 +164,7 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
   a.Q = Q; a.K = K; a.V = V; a.O = O;
   a.B = B; a.H = H; a.N = N; a.d = d; a.dv = d_v; a.r = sh.r;
   a.io = io; a.phi = phi; a.omega = omega; a.causal = causal;
-  a.chunk = sh.chunk; a.n_span = sh.n_span; a.fused = sh.fused; a.group = fused_group();
+  a.chunk = sh.chunk; a.n_span = sh.n_span;
   a.S0 = S0; a.z0 = z0; a.S_out = S_out; a.z_out = z_out;
   a.workspace = workspace; a.stream = stream; a.events = events;
   a.gamma = gamma; a.normalize = normalize; a.log_a = log_a; a.log_a_ch = log_a_ch;
@@ -174,6 +174,14 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
 }  // namespace
 
 extern "C" {
+
+la_status la_set_span_tokens(int tokens) {
+  if (tokens < 0 || tokens > (1 << 24) || tokens % 16 != 0) return LA_ERR_SHAPE;
+  g_span_tokens.store(tokens, std::memory_order_relaxed);
+  return LA_OK;
+}
+
+int la_get_span_tokens(void) { return g_span_tokens.load(std::memory_order_relaxed); }
 
 size_t la_forward_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int causal,
                                   int chunk) {
@@ -188,7 +196,7 @@ la_status la_forward_config(int B, int H, int N, int d, int d_v, int io_dtype, i
   const la_status st = check_forward_shape(B, H, N, d, d_v, io_dtype, phi, r, causal, chunk, &sh);
   if (st != LA_OK) return st;
   if (n_span) *n_span = sh.n_span;
-  if (single_pass) *single_pass = sh.fused;
+  if (single_pass) *single_pass = 0;
   return LA_OK;
 }
 

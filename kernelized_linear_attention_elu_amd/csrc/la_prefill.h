@@ -25,8 +25,6 @@ struct PrefillArgs {
   void* workspace;
   void* stream;
   void* const* events;  // optional: 6 hipEvent_t recorded around the three kernels
-  int fused;            // single-pass kernel (n_span = ceil(N / kFusedSpan))
-  int group;            // single pass: spans per look-back block
   // fixed per-head decay (device [H] fp32 in (0, 1]; null: none), causal
   // pointwise maps only: S_t = gamma S_{t-1} + phi(k_t) v_t^T, z likewise
   const float* gamma = nullptr;
@@ -52,19 +50,6 @@ inline size_t prefill_workspace_bytes(long long BH, int n_span, int r, int dv, b
 }
 // Shapes the per-channel gated prefill supports (causal, ELU+1 / identity).
 bool gla_supported(int io, int d, int dv, int r, int chunk);
-
-// Single-pass causal prefill (la_prefill.hip): tokens per workgroup and the
-// default number of spans per look-back block.
-constexpr int kFusedSpan = 256;
-constexpr int kFusedGroup = 8;
-bool fused_supported(int io, int phi, int d, int dv, int r, int chunk, int causal);
-// Workspace: 256-byte header, one flag word per (head, span) rounded up to
-// 256 bytes, then two fp32 state slots of r*d_v + r per (head, span).
-inline size_t fused_slots_offset(long long n_flags) { return 256 + (size_t)((n_flags * 4 + 255) / 256) * 256; }
-inline size_t fused_workspace_bytes(long long BH, int n_span, int r, int dv) {
-  const long long n = BH * n_span;
-  return fused_slots_offset(n) + (size_t)n * 2 * ((size_t)r * dv + r) * sizeof(float);
-}
 
 bool prefill_supported(int io, int phi, int d, int dv, int r, int chunk);
 hipError_t prefill_launch(const PrefillArgs& a);

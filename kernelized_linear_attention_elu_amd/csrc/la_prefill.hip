@@ -2429,266 +2429,6 @@ __global__ __launch_bounds__(CF::NT, CF::NW == 8 ? 1 : 2) void la_bwd_dkv_kernel
   }
 }
 
-// ------------------------------------------------------------------ single pass
-
-// One kernel per causal prefill: each workgroup takes one span of
-// kFusedSpan tokens, in ticket order (span-major: all heads' span 0, then
-// span 1, ...), and
-//   1. loads the span's K, V and Q at once (registers), stages phi(K) (bf16
-//      hi, with the lo word per chunk) and V in LDS, where they stay, and
-//      accumulates the span's own sums dS, dz (hi + lo, fp32);
-//   2. publishes them and forms the exclusive prefix of its span: the
-//      inclusive prefix at the end of the previous look-back block (published
-//      by that block's last span; S0/z0 for the first block) plus the sums
-//      of the earlier spans of its own block, always added in span order, so
-//      that results do not depend on timing.  The last span of a block
-//      publishes its inclusive prefix;
-//   3. walks its chunks as la_output_kernel does, with K and V already in
-//      LDS.
-// A workgroup only ever waits for spans with smaller tickets, whose
-// workgroups are already running, so the waits always end; they are also
-// bounded (a timeout is counted in the workspace header and the kernel
-// goes on).  The spans of one head may run on different XCDs: the exchanged
-// states use device-scope accesses and the flags device-scope atomics.
-constexpr int kSpinLimit = 1 << 20;
-
-__global__ void la_fused_reset_kernel(unsigned* __restrict__ words, int n) {
-  const int i = blockIdx.x * kThreads + threadIdx.x;
-  if (i < n) words[i] = 0u;
-}
-
-__device__ __forceinline__ void wait_flag(const unsigned* f, unsigned bit, unsigned* timeouts) {
-  int i = 0;
-  while (!(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & bit)) {
-    if (++i == kSpinLimit) {
-      atomicAdd(timeouts, 1u);
-      return;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-}
-
-// Exchanged span states are written and read with device-scope (sc1) buffer
-// accesses: they are coherent across XCDs by themselves, with no cache
-// write-back or invalidation.  A writer waits for its stores to complete
-// (vmcnt(0)) before the workgroup barrier that precedes the flag.
-constexpr int kDeviceScope = 0x10;           // buffer cache policy: sc1
-__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-
-// State tiles of this thread (the ownership of state_mfma) -> a slot.
-template <class CF>
-__device__ __forceinline__ void slot_store(float* slot, const f32x4 (&S)[CF::TPW], const f32x4 (&z)[CF::ZPW], int w,
-                                           int g, int li) {
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(slot, (CF::R * CF::DV + CF::R) * 4);
-#pragma unroll
-  for (int i = 0; i < CF::TPW; ++i) {
-    int ct, ft;
-    state_tile<CF>(w, i, ct, ft);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S[i]), r,
-                                           ((16 * ft + li) * CF::DV + 16 * ct + 4 * g) * 4, 0, kDeviceScope);
-  }
-  if (g == 0) {
-#pragma unroll
-    for (int k = 0; k < CF::ZPW; ++k)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z[k][0]), r,
-                                            (CF::R * CF::DV + 16 * (w + CF::NW * k) + li) * 4, 0, kDeviceScope);
-  }
-}
-
-// S, z += a slot ([R][DV] then [R]) read with device-scope loads.
-template <class CF>
-__device__ __forceinline__ void slot_add(const float* slot, f32x4 (&S)[CF::TPW], f32x4 (&z)[CF::ZPW], int w, int g,
-                                         int li) {
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(slot, (CF::R * CF::DV + CF::R) * 4);
-#pragma unroll
-  for (int i = 0; i < CF::TPW; ++i) {
-    int ct, ft;
-    state_tile<CF>(w, i, ct, ft);
-    S[i] += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                          r, ((16 * ft + li) * CF::DV + 16 * ct + 4 * g) * 4, 0, kDeviceScope));
-  }
-#pragma unroll
-  for (int k = 0; k < CF::ZPW; ++k) {
-    const float v = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(r, (CF::R * CF::DV + 16 * (w + CF::NW * k) + li) * 4, 0, kDeviceScope));
-    z[k] += f32x4{v, v, v, v};
-  }
-}
-
-// S, z += the caller's initial state of head bh (plain loads).
-template <class CF>
-__device__ __forceinline__ void state_add(const float* Sm, const float* zv, f32x4 (&S)[CF::TPW],
-                                          f32x4 (&z)[CF::ZPW], int w, int g, int li) {
-#pragma unroll
-  for (int i = 0; i < CF::TPW; ++i) {
-    int ct, ft;
-    state_tile<CF>(w, i, ct, ft);
-    S[i] += *reinterpret_cast<const f32x4*>(Sm + (16 * ft + li) * CF::DV + 16 * ct + 4 * g);
-  }
-#pragma unroll
-  for (int k = 0; k < CF::ZPW; ++k) {
-    const float v = zv[16 * (w + CF::NW * k) + li];
-    z[k] += f32x4{v, v, v, v};
-  }
-}
-
-template <class CF>
-__global__ __launch_bounds__(CF::NT, 2) void la_fused_kernel(
-    const typename CF::IO* __restrict__ Q, const typename CF::IO* __restrict__ K,
-    const typename CF::IO* __restrict__ V, typename CF::IO* __restrict__ O, float* __restrict__ slots,
-    unsigned* __restrict__ hdr, int N, int n_span, int BH, int group, const float* __restrict__ S0,
-    const float* __restrict__ z0, float* __restrict__ S_out, float* __restrict__ z_out) {
-  using OP = typename CF::OP;
-  constexpr int C = CF::C, NC = kFusedSpan / C;
-  constexpr int TE = Tile<OP, CF::R>::elems(C);
-  constexpr int TV = Tile<OP, CF::DV>::elems(C);
-  constexpr int E = CF::R * CF::DV + CF::R;
-  struct P3 {
-    OP s[Tile<OP, CF::DV>::elems(CF::R)];
-    alignas(16) typename CF::ZT z[CF::ZE];
-  };
-  union X {
-    OP klo[TE];  // lo words of the chunk being accumulated (step 1)
-    P3 p;        // carried state published for the read-out (step 3)
-  };
-  __shared__ OP sk[NC * TE];
-  __shared__ OP sv[NC * TV];
-  __shared__ X sx;
-  __shared__ int s_ticket;
-
-  const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
-  unsigned* const timeouts = hdr + 1;
-  unsigned* const flags = hdr + 64;
-  if (tid == 0) s_ticket = (int)atomicAdd(hdr, 1u);
-  __syncthreads();
-  const int tk = __builtin_amdgcn_readfirstlane(s_ticket);
-  const int s = tk / BH, bh = tk % BH;
-  const int t_begin = min(N, s * kFusedSpan);
-  const int t_end = min(N, t_begin + kFusedSpan);
-  const int nck = (t_end - t_begin + C - 1) / C;
-  const HeadBufs hb = head_bufs<CF>(Q, K, V, O, bh, N);
-
-  // ---- 1. all loads of the span, then the span's own sums
-  ChunkRegs<CF, false> cr[NC];
-  QRegs<CF, false> qr[NC];  // fragments loaded directly (no LDS room for row staging)
-#pragma unroll
-  for (int c = 0; c < NC; ++c) load_chunk<CF, false>(cr[c], hb, t_begin + c * C);
-#pragma unroll
-  for (int c = 0; c < NC; ++c) qr[c].load(hb.q, t_begin + c * C, w, g, li);
-
-  f32x4 acc[CF::TPW];
-  f32x4 zt[CF::ZPW];
-#pragma unroll
-  for (int i = 0; i < CF::TPW; ++i) acc[i] = zero4();
-#pragma unroll
-  for (int k = 0; k < CF::ZPW; ++k) zt[k] = zero4();
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (c < nck) {
-      stage_chunk<CF, false>(cr[c], nullptr, sk + c * TE, sx.klo, sv + c * TV, t_begin + c * C, N);
-      __syncthreads();
-      state_mfma<CF>(acc, zt, sk + c * TE, sx.klo, sv + c * TV, w, g, li);
-      __syncthreads();
-    }
-  }
-
-  // ---- 2. publish the span's sums, then form the prefix
-  float* const head_slots = slots + (size_t)bh * n_span * 2 * E;
-  unsigned* const head_flags = flags + (size_t)bh * n_span;
-  slot_store<CF>(head_slots + (size_t)s * 2 * E, acc, zt, w, g, li);
-  wait_stores();
-  __syncthreads();
-  if (tid == 0) __hip_atomic_fetch_or(head_flags + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int first = s - s % group;
-  if (tid == 0) {
-    if (first > 0) wait_flag(head_flags + first - 1, 2u, timeouts);
-    for (int j = first; j < s; ++j) wait_flag(head_flags + j, 1u, timeouts);
-  }
-  __syncthreads();
-  f32x4 sacc[CF::TPW];
-  f32x4 zc[CF::ZPW];
-#pragma unroll
-  for (int i = 0; i < CF::TPW; ++i) sacc[i] = zero4();
-#pragma unroll
-  for (int k = 0; k < CF::ZPW; ++k) zc[k] = zero4();
-  if (first > 0) {
-    slot_add<CF>(head_slots + (size_t)(first - 1) * 2 * E + E, sacc, zc, w, g, li);
-  } else if (S0) {
-    state_add<CF>(S0 + (size_t)bh * CF::R * CF::DV, z0 + (size_t)bh * CF::R, sacc, zc, w, g, li);
-  }
-  for (int j = first; j < s; ++j) slot_add<CF>(head_slots + (size_t)j * 2 * E, sacc, zc, w, g, li);
-  if (s % group == group - 1 || s == n_span - 1) {
-    f32x4 is[CF::TPW];
-    f32x4 iz[CF::ZPW];
-#pragma unroll
-    for (int i = 0; i < CF::TPW; ++i) is[i] = sacc[i] + acc[i];
-#pragma unroll
-    for (int k = 0; k < CF::ZPW; ++k) iz[k] = zc[k] + zt[k];
-    slot_store<CF>(head_slots + (size_t)s * 2 * E + E, is, iz, w, g, li);
-    if (s == n_span - 1 && S_out) {
-      // the final state S_N, z_N (z_out rows use the same ownership)
-#pragma unroll
-      for (int i = 0; i < CF::TPW; ++i) {
-        int ct, ft;
-        state_tile<CF>(w, i, ct, ft);
-        *reinterpret_cast<f32x4*>(S_out + (size_t)bh * CF::R * CF::DV + (16 * ft + li) * CF::DV + 16 * ct + 4 * g) =
-            is[i];
-      }
-      if (g == 0) {
-#pragma unroll
-        for (int k = 0; k < CF::ZPW; ++k) z_out[(size_t)bh * CF::R + 16 * (w + CF::NW * k) + li] = iz[k][0];
-      }
-    }
-    wait_stores();
-    __syncthreads();
-    if (tid == 0) __hip_atomic_fetch_or(head_flags + s, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  // ---- 3. outputs, chunk by chunk, K and V from LDS
-  OutRegs<CF> out;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (c < nck) {
-      publish_state<CF>(sacc, zc, sx.p.s, sx.p.z, w, g, li);
-      __syncthreads();
-      typename QRegs<CF>::frag qf[CF::RBW][CF::R / CF::KS];
-      qr[c].to_frags(qf, nullptr, g, li);
-      chunk_outputs<CF, true>(qf, sk + c * TE, sv + c * TV, sx.p.s, sx.p.z, out, w, g, li);
-      store_outputs<CF, false>(out, hb.o, t_begin + c * C, w, g, li, false, nullptr);
-      if (c + 1 < nck) {
-        state_mfma<CF>(sacc, zc, sk + c * TE, nullptr, sv + c * TV, w, g, li);
-        __syncthreads();
-      }
-    }
-  }
-}
-
-template <class CF>
-static hipError_t launch_fused(const PrefillArgs& a) {
-  using T = typename CF::IO;
-  const int BH = a.B * a.H;
-  hipStream_t st = static_cast<hipStream_t>(a.stream);
-  const long long n_flags = (long long)BH * a.n_span;
-  unsigned* hdr = static_cast<unsigned*>(a.workspace);
-  float* slots = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + fused_slots_offset(n_flags));
-  (void)hipGetLastError();
-  auto rec = [&](int i) {
-    if (a.events && a.events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a.events[i]), st);
-  };
-  rec(0);
-  const int nw = (int)(64 + n_flags);
-  hipLaunchKernelGGL(la_fused_reset_kernel, dim3((nw + kThreads - 1) / kThreads), dim3(kThreads), 0, st, hdr, nw);
-  rec(1);
-  rec(2);
-  rec(3);
-  rec(4);
-  hipLaunchKernelGGL((la_fused_kernel<CF>), dim3(BH * a.n_span), dim3(CF::NT), 0, st,
-                     static_cast<const T*>(a.Q), static_cast<const T*>(a.K), static_cast<const T*>(a.V),
-                     static_cast<T*>(a.O), slots, hdr, a.N, a.n_span, BH, a.group, a.S0, a.z0, a.S_out, a.z_out);
-  rec(5);
-  return hipGetLastError();
-}
-
 // ------------------------------------------------------------------ launcher
 
 template <class CF>
@@ -2892,18 +2632,8 @@ bool gla_supported(int io, int d, int dv, int r, int chunk) {
   return false;
 }
 
-bool fused_supported(int io, int phi, int d, int dv, int r, int chunk, int causal) {
-  return io == 1 && (phi == PHI_ELU1 || phi == PHI_IDENTITY) && d == 64 && dv == 64 && r == 64 && chunk == 64 &&
-         causal == 1;
-}
-
 hipError_t prefill_launch(const PrefillArgs& a) {
   if (a.phi == PHI_FAVOR) return favor_prefill_launch(a);
-  if (a.fused) {
-    if (!fused_supported(a.io, a.phi, a.d, a.dv, a.r, a.chunk, a.causal)) return hipErrorInvalidValue;
-    return a.phi == PHI_ELU1 ? launch_fused<Cfg<bf16, 64, 64, 64, 64, PHI_ELU1>>(a)
-                             : launch_fused<Cfg<bf16, 64, 64, 64, 64, PHI_IDENTITY>>(a);
-  }
   if (a.io == 1) {
     if (a.d == 64) return a.phi == PHI_ELU1 ? dispatch_chunk<bf16, 64, PHI_ELU1>(a) : dispatch_chunk<bf16, 64, PHI_IDENTITY>(a);
     if (a.d == 128)

@@ -40,28 +40,33 @@ def _ws(B, H, N, d=64, dv=64, phi=0, r=0, causal=1, chunk=64, io=1):
     return la.load_library().la_forward_workspace_bytes(B, H, N, d, dv, io, phi, r, causal, chunk)
 
 
-def test_forward_config(lib, monkeypatch):
-    monkeypatch.delenv("LA_FUSED", raising=False)
-    monkeypatch.delenv("LA_SPAN", raising=False)
-    assert la.forward_config(1, 32, 32768, 64, 64) == (24, False)    # default: three kernels
-    monkeypatch.setenv("LA_FUSED", "1")
-    # causal bf16 d64 chunk 64: single pass, 256-token spans
-    assert la.forward_config(1, 32, 32768, 64, 64) == (128, True)
-    assert la.forward_config(1, 1, 300, 64, 64) == (2, True)
-    assert la.forward_config(1, 1, 300, 64, 64, causal=False)[1] is False
-    assert la.forward_config(1, 1, 300, 64, 64, chunk=32)[1] is False
-    assert la.forward_config(1, 1, 300, 128, 128)[1] is False
-    assert la.forward_config(1, 1, 300, 64, 64, io="f32")[1] is False
+@pytest.fixture
+def span_tokens(lib):
+    """la_set_span_tokens for one test, restored to the default afterwards."""
+    lib.la_set_span_tokens(0)
+    yield lambda t: lib.la_set_span_tokens(t)
+    lib.la_set_span_tokens(0)
+
+
+def test_forward_config(lib, span_tokens):
+    assert la.forward_config(1, 32, 32768, 64, 64) == (24, False)    # three kernels
     assert la.forward_config(1, 1, 0, 64, 64) == (0, False)
-    monkeypatch.setenv("LA_FUSED", "0")
-    assert la.forward_config(1, 32, 32768, 64, 64) == (24, False)
     with pytest.raises(la.LinAttnError):
         la.forward_config(1, 1, 10, 96, 96)
 
 
-def test_workspace_sizes(lib, monkeypatch):
-    monkeypatch.delenv("LA_SPAN", raising=False)
-    monkeypatch.setenv("LA_FUSED", "0")
+def test_span_setter(lib, span_tokens):
+    assert lib.la_get_span_tokens() == 0
+    for bad in (-16, 24, (1 << 24) + 16):
+        assert lib.la_set_span_tokens(bad) == 2                           # LA_ERR_SHAPE
+    assert lib.la_get_span_tokens() == 0
+    assert span_tokens(128) == 0 and lib.la_get_span_tokens() == 128
+    assert la.forward_config(1, 1, 1000, 64, 64) == (8, False)
+    assert span_tokens(0) == 0
+    assert la.forward_config(1, 1, 1000, 64, 64) == (4, False)           # 16 chunks, at least 4 per span
+
+
+def test_workspace_sizes(lib, span_tokens):
     E = 64 * 64 + 64
     # long prefill B1 H32 N32768 (512 chunks per head): 768 output workgroups
     # (256 CUs x 3) -> 24 spans per head
@@ -77,10 +82,11 @@ def test_workspace_sizes(lib, monkeypatch):
     assert _ws(1, 8, 65536, io=0) == 8 * 97 * E * 4
     # N = 0 still needs one slot per head for the (initial = final) state
     assert _ws(1, 2, 0) == 2 * 1 * E * 4
-    monkeypatch.setenv("LA_SPAN", "64")
+    span_tokens(64)
     assert _ws(1, 1, 256) == 1 * 5 * E * 4
-    monkeypatch.setenv("LA_SPAN", "48")  # not a multiple of the chunk: ignored
+    span_tokens(48)  # not a multiple of the chunk: ignored
     assert _ws(1, 1, 256) == 1 * 2 * E * 4
+    span_tokens(0)
     # unsupported shapes report 0
     assert _ws(1, 1, 16, 96, 96) == 0
     assert _ws(1, 1, 16, 64, 64, chunk=24) == 0
@@ -90,11 +96,6 @@ def test_workspace_sizes(lib, monkeypatch):
     assert _ws(1, 1, 100, phi=1, r=128) == 0
     assert _ws(1, 1, 100, phi=1, r=256, chunk=32) == 0
     assert _ws(1, 1, 100, phi=1, r=256, io=0) == 0
-    # single pass: 256-byte header, flags rounded to 256 bytes, two slots
-    # per (head, span)
-    monkeypatch.setenv("LA_FUSED", "1")
-    assert _ws(1, 32, 32768) == 256 + 32 * 128 * 4 + 32 * 128 * 2 * E * 4
-    assert _ws(1, 1, 300) == 256 + 256 + 1 * 2 * 2 * E * 4
 
 
 FAKE = ctypes.c_void_p(0x100000)      # aligned, never dereferenced

@@ -32,7 +32,7 @@ def _check_state(got, ref, io, what):
         check_close(got, ref, io, what)
 
 
-def _case(lib, rng, om, monkeypatch):
+def _case(lib, rng, om, span_set):
     import torch
     pick = lambda xs: xs[int(rng.integers(0, len(xs)))]
     kind = pick(KINDS)
@@ -52,10 +52,7 @@ def _case(lib, rng, om, monkeypatch):
     span = pick([None, None, chunk, 2 * chunk, 3 * chunk])
     seed = int(rng.integers(0, 2**31))
     what = f"{kind} B{B} H{H} N{N} d{d} {io} chunk {chunk} span {span} seed {seed}"
-    if span is None:
-        monkeypatch.delenv("LA_SPAN", raising=False)
-    else:
-        monkeypatch.setenv("LA_SPAN", str(span))
+    span_set(span)
     q, k, v = synth.draw_qkv(B, H, N, d, d, seed=seed, io=io)
     Q, K, V = (to_dev(x, io) for x in (q, k, v))
     if kind in ("plain", "noncausal"):
@@ -138,8 +135,8 @@ def _decode_case(lib, rng, pick):
 
 
 @pytest.mark.parametrize("seed", [101, 202, 303])
-def test_random_sweep(lib, monkeypatch, seed):
+def test_random_sweep(lib, span, seed):
     rng = np.random.default_rng(seed)
     om = synth.draw_omega(256, 64)
     for _ in range(60):
-        _case(lib, rng, om, monkeypatch)
+        _case(lib, rng, om, span)
