@@ -1,20 +1,22 @@
-"""Magnitude sums of the gradient terms, for the cancellation floor of the
-gradient gate (tests/gates.py, check_grad).
+"""Magnitudes of the intermediate sums the backward kernels form, for the
+cancellation floor of the gradient gate (tests/gates.py, check_grad).
 
-Each gradient entry is a sum of terms of mixed sign:
-    dQ_i = phi'(q_i) sum_{j<=i} (dO_i.v_j + rho_i) / D_i phi(k_j),
-    dK_j = phi'(k_j) sum_{i>=j} (dO_i.v_j + rho_i) / D_i phi(q_i),
-    dV_j = sum_{i>=j} A_ij / D_i dO_i,
-with A_ij = phi(q_i).phi(k_j), D_i = sum_{j<=i} A_ij and rho_i = -dO_i.O_i.
-The scale of an entry is the same sum with every factor replaced by its
-magnitude.  With phi >= 0 these are prefix and suffix sums again:
-    scale(dQ_i) = |phi'(q_i)| (Sa_i |dO_i| + |rho_i| z_i) / D_i,
-        Sa_i = sum_{j<=i} phi(k_j) |v_j|^T,  z_i = sum_{j<=i} phi(k_j);
-    scale(dK_j) = |phi'(k_j)| (Ra_j |v_j| + ua_j),
-        Ra_j = sum_{i>=j} phi(q_i) |dO_i|^T / D_i,  ua_j = sum_{i>=j} phi(q_i) |rho_i| / D_i;
-    scale(dV_j) = Ra_j^T phi(k_j).
-One forward and one reverse token loop, vectorised over the leading axes.
-Test infrastructure: NumPy, built on the oracle's feature maps.
+Each gradient row is a difference of two large sums that cancel most of
+each other:
+    dphi(q_i) = S_i g_i + h_i z_i,                  (forward prefix sums)
+    dphi(k_j) = R_j v_j + u_j,                      (reverse suffix sums)
+with S_i = sum_{j<=i} phi(k_j) v_j^T, z_i = sum_{j<=i} phi(k_j),
+g_i = dO_i / D_i, h_i = -(dO_i . O_i) / D_i, R_j = sum_{i>=j} phi(q_i) g_i^T,
+u_j = sum_{i>=j} phi(q_i) h_i (the chain rule of oracle/backward.py,
+regrouped by the associativity of the recurrent form).  bf16 rounding
+inside the kernels is relative to these sums, not to their difference, so
+the floor of a row is taken relative to
+    m(dQ_i) = |phi'(q_i)| (|S_i g_i| + |h_i| z_i),
+    m(dK_j) = |phi'(k_j)| (|R_j v_j| + |u_j|),
+    m(dV_j) = Ra_j^T phi(k_j),  Ra_j = sum_{i>=j} phi(q_i) |dO_i|^T / D_i
+(dV is a single sum of mixed-sign terms; its magnitude sum).
+One forward and one reverse fp64 token loop, vectorised over the leading
+axes.  Test infrastructure: NumPy, built on the oracle's feature maps.
 """
 
 from __future__ import annotations
@@ -33,31 +35,33 @@ def grad_scales(q, k, v, dO, phi="elu1"):
     lead = fq.shape[:-2]
     n, r = fq.shape[-2], fq.shape[-1]
     dv = v.shape[-1]
-    av, adO = np.abs(v), np.abs(dO)
-    Sa = np.zeros(lead + (r, dv))
     S = np.zeros(lead + (r, dv))
     z = np.zeros(lead + (r,))
     D = np.empty(lead + (n,))
-    rho = np.empty(lead + (n,))
+    g = np.empty(lead + (n, dv))
+    h = np.empty(lead + (n,))
     sq = np.empty(fq.shape)
     for t in range(n):
         S += fk[..., t, :, None] * v[..., t, None, :]
-        Sa += fk[..., t, :, None] * av[..., t, None, :]
         z += fk[..., t, :]
         Dt = np.einsum("...r,...r->...", fq[..., t, :], z)
         Ot = np.einsum("...r,...rc->...c", fq[..., t, :], S) / Dt[..., None]
         D[..., t] = Dt
-        rho[..., t] = np.abs(np.einsum("...c,...c->...", dO[..., t, :], Ot))
-        sq[..., t, :] = (np.einsum("...rc,...c->...r", Sa, adO[..., t, :]) + rho[..., t, None] * z) / Dt[..., None]
+        g[..., t, :] = dO[..., t, :] / Dt[..., None]
+        h[..., t] = -np.einsum("...c,...c->...", dO[..., t, :], Ot) / Dt
+        sq[..., t, :] = np.abs(np.einsum("...rc,...c->...r", S, g[..., t, :])) + np.abs(h[..., t, None]) * z
     sq *= np.abs(bwd.phi_prime(phi, q))
+    R = np.zeros(lead + (r, dv))
     Ra = np.zeros(lead + (r, dv))
-    ua = np.zeros(lead + (r,))
+    u = np.zeros(lead + (r,))
     sk = np.empty(fk.shape)
     sv = np.empty(v.shape)
+    adO = np.abs(dO)
     for t in range(n - 1, -1, -1):
+        R += fq[..., t, :, None] * g[..., t, None, :]
         Ra += fq[..., t, :, None] * (adO[..., t, None, :] / D[..., t, None, None])
-        ua += fq[..., t, :] * (rho[..., t, None] / D[..., t, None])
-        sk[..., t, :] = np.einsum("...rc,...c->...r", Ra, av[..., t, :]) + ua
+        u += fq[..., t, :] * h[..., t, None]
+        sk[..., t, :] = np.abs(np.einsum("...rc,...c->...r", R, v[..., t, :])) + np.abs(u)
         sv[..., t, :] = np.einsum("...rc,...r->...c", Ra, fk[..., t, :])
     sk *= np.abs(bwd.phi_prime(phi, k))
     return sq, sk, sv

@@ -3,10 +3,10 @@ oracle (oracle/backward.py): dQ, dK, dV of sum(dO * O), with O the
 library's own forward output for the same bf16 Q, K, V (as a training step
 would pass it).
 
-Gate (tests/gates.py, check_grad): per head, the relative RMS error of the
-whole gradient array <= 3e-2; per row, the error <= 1e-1 of the row's norm,
-or, for a row whose terms cancel exactly by the algebra (dQ of a head's
-first token), <= 4 x 2^-9 of its terms' magnitude sum (tests/grad_scales.py).
+Gates (tests/gates.py, check_grad): per head, the relative RMS error of the
+whole gradient array <= 3e-2; per block of 64 rows <= 5e-2; per row, the
+error <= 1e-1 of the row's norm or <= 2^-4 of the magnitude of the two sums
+the kernels form for it (tests/grad_scales.py), whichever is larger.
 Every row is compared, at the long workload too.
 """
 
@@ -110,5 +110,6 @@ def test_backward_long_workload_full(lib):
     refs = heads.map_heads(_grad_rows_all, q, k, v, dO)
     scales = heads.map_heads(grad_scales, q, k, v, dO)
     for name, g, r, sc in zip(("dQ", "dK", "dV"), got, refs, scales):
-        head, row = check_grad(g, r, sc, name)
-        print(f"backward long {name}: head RMS error {head:.3e}, worst row {row:.3f} of its bound", flush=True)
+        head, block, row = check_grad(g, r, sc, name)
+        print(f"backward long {name}: head RMS error {head:.3e}, block RMS error {block:.3e}, "
+              f"worst row {row:.3f} of its bound", flush=True)

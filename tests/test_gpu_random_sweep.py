@@ -16,7 +16,8 @@ from oracle import gated as gat
 from oracle import gla as glo
 from oracle import linear_attention as ora
 from kernelized_linear_attention_elu_amd import synth
-from tests import test_gpu_backward as tb
+from tests.gates import check_grad
+from tests.grad_scales import grad_scales
 from tests.gpu_util import check_close, f32_dev, to_dev, to_host
 from tests.test_gpu_gla import FLOOR
 
@@ -91,8 +92,8 @@ def _case(lib, rng, om, span_set):
         O = lib.forward(Q, K, V)
         grads = lib.backward(Q, K, V, O, to_dev(dO, "bf16"))
         torch.cuda.synchronize()
-        for nm, gt, rf, sc in zip(("dQ", "dK", "dV"), grads, bwd.grad_causal(q, k, v, dO), tb._scales(q, k, v, dO)):
-            tb._check(to_host(gt), rf, sc, f"{what} {nm}")
+        for nm, gt, rf, sc in zip(("dQ", "dK", "dV"), grads, bwd.grad_causal(q, k, v, dO), grad_scales(q, k, v, dO)):
+            check_grad(to_host(gt), rf, sc, f"{what} {nm}")
 
 
 def _decode_case(lib, rng, pick):
