@@ -84,7 +84,8 @@ typedef enum la_status {
   LA_ERR_UNSUPPORTED = 3, /* valid request outside the supported shapes         */
   LA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                   */
   LA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required            */
-  LA_ERR_HIP = 6          /* the HIP runtime reported an error                  */
+  LA_ERR_HIP = 6,         /* the HIP runtime reported an error                  */
+  LA_ERR_SCRATCH = 7      /* la_forward_noalloc: the call needs more than its fixed scratch */
 } la_status;
 
 typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
@@ -167,6 +168,28 @@ la_status la_forward_timed(const void *Q, const void *K, const void *V, void *O,
                            int d_v, int io_dtype, int phi, int r, const float *omega, int causal, int chunk,
                            const float *S0, const float *z0, float *S_out, float *z_out, void *workspace,
                            size_t workspace_bytes, void *stream, void *const *events);
+
+/*
+ * la_forward without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results and errors as la_forward, except that the span states live in a
+ * fixed scratch array of LA_NOALLOC_SCRATCH_BYTES bytes inside the library,
+ * of which each GPU holds one copy from its first call until the process
+ * ends (its device address is looked up once per device).  A call whose
+ * workspace (la_forward_workspace_bytes) would exceed that size returns
+ * LA_ERR_SCRATCH before any device call; use la_forward with a workspace for
+ * such shapes.  The function calls no hipMalloc, hipFree or other
+ * allocating routine.  Every call on one GPU shares that GPU's scratch, so
+ * calls that overlap on one GPU (different streams, different threads
+ * without ordering between them) race and give wrong results; calls
+ * ordered on one stream are safe.  Nothing in the scratch has to start at
+ * zero: every call writes each span state it reads.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (32u << 20)
+la_status la_forward_noalloc(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int d,
+                             int d_v, int io_dtype, int phi, int r, const float *omega, int causal, int chunk,
+                             const float *S0, const float *z0, float *S_out, float *z_out, void *stream);
 
 /*
  * Decode step for B*H independent sequences/heads ("Efficient attention

@@ -27,7 +27,7 @@ PHI = {"elu1": 0, "favor": 1, "identity": 2}
 LA_FORWARD_KERNELS = 3
 LA_BACKWARD_KERNELS = 5
 STATUS = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_UNSUPPORTED",
-          4: "LA_ERR_ALIGN", 5: "LA_ERR_WORKSPACE", 6: "LA_ERR_HIP"}
+          4: "LA_ERR_ALIGN", 5: "LA_ERR_WORKSPACE", 6: "LA_ERR_HIP", 7: "LA_ERR_SCRATCH"}
 
 _lib = None
 
@@ -40,6 +40,7 @@ _SIGS = {
     "la_forward_config": (_i, [_i] * 10 + [ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "la_forward": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
     "la_forward_timed": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp, _vp]),
+    "la_forward_noalloc": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5),
     "la_decode_step": (_i, [_vp] * 8 + [_i] * 7 + [_vp, _vp]),
     "la_forward_decay_config": (_i, [_i] * 9 + [ctypes.POINTER(_i)]),
     "la_forward_decay": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _i, _i] + [_vp] * 5 + [ctypes.c_size_t, _vp]),
@@ -327,6 +328,49 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
     else:
         arr = (ctypes.c_void_p * (2 * LA_FORWARD_KERNELS))(*events)
         _check(fn(*args, arr), name)
+    if return_state:
+        return out, S_out, z_out
+    return out
+
+
+def forward_noalloc(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, z0=None,
+                    return_state=False, out=None):
+    """la_forward_noalloc: the same result as :func:`forward`, computed with
+    the library's fixed per-GPU scratch instead of a workspace (the entry
+    point allocates nothing; this binding allocates ``out`` and the returned
+    state through torch unless they are given)."""
+    torch = _torch()
+    lib = load_library()
+    if Q.dim() != 4 or K.dim() != 4 or V.dim() != 4:
+        raise ValueError("Q, K, V must be [B, H, N, d]")
+    B, H, N, d = Q.shape
+    dv = V.shape[-1]
+    if K.shape != Q.shape or V.shape[:3] != Q.shape[:3]:
+        raise ValueError("shape mismatch between Q, K, V")
+    dev = Q.device
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        _require(t, name, Q.dtype, dev)
+    io = _io_code(Q)
+    _require(omega, "omega", torch.float32, dev)
+    r = _omega_rows(omega, phi, d)
+    if (S0 is None) != (z0 is None):
+        raise ValueError("give both S0 and z0 or neither")
+    _require(S0, "S0", torch.float32, dev)
+    _require(z0, "z0", torch.float32, dev)
+    if S0 is not None and (tuple(S0.shape) != (B, H, r, dv) or tuple(z0.shape) != (B, H, r)):
+        raise ValueError("S0 must be [B,H,r,dv] and z0 [B,H,r]")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=Q.dtype, device=dev)
+    _require(out, "out", Q.dtype, dev)
+    if tuple(out.shape) != (B, H, N, dv):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(B, H, N, dv)}")
+    S_out = z_out = None
+    if return_state:
+        S_out = torch.empty((B, H, r, dv), dtype=torch.float32, device=dev)
+        z_out = torch.empty((B, H, r), dtype=torch.float32, device=dev)
+    _check(lib.la_forward_noalloc(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, d, dv, io, PHI[phi], r,
+                                  _ptr(omega), int(causal), chunk, _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out),
+                                  _stream(dev)), "la_forward_noalloc")
     if return_state:
         return out, S_out, z_out
     return out

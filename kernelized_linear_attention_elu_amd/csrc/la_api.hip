@@ -6,6 +6,7 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -171,6 +172,37 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
   return hip_status(la::prefill_launch(a));
 }
 
+// ------------------------------------------------------------------ fixed scratch
+
+// Device memory of la_forward_noalloc, for callers that cannot allocate: the
+// span states of the three-kernel path live in this file-scope array, of
+// which every GPU the library runs on holds its own copy until the process
+// ends.  Host code never passes the array's name to a kernel: its device
+// address on the current GPU comes from hipGetSymbolAddress, looked up once
+// per device on that device's first call and kept below.
+constexpr size_t kScratchBytes = LA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+la_status scratch_address(void** out) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return LA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (es != hipSuccess) return hip_status(es);
+    if (!p) return LA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,6 +255,22 @@ la_status la_forward_timed(const void* Q, const void* K, const void* V, void* O,
                            size_t workspace_bytes, void* stream, void* const* events) {
   return forward_impl(Q, K, V, O, B, H, N, d, d_v, io_dtype, phi, r, omega, causal, chunk, S0, z0, S_out, z_out,
                       workspace, workspace_bytes, stream, events);
+}
+
+la_status la_forward_noalloc(const void* Q, const void* K, const void* V, void* O, int B, int H, int N, int d,
+                             int d_v, int io_dtype, int phi, int r, const float* omega, int causal, int chunk,
+                             const float* S0, const float* z0, float* S_out, float* z_out, void* stream) {
+  // the size limit is checked before any runtime call
+  Shape sh;
+  const la_status st = check_forward_shape(B, H, N, d, d_v, io_dtype, phi, r, causal, chunk, &sh);
+  if (st != LA_OK) return st;
+  if (workspace_for(sh) > kScratchBytes) return LA_ERR_SCRATCH;
+  if (sh.BH == 0) return LA_OK;
+  void* ws = nullptr;
+  const la_status sa = scratch_address(&ws);
+  if (sa != LA_OK) return sa;
+  return forward_impl(Q, K, V, O, B, H, N, d, d_v, io_dtype, phi, r, omega, causal, chunk, S0, z0, S_out, z_out,
+                      ws, kScratchBytes, stream, nullptr);
 }
 
 namespace {
@@ -472,6 +520,7 @@ const char* la_status_string(int status) {
     case LA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case LA_ERR_WORKSPACE: return "workspace missing or too small";
     case LA_ERR_HIP: return "HIP runtime error";
+    case LA_ERR_SCRATCH: return "the call needs more device memory than the fixed scratch of la_forward_noalloc holds";
     default: return "unknown status";
   }
 }

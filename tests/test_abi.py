@@ -30,8 +30,8 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
-        assert lib.la_status_string(code).decode()
+    for code in range(8):
+        assert lib.la_status_string(code).decode() != "unknown status"
     assert lib.la_status_string(99).decode() == "unknown status"
     assert lib.la_version() >= 100
 
@@ -297,3 +297,21 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(la, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         la.load_library(str(tmp_path / "nope.so"))
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch(lib, span_tokens):
+    """la_forward_noalloc returns LA_ERR_SCRATCH, before any device call, for
+    a call whose span states exceed its fixed 32 MiB scratch, and validates
+    its arguments like la_forward."""
+    E = 64 * 64 + 64
+    nf = lambda B, H, N, **kw: lib.la_forward_noalloc(FAKE, FAKE, FAKE, FAKE, B, H, N, 64, 64, 1, 0, 0, None, 1,
+                                                      kw.get("chunk", 64), None, None, None, None, None)
+    assert _ws(1, 1024, 32768) == 1024 * 2 * E * 4 > (32 << 20)
+    assert nf(1, 1024, 32768) == 7                                      # LA_ERR_SCRATCH
+    span_tokens(64)
+    assert _ws(1, 4, 32768) > (32 << 20)
+    assert nf(1, 4, 32768) == 7
+    span_tokens(0)
+    assert nf(1, 1, 64, chunk=24) == 3                                   # LA_ERR_UNSUPPORTED
+    assert nf(-1, 1, 64) == 2                                            # LA_ERR_SHAPE
+    assert lib.la_status_string(7).decode().startswith("the call needs more device memory")
