@@ -40,8 +40,8 @@
  *     the matrix cores as bf16 with fp32 accumulation.  Outputs are rounded
  *     to nearest-even.
  *   - r: feature dimension.  For LA_PHI_ELU1 and LA_PHI_IDENTITY r must equal d
- *     (0 is accepted and means d).  For LA_PHI_FAVOR r is the number of omega
- *     rows.
+ *     (0 is accepted and means d).  For LA_PHI_FAVOR (and
+ *     LA_PHI_FAVOR_PRECISE) r is the number of omega rows.
  *   - stream: a hipStream_t (NULL = the default stream).  All work is enqueued
  *     asynchronously on it; the library allocates no memory, keeps no state
  *     between calls and is re-entrant.
@@ -90,7 +90,24 @@ typedef enum la_status {
 
 typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 
-typedef enum la_phi_kind { LA_PHI_ELU1 = 0, LA_PHI_FAVOR = 1, LA_PHI_IDENTITY = 2 } la_phi_kind;
+/* Feature maps.  LA_PHI_FAVOR_PRECISE is FAVOR+ with the same features and
+ * results up to rounding ("Efficient attention variants", sec. 6); only
+ * la_forward's output pass differs: it projects with omega carried as a bf16
+ * hi + lo pair instead of bf16 hi, which keeps bf16-level accuracy for inputs
+ * whose norms exceed the workloads' (|u| / d^(1/4) of 2 and more, where the
+ * fast form's relative error per output row grows to about 1.5e-2 and, at
+ * 8, 5e-2), at about 1.45 times that pass's time.  Everywhere else it is
+ * LA_PHI_FAVOR.  Both FAVOR+ forms evaluate the features of a query row
+ * shifted by a constant of that row, and every key of a (batch, head) by one
+ * constant taken from its first key; both constants cancel in the ratio,
+ * keep the features' products inside fp32's range for large norms, and are
+ * taken out of the returned S_N, z_N (and put into a given S0, z0). */
+typedef enum la_phi_kind {
+  LA_PHI_ELU1 = 0,
+  LA_PHI_FAVOR = 1,
+  LA_PHI_IDENTITY = 2,
+  LA_PHI_FAVOR_PRECISE = 3
+} la_phi_kind;
 
 /* Number of kernels la_forward enqueues (per-span state, span scan, output). */
 #define LA_FORWARD_KERNELS 3

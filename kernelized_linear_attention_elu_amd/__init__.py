@@ -23,7 +23,10 @@ LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "la.h")
 
 LA_F32, LA_BF16 = 0, 1
-PHI = {"elu1": 0, "favor": 1, "identity": 2}
+# "favor_precise": FAVOR+ whose prefill output pass projects with omega in
+# bf16 hi + lo (for inputs of large norm; la.h, LA_PHI_FAVOR_PRECISE)
+PHI = {"elu1": 0, "favor": 1, "identity": 2, "favor_precise": 3}
+FAVOR = ("favor", "favor_precise")
 LA_FORWARD_KERNELS = 3
 LA_BACKWARD_KERNELS = 5
 STATUS = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE", 3: "LA_ERR_UNSUPPORTED",
@@ -160,7 +163,7 @@ def _require(t, name, dtype=None, device=None):
 
 def _omega_rows(omega, phi, d):
     """Feature count r: omega's rows for FAVOR+ (omega must be [r, d]), else d."""
-    if phi != "favor":
+    if phi not in FAVOR:
         return d
     if omega is None or omega.dim() != 2 or omega.shape[1] != d:
         raise ValueError(f"FAVOR+ needs omega of shape [r, {d}], got "
@@ -295,7 +298,7 @@ def forward(Q, K, V, *, phi="elu1", omega=None, causal=True, chunk=64, S0=None, 
         raise ValueError("give at most one of gamma, log_gate, log_gate_ch")
     if n_decay == 0 and not normalize:
         raise ValueError("normalize=False is available with a decay (gamma, log_gate or log_gate_ch) only")
-    if n_decay and phi == "favor":
+    if n_decay and phi in FAVOR:
         raise ValueError("the decay is available for the pointwise feature maps only")
     if log_gate_ch is not None:
         need = int(lib.la_forward_gla_workspace_bytes(B, H, N, d, dv, io, PHI[phi], r, chunk))

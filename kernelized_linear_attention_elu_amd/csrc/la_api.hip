@@ -28,6 +28,10 @@ la_status hip_status(hipError_t e) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The precise FAVOR+ form computes the same features as LA_PHI_FAVOR (only
+// the prefill output pass differs): everything but that pass sees FAVOR.
+int canon_phi(int phi) { return phi == LA_PHI_FAVOR_PRECISE ? LA_PHI_FAVOR : phi; }
+
 int norm_r(int phi, int d, int r) {
   if (phi == LA_PHI_ELU1 || phi == LA_PHI_IDENTITY) return r == 0 ? d : r;
   return r;
@@ -135,6 +139,7 @@ la_status check_forward_shape(int B, int H, int N, int d, int d_v, int io, int p
 }
 
 size_t workspace_for(const Shape& sh, bool gated = false, bool per_channel = false) {
+  if (sh.phi == LA_PHI_FAVOR) return la::favor_workspace_bytes(sh.BH, sh.n_span, sh.r, sh.dv);
   return la::prefill_workspace_bytes(sh.BH, sh.n_span, sh.r, sh.dv, gated, per_channel);
 }
 
@@ -145,6 +150,8 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
                        const float* z0, float* S_out, float* z_out, void* workspace, size_t workspace_bytes,
                        void* stream, void* const* events, const float* gamma = nullptr, int normalize = 1,
                        const float* log_a = nullptr, const float* log_a_ch = nullptr) {
+  const bool precise = phi == LA_PHI_FAVOR_PRECISE;
+  phi = canon_phi(phi);
   Shape sh;
   const int decay = log_a_ch != nullptr ? 2 : (gamma != nullptr || log_a != nullptr) ? 1 : 0;
   la_status st = check_forward_shape(B, H, N, d, d_v, io, phi, r, causal, chunk, &sh, decay);
@@ -169,6 +176,7 @@ la_status forward_impl(const void* Q, const void* K, const void* V, void* O, int
   a.S0 = S0; a.z0 = z0; a.S_out = S_out; a.z_out = z_out;
   a.workspace = workspace; a.stream = stream; a.events = events;
   a.gamma = gamma; a.normalize = normalize; a.log_a = log_a; a.log_a_ch = log_a_ch;
+  a.favor_precise = precise ? 1 : 0;
   return hip_status(la::prefill_launch(a));
 }
 
@@ -218,14 +226,14 @@ int la_get_span_tokens(void) { return g_span_tokens.load(std::memory_order_relax
 size_t la_forward_workspace_bytes(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int causal,
                                   int chunk) {
   Shape sh;
-  if (check_forward_shape(B, H, N, d, d_v, io_dtype, phi, r, causal, chunk, &sh) != LA_OK) return 0;
+  if (check_forward_shape(B, H, N, d, d_v, io_dtype, canon_phi(phi), r, causal, chunk, &sh) != LA_OK) return 0;
   return workspace_for(sh);
 }
 
 la_status la_forward_config(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int causal, int chunk,
                             int* n_span, int* single_pass) {
   Shape sh;
-  const la_status st = check_forward_shape(B, H, N, d, d_v, io_dtype, phi, r, causal, chunk, &sh);
+  const la_status st = check_forward_shape(B, H, N, d, d_v, io_dtype, canon_phi(phi), r, causal, chunk, &sh);
   if (st != LA_OK) return st;
   if (n_span) *n_span = sh.n_span;
   if (single_pass) *single_pass = 0;
@@ -262,7 +270,7 @@ la_status la_forward_noalloc(const void* Q, const void* K, const void* V, void* 
                              const float* S0, const float* z0, float* S_out, float* z_out, void* stream) {
   // the size limit is checked before any runtime call
   Shape sh;
-  const la_status st = check_forward_shape(B, H, N, d, d_v, io_dtype, phi, r, causal, chunk, &sh);
+  const la_status st = check_forward_shape(B, H, N, d, d_v, io_dtype, canon_phi(phi), r, causal, chunk, &sh);
   if (st != LA_OK) return st;
   if (workspace_for(sh) > kScratchBytes) return LA_ERR_SCRATCH;
   if (sh.BH == 0) return LA_OK;
@@ -279,6 +287,7 @@ la_status decode_impl(const float* S, const float* z, const void* q, const void*
                       float* S_new, float* z_new, int B, int H, int d, int d_v, int io_dtype, int phi, int r,
                       const float* omega, void* stream, const float* gamma, int normalize,
                       const float* log_a = nullptr, const float* log_a_ch = nullptr) {
+  if (!gamma && !log_a && !log_a_ch) phi = canon_phi(phi);
   if (B < 0 || H < 0 || d <= 0 || d_v <= 0 || r < 0) return LA_ERR_SHAPE;
   if (static_cast<long long>(B) * H > 0x7fffffffLL) return LA_ERR_SHAPE;
   if (io_dtype != LA_F32 && io_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
@@ -493,6 +502,7 @@ la_status la_backward_timed(const void* Q, const void* K, const void* V, const v
 
 la_status la_feature_map(const void* X, float* Y, long long rows, int d, int io_dtype, int phi, int r,
                          const float* omega, void* stream) {
+  phi = canon_phi(phi);
   if (rows < 0 || d <= 0 || r < 0 || d > kMaxDim) return LA_ERR_SHAPE;
   if (io_dtype != LA_F32 && io_dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
   if (phi != LA_PHI_ELU1 && phi != LA_PHI_FAVOR && phi != LA_PHI_IDENTITY) return LA_ERR_UNSUPPORTED;

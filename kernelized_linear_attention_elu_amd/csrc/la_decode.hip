@@ -47,9 +47,13 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
 // Features of one input vector u (length D) into out[R] (LDS), fp32.
 // FAVOR+ ("Efficient attention variants" sec. 6): x = u / D^(1/4),
 // phi(u)_f = exp(w_f . x - |x|^2 / 2) / sqrt(R) with w_f the f-th row of omega.
+// For the query (query_row) the row's constant exp(4 |x| - |x|^2 / 2) is
+// taken out, exp(w_f . x - 4 |x|) / sqrt(R): it cancels in the normalised
+// read-out (FAVOR+ decode is always normalised) and keeps phi(q) . S within
+// fp32's range for queries of large norm, as in the prefill.
 template <typename T, int D, int R, int PHI>
 __device__ __forceinline__ void features_to_lds(const T* u, const float* __restrict__ omega, float* out,
-                                                float* xbuf, float* scratch) {
+                                                float* xbuf, float* scratch, bool query_row) {
   const int tid = threadIdx.x;
   if constexpr (PHI == PHI_FAVOR) {
     const float scale = 1.0f / sqrtf(sqrtf(static_cast<float>(D)));
@@ -61,12 +65,13 @@ __device__ __forceinline__ void features_to_lds(const T* u, const float* __restr
     }
     sq = block_sum(sq, scratch);  // contains a barrier: xbuf is visible after it
     const float inv_sqrt_r = 1.0f / sqrtf(static_cast<float>(R));
+    const float shift = query_row ? 4.0f * sqrtf(sq) : 0.5f * sq;
     for (int f = tid; f < R; f += kThreads) {
       const float* wrow = omega + (size_t)f * D;
       float p = 0.f;
 #pragma unroll 8
       for (int i = 0; i < D; ++i) p += wrow[i] * xbuf[i];
-      out[f] = __expf(p - 0.5f * sq) * inv_sqrt_r;
+      out[f] = __expf(p - shift) * inv_sqrt_r;
     }
     __syncthreads();
   } else {
@@ -101,8 +106,8 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
   const float gm = log_a ? __builtin_amdgcn_exp2f(fmaxf(log_a[bh] * 1.4426950408889634f, -126.f))
                         : gamma ? gamma[bh % H] : 1.f;
 
-  features_to_lds<T, D, R, PHI>(q + (size_t)bh * D, omega, fq, xbuf, scratch[0]);
-  features_to_lds<T, D, R, PHI>(k + (size_t)bh * D, omega, fk, xbuf, scratch[1]);
+  features_to_lds<T, D, R, PHI>(q + (size_t)bh * D, omega, fq, xbuf, scratch[0], true);
+  features_to_lds<T, D, R, PHI>(k + (size_t)bh * D, omega, fk, xbuf, scratch[1], false);
   for (int c = tid; c < DV; c += kThreads) vv[c] = load_io<T>(v + (size_t)bh * DV + c);
   // per-channel gates (state row f keeps a_f of itself; the floor of the
   // per-channel gated prefill, log2 a >= -14)

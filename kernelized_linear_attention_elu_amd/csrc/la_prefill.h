@@ -25,6 +25,7 @@ struct PrefillArgs {
   void* workspace;
   void* stream;
   void* const* events;  // optional: 6 hipEvent_t recorded around the three kernels
+  int favor_precise = 0;  // FAVOR+: output-pass projections with omega hi + lo
   // fixed per-head decay (device [H] fp32 in (0, 1]; null: none), causal
   // pointwise maps only: S_t = gamma S_{t-1} + phi(k_t) v_t^T, z likewise
   const float* gamma = nullptr;
@@ -48,6 +49,15 @@ inline size_t prefill_workspace_bytes(long long BH, int n_span, int r, int dv, b
   const size_t tot = per_channel ? (size_t)BH * n_span * r : gated ? (size_t)BH * n_span : 0;
   return (size_t)BH * ((size_t)n_span + 1) * E * sizeof(float) + tot * sizeof(float);
 }
+// FAVOR+ workspace: the span states, then one fp32 per head (the log2
+// scale kappa of its stored states), at a 256-byte boundary.
+inline size_t favor_workspace_bytes(long long BH, int n_span, int r, int dv) {
+  const size_t states = ((prefill_workspace_bytes(BH, n_span, r, dv, false) + 255) / 256) * 256;
+  return states + (size_t)BH * sizeof(float);
+}
+inline size_t favor_kappa_offset(long long BH, int n_span, int r, int dv) {
+  return ((prefill_workspace_bytes(BH, n_span, r, dv, false) + 255) / 256) * 256;
+}
 // Shapes the per-channel gated prefill supports (causal, ELU+1 / identity).
 bool gla_supported(int io, int d, int dv, int r, int chunk);
 
@@ -63,11 +73,14 @@ hipError_t favor_prefill_launch(const PrefillArgs& a);
 // gamma^L; span lengths follow from N, the chunk and n_span.  With gates
 // (totals: [BH][n_span] total log2 gate of each span), span s multiplies it
 // by 2^totals[s].  total_only (no decay or gates): only the total, slot
-// n_span, is written (what the non-causal form reads).
+// n_span, is written (what the non-causal form reads).  kappa (no decay or
+// gates; device [BH] fp32, null: none): the span states are stored at
+// 2^kappa[bh] times their value, so S0/z0 are multiplied by 2^kappa on entry
+// and S_out/z_out by 2^-kappa.
 hipError_t scan_launch(float* ws, int BH, int R, int DV, int n_span, const float* S0, const float* z0,
                        float* S_out, float* z_out, hipStream_t stream, const float* gamma = nullptr, int H = 1,
                        int N = 0, int chunk = 64, const float* totals = nullptr, int per_channel = 0,
-                       int total_only = 0);
+                       int total_only = 0, const float* kappa = nullptr);
 
 // Gradients of the causal normalised output (la_prefill.hip).
 struct BackwardArgs {

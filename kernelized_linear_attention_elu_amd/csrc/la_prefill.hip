@@ -1040,19 +1040,24 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
                                                            float* __restrict__ S_out,
                                                            float* __restrict__ z_out,
                                                            const float* __restrict__ gamma, int H, int N,
-                                                           int chunk, const float* __restrict__ totals) {
+                                                           int chunk, const float* __restrict__ totals,
+                                                           const float* __restrict__ kappa) {
   constexpr bool DECAY = DK == kFixed;
   const int E = R * DV + R;
   const int e = blockIdx.x * kThreads + threadIdx.x;
   const int bh = blockIdx.y;
   if (e >= E) return;
   const bool is_s = e < R * DV;
+  // states stored at 2^kappa times their value (kappa: log2 per head): the
+  // initial state enters, and the final state leaves, rescaled
+  const float kp = kappa ? kappa[bh] : 0.f;
   float acc = 0.f;
   if (is_s) {
     if (S0) acc = S0[(size_t)bh * R * DV + e];
   } else {
     if (z0) acc = z0[(size_t)bh * R + (e - R * DV)];
   }
+  if (kappa) acc *= __builtin_amdgcn_exp2f(kp);
   float* p = ws + (size_t)bh * (n_span + 1) * E + e;
   float lg = 0.f;                    // log2(gamma)
   int q_ch = 0, r_ch = 0, rem = 0;   // n_chunks = q_ch n_span + r_ch; running remainder
@@ -1099,6 +1104,7 @@ __global__ __launch_bounds__(kThreads) void la_scan_kernel(float* __restrict__ w
     }
   }
   p[(size_t)n_span * E] = acc;
+  if (kappa) acc *= __builtin_amdgcn_exp2f(-kp);
   if (is_s) {
     if (S_out) S_out[(size_t)bh * R * DV + e] = acc;
   } else {
@@ -2530,25 +2536,25 @@ static hipError_t dispatch_chunk(const PrefillArgs& a) {
 
 hipError_t scan_launch(float* ws, int BH, int R, int DV, int n_span, const float* S0, const float* z0,
                        float* S_out, float* z_out, hipStream_t stream, const float* gamma, int H, int N, int chunk,
-                       const float* totals, int per_channel, int total_only) {
+                       const float* totals, int per_channel, int total_only, const float* kappa) {
   const int E = R * DV + R;
   if (BH > 0) {
     const dim3 grid((E + kThreads - 1) / kThreads, BH);
     if (totals && per_channel)
       hipLaunchKernelGGL(la_scan_kernel<kChannel>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0,
-                         S_out, z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, totals);
+                         S_out, z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, totals, nullptr);
     else if (totals)
       hipLaunchKernelGGL(la_scan_kernel<kGated>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0, S_out,
-                         z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, totals);
+                         z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, totals, nullptr);
     else if (gamma)
       hipLaunchKernelGGL(la_scan_kernel<kFixed>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0, S_out,
-                         z_out, gamma, H > 0 ? H : 1, N, chunk > 0 ? chunk : 64, nullptr);
+                         z_out, gamma, H > 0 ? H : 1, N, chunk > 0 ? chunk : 64, nullptr, nullptr);
     else if (total_only)
       hipLaunchKernelGGL((la_scan_kernel<kNoDecay, true>), grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0,
-                         z0, S_out, z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, nullptr);
+                         z0, S_out, z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, nullptr, kappa);
     else
       hipLaunchKernelGGL(la_scan_kernel<kNoDecay>, grid, dim3(kThreads), 0, stream, ws, R, DV, n_span, S0, z0,
-                         S_out, z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, nullptr);
+                         S_out, z_out, nullptr, 1, N, chunk > 0 ? chunk : 64, nullptr, kappa);
   }
   return hipGetLastError();
 }

@@ -67,9 +67,64 @@ __device__ __forceinline__ FavorConsts favor_consts() {
   return FavorConsts{log2e * 0.35355339059327373f /* 64^(-1/4) */, log2e / 16.0f /* 1 / (2 sqrt(64)) */,
                      4.0f /* log2(sqrt(256)) */};
 }
-// Per-token part of the exponent, formed once per token when its squared
-// norm is summed: -(|u|^2 log2(e) / (2 sqrt(d)) + log2(sqrt(r))).
+// Per-token part of the exponent of a key: -(|u|^2 log2(e) / (2 sqrt(d)) +
+// log2(sqrt(r))), plus the head's shift kappa; -inf for a token past the
+// end of the sequence, whose features are then exp2(-inf) = 0.
 __device__ __forceinline__ float favor_bias(const FavorConsts& c, float norm2) { return -(norm2 * c.a2 + c.a3); }
+__device__ __forceinline__ float favor_kbias(const FavorConsts& c, float norm2, float kappa, bool valid) {
+  return valid ? favor_bias(c, norm2) + kappa : -__builtin_inff();
+}
+
+// Numeric range ("Efficient attention variants", sec. 6 asks for a stable
+// estimator).  Each feature of a query carries the factor exp(-|x|^2 / 2),
+// each feature of a key as well; for |x| beyond about 12 their products
+// leave the fp32 range and the ratio becomes 0/0.  A constant factor per
+// query row cancels in num/den, and so does one per (batch, head) on all
+// keys, so the kernels evaluate
+//   queries:  exp(w . x - 4 |x|) / sqrt(r)        (the row's factor
+//             exp(4 |x| - |x|^2 / 2) taken out; 4 |x| is about the largest
+//             w . x over 256 features, so the row's largest feature stays
+//             near 1 for any |x|),
+//   keys:     exp(w . x - |x|^2 / 2 + kappa_h) / sqrt(r),
+//             kappa_h = |x_0|^2 / 2 - 4 |x_0|, x_0 the head's first key
+//             (its own largest feature near 1; the first key enters every
+//             output, so no later token changes a result).
+// The span states carry the factor 2^kappa_h (log2 units below); the scan
+// takes it out of the returned S_N, z_N and puts it into a given S0, z0.
+// Key norms that differ from the first key's by much more than the first
+// key's own norm can still leave the range.
+constexpr float kQueryShift = 4.0f;
+__device__ __forceinline__ float favor_qbias(const FavorConsts& c, float norm2) {
+  return -(c.a1 * kQueryShift * __builtin_sqrtf(norm2) + c.a3);
+}
+// (the same in every lane: kept in a scalar register)
+__device__ __forceinline__ float favor_kappa(const FavorConsts& c, float norm2_first) {
+  const float k = norm2_first * c.a2 - c.a1 * kQueryShift * __builtin_sqrtf(norm2_first);
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(k)));
+}
+// |u|^2 of the head's first key, in every thread (8 threads per 16-byte
+// piece of the row, a 3-step butterfly); 0 for an empty head.
+__device__ __forceinline__ float favor_first_norm2(__amdgpu_buffer_rsrc_t k) {
+  float f[8];
+  unpack16<bf16>(__builtin_amdgcn_raw_buffer_load_b128(k, (threadIdx.x & 7) * 16, 0, 0), f);
+  float n2 = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) n2 += f[e] * f[e];
+  n2 += __shfl_xor(n2, 1);
+  n2 += __shfl_xor(n2, 2);
+  n2 += __shfl_xor(n2, 4);
+  return n2;
+}
+// Precision of the output pass's projections.  By default they use omega's
+// bf16 hi part only: omega's rounding (2^-9 relative) puts an error of about
+// 2^-9 |w . x| into the exponent of each feature, which at the workload's
+// norms (|x| near 1) is below the bf16 rounding of the features themselves,
+// but at |x| of 2 and more shows in the outputs (about 1.5e-2 relative per
+// row at |x| = 2, 5e-2 at 8).  The precise form (LA_PHI_FAVOR_PRECISE) adds
+// the lo part, as the span state pass always does, at about 1.45 times the
+// output pass's time.  Selecting the form per token inside the pass would
+// keep the fast form's speed only if it cost no registers, which it does
+// not at 256 VGPRs, so the caller chooses.
 // phi for one feature: exp2(proj log2(e) d^(-1/4) + bias) - one FMA and one exp2
 // (0 for the bias -inf of a masked token, whose projection is 0).
 __device__ __forceinline__ float favor_phi(const FavorConsts& c, float proj, float bias) {
@@ -104,6 +159,25 @@ struct OmegaFrags {
   }
 };
 
+// omega's lo fragment (round(x - hi)) for feature tile j, k-step ks of wave
+// w, read from memory where needed (the output pass keeps only hi in
+// registers).  The lane's byte offset is formed here, behind an empty asm
+// statement, so that it is not kept live across the chunk loop.
+__device__ __forceinline__ bf16x8 omega_lo_frag(__amdgpu_buffer_rsrc_t om, int w, int j, int ks) {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int off = (((16 * (FPW * w + j) + (lane & 15)) * FD + 32 * ks + 8 * (lane >> 4)) * 4);
+  const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(om, off, 0, 0));
+  const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(om, off + 16, 0, 0));
+  bf16x8 lo;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = e < 4 ? a[e] : b[e - 4];
+    lo[e] = static_cast<bf16>(x - static_cast<float>(static_cast<bf16>(x)));
+  }
+  return lo;
+}
+
 // Raw (unmapped) chunk rows held in registers between load and staging.
 template <int NS>
 struct RawRegs {
@@ -125,14 +199,15 @@ __device__ __forceinline__ void load_raw(RawRegs<NS>& rr, const __amdgpu_buffer_
 }
 
 // Registers -> LDS (row-major swizzled 64 x 64 tiles).  For the streams
-// flagged in `norms`, the squared norm of each token row is summed in fp32
-// (8 threads hold one row: a 3-step butterfly) and its exponent bias is
-// written to nrm.  For the streams flagged in `masked`, rows at or beyond
-// `live` (tokens past the end of the sequence; their raw rows read as zero)
-// get the bias -inf instead, so that every feature of theirs is exp2(-inf) = 0.
+// flagged in `norms`, the squared norm |u|^2 of each token row is summed in
+// fp32 (8 threads hold one row: a 3-step butterfly) and its exponent bias
+// is written to nrm: the query form for the streams flagged in `queries`,
+// otherwise the key form with the head's shift kappa, and -inf for rows at
+// or beyond `live` (tokens past the end of the sequence; their raw rows
+// read as zero), so that every feature of theirs is exp2(-inf) = 0.
 template <int NS>
 __device__ __forceinline__ void stage_raw(const RawRegs<NS>& rr, bf16* const (&dst)[NS], float* const (&nrm)[NS],
-                                          int norms, int masked, int live) {
+                                          int norms, int queries, float kappa, int live) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < FLQ; ++i) {
@@ -150,8 +225,10 @@ __device__ __forceinline__ void stage_raw(const RawRegs<NS>& rr, bf16* const (&d
         n2 += __shfl_xor(n2, 1);
         n2 += __shfl_xor(n2, 2);
         n2 += __shfl_xor(n2, 4);
-        if ((tid & 7) == 0)
-          nrm[s][tok] = (masked & (1 << s)) && tok >= live ? -__builtin_inff() : favor_bias(favor_consts(), n2);
+        if ((tid & 7) == 0) {
+          const FavorConsts c = favor_consts();
+          nrm[s][tok] = (queries & (1 << s)) ? favor_qbias(c, n2) : favor_kbias(c, n2, kappa, tok < live);
+        }
       }
     }
   }
@@ -195,7 +272,9 @@ __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
 __global__ __launch_bounds__(FNT, 1) void la_state_favor_kernel(const bf16* __restrict__ K,
                                                                      const bf16* __restrict__ V,
                                                                      const float* __restrict__ omega,
-                                                                     float* __restrict__ ws, int N, int n_span) {
+                                                                     float* __restrict__ ws,
+                                                                     float* __restrict__ kappa_out, int N,
+                                                                     int n_span) {
   __shared__ bf16 kraw[2][FC * FD];
   __shared__ bf16 vt[2][FC * FDV];
   __shared__ float kn[2][FC];
@@ -210,6 +289,8 @@ __global__ __launch_bounds__(FNT, 1) void la_state_favor_kernel(const bf16* __re
   const FavorConsts fc = favor_consts();
   OmegaFrags<true> om;
   om.load(omega, w, g, li);
+  const float kappa = favor_kappa(fc, favor_first_norm2(src[0]));
+  if (s == 0 && tid == 0) kappa_out[bh] = kappa;
 
   // dz on the MFMA as well (a ones operand against the same hi + lo feature
   // fragments), off the VALU, which the features keep busy: lane (g, li) of
@@ -236,7 +317,7 @@ __global__ __launch_bounds__(FNT, 1) void la_state_favor_kernel(const bf16* __re
     {
       bf16* const dst[2] = {kraw[buf], vt[buf]};
       float* const nrm[2] = {kn[buf], nullptr};
-      stage_raw<2>(rr, dst, nrm, 1, 1, N - t0);
+      stage_raw<2>(rr, dst, nrm, 1, 0, kappa, N - t0);
     }
     if (k + 1 < nch) load_raw<2>(rr, src, t0 - FC);
     __syncthreads();
@@ -356,7 +437,7 @@ __device__ __forceinline__ bf16x8 tr2(const bf16* p0, const bf16* p1) { return c
 // block's weights and denominator and produces value tiles 2 (w / 4) and
 // 2 (w / 4) + 1.  Carried state: wave w owns value tile w mod 4 and feature
 // tiles 8 (w / 4) .. +7, and z tiles w and w + 8.
-template <bool CAUSAL>
+template <bool CAUSAL, bool PRECISE>
 __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __restrict__ Q,
                                                                  const bf16* __restrict__ K,
                                                                  const bf16* __restrict__ V,
@@ -377,8 +458,9 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
                                          make_rsrc(V + bh * head, hbytes)};
   const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(O + bh * head, hbytes);
   const FavorConsts fc = favor_consts();
-  OmegaFrags<false> om;  // phi tiles are rounded to bf16 here: omega hi suffices
+  OmegaFrags<false> om;  // phi tiles are rounded to bf16 here: omega hi (lo in the precise form)
   om.load(omega, w, g, li);
+  const float kappa = CAUSAL ? favor_kappa(fc, favor_first_norm2(src[1])) : 0.f;
 
   constexpr int TPW = FFT * FCT / FNW;  // carried state tiles per wave (8)
   constexpr int ZPW = FFT / FNW;        // z tiles per wave (2)
@@ -468,7 +550,7 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
     {
       bf16* const dst[3] = {sm.qraw[buf], sm.kraw[buf], sm.v[buf]};
       float* const nrm[3] = {sm.qn[buf], sm.kn[buf], nullptr};
-      stage_raw<3>(rr, dst, nrm, CAUSAL ? 3 : 1, 2, N - t0);
+      stage_raw<3>(rr, dst, nrm, CAUSAL ? 3 : 1, 1, kappa, N - t0);
     }
     if (t0 + FC < t_end) load_raw<3>(rr, src, t0 + FC);
     __syncthreads();
@@ -494,6 +576,15 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
           nb[p][st] = nrm[st][16 * tb + li];
         }
       };
+      // the precise form: omega's lo fragments, read once per chunk (from cache)
+      bf16x8 olo[PRECISE ? FPW : 1][2];
+      if constexpr (PRECISE) {
+        const __amdgpu_buffer_rsrc_t omrsrc = make_rsrc(omega, FR * FD * 4);
+#pragma unroll
+        for (int j = 0; j < FPW; ++j)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) olo[j][ks] = omega_lo_frag(omrsrc, w, j, ks);
+      }
       read_block(0, 0);
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
@@ -506,7 +597,10 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
           for (int j = 0; j < FPW; ++j) {
             pr[st][j] = zero4();
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) pr[st][j] = mfma16(om.hi[j][ks], xf[p][st][ks], pr[st][j]);
+            for (int ks = 0; ks < 2; ++ks) {
+              pr[st][j] = mfma16(om.hi[j][ks], xf[p][st][ks], pr[st][j]);
+              if constexpr (PRECISE) pr[st][j] = mfma16(olo[j][ks], xf[p][st][ks], pr[st][j]);
+            }
           }
 #pragma unroll
         for (int st = 0; st < NST; ++st)
@@ -632,24 +726,34 @@ hipError_t favor_prefill_launch(const PrefillArgs& a) {
   auto rec = [&](int i) {
     if (a.events && a.events[i]) (void)hipEventRecord(static_cast<hipEvent_t>(a.events[i]), st);
   };
+  // one log2 state scale per head after the span states (written by the
+  // state pass; with no spans, none is applied)
+  float* kappa = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + favor_kappa_offset(BH, n_span, FR, FDV));
   rec(0);
   if (n_span > 0 && BH > 0)
-    hipLaunchKernelGGL(la_state_favor_kernel, dim3(BH * n_span), dim3(FNT), 0, st, K, V, a.omega, ws, a.N,
+    hipLaunchKernelGGL(la_state_favor_kernel, dim3(BH * n_span), dim3(FNT), 0, st, K, V, a.omega, ws, kappa, a.N,
                        n_span);
   rec(1);
   rec(2);
   hipError_t e = scan_launch(ws, BH, FR, FDV, n_span, a.S0, a.z0, a.S_out, a.z_out, st, nullptr, 1, 0, 64, nullptr,
-                             0, !a.causal);
+                             0, !a.causal, n_span > 0 ? kappa : nullptr);
   if (e != hipSuccess) return e;
   rec(3);
   rec(4);
   if (n_span > 0 && BH > 0) {
-    if (a.causal)
-      hipLaunchKernelGGL((la_output_favor_kernel<true>), dim3(BH * n_span), dim3(FNT), 0, st, Q, K, V, O,
-                         a.omega, ws, a.N, n_span);
+    const dim3 grid(BH * n_span), block(FNT);
+    if (a.causal && a.favor_precise)
+      hipLaunchKernelGGL((la_output_favor_kernel<true, true>), grid, block, 0, st, Q, K, V, O, a.omega, ws, a.N,
+                         n_span);
+    else if (a.causal)
+      hipLaunchKernelGGL((la_output_favor_kernel<true, false>), grid, block, 0, st, Q, K, V, O, a.omega, ws, a.N,
+                         n_span);
+    else if (a.favor_precise)
+      hipLaunchKernelGGL((la_output_favor_kernel<false, true>), grid, block, 0, st, Q, K, V, O, a.omega, ws, a.N,
+                         n_span);
     else
-      hipLaunchKernelGGL((la_output_favor_kernel<false>), dim3(BH * n_span), dim3(FNT), 0, st, Q, K, V, O,
-                         a.omega, ws, a.N, n_span);
+      hipLaunchKernelGGL((la_output_favor_kernel<false, false>), grid, block, 0, st, Q, K, V, O, a.omega, ws, a.N,
+                         n_span);
   }
   rec(5);
   return hipGetLastError();

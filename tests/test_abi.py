@@ -90,9 +90,12 @@ def test_workspace_sizes(lib, span_tokens):
     # unsupported shapes report 0
     assert _ws(1, 1, 16, 96, 96) == 0
     assert _ws(1, 1, 16, 64, 64, chunk=24) == 0
-    # FAVOR+ (r = 256, one output workgroup per CU): B2 H16 N16384 -> 8 spans
+    # FAVOR+ (r = 256, one output workgroup per CU): B2 H16 N16384 -> 8 spans;
+    # the span states, padded to 256 bytes, then one fp32 state scale per head
     EF = 256 * 64 + 256
-    assert _ws(2, 16, 16384, phi=1, r=256) == 32 * 9 * EF * 4
+    states = (32 * 9 * EF * 4 + 255) // 256 * 256
+    assert _ws(2, 16, 16384, phi=1, r=256) == states + 32 * 4
+    assert _ws(2, 16, 16384, phi=3, r=256) == states + 32 * 4  # the precise form: same workspace
     assert _ws(1, 1, 100, phi=1, r=128) == 0
     assert _ws(1, 1, 100, phi=1, r=256, chunk=32) == 0
     assert _ws(1, 1, 100, phi=1, r=256, io=0) == 0
@@ -119,6 +122,8 @@ def test_forward_argument_errors(lib):
     assert _fwd(lib, causal=2) == 3
     assert _fwd(lib, r=32) == 3                         # ELU+1 keeps r = d
     assert _fwd(lib, phi=1, r=256) == 1                 # FAVOR+ needs omega
+    assert _fwd(lib, phi=3, r=256) == 1                 # ... in its precise form too
+    assert _fwd(lib, phi=4) == 3
     assert _fwd(lib, phi=1, r=256, omega=MISALIGNED) == 4
     assert _fwd(lib, phi=1, r=64, omega=FAKE) == 3
     assert _fwd(lib, O=MISALIGNED) == 4                 # LA_ERR_ALIGN

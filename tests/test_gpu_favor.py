@@ -11,6 +11,7 @@ import pytest
 from oracle import heads
 from oracle import linear_attention as ora
 from kernelized_linear_attention_elu_amd import synth
+from tests.gates import row_errors
 from tests.gpu_util import check_close, f32_dev, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -23,10 +24,10 @@ def omega():
     return synth.draw_omega(R, 64)
 
 
-def _run(lib, q, k, v, om, **kw):
+def _run(lib, q, k, v, om, phi="favor", **kw):
     import torch
     Q, K, V = (to_dev(x, "bf16") for x in (q, k, v))
-    out = lib.forward(Q, K, V, phi="favor", omega=f32_dev(om), **kw)
+    out = lib.forward(Q, K, V, phi=phi, omega=f32_dev(om), **kw)
     torch.cuda.synchronize()
     return out
 
@@ -99,15 +100,16 @@ def test_favor_split_prefill_and_decode(lib, span, omega):
     check_close(to_host(o), O_ref[:, :, -1], "bf16", "decode step")
 
 
-def test_favor_no_future_leakage_bitwise(lib, span, omega):
+@pytest.mark.parametrize("phi", ["favor", "favor_precise"])
+def test_favor_no_future_leakage_bitwise(lib, span, omega, phi):
     span(128)
     q, k, v = synth.draw_qkv(1, 2, 400, 64, 64, seed=8)
-    base = to_host(_run(lib, q, k, v, omega))
+    base = to_host(_run(lib, q, k, v, omega, phi=phi))
     for t0 in (256, 200, 37):
         k2, v2 = k.copy(), v.copy()
         k2[..., t0:, :] = synth.round_to_io(k2[..., t0:, :] + 1.0, "bf16")
         v2[..., t0:, :] = synth.round_to_io(v2[..., t0:, :] - 2.0, "bf16")
-        out = to_host(_run(lib, q, k2, v2, omega))
+        out = to_host(_run(lib, q, k2, v2, omega, phi=phi))
         np.testing.assert_array_equal(out[..., :t0, :], base[..., :t0, :])
         assert np.max(np.abs(out[..., t0:, :] - base[..., t0:, :])) > 1e-3
 
@@ -121,3 +123,76 @@ def test_favor_empty_sequence(lib, omega):
     torch.cuda.synchronize()
     assert O.shape == (1, 2, 0, 64) and q.size == 0
     assert np.all(to_host(S) == 0) and np.all(to_host(z) == 0)
+
+
+def _scaled(B, H, N, scale, seed):
+    """Workload-distributed Q, K (norms scale times the workload's, |x| about
+    scale) and V, rounded to bf16."""
+    q, k, v = synth.draw_qkv(B, H, N, 64, 64, seed=seed)
+    return synth.round_to_io(q * scale, "bf16"), synth.round_to_io(k * scale, "bf16"), v
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("scale", [2.0, 6.0, 14.0])
+def test_favor_precise_large_norm(lib, span, omega, scale, causal):
+    """Query and key norms 2, 6 and 14 times the workload's, with the precise
+    form (omega hi + lo in the output pass; "Efficient attention variants",
+    sec. 6: the estimator must stay numerically stable).  At 14 the features'
+    products exp(w . (x_q + x_k) - |x_q|^2 / 2 - |x_k|^2 / 2) / r fall below
+    fp32's range for most rows (tests/test_favor_range.py shows it), so only
+    the per-row query shift and the per-head key shift of the kernels keep
+    the ratio finite.  Outputs and the final state against the fp64 oracle,
+    to the bf16 gates; several spans per head."""
+    span(128)
+    q, k, v = _scaled(1, 2, 333, scale, 21)
+    O, S, z = _run(lib, q, k, v, omega, phi="favor_precise", causal=causal, return_state=True)
+    if causal:
+        ref, S_ref, z_ref = ora.recurrent_attention(q, k, v, phi="favor", omega=omega)
+    else:
+        ref, S_ref, z_ref = ora.noncausal_attention(q, k, v, phi="favor", omega=omega)
+    O, S, z = to_host(O), to_host(S), to_host(z)
+    assert np.all(np.isfinite(O))
+    _, _, worst = check_close(O, ref, "bf16", "O")
+    print(f"favor_precise scale {scale} causal={causal}: worst row relative error {worst:.3e}", flush=True)
+    # S_N, z_N are tiny at these norms (the absolute floor of the elementwise
+    # rule says nothing); the per-row relative gate carries the comparison
+    check_close(S, S_ref, "bf16", "S_N")
+    check_close(z[..., None], z_ref[..., None], "bf16", "z_N")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_favor_fast_form_stays_finite_at_large_norm(lib, span, omega, causal):
+    """The default form at 14 times the workload's norms: the shifts keep every
+    output finite (no 0/0), and the outputs stay within 0.1 of the oracle row
+    by row (relative); what is left is omega's bf16 rounding in the output
+    pass's projections, which the precise form removes."""
+    span(128)
+    q, k, v = _scaled(1, 2, 333, 14.0, 21)
+    O = to_host(_run(lib, q, k, v, omega, causal=causal))
+    form = ora.recurrent_attention if causal else ora.noncausal_attention
+    ref = form(q, k, v, phi="favor", omega=omega)[0]
+    assert np.all(np.isfinite(O))
+    rel = row_errors(O, ref)
+    print(f"favor fast form scale 14 causal={causal}: worst row relative error {np.max(rel):.3e}", flush=True)
+    assert np.max(rel) < 0.1
+
+
+def test_favor_precise_large_norm_split_prefill_and_decode(lib, span, omega):
+    """Large norms across a split prefill and a decode step: the second call
+    starts from the first call's (unscaled) final state, under its own key
+    shift; the decode step reads the second call's state."""
+    import torch
+    span(128)
+    q, k, v = _scaled(1, 2, 401, 14.0, 23)
+    cut = 150
+    ref, _, _ = ora.recurrent_attention(q, k, v, phi="favor", omega=omega)
+    O1, S1, z1 = _run(lib, q[:, :, :cut], k[:, :, :cut], v[:, :, :cut], omega, phi="favor_precise",
+                      return_state=True)
+    O2, S2, z2 = _run(lib, q[:, :, cut:-1], k[:, :, cut:-1], v[:, :, cut:-1], omega, phi="favor_precise",
+                      S0=S1, z0=z1, return_state=True)
+    check_close(to_host(O1), ref[:, :, :cut], "bf16", "first part")
+    check_close(to_host(O2), ref[:, :, cut:-1], "bf16", "second part")
+    o = lib.decode_step(S2, z2, to_dev(q[:, :, -1], "bf16"), to_dev(k[:, :, -1], "bf16"),
+                        to_dev(v[:, :, -1], "bf16"), phi="favor", omega=f32_dev(omega))
+    torch.cuda.synchronize()
+    check_close(to_host(o), ref[:, :, -1], "bf16", "decode step")
