@@ -122,6 +122,8 @@ def parse_args(argv=None):
                    help="chunk size (default: the workload's, 0 = the library's choice)")
     p.add_argument("--settle", type=float, default=SETTLE_S,
                    help="seconds of untimed steps after the warm-up steps (clock/power steady state)")
+    p.add_argument("--precise", action="store_true",
+                   help="FAVOR+ workload: the precise form (omega hi + lo in the output pass)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     return p.parse_args(argv)
 
@@ -200,6 +202,7 @@ def bench_prefill(args, torch, la, synth):
     sets = [(Q0, K0, V0)] + [(Q0.clone(), K0.clone(), V0.clone()) for _ in range(ROTATE - 1)]
     outs = [torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.bfloat16, device=dev) for _ in range(ROTATE)]
     omega = synth.draw_omega(w.r, w.d) if w.phi == "favor" else None
+    lib_phi = "favor_precise" if (w.phi == "favor" and args.precise) else w.phi
     om_dev = hostio.upload_f32(omega, dev) if omega is not None else None
     gamma_dev = hostio.upload_f32(gamma, dev) if gamma is not None else None
     gates = gates_ch = None
@@ -209,13 +212,13 @@ def bench_prefill(args, torch, la, synth):
     if log_a_ch is not None:
         g0 = hostio.upload_f32(log_a_ch, dev)
         gates_ch = [g0] + [g0.clone() for _ in range(ROTATE - 1)]
-    ws = torch.empty(la.workspace_bytes(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
+    ws = torch.empty(la.workspace_bytes(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=lib_phi, r=w.r, causal=causal,
                                         chunk=w.chunk, gated=log_a is not None, gla=log_a_ch is not None),
                      dtype=torch.uint8, device=dev)
 
     def step(i, events=None):
         Q, K, V = sets[i % ROTATE]
-        la.forward(Q, K, V, phi=w.phi, omega=om_dev, causal=causal, chunk=w.chunk, out=outs[i % ROTATE],
+        la.forward(Q, K, V, phi=lib_phi, omega=om_dev, causal=causal, chunk=w.chunk, out=outs[i % ROTATE],
                    workspace=ws, events=events, gamma=gamma_dev,
                    log_gate=gates[i % ROTATE] if gates is not None else None,
                    log_gate_ch=gates_ch[i % ROTATE] if gates_ch is not None else None)
@@ -263,7 +266,7 @@ def bench_prefill(args, torch, la, synth):
     feat_flops = 2 * 2 * w.d * w.r if w.phi == "favor" else 0
     alg_flops = token_heads * (feat_flops + 4 * w.r * w.dv + (2 * w.chunk * (w.r + w.dv) if causal else 0))
     out_ms = out_live_ms
-    n_span, single_pass = la.forward_config(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=w.phi, r=w.r, causal=causal,
+    n_span, single_pass = la.forward_config(w.B, w.H, w.N, w.d, w.dv, io=w.io, phi=lib_phi, r=w.r, causal=causal,
                                             chunk=w.chunk, decay=gamma is not None, gated=log_a is not None,
                                             gla=log_a_ch is not None)
     names = (FAVOR_KERNEL_NAMES if w.phi == "favor" else GLA_KERNEL_NAMES if log_a_ch is not None
@@ -280,14 +283,16 @@ def bench_prefill(args, torch, la, synth):
                                    + (2 * w.chunk * (w.r + w.dv) if causal else 0))
         achieved = out_flops / (out_ms * 1e-3) / 1e12
         roof = {"kernel": out_kernel, "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic}
+                "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic,
+                "scope": "dominant kernel only; the whole call: path_roofline"}
     else:
         # the output kernel reads Q, K, V and writes O (causal); non-causal it
         # reads Q and writes O only
         out_bytes = alg_bytes if causal else token_heads * (w.d + w.dv) * 2  # (gated: with the gates)
         achieved = out_bytes / (out_ms * 1e-3) / 1e9
         roof = {"kernel": out_kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "scope": "dominant kernel only; the whole call: path_roofline"}
     step_gbs = alg_bytes / (ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -304,7 +309,8 @@ def bench_prefill(args, torch, la, synth):
         "data": "synthetic",
         "config": {
             "workload": f"{w.name} prefill B{w.B} H{w.H} N{w.N} d{w.d} dv{w.dv} bf16 I/O, fp32 state, "
-                        f"phi={'FAVOR+ r=%d' % w.r if w.phi == 'favor' else 'elu+1'}, "
+                        f"phi={'FAVOR+ r=%d' % w.r if w.phi == 'favor' else 'elu+1'}"
+                        f"{' (precise form)' if lib_phi == 'favor_precise' else ''}, "
                         f"{'causal' if causal else 'non-causal'}, chunk {w.chunk}"
                         + (", per-head decay gamma_h = 1 - 2^-(5 + 7h/(H-1)) (RetNet form)" if gamma is not None else "")
                         + (", per-token gates log a = -dt A_h, dt log-uniform [1e-3, 1e-1], A_h = 1 + 15h/(H-1)"
@@ -317,6 +323,7 @@ def bench_prefill(args, torch, la, synth):
         },
         "roofline": roof,
         "path_roofline": {
+            "scope": "whole call: every kernel of the step, algorithmic bytes over the step time",
             "bound": "hbm",
             "alg_bytes": alg_bytes,
             "alg_flops": alg_flops,
@@ -430,8 +437,9 @@ def bench_backward(args, torch, la, synth):
         },
         "roofline": {"kernel": "la_bwd_dkv_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": read_traffic(args.workload + "_backward", "la_bwd_dkv_kernel")},
-        "path_roofline": {"bound": "hbm", "alg_bytes": step_bytes,
+                     "traffic": read_traffic(args.workload + "_backward", "la_bwd_dkv_kernel"),
+                     "scope": "dominant kernel only; the whole call: path_roofline"},
+        "path_roofline": {"scope": "whole call", "bound": "hbm", "alg_bytes": step_bytes,
                           "achieved_gbs": step_bytes / (ms * 1e-3) / 1e9,
                           "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "kernels_us": {n: t * 1e3 for n, t in zip(BACKWARD_KERNEL_NAMES, kern_ms)},

@@ -82,49 +82,68 @@ def test_same_key_written_twice_reads_the_mean():
     assert dense[1, 0] == g["normalised_readout"]
 
 
-# ---------------------------------------------------------------- the page's numpy check
+# ---------------------------------------------------------------- invariants on several inputs
+#
+# Three invariants of the definitions, each checked on a set of inputs: the
+# explicit masked form equals the token recurrence; changing keys and values
+# from token t0 on leaves every earlier output unchanged ("Efficient
+# attention variants", sec. 11's self-test); the non-causal explicit form
+# equals its reassociated product (sec. 4).  One input is the small case of
+# the hands-on section (sec. 10): its seed, shapes, perturbation and reported
+# error level are fixture data (tests/golden/numpy_check.txt); the others are
+# a random small case and a case with a long tail of negative inputs.
 
-@pytest.fixture(scope="module")
-def page_check():
-    g = load("numpy_check.txt")
-    rng = np.random.default_rng(int(g["seed"]))
-    n, d, dv = int(g["N"]), int(g["d"]), int(g["dv"])
-    q = rng.normal(size=(n, d))
-    k = rng.normal(size=(n, d))
-    v = rng.normal(size=(n, dv))
-    return g, q, k, v
+def _inputs(name):
+    """(q, k, v, t0, k_add, v_add, err_level) for the named case."""
+    if name == "hands_on_sec10":
+        g = load("numpy_check.txt")
+        rng = np.random.default_rng(int(g["seed"]))
+        n, d, dv = int(g["N"]), int(g["d"]), int(g["dv"])
+        q, k, v = (rng.normal(size=(n, w)) for w in (d, d, dv))
+        return q, k, v, int(g["perturb_from"]), g["perturb_k_add"], g["perturb_v_add"], g["reported_max_abs_error"]
+    rng = np.random.default_rng(7 if name == "random_small" else 11)
+    n, d = (40, 8) if name == "random_small" else (64, 16)
+    q, k, v = (rng.normal(size=(n, d)) for _ in range(3))
+    if name == "negative_tail":
+        q -= 3.0
+        k -= 3.0
+    return q, k, v, n // 3, 0.75, -4.0, None
 
 
-def test_explicit_equals_recurrent_page_inputs(page_check):
-    g, q, k, v = page_check
+CASES = ["hands_on_sec10", "random_small", "negative_tail"]
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_explicit_equals_recurrent(name):
+    q, k, v, _, _, _, err_level = _inputs(name)
     dense = ora.explicit_attention(q, k, v)
     rec, _, _ = ora.recurrent_attention(q, k, v)
-    tol = g["tolerance"]
-    np.testing.assert_allclose(dense, rec, rtol=tol, atol=tol)
-    # same order of magnitude as the page's reported rounding-level error
-    assert np.max(np.abs(dense - rec)) < 100 * g["reported_max_abs_error"]
+    np.testing.assert_allclose(dense, rec, rtol=1e-12, atol=1e-12)
+    if err_level is not None:
+        # the same order of magnitude as the rounding-level difference the page reports
+        assert np.max(np.abs(dense - rec)) < 100 * err_level
 
 
-def test_no_future_leakage_page_inputs(page_check):
-    g, q, k, v = page_check
-    t0 = int(g["perturb_from"])
+@pytest.mark.parametrize("name", CASES)
+def test_future_tokens_leave_earlier_rows_unchanged(name):
+    q, k, v, t0, k_add, v_add, _ = _inputs(name)
     k2, v2 = k.copy(), v.copy()
-    k2[t0:] += g["perturb_k_add"]
-    v2[t0:] += g["perturb_v_add"]
+    k2[t0:] += k_add
+    v2[t0:] += v_add
     a, _, _ = ora.recurrent_attention(q, k, v)
     b, _, _ = ora.recurrent_attention(q, k2, v2)
     np.testing.assert_array_equal(a[:t0], b[:t0])
-    assert np.max(np.abs(a[t0:] - b[t0:])) > 1e-3   # the perturbation does reach later rows
-    da = ora.explicit_attention(q, k, v)
-    db = ora.explicit_attention(q, k2, v2)
-    np.testing.assert_allclose(da[:t0], db[:t0], rtol=0, atol=1e-15)
+    assert np.max(np.abs(a[t0:] - b[t0:])) > 1e-3   # the change does reach the later rows
+    np.testing.assert_allclose(ora.explicit_attention(q, k, v)[:t0], ora.explicit_attention(q, k2, v2)[:t0],
+                               rtol=0, atol=1e-15)
 
 
-def test_noncausal_reassociation_page_inputs(page_check):
-    g, q, k, v = page_check
+@pytest.mark.parametrize("name", CASES)
+def test_noncausal_explicit_equals_reassociated(name):
+    q, k, v, _, _, _, _ = _inputs(name)
     dense = ora.explicit_attention(q, k, v, causal=False)
     reas, _, _ = ora.noncausal_attention(q, k, v)
-    np.testing.assert_allclose(dense, reas, rtol=g["tolerance"], atol=g["tolerance"])
+    np.testing.assert_allclose(dense, reas, rtol=1e-12, atol=1e-12)
 
 
 # ---------------------------------------------------------------- feature maps
