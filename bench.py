@@ -274,7 +274,8 @@ def bench_prefill(args, torch, la, synth):
     out_kernel = names[2]
     # the decayed and gated variants of la_output_kernel are other kernels:
     # their counter figures are kept under their own workload tag
-    mode = "_decay" if gamma is not None else "_gated" if log_a is not None else ""
+    mode = ("_decay" if gamma is not None else "_gated" if log_a is not None
+            else "_precise" if lib_phi == "favor_precise" else "")
     traffic = read_traffic(args.workload + ("" if causal else "_noncausal") + mode, out_kernel)
     if w.phi == "favor":
         # the output kernel's own work: phi(Q) and phi(K) projections, the
