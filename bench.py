@@ -122,6 +122,8 @@ def parse_args(argv=None):
                    help="chunk size (default: the workload's, 0 = the library's choice)")
     p.add_argument("--settle", type=float, default=SETTLE_S,
                    help="seconds of untimed steps after the warm-up steps (clock/power steady state)")
+    p.add_argument("--span-tokens", type=int, default=0,
+                   help="span length of the chunkwise prefill (a multiple of the chunk; 0: the library's choice)")
     p.add_argument("--precise", action="store_true",
                    help="FAVOR+ workload: the precise form (omega hi + lo in the output pass)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -177,6 +179,8 @@ def time_oracle_prefill(q, k, v, causal, phi="elu1", omega=None, gamma=None, log
 def bench_prefill(args, torch, la, synth):
     from kernelized_linear_attention_elu_amd import hostio
     w = synth.WORKLOADS[args.workload]
+    if args.span_tokens:
+        la.set_span_tokens(args.span_tokens)
     if args.chunk is not None:
         w = dataclasses.replace(w, chunk=args.chunk)
     causal = not args.noncausal

@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -95,7 +96,15 @@ int choose_n_span(long long BH, int N, int chunk, int d, int io, int phi, int ca
   const long long n_chunks = (static_cast<long long>(N) + chunk - 1) / chunk;
   const int v = g_span_tokens.load(std::memory_order_relaxed);
   if (v >= chunk && v % chunk == 0) return static_cast<int>((static_cast<long long>(N) + v - 1) / v);
-  const long long slots = static_cast<long long>(device_cus()) * output_occupancy(io, phi, d, chunk, causal, decay);
+  // Spans fill two workgroups per CU, or the output kernel's occupancy when
+  // that is lower: an even two per CU (every CU holds two state and two
+  // output workgroups for the whole kernel) measured faster than filling
+  // the kernel's three (causal) or six (non-causal) workgroups per CU with
+  // shorter spans - long causal 151 -> 148 us, prefill B4 H16 N4096 51 ->
+  // 48 us, long non-causal 119 -> 110 us - and counts that do not divide
+  // over the CUs were slower than either.
+  const int per_cu = std::min(output_occupancy(io, phi, d, chunk, causal, decay), 2);
+  const long long slots = static_cast<long long>(device_cus()) * per_cu;
   long long n = (slots + BH - 1) / (BH > 0 ? BH : 1);
   const long long cap = n_chunks / 4 > 0 ? n_chunks / 4 : 1;
   if (n > cap) n = cap;

@@ -49,7 +49,7 @@ def span_tokens(lib):
 
 
 def test_forward_config(lib, span_tokens):
-    assert la.forward_config(1, 32, 32768, 64, 64) == (24, False)    # three kernels
+    assert la.forward_config(1, 32, 32768, 64, 64) == (16, False)    # three kernels, two workgroups per CU
     assert la.forward_config(1, 1, 0, 64, 64) == (0, False)
     with pytest.raises(la.LinAttnError):
         la.forward_config(1, 1, 10, 96, 96)
@@ -68,18 +68,18 @@ def test_span_setter(lib, span_tokens):
 
 def test_workspace_sizes(lib, span_tokens):
     E = 64 * 64 + 64
-    # long prefill B1 H32 N32768 (512 chunks per head): 768 output workgroups
-    # (256 CUs x 3) -> 24 spans per head
-    assert _ws(1, 32, 32768) == 32 * 25 * E * 4
-    # prefill B4 H16 N4096 (64 chunks per head): 12 spans per head
-    assert _ws(4, 16, 4096) == 64 * 13 * E * 4
+    # long prefill B1 H32 N32768 (512 chunks per head): 512 output workgroups
+    # (256 CUs x 2) -> 16 spans per head
+    assert _ws(1, 32, 32768) == 32 * 17 * E * 4
+    # prefill B4 H16 N4096 (64 chunks per head): 8 spans per head
+    assert _ws(4, 16, 4096) == 64 * 9 * E * 4
     # wide heads B2 H16 N65536 d128 (one workgroup per CU): 8 spans per head
     assert _ws(2, 16, 65536, 128, 128) == 32 * 9 * (128 * 128 + 128) * 4
     # short sequences keep at least 4 chunks per span
     assert _ws(1, 1, 256) == 1 * 2 * E * 4
     assert _ws(1, 2, 4096) == 2 * 17 * E * 4
-    # fp32 I/O at chunk 64: three workgroups per CU, 768 slots
-    assert _ws(1, 8, 65536, io=0) == 8 * 97 * E * 4
+    # fp32 I/O at chunk 64: two workgroups per CU, 512 slots
+    assert _ws(1, 8, 65536, io=0) == 8 * 65 * E * 4
     # N = 0 still needs one slot per head for the (initial = final) state
     assert _ws(1, 2, 0) == 2 * 1 * E * 4
     span_tokens(64)
