@@ -368,6 +368,8 @@ def bench_backward(args, torch, la, synth):
     w = synth.WORKLOADS[args.workload]
     if w.phi == "favor" or w.d not in (64, 128) or args.noncausal:
         raise SystemExit("--backward: causal, d = 64 or 128, pointwise feature maps")
+    if args.span_tokens:
+        la.set_span_tokens(args.span_tokens)
     dev = torch.device("cuda:0")
     q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
     rng = np.random.default_rng(91)
