@@ -1183,10 +1183,11 @@ __global__ __launch_bounds__(CF::NT, DK != kNoDecay ? CF::MINB_DECAY : CF::MINB)
     }
   } else {
     // every memory operation is issued on every iteration (loads past the
-    // span re-read its last chunk from L2), and the prologue issues the
-    // loop's memory operations in the loop's order (K and V, Q, then the
-    // stores, dropped), so the counter wait at the loop head is exact: it
-    // waits for the prefetched chunk, not for the previous chunk's stores
+    // span re-read its last chunk from L2), and the prologue ends with the
+    // loop's memory operations in the loop's order (K and V, then the
+    // stores, dropped, then the next chunk's Q), so the counter wait at the
+    // loop head is exact: it waits for the prefetched chunk, not for the
+    // previous chunk's stores or the Q rows loaded after them
     // (an empty span returns here, so that the prologue and the loop entry
     // are one block and the compiler keeps the prologue's issue order)
     if (t_begin >= t_end) return;
@@ -1200,19 +1201,24 @@ __global__ __launch_bounds__(CF::NT, DK != kNoDecay ? CF::MINB_DECAY : CF::MINB)
     dummy_stores<CF>(hb.o);
     typename CF::OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
     int t0 = t_begin;
+    // phi(Q) of a chunk is formed at the end of the previous chunk's
+    // outputs, in the wave's own scratch (no barrier involved), where its
+    // VALU work can issue beside the carry's MFMAs; its Q rows are loaded
+    // one chunk ahead of that
+    typename QRegs<CF>::frag qf[CF::RBW][CF::R / CF::KS];
+    qr.to_frags(qf, scr, g, li);
+    qr.load(hb.q, min(t0 + CF::C, last), w, g, li);
     do {
       __syncthreads();  // every wave is done with the previous chunk's S, z, phi(K), V
       publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
       const float l2 =
           stage_chunk<CF, false, DK>(cr, nullptr, sm.k, nullptr, sm.v, t0, N, lg, CF::C, sm.kw_tile(), sm.cum_tile());
-      typename QRegs<CF>::frag qf[CF::RBW][CF::R / CF::KS];
-      qr.to_frags(qf, scr, g, li);
-      const int tn = min(t0 + CF::C, last);
-      load_chunk<CF, false, GATED>(cr, hb, tn);
-      qr.load(hb.q, tn, w, g, li);
+      load_chunk<CF, false, GATED>(cr, hb, min(t0 + CF::C, last));
       __syncthreads();
       chunk_outputs<CF, true, DK>(qf, sm.k, sm.v, sm.s, sm.z, out, w, g, li, lg, normalize, sm.cum_tile());
       store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
+      qr.to_frags(qf, scr, g, li);
+      qr.load(hb.q, min(t0 + 2 * CF::C, last), w, g, li);
       if constexpr (DECAY) {
         // the carry past this chunk (unused after a span's last chunk, so a
         // partial last chunk needs no other length; gates past N are one)
