@@ -2331,6 +2331,13 @@ __global__ __launch_bounds__(CF::NT, CF::NW == 8 ? 1 : 2) void la_bwd_dkv_kernel
   };
   if constexpr (PREFETCH) load_all(last);
   for (int t0 = last; t0 >= t_begin; t0 -= CF::C) {
+    // eight waves: the lane indices pass through an empty asm statement on
+    // every chunk, so that the swizzled LDS offsets derived from them are
+    // formed inside the loop instead of being kept live across it (which
+    // spilled about ten VGPRs)
+    int g_in = g, li_in = li;
+    if constexpr (!PREFETCH) asm volatile("" : "+v"(g_in), "+v"(li_in));
+    const int g = g_in, li = li_in;
     if constexpr (!PREFETCH) load_all(t0);
     __syncthreads();  // every wave is done with the previous chunk's tiles
     // the carried R (bf16) and u
