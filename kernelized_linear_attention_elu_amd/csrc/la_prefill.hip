@@ -99,6 +99,23 @@ __device__ __forceinline__ void state_tile(int w, int i, int& ct, int& ft) {
   ct = i;
 }
 
+// Row block (16 query tokens of the chunk) of wave w, its rbi-th.  With more
+// waves than row blocks, wave w belongs to group p = w / RB (which takes
+// value or feature tiles p CTW ..) and takes block w mod RB when p is even,
+// RB - 1 - (w mod RB) when p is odd.  Waves w and w + 4 share a SIMD, so at
+// eight waves and four row blocks each SIMD holds blocks b and 3 - b, and
+// the causal weight tiles (b + 1 key blocks for block b) split evenly over
+// the SIMDs.
+template <class CF>
+__device__ __forceinline__ int wave_row_block(int rbi, int w) {
+  if constexpr (CF::RB >= CF::NW) {
+    return w + CF::NW * rbi;
+  } else {
+    const int b = w % CF::RB;
+    return ((w / CF::RB) & 1) ? CF::RB - 1 - b : b;
+  }
+}
+
 // ------------------------------------------------------------------ decay kinds
 
 // How the state decays from one token to the next.
@@ -413,7 +430,7 @@ struct QRegs {
   u32x4 raw[CF::RBW][NV];
   __device__ static __forceinline__ int feature(int ks, int g) { return CF::PL == 8 ? 32 * ks + 8 * g : 16 * g + ks; }
   __device__ static __forceinline__ int row_block(int rbi, int w) {
-    return (CF::RB >= CF::NW) ? (w + CF::NW * rbi) : (w % CF::RB);
+    return wave_row_block<CF>(rbi, w);
   }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t q, int t0, int w, int g, int li) {
     using T = typename CF::IO;
@@ -593,7 +610,7 @@ __device__ __forceinline__ void chunk_outputs(const typename QRegs<CF>::frag (&q
   const int zrow = min(li & 3, 2);                                    // z_hi, z_lo or zeros
 #pragma unroll
   for (int rbi = 0; rbi < CF::RBW; ++rbi) {
-    const int ib = (RB >= CF::NW) ? (w + CF::NW * rbi) : (w % RB);
+    const int ib = wave_row_block<CF>(rbi, w);
     const int ct0 = (RB >= CF::NW) ? 0 : (w / RB) * CTW;
 
     float den = 0.f;
@@ -1462,7 +1479,7 @@ __device__ __forceinline__ void chunk_outputs_gla(const float (&fq)[CF::RBW][CF:
   };
 #pragma unroll
   for (int rbi = 0; rbi < CF::RBW; ++rbi) {
-    const int ib = (RB >= CF::NW) ? (w + CF::NW * rbi) : (w % RB);
+    const int ib = wave_row_block<CF>(rbi, w);
     const int ct0 = (RB >= CF::NW) ? 0 : (w / RB) * CTW;
     // phi(q_i) scaled by 2^x, rounded to MFMA operands
     auto scaled = [&](const float (&x)[NQ], frag (&qs)[R / KS]) {
@@ -1966,7 +1983,7 @@ __global__ __launch_bounds__(CF::NT, CF::NW == 8 ? 1 : 2) void la_bwd_dq_kernel(
   // four waves form the span's reverse sums here; eight (d = 128) leave
   // them to la_bwd_rsum_kernel (no registers for a second 128 x 128 state)
   constexpr bool RSUM = CF::NW == 4;
-  const int ib = w % RB, half = w / RB, ft0 = half * FTW;
+  const int ib = wave_row_block<CF>(0, w), half = w / RB, ft0 = half * FTW;
   OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
 
   // four waves: chunk c+1 is loaded into registers while chunk c is
@@ -2304,7 +2321,7 @@ __global__ __launch_bounds__(CF::NT, CF::NW == 8 ? 1 : 2) void la_bwd_dkv_kernel
   // this wave's key block; with eight waves two share a block and each
   // takes half of the value tiles of dV and half of the feature tiles of dK
   constexpr int FTW = FT / CF::WPR, CTW = CT / CF::WPR;
-  const int jb = w % RB, half = w / RB, ft0 = half * FTW, ct0 = half * CTW;
+  const int jb = wave_row_block<CF>(0, w), half = w / RB, ft0 = half * FTW, ct0 = half * CTW;
   OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
   constexpr int VVR = DV / 8;
   if (t_begin >= t_end) return;
