@@ -554,6 +554,52 @@ struct QRegs {
   }
 };
 
+// phi(Q) shared by the two waves of a row block (eight waves, chunk 64,
+// bf16): each wave loads half of the block's Q columns, [64 h, 64 h + 64)
+// for its group h = w / RB (128-byte half rows), applies phi to them and
+// writes them as operand fragments (k-steps 2 h, 2 h + 1) into a phi(Q)
+// tile of the chunk, from which both waves read all of them.  That halves
+// the phi evaluations and the Q row traffic per wave against each wave
+// forming the whole row block itself.
+template <class CF>
+struct SharedQ {
+  static constexpr bool on = CF::NW == 8 && CF::RB == 4 && CF::RBW == 1 && sizeof(typename CF::OP) == 2 &&
+                             CF::PL == 8 && CF::D == 128;
+  static constexpr int HC = CF::D / 2;       // columns per half
+  static constexpr int UPH = HC / 8;         // 16-byte units per half row
+  static constexpr int NV = 16 * UPH / 64;   // vectors per lane
+  u32x4 raw[NV];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t q, int t0, int ib, int h) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int qi = v * 64 + lane;
+      const int row = t0 + 16 * ib + qi / UPH, col = HC * h + 8 * (qi % UPH);
+      raw[v] = __builtin_amdgcn_raw_buffer_load_b128(q, (row * CF::D + col) * 2, 0, kStreamLoad);
+    }
+  }
+  // the loaded half rows -> the wave's scratch -> phi -> tile sq (rows 16 ib
+  // + li, the half's k-steps, in the layout of the key tiles)
+  __device__ __forceinline__ void to_tile(bf16* scr, bf16* sq, int ib, int h, int g, int li) const {
+    using TS = Tile<bf16, HC>;
+    using TQ = Tile<bf16, CF::R>;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int qi = v * 64 + lane;
+      *reinterpret_cast<u32x4*>(scr + TS::off(qi / UPH, 8 * (qi % UPH))) = raw[v];
+    }
+#pragma unroll
+    for (int kk = 0; kk < HC / 32; ++kk) {
+      float f[8];
+      unpack16<bf16>(*reinterpret_cast<const u32x4*>(scr + TS::off(li, 32 * kk + 8 * g)), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = phi_pointwise<CF::PHI>(f[e]);
+      *reinterpret_cast<bf16x8*>(sq + TQ::off(16 * ib + li, HC * h + 32 * kk + 8 * g)) = cvt_bf16x8(f);
+    }
+  }
+};
+
 // Per-wave LDS scratch of the output kernels (bf16 row staging of Q and O).
 template <class CF>
 struct Scratch {
@@ -898,6 +944,8 @@ struct SmemOut {
   OP s[Tile<OP, CF::DV>::elems(CF::R)];
   alignas(16) typename CF::ZT z[CF::ZE];
   alignas(16) OP scr[Scratch<CF>::ELEMS];
+  // phi(Q) tiles of two consecutive chunks (SharedQ)
+  alignas(16) OP sq[SharedQ<CF>::on ? 2 : 1][SharedQ<CF>::on ? Tile<OP, CF::R>::elems(CF::C) : 8];
   __device__ OP* kw_tile() { return nullptr; }
   __device__ float* cum_tile() { return nullptr; }
 };
@@ -1209,11 +1257,20 @@ __global__ __launch_bounds__(CF::NT, DK != kNoDecay ? CF::MINB_DECAY : CF::MINB)
     // are one block and the compiler keeps the prologue's issue order)
     if (t_begin >= t_end) return;
     const int last = t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C;
+    constexpr bool SQ = SharedQ<CF>::on;
+    const int qib = wave_row_block<CF>(0, w), qh = w / CF::RB;  // (SQ) row block and column half
     ChunkRegs<CF, false> cr;
     QRegs<CF> qr;
+    SharedQ<CF> qs;
+    auto q_load = [&](int t) {
+      if constexpr (SQ)
+        qs.load(hb.q, t, qib, qh);
+      else
+        qr.load(hb.q, t, w, g, li);
+    };
     load_chunk<CF, false, GATED>(cr, hb, t_begin);
     mem_order_fence();
-    qr.load(hb.q, t_begin, w, g, li);
+    q_load(t_begin);
     mem_order_fence();
     dummy_stores<CF>(hb.o);
     typename CF::OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
@@ -1221,10 +1278,17 @@ __global__ __launch_bounds__(CF::NT, DK != kNoDecay ? CF::MINB_DECAY : CF::MINB)
     // phi(Q) of a chunk is formed at the end of the previous chunk's
     // outputs, in the wave's own scratch (no barrier involved), where its
     // VALU work can issue beside the carry's MFMAs; its Q rows are loaded
-    // one chunk ahead of that
+    // one chunk ahead of that.  SQ: into the chunk's phi(Q) tile, which
+    // both waves of the row block read after the chunk's second barrier
+    // (the tile of chunk c + 1 is written after the second barrier of
+    // chunk c, by which every wave has read the tile of chunk c - 1)
     typename QRegs<CF>::frag qf[CF::RBW][CF::R / CF::KS];
-    qr.to_frags(qf, scr, g, li);
-    qr.load(hb.q, min(t0 + CF::C, last), w, g, li);
+    int qbuf = 0;
+    if constexpr (SQ)
+      qs.to_tile(scr, sm.sq[0], qib, qh, g, li);
+    else
+      qr.to_frags(qf, scr, g, li);
+    q_load(min(t0 + CF::C, last));
     do {
       __syncthreads();  // every wave is done with the previous chunk's S, z, phi(K), V
       publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
@@ -1232,10 +1296,21 @@ __global__ __launch_bounds__(CF::NT, DK != kNoDecay ? CF::MINB_DECAY : CF::MINB)
           stage_chunk<CF, false, DK>(cr, nullptr, sm.k, nullptr, sm.v, t0, N, lg, CF::C, sm.kw_tile(), sm.cum_tile());
       load_chunk<CF, false, GATED>(cr, hb, min(t0 + CF::C, last));
       __syncthreads();
+      if constexpr (SQ) {
+        using TQ = Tile<typename CF::OP, CF::R>;
+#pragma unroll
+        for (int ks = 0; ks < CF::R / CF::KS; ++ks)
+          qf[0][ks] = load_frag(sm.sq[qbuf] + TQ::off(16 * qib + li, ks * CF::KS + g * 8));
+      }
       chunk_outputs<CF, true, DK>(qf, sm.k, sm.v, sm.s, sm.z, out, w, g, li, lg, normalize, sm.cum_tile());
       store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
-      qr.to_frags(qf, scr, g, li);
-      qr.load(hb.q, min(t0 + 2 * CF::C, last), w, g, li);
+      if constexpr (SQ) {
+        qbuf ^= 1;
+        qs.to_tile(scr, sm.sq[qbuf], qib, qh, g, li);
+      } else {
+        qr.to_frags(qf, scr, g, li);
+      }
+      q_load(min(t0 + 2 * CF::C, last));
       if constexpr (DECAY) {
         // the carry past this chunk (unused after a span's last chunk, so a
         // partial last chunk needs no other length; gates past N are one)
