@@ -244,7 +244,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<CF, WITH_Q>& cr, const Head
 // the decay from the chunk's end to a later reference token.
 // Returns the log2 of the chunk's whole decay over its len tokens (what a
 // state carried across the chunk is multiplied by), 0 without a decay.
-template <class CF, bool WITH_Q, int DK = kNoDecay>
+template <class CF, bool WITH_Q, int DK = kNoDecay, bool WITH_V = true>
 __device__ __forceinline__ float stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, typename CF::OP* sq,
                                              typename CF::OP* sk, typename CF::OP* sk_lo,
                                              typename CF::OP* sv, int t0, int N, float lg = 0.f, int len = 0,
@@ -335,13 +335,29 @@ __device__ __forceinline__ float stage_chunk(const ChunkRegs<CF, WITH_Q>& cr, ty
     keys(std::true_type{});
   else
     keys(std::false_type{});
+  if constexpr (WITH_V) {  // (otherwise the keys only)
+#pragma unroll
+    for (int i = 0; i < CF::LV; ++i) {
+      const int vi = tid + i * CF::NT;
+      if (CF::VV % CF::NT == 0 || vi < CF::VV)
+        *reinterpret_cast<u32x4*>(sv + TV::off(vi / VVR, (vi % VVR) * CF::EPL)) = cr.v[i];
+    }
+  }
+  return total;
+}
+
+// V rows of the chunk -> LDS (the value half of stage_chunk).
+template <class CF, bool WITH_Q>
+__device__ __forceinline__ void stage_values(const ChunkRegs<CF, WITH_Q>& cr, typename CF::OP* sv) {
+  using TV = Tile<typename CF::OP, CF::DV>;
+  constexpr int VVR = CF::DV / CF::EPL;
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < CF::LV; ++i) {
     const int vi = tid + i * CF::NT;
     if (CF::VV % CF::NT == 0 || vi < CF::VV)
       *reinterpret_cast<u32x4*>(sv + TV::off(vi / VVR, (vi % VVR) * CF::EPL)) = cr.v[i];
   }
-  return total;
 }
 
 // ------------------------------------------------------------------ state update
@@ -934,18 +950,21 @@ struct SmemState {
 };
 
 // LDS of the output kernel: phi(K) and V of the chunk, the carried state (S
-// as an MFMA operand, z), and the per-wave row scratch.  All single buffers:
-// the barrier at the top of each chunk orders every reuse.
-template <class CF>
+// as an MFMA operand, z), and the per-wave row scratch.  The barrier at the
+// top of each chunk orders every reuse; with EK the phi(K) tiles of two
+// consecutive chunks (the next chunk's is formed during this chunk's
+// outputs).
+template <class CF, bool EK = false>
 struct SmemOut {
   using OP = typename CF::OP;
-  OP k[Tile<OP, CF::R>::elems(CF::C)];
+  OP k[EK ? 2 : 1][Tile<OP, CF::R>::elems(CF::C)];
   OP v[Tile<OP, CF::DV>::elems(CF::C)];
   OP s[Tile<OP, CF::DV>::elems(CF::R)];
   alignas(16) typename CF::ZT z[CF::ZE];
   alignas(16) OP scr[Scratch<CF>::ELEMS];
   // phi(Q) tiles of two consecutive chunks (SharedQ)
   alignas(16) OP sq[SharedQ<CF>::on ? 2 : 1][SharedQ<CF>::on ? Tile<OP, CF::R>::elems(CF::C) : 8];
+  __device__ OP* kt(int b) { return k[EK ? b : 0]; }
   __device__ OP* kw_tile() { return nullptr; }
   __device__ float* cum_tile() { return nullptr; }
 };
@@ -953,7 +972,7 @@ struct SmemOut {
 // of the chunk, which the state carry contracts (the weights use the plain
 // features), and (gated) the chunk's running log2 gates.
 template <class CF>
-struct SmemOutDecay : SmemOut<CF> {
+struct SmemOutDecay : SmemOut<CF, false> {
   using OP = typename CF::OP;
   alignas(16) OP kw[Tile<OP, CF::R>::elems(CF::C)];
   alignas(16) float cum[CF::C > 64 ? CF::C : 64];
@@ -1194,7 +1213,8 @@ __global__ __launch_bounds__(CF::NT, DK != kNoDecay ? CF::MINB_DECAY : CF::MINB)
     int n_span, const float* __restrict__ gamma, int H, int normalize, const float* __restrict__ log_a) {
   constexpr bool DECAY = DK != kNoDecay, GATED = DK == kGated;
   static_assert(CAUSAL || !DECAY, "the decay is defined for the causal form");
-  __shared__ typename std::conditional<CAUSAL, typename std::conditional<DECAY, SmemOutDecay<CF>, SmemOut<CF>>::type,
+  __shared__ typename std::conditional<CAUSAL,
+                                       typename std::conditional<DECAY, SmemOutDecay<CF>, SmemOut<CF, CF::NW == 8>>::type,
                                        SmemOutNC<CF>>::type sm;
   const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, li = l & 15;
   // heads in the reverse order of la_state_kernel: the keys and values
@@ -1289,11 +1309,27 @@ __global__ __launch_bounds__(CF::NT, DK != kNoDecay ? CF::MINB_DECAY : CF::MINB)
     else
       qr.to_frags(qf, scr, g, li);
     q_load(min(t0 + CF::C, last));
+    // Without a decay, phi(K) of a chunk is likewise formed during the
+    // previous chunk's outputs (from the raw rows loaded in its staging
+    // phase), into the other of two phi(K) tiles, and the staging phase
+    // only publishes the state and copies V: the feature map's VALU work
+    // then issues beside MFMAs instead of in a phase of its own.  The tile
+    // of chunk c + 1 is written after the second barrier of chunk c, by
+    // which every wave is done with the tile of chunk c - 1.  (Eight waves:
+    // at four, where two workgroups share a CU and the kernel is bound by
+    // its memory stream, back-to-back steps measured slower with it.)
+    constexpr bool EK = !DECAY && CF::NW == 8;
+    int kb = 0;
+    if constexpr (EK) stage_chunk<CF, false, kNoDecay, false>(cr, nullptr, sm.kt(0), nullptr, nullptr, t0, N);
     do {
       __syncthreads();  // every wave is done with the previous chunk's S, z, phi(K), V
       publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
-      const float l2 =
-          stage_chunk<CF, false, DK>(cr, nullptr, sm.k, nullptr, sm.v, t0, N, lg, CF::C, sm.kw_tile(), sm.cum_tile());
+      float l2 = 0.f;
+      if constexpr (EK)
+        stage_values<CF>(cr, sm.v);
+      else
+        l2 = stage_chunk<CF, false, DK>(cr, nullptr, sm.kt(0), nullptr, sm.v, t0, N, lg, CF::C, sm.kw_tile(),
+                                        sm.cum_tile());
       load_chunk<CF, false, GATED>(cr, hb, min(t0 + CF::C, last));
       __syncthreads();
       if constexpr (SQ) {
@@ -1302,7 +1338,7 @@ __global__ __launch_bounds__(CF::NT, DK != kNoDecay ? CF::MINB_DECAY : CF::MINB)
         for (int ks = 0; ks < CF::R / CF::KS; ++ks)
           qf[0][ks] = load_frag(sm.sq[qbuf] + TQ::off(16 * qib + li, ks * CF::KS + g * 8));
       }
-      chunk_outputs<CF, true, DK>(qf, sm.k, sm.v, sm.s, sm.z, out, w, g, li, lg, normalize, sm.cum_tile());
+      chunk_outputs<CF, true, DK>(qf, sm.kt(kb), sm.v, sm.s, sm.z, out, w, g, li, lg, normalize, sm.cum_tile());
       store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
       if constexpr (SQ) {
         qbuf ^= 1;
@@ -1311,6 +1347,9 @@ __global__ __launch_bounds__(CF::NT, DK != kNoDecay ? CF::MINB_DECAY : CF::MINB)
         qr.to_frags(qf, scr, g, li);
       }
       q_load(min(t0 + 2 * CF::C, last));
+      // (past the span's last chunk the rows re-read are staged and unused)
+      if constexpr (EK)
+        stage_chunk<CF, false, kNoDecay, false>(cr, nullptr, sm.kt(kb ^ 1), nullptr, nullptr, t0 + CF::C, N);
       if constexpr (DECAY) {
         // the carry past this chunk (unused after a span's last chunk, so a
         // partial last chunk needs no other length; gates past N are one)
@@ -1321,8 +1360,9 @@ __global__ __launch_bounds__(CF::NT, DK != kNoDecay ? CF::MINB_DECAY : CF::MINB)
         for (int k = 0; k < CF::ZPW; ++k) zt[k] *= dg;
         state_mfma<CF>(sacc, zt, sm.kw_tile(), nullptr, sm.v, w, g, li);
       } else {
-        state_mfma<CF>(sacc, zt, sm.k, nullptr, sm.v, w, g, li);
+        state_mfma<CF>(sacc, zt, sm.kt(kb), nullptr, sm.v, w, g, li);
       }
+      kb ^= 1;
       t0 += CF::C;
     } while (t0 < t_end);
   }
@@ -1415,20 +1455,6 @@ __device__ __forceinline__ void gla_prefix_to_lds(const GateRegsGla<CF>& gr, flo
     int tok, ch;
     gla_unit<CF>(k, w, lane, tok, ch);
     *reinterpret_cast<f32x4*>(sp + TP::off(tok, ch)) = x;
-  }
-}
-
-// V rows of the chunk -> LDS (the value half of stage_chunk).
-template <class CF>
-__device__ __forceinline__ void stage_values(const ChunkRegs<CF, false>& cr, typename CF::OP* sv) {
-  using TV = Tile<typename CF::OP, CF::DV>;
-  constexpr int VVR = CF::DV / CF::EPL;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < CF::LV; ++i) {
-    const int vi = tid + i * CF::NT;
-    if (CF::VV % CF::NT == 0 || vi < CF::VV)
-      *reinterpret_cast<u32x4*>(sv + TV::off(vi / VVR, (vi % VVR) * CF::EPL)) = cr.v[i];
   }
 }
 
