@@ -430,13 +430,18 @@ __device__ __forceinline__ bf16x8 tr2(const bf16* p0, const bf16* p1) { return c
 
 // Outputs of one span (carried state from the scanned slot when causal, the
 // full-sequence sums otherwise).  Per chunk: stage raw Q, K, V (double
-// buffered) -> barrier -> feature tiles of phi(Q), phi(K) (wave w: features
-// 32 w .. +31 of every token) and the carried state -> LDS -> barrier ->
-// outputs, then the state carry.  Outputs: the two waves w and 7 - w share
-// row block ib = min(w, 7 - w) (query tokens 16 ib + li); each forms the row
+// buffered) -> barrier -> the carried state -> LDS, feature tiles of phi(Q),
+// phi(K) (wave w: features 32 w .. +31 of every token) -> LDS, and the state
+// carry -> barrier -> outputs.  Outputs: the two waves w and 7 - w share row
+// block ib = min(w, 7 - w) (query tokens 16 ib + li); each forms the row
 // block's weights and denominator and produces value tiles 2 (w / 4) and
-// 2 (w / 4) + 1.  Carried state: wave w owns value tile w mod 4 and feature
-// tiles 8 (w / 4) .. +7, and z tiles w and w + 8.
+// 2 (w / 4) + 1.  Carried state: wave w owns the features it projects,
+// 32 w .. +31 (feature tiles 2 w, 2 w + 1), for all four value tiles, and
+// their z tiles, so that it carries the state from its own phi(K) values in
+// registers, beside the exponentials of the feature phase, where the matrix
+// cores would otherwise idle.  phi(K) goes to LDS feature-major ([feature]
+// [token], in the state tile's layout), which is what the weights' operand
+// reads take, like the state read-out.
 template <bool CAUSAL, bool PRECISE>
 __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __restrict__ Q,
                                                                  const bf16* __restrict__ K,
@@ -462,11 +467,10 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
   om.load(omega, w, g, li);
   const float kappa = CAUSAL ? favor_kappa(fc, favor_first_norm2(src[1])) : 0.f;
 
-  constexpr int TPW = FFT * FCT / FNW;  // carried state tiles per wave (8)
+  constexpr int TPW = FFT * FCT / FNW;  // carried state tiles per wave (8): [FCT j + ct]
   constexpr int ZPW = FFT / FNW;        // z tiles per wave (2)
+  static_assert(TPW == FPW * FCT && ZPW == FPW, "a wave carries the features it projects");
   constexpr int OCT = FCT / 2;          // value tiles per wave in the outputs (2)
-  const int sct = w % FCT;              // value tile of this wave's carried state tiles
-  const int sft0 = TPW * (w / FCT);     // first feature tile of them
   // output row block: waves w and w + 4 run on one SIMD, so they take row
   // blocks b and 3 - b, which balances the causal weight tiles per SIMD
   const int ib = w < 4 ? w : 7 - w;
@@ -474,30 +478,29 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
 
   // Lane offsets (elements) into the LDS tiles, formed once.  Rows 16 apart
   // share a hash, so every access of the chunk loop is one of these plus a
-  // compile-time constant - except the transposing phi(K) reads of the state
-  // carry, where feature tile sft0 + i is the offset XOR 16 i (the hash acts
-  // on the 32 pieces of a half row; see phi_off).
+  // compile-time constant.  In the 64-element rows of the state-layout
+  // tiles (S and phi(K)^T), piece 4 c + x (c < 4) of a row r sits at
+  // 16 (c ^ (H >> 2)) + 4 (x ^ (H & 3)), H = st_hash(r mod 16): a base per
+  // row and lane plus 16 (c ^ hh), formed where used.
   int o_raw[2];      // raw Q/K rows (projection operands): row li, columns 32 ks + 8 g
-  int o_phw[FPW];    // phi writes: row li, features 16 (FPW w + j) + 4 g
-  int o_prow[4][2];  // phi row reads: row li, features 32 kq + 16 h + 4 g (k-step kq + 4: + 128)
+  int o_phw[FPW];    // phi(Q) writes: row li, features 16 (FPW w + j) + 4 g
+  int o_prow[4][2];  // phi(Q) row reads: row li, features 32 kq + 16 h + 4 g (k-step kq + 4: + 128)
   int o_vo[OCT];     // V transposing reads (outputs): row 4 g + li / 4, values 16 (oct0 + c) + 4 (li % 4)
   int o_so[OCT];     // S transposing reads: the same rows and columns of the state tile
-  int o_vc[2];       // V transposing reads (state carry): row 8 g + 4 h + li / 4, values 16 sct + 4 (li % 4)
-  int o_kc[2];       // phi(K) transposing reads: the same rows, features 16 sft0 + 4 (li % 4)
-  int o_kz[2];       // ... features 16 w + 4 (li % 4) (z tile w; tile w + 8: + 128)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     o_raw[h] = T64::off(li, 32 * h + 8 * g);
     o_phw[h] = phi_off(li, 16 * (FPW * w + h) + 4 * g);
-    o_vc[h] = T64::off(8 * g + 4 * h + q4, 16 * sct + 4 * r4);
-    o_kc[h] = phi_off(8 * g + 4 * h + q4, 16 * sft0 + 4 * r4);
-    o_kz[h] = phi_off(8 * g + 4 * h + q4, 16 * w + 4 * r4);
     o_vo[h] = T64::off(4 * g + q4, 16 * (oct0 + h) + 4 * r4);
     o_so[h] = st_off(4 * g + q4, 16 * (oct0 + h) + 4 * r4);
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) o_prow[kq][h] = phi_off(li, 32 * kq + 16 * h + 4 * g);
   }
-  const int o_sw = st_off(16 * sft0 + li, 16 * sct + 4 * g);  // S writes (tile sft0 + i: + 16 i rows)
+  // S and phi(K)^T writes: row 16 FPW w + li (+ 16 j), piece 4 c + g
+  int b_sw = (16 * FPW * w + li) * FDV + 4 * ((g ^ st_hash(li)) & 3), h_sw = st_hash(li) >> 2;
+  // phi(K)^T transposing reads (weights): rows 4 g + li / 4 (+ 32 ks, + 16), piece 4 jb + li % 4
+  const int h_tr = st_hash((4 * g + q4) & 15);
+  int b_kw = (4 * g + q4) * FC + 4 * ((r4 ^ h_tr) & 3), hh_kw = h_tr >> 2;
   const int zrow = min(r4, 2);                                 // z_hi, z_lo or zeros
   const int o_z = zrow * FZS + 4 * g;                          // z row reads (+ 32 ks, + 16)
   // phi operand fragment of row `row` (a multiple of 16 plus li) at k-step ks
@@ -509,13 +512,15 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
   const float* pre = ws + ((size_t)bh * (n_span + 1) + (CAUSAL ? s : n_span)) * FE;
   f32x4 sacc[TPW];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i)
-    sacc[i] = *reinterpret_cast<const f32x4*>(pre + (16 * (sft0 + i) + li) * FDV + 16 * sct + 4 * g);
+  for (int j = 0; j < FPW; ++j)
+#pragma unroll
+    for (int ct = 0; ct < FCT; ++ct)
+      sacc[FCT * j + ct] = *reinterpret_cast<const f32x4*>(pre + (16 * (FPW * w + j) + li) * FDV + 16 * ct + 4 * g);
   f32x4 zt[ZPW];
 #pragma unroll
-  for (int k = 0; k < ZPW; ++k) {
-    const float zv = pre[FR * FDV + 16 * (w + FNW * k) + li];
-    zt[k] = f32x4{zv, zv, zv, zv};
+  for (int j = 0; j < ZPW; ++j) {
+    const float zv = pre[FR * FDV + 16 * (FPW * w + j) + li];
+    zt[j] = f32x4{zv, zv, zv, zv};
   }
   const bf16 one = static_cast<bf16>(1.0f), zero = static_cast<bf16>(0.0f);
   const bf16x8 ones = bf16x8{one, one, one, one, one, one, one, one};
@@ -543,10 +548,10 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
   __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, orsrc, kDropOffset, 0, kStreamStore);
   int buf = 0;
   for (int t0 = t_begin; t0 < t_end; t0 += FC, buf ^= 1) {
-    // the XORed offsets of the state carry and the output tile are formed in
-    // the loop rather than kept live across it (registers are tight at two
-    // waves per SIMD)
-    asm volatile("" : "+v"(o_kc[0]), "+v"(o_kc[1]), "+v"(o_or), "+v"(o_ow));
+    // the XORed offsets of the state-layout tiles and the output tile are
+    // formed in the loop rather than kept live across it (registers are
+    // tight at two waves per SIMD)
+    asm volatile("" : "+v"(b_sw), "+v"(h_sw), "+v"(b_kw), "+v"(hh_kw), "+v"(o_or), "+v"(o_ow));
     {
       bf16* const dst[3] = {sm.qraw[buf], sm.kraw[buf], sm.v[buf]};
       float* const nrm[3] = {sm.qn[buf], sm.kn[buf], nullptr};
@@ -556,26 +561,50 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
     __syncthreads();
     store_rows(t0 - FC, t0 != t_begin);  // the previous chunk's outputs (rows past N are dropped)
 
-    // feature tiles: lane (g, li) gets features 16 ft + 4 g + r of token 16 tb + li
-    // (features of tokens past the end are 0 through their -inf bias).  Token
-    // block by token block, both feature tiles of the wave from one read of
-    // the raw rows; the raw rows of block tb + 1 are read before the tiles of
-    // block tb are written, so that the reads do not wait behind the writes.
+    // the carried state before this chunk -> LDS (the carry below then
+    // updates the registers)
+    if (CAUSAL || t0 == t_begin) {
+#pragma unroll
+      for (int j = 0; j < FPW; ++j)
+#pragma unroll
+        for (int ct = 0; ct < FCT; ++ct)
+          sts4(sm.ss + 16 * j * FDV + b_sw + 16 * (ct ^ h_sw), cvt_bf16x4(sacc[FCT * j + ct]));
+      // lane group 0 writes z_hi, group 1 z_lo, group 2 the zero row
+      if (g < 3) {
+#pragma unroll
+        for (int j = 0; j < ZPW; ++j) {
+          const float z = zt[j][0];
+          const bf16 h = static_cast<bf16>(z);
+          const bf16 v = g == 0 ? h : g == 1 ? static_cast<bf16>(z - static_cast<float>(h)) : zero;
+          sm.sz[g * FZS + 16 * (FPW * w + j) + li] = v;
+        }
+      }
+    }
+
+    // feature tiles (features of tokens past the end are 0 through their
+    // -inf bias).  phi(Q): lane (g, li) gets features 16 ft + 4 g + r of
+    // token 16 tb + li; phi(K), projected the other way round: tokens
+    // 16 tb + 4 g + r of feature 16 ft + li, kept in registers for the carry.
+    // Token block by token block, both feature tiles of the wave from one
+    // read of the raw rows; the raw rows of block tb + 1 are read before the
+    // tiles of block tb are written, so that the reads do not wait behind
+    // the writes.
     {
       constexpr int NST = CAUSAL ? 2 : 1;  // streams with features: Q, and K when causal
       const bf16* const raw[2] = {sm.qraw[buf], sm.kraw[buf]};
-      const float* const nrm[2] = {sm.qn[buf], sm.kn[buf]};
-      bf16* const phi[2] = {sm.sq, sm.sk};
       bf16x8 xf[2][NST][2];  // [token block parity][stream][k-step]
-      float nb[2][NST];
+      float nb[2];           // phi(Q) biases of token 16 tb + li
+      f32x4 kb[2];           // phi(K) biases of tokens 16 tb + 4 g + r
       auto read_block = [&](int tb, int p) {
 #pragma unroll
         for (int st = 0; st < NST; ++st) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) xf[p][st][ks] = load_frag(raw[st] + 16 * tb * FD + o_raw[ks]);
-          nb[p][st] = nrm[st][16 * tb + li];
         }
+        nb[p] = sm.qn[buf][16 * tb + li];
+        if constexpr (CAUSAL) kb[p] = *reinterpret_cast<const f32x4*>(&sm.kn[buf][16 * tb + 4 * g]);
       };
+      bf16x4 kh[FPW][4];  // phi(K) of the wave's features, [j][tb]
       // the precise form: omega's lo fragments, read once per chunk (from cache)
       bf16x8 olo[PRECISE ? FPW : 1][2];
       if constexpr (PRECISE) {
@@ -598,33 +627,49 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
             pr[st][j] = zero4();
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-              pr[st][j] = mfma16(om.hi[j][ks], xf[p][st][ks], pr[st][j]);
-              if constexpr (PRECISE) pr[st][j] = mfma16(olo[j][ks], xf[p][st][ks], pr[st][j]);
+              if (st == 0) {
+                pr[st][j] = mfma16(om.hi[j][ks], xf[p][st][ks], pr[st][j]);
+                if constexpr (PRECISE) pr[st][j] = mfma16(olo[j][ks], xf[p][st][ks], pr[st][j]);
+              } else {
+                pr[st][j] = mfma16(xf[p][st][ks], om.hi[j][ks], pr[st][j]);
+                if constexpr (PRECISE) pr[st][j] = mfma16(xf[p][st][ks], olo[j][ks], pr[st][j]);
+              }
             }
           }
 #pragma unroll
-        for (int st = 0; st < NST; ++st)
+        for (int j = 0; j < FPW; ++j) {
+          bf16x4 h;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] = static_cast<bf16>(favor_phi(fc, pr[0][j][r], nb[p]));
+          sts4(sm.sq + 16 * tb * FR + o_phw[j], h);
+        }
+        if constexpr (CAUSAL) {
 #pragma unroll
           for (int j = 0; j < FPW; ++j) {
-            bf16x4 h;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) h[r] = static_cast<bf16>(favor_phi(fc, pr[st][j][r], nb[p][st]));
-            sts4(phi[st] + 16 * tb * FR + o_phw[j], h);
+            for (int r = 0; r < 4; ++r) kh[j][tb][r] = static_cast<bf16>(favor_phi(fc, pr[NST - 1][j][r], kb[p][r]));
+            sts4(sm.sk + 16 * j * FC + b_sw + 16 * (tb ^ h_sw), kh[j][tb]);
           }
+        }
       }
-    }
-    if (CAUSAL || t0 == t_begin) {
+      // ---- state carry: S += phi(K_c)^T V_c, z += phi(K_c)^T 1, from the
+      // wave's own phi(K) values (bf16, as the weights use them).  V^T
+      // fragments: k-slots 0-3 = tokens 32 kp + 4 g + r, 4-7 = tokens
+      // 32 kp + 16 + 4 g + r, the token order of token blocks 2 kp, 2 kp + 1.
+      if constexpr (CAUSAL) {
 #pragma unroll
-      for (int i = 0; i < TPW; ++i)
-        sts4(sm.ss + 16 * i * FDV + o_sw, cvt_bf16x4(sacc[i]));
-      // lane group 0 writes z_hi, group 1 z_lo, group 2 the zero row
-      if (g < 3) {
+        for (int kp = 0; kp < 2; ++kp) {
+          bf16x8 bk[FPW];
 #pragma unroll
-        for (int k = 0; k < ZPW; ++k) {
-          const float z = zt[k][0];
-          const bf16 h = static_cast<bf16>(z);
-          const bf16 v = g == 0 ? h : g == 1 ? static_cast<bf16>(z - static_cast<float>(h)) : zero;
-          sm.sz[g * FZS + 16 * (w + FNW * k) + li] = v;
+          for (int j = 0; j < FPW; ++j) bk[j] = cat4(kh[j][2 * kp], kh[j][2 * kp + 1]);
+#pragma unroll
+          for (int ct = 0; ct < FCT; ++ct) {
+            const bf16x8 va = tr_frag<64>(sm.v[buf], 32 * kp + 4 * g, 32 * kp + 16 + 4 * g, 16 * ct, li);
+#pragma unroll
+            for (int j = 0; j < FPW; ++j) sacc[FCT * j + ct] = mfma16(va, bk[j], sacc[FCT * j + ct]);
+          }
+#pragma unroll
+          for (int j = 0; j < FPW; ++j) zt[j] = mfma16(ones, bk[j], zt[j]);
         }
       }
     }
@@ -649,8 +694,12 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
       // the diagonal block is masked to j <= i by selection
       auto weights = [&](int jb) {
         f32x4 t = zero4();
+        const bf16* kbase = sm.sk + b_kw + 16 * (jb ^ hh_kw);
 #pragma unroll
-        for (int ks = 0; ks < FR / 32; ++ks) t = mfma16(prow(sm.sk + 16 * jb * FR, ks), qf[ks], t);
+        for (int ks = 0; ks < FR / 32; ++ks) {
+          const bf16* p0 = kbase + 32 * ks * FC;
+          t = mfma16(tr2(p0, p0 + 16 * FC), qf[ks], t);
+        }
         if (jb == ib) {  // wave-uniform: only the diagonal block is masked
 #pragma unroll
           for (int r = 0; r < 4; ++r) t[r] = 4 * g + r > li ? 0.f : t[r];
@@ -686,20 +735,6 @@ __global__ __launch_bounds__(FNT, 1) void la_output_favor_kernel(const bf16* __r
 #pragma unroll
     for (int c = 0; c < OCT; ++c) sts4(sm.so + (o_ow ^ (16 * c)), cvt_bf16x4(o[c] * rden));
 
-    // ---- state carry: S += phi(K_c)^T V_c, z += phi(K_c)^T 1 (bf16 features)
-    if constexpr (CAUSAL) {
-#pragma unroll
-      for (int ks = 0; ks < FC / 32; ++ks) {
-        const bf16* kb = sm.sk + 32 * ks * FR;
-        const bf16x8 a = tr2(vb + o_vc[0] + 32 * ks * FDV, vb + o_vc[1] + 32 * ks * FDV);
-#pragma unroll
-        for (int i = 0; i < TPW; ++i)
-          sacc[i] = mfma16(a, tr2(kb + (o_kc[0] ^ (16 * i)), kb + (o_kc[1] ^ (16 * i))), sacc[i]);
-#pragma unroll
-        for (int k = 0; k < ZPW; ++k)
-          zt[k] = mfma16(ones, tr2(kb + o_kz[0] + 128 * k, kb + o_kz[1] + 128 * k), zt[k]);
-      }
-    }
   }
   if (t_end > t_begin) {
     __syncthreads();
