@@ -25,15 +25,15 @@
 //                            operands (no LDS round trip); dz comes from a
 //                            ones operand against the same fragments.
 //   la_output_favor_kernel - per span, chunk by chunk: phi(Q), phi(K) tiles
-//                            -> LDS, then the masked intra-chunk product,
-//                            read-out of the carried state and divide, and
-//                            the state carry (as for the pointwise maps).
-//                            phi(Q) and phi(K) are contracted over features
-//                            in a permuted order: k-slot e of lane group g
-//                            at k-step ks is feature 32 ks + 16 (e / 4) +
-//                            4 g + e % 4, which is how the projection
-//                            accumulators lay them out.  S and z are read in
-//                            the same order.
+//                            -> LDS and the state carry (from phi(K) in
+//                            registers, as in the span-state kernel), then
+//                            the masked intra-chunk product, read-out of the
+//                            carried state and divide.  phi(Q) and phi(K)
+//                            are contracted over features in a permuted
+//                            order: k-slot e of lane group g at k-step ks is
+//                            feature 32 ks + 16 (e / 4) + 4 g + e % 4, which
+//                            is how the projection accumulators lay them
+//                            out.  S and z are read in the same order.
 #include "la_common.h"
 #include "la_prefill.h"
 #include "la_tiles.h"
@@ -121,10 +121,11 @@ __device__ __forceinline__ float favor_first_norm2(__amdgpu_buffer_rsrc_t k) {
 // norms (|x| near 1) is below the bf16 rounding of the features themselves,
 // but at |x| of 2 and more shows in the outputs (about 1.5e-2 relative per
 // row at |x| = 2, 5e-2 at 8).  The precise form (LA_PHI_FAVOR_PRECISE) adds
-// the lo part, as the span state pass always does, at about 1.45 times the
+// the lo part, as the span state pass always does, at about 1.4 times the
 // output pass's time.  Selecting the form per token inside the pass would
 // keep the fast form's speed only if it cost no registers, which it does
-// not at 256 VGPRs, so the caller chooses.
+// not (the lo fragments of the projections are live across the feature
+// phase), so the caller chooses.
 // phi for one feature: exp2(proj log2(e) d^(-1/4) + bias) - one FMA and one exp2
 // (0 for the bias -inf of a masked token, whose projection is 0).
 __device__ __forceinline__ float favor_phi(const FavorConsts& c, float proj, float bias) {
