@@ -122,6 +122,25 @@ def test_prefill_bf16_split_spans(lib, span, prefill_data):
         check_close(to_host(_run(lib, q, k, v, "bf16")), ref, "bf16", f"span={tokens}")
 
 
+# ---------------------------------------------------------------- d = 128 at every chunk
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("tokens", [None, "2c"])
+def test_d128_every_chunk(lib, span, chunk, causal, tokens):
+    """d = 128 (eight waves per workgroup: two waves per row block at chunk
+    64, four at 32, eight at 16) at every chunk it supports, with one span or
+    several per head and a ragged last chunk: every element, S_N and z_N."""
+    if tokens == "2c":
+        span(2 * chunk)
+    q, k, v = synth.draw_qkv(2, 3, 333, 128, 128, seed=1280 + chunk)
+    ref, S_ref, z_ref = ora.recurrent_attention(q, k, v) if causal else ora.noncausal_attention(q, k, v)
+    O, S, z = _run(lib, q, k, v, "bf16", chunk=chunk, causal=causal, return_state=True)
+    check_close(to_host(O), ref, "bf16", f"O d128 chunk={chunk} causal={causal}")
+    check_close(to_host(S), S_ref, "bf16", "S_N")
+    check_close(to_host(z), z_ref, "bf16", "z_N")
+
+
 # ---------------------------------------------------------------- long and wide workloads (full)
 
 def _recurrent_head(q, k, v, phi="elu1", omega=None):
