@@ -141,6 +141,19 @@ def test_d128_every_chunk(lib, span, chunk, causal, tokens):
     check_close(to_host(z), z_ref, "bf16", "z_N")
 
 
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("N", [1, 17])
+def test_d128_short(lib, span, chunk, N):
+    """d = 128 with fewer tokens than one chunk (the staging masks and the
+    loads past the end), causal."""
+    q, k, v = synth.draw_qkv(1, 2, N, 128, 128, seed=1290 + N + chunk)
+    ref, S_ref, z_ref = ora.recurrent_attention(q, k, v)
+    O, S, z = _run(lib, q, k, v, "bf16", chunk=chunk, return_state=True)
+    check_close(to_host(O), ref, "bf16", f"O d128 N={N} chunk={chunk}")
+    check_close(to_host(S), S_ref, "bf16", "S_N")
+    check_close(to_host(z), z_ref, "bf16", "z_N")
+
+
 # ---------------------------------------------------------------- long and wide workloads (full)
 
 def _recurrent_head(q, k, v, phi="elu1", omega=None):
