@@ -19,7 +19,7 @@
 // vector ALUs.  One workgroup per (batch, head); a thread owns 4 consecutive
 // value columns of every (256 / (DV/4))-th state row and keeps its partial
 // read-out in registers; S' may alias S (every element is read and then
-// written by the same thread).
+// written by the same thread), and z' may alias z.
 #include "la_common.h"
 #include "la_prefill.h"
 
@@ -106,27 +106,50 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
   const float gm = log_a ? __builtin_amdgcn_exp2f(fmaxf(log_a[bh] * 1.4426950408889634f, -126.f))
                         : gamma ? gamma[bh % H] : 1.f;
 
-  features_to_lds<T, D, R, PHI>(q + (size_t)bh * D, omega, fq, xbuf, scratch[0], true);
-  features_to_lds<T, D, R, PHI>(k + (size_t)bh * D, omega, fk, xbuf, scratch[1], false);
-  for (int c = tid; c < DV; c += kThreads) vv[c] = load_io<T>(v + (size_t)bh * DV + c);
-  // per-channel gates (state row f keeps a_f of itself; the floor of the
-  // per-channel gated prefill, log2 a >= -14)
-  for (int f = tid; f < R; f += kThreads)
-    gch[f] = log_a_ch ? __builtin_amdgcn_exp2f(fmaxf(log_a_ch[(size_t)bh * R + f] * 1.4426950408889634f, -14.f))
-                      : gm;
-  __syncthreads();
-
   const int c4 = tid % TPR;
   const int r0 = tid / TPR;
-  const f32x4 v4 = f32x4{vv[4 * c4], vv[4 * c4 + 1], vv[4 * c4 + 2], vv[4 * c4 + 3]};
   const float* Sh = S + (size_t)bh * R * DV + 4 * c4;
   float* Sn = S_new + (size_t)bh * R * DV + 4 * c4;
-  // all loads first: S_new may alias S, so a store could not be moved above
-  // a later load and the loads would otherwise serialise
+  // S_new may alias S, so every S load comes before the first store (a store
+  // could not be moved above a later load, and the loads would serialise).
+  // With a pointwise map S is requested first and the token's few loads and
+  // its features overlap the S stream: one round trip to memory, not two.
+  // FAVOR+ forms its features from omega first and requests S after them.
+  constexpr bool EARLY = PHI != PHI_FAVOR && R <= kThreads && DV <= kThreads;
   f32x4 s[R / RPP];
+  auto load_state = [&]() {
 #pragma unroll
-  for (int it = 0; it < R / RPP; ++it)
-    s[it] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sh + (size_t)(r0 + it * RPP) * DV));
+    for (int it = 0; it < R / RPP; ++it)
+      s[it] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sh + (size_t)(r0 + it * RPP) * DV));
+  };
+  float zx = 0.f;  // pointwise maps: z[tid] (state row f = tid, tid < R)
+  if constexpr (EARLY) {
+    load_state();
+    // every thread loads (rows and columns wrapped), with no branch around
+    // the loads
+    const int f = tid % R, c = tid % DV;
+    const T qr = q[(size_t)bh * D + f], kr = k[(size_t)bh * D + f], vr = v[(size_t)bh * DV + c];
+    const float ar = (log_a_ch ? log_a_ch : z)[(size_t)bh * R + f];
+    zx = z[(size_t)bh * R + f];
+    if (tid < R) {
+      fq[tid] = phi_pointwise<PHI>(static_cast<float>(qr));
+      fk[tid] = phi_pointwise<PHI>(static_cast<float>(kr));
+      // per-channel gates (state row f keeps a_f of itself; the floor of the
+      // per-channel gated prefill, log2 a >= -14)
+      gch[tid] = log_a_ch ? __builtin_amdgcn_exp2f(fmaxf(ar * 1.4426950408889634f, -14.f)) : gm;
+    }
+    if (tid < DV) vv[tid] = static_cast<float>(vr);
+  } else {
+    features_to_lds<T, D, R, PHI>(q + (size_t)bh * D, omega, fq, xbuf, scratch[0], true);
+    features_to_lds<T, D, R, PHI>(k + (size_t)bh * D, omega, fk, xbuf, scratch[1], false);
+    for (int c = tid; c < DV; c += kThreads) vv[c] = load_io<T>(v + (size_t)bh * DV + c);
+    for (int f = tid; f < R; f += kThreads)
+      gch[f] = log_a_ch ? __builtin_amdgcn_exp2f(fmaxf(log_a_ch[(size_t)bh * R + f] * 1.4426950408889634f, -14.f))
+                        : gm;
+  }
+  __syncthreads();
+  if constexpr (!EARLY) load_state();
+  const f32x4 v4 = f32x4{vv[4 * c4], vv[4 * c4 + 1], vv[4 * c4 + 2], vv[4 * c4 + 3]};
   f32x4 num = zero4();
 #pragma unroll
   for (int it = 0; it < R / RPP; ++it) {
@@ -142,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(const float* S, con
 
   float dpart = 0.f;
   for (int f = tid; f < R; f += kThreads) {
-    const float zn = z[(size_t)bh * R + f] * gch[f] + fk[f];
+    const float zn = (EARLY ? zx : z[(size_t)bh * R + f]) * gch[f] + fk[f];
     z_new[(size_t)bh * R + f] = zn;
     dpart += fq[f] * zn;
   }
