@@ -72,6 +72,24 @@ def draw_qkv(B, H, N, d, dv, seed=DATA_SEED, std=None, io="bf16"):
     return tuple(out)
 
 
+def draw_qkv_device(B, H, N, d, dv, seed=DATA_SEED, std=None, device="cuda"):
+    """Q, K [B,H,N,d] and V [B,H,N,dv] as bf16 device tensors, drawn from
+    torch's seeded generator on the device: N(0, std^2) in float32
+    (std=None means d**-0.25), then rounded to bf16 (nearest even).  For
+    sizes whose host draw would take minutes; a comparison reads the values
+    back from the device."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(int(seed))
+    s = default_std(d) if std is None else float(std)
+    out = []
+    for shape in ((B, H, N, d), (B, H, N, d), (B, H, N, dv)):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        x.mul_(s)
+        out.append(x.to(torch.bfloat16))
+        del x
+    return tuple(out)
+
+
 def draw_omega(r, d, seed=OMEGA_SEED):
     """FAVOR+ projection rows, float32 [r, d]: block-orthogonal Gaussian rows."""
     rng = np.random.default_rng(seed)

@@ -55,6 +55,23 @@ def test_forward_config(lib, span_tokens):
         la.forward_config(1, 1, 10, 96, 96)
 
 
+def test_longest_sequence_per_head(lib):
+    """A head's Q/K/V/O are addressed through 32-bit buffer offsets, so the
+    entry points accept N only while N times the widest row stays below 2^31
+    bytes (shape queries only: nothing is launched)."""
+    n, sp = ctypes.c_int(), ctypes.c_int()
+
+    def cfg(N, d, io):
+        return lib.la_forward_config(1, 1, N, d, d, io, 0, 0, 1, 64, ctypes.byref(n), ctypes.byref(sp))
+
+    for d, io, n_max in ((64, 1, (1 << 24) - 1), (128, 1, (1 << 23) - 1), (64, 0, (1 << 23) - 1)):
+        assert cfg(n_max, d, io) == 0, (d, io)
+        assert n.value >= 1
+        assert cfg(n_max + 1, d, io) == 2, (d, io)                     # LA_ERR_SHAPE
+        assert _ws(1, 1, n_max, d=d, dv=d, io=io) > 0
+        assert _ws(1, 1, n_max + 1, d=d, dv=d, io=io) == 0
+
+
 def test_span_setter(lib, span_tokens):
     assert lib.la_get_span_tokens() == 0
     for bad in (-16, 24, (1 << 24) + 16):

@@ -203,6 +203,66 @@ def test_wide_bf16_full(lib, span):
     check_close(z, z_ref, "bf16", "z_N")
 
 
+# ---------------------------------------------------------------- the longest sequence of one head
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_longest_head(lib, d):
+    """The longest sequence one head takes in bf16: a head's Q/K/V/O are
+    addressed through 32-bit buffer offsets, so N * 2d bytes must stay below
+    2^31 (N <= 2^24 - 1 at d = 64, 2^23 - 1 at d = 128); here
+    N = 2^31 / (2d) - 37, with a ragged last chunk.  The inputs are drawn on the device (a host draw of 3 x 2^30 values takes
+    minutes) and read back for the oracle.  Compared: sampled rows (both
+    ends, chunk and span edges, the rows whose byte offsets pass 2^30 and
+    come within a chunk of 2^31) and the final state.  The oracle's state
+    before a sampled row is the sum of its full-sequence sums over the
+    whole 2^20-token pieces before the row's piece; from there causal_rows
+    takes the row's piece with that state as S0, z0 (the split-prefill
+    handoff, pinned on the CPU)."""
+    import torch
+    from kernelized_linear_attention_elu_amd import hostio
+    N = (1 << 31) // (2 * d) - 37
+    Q, K, V = synth.draw_qkv_device(1, 1, N, d, d)
+    O, S, z = lib.forward(Q, K, V, return_state=True)
+    torch.cuda.synchronize()
+    n_span = lib.forward_config(1, 1, N, d, d)[0]
+    n_ch = (N + 63) // 64
+    edges = [s * n_ch // n_span * 64 for s in (1, n_span // 2, n_span - 1)]
+    half = (1 << 30) // (2 * d)  # the first row at byte offset 2^30
+    rows = sorted({0, 1, 63, 64, half - 1, half, N - 65, ((N - 1) // 64) * 64, N - 2, N - 1}
+                  | {e - 1 for e in edges} | set(edges))
+    idx = torch.tensor(rows, device=Q.device)
+    got = to_host(O[0, 0].index_select(0, idx))
+    qrows = to_host(Q[0, 0].index_select(0, idx))
+    S, z = to_host(S)[0, 0], to_host(z)[0, 0]
+    del O
+    kb, vb = (hostio.download_bytes(t).view(np.uint16) for t in (K, V))
+    del Q, K, V
+    torch.cuda.empty_cache()
+
+    def vals(bits, a, b):
+        return (bits[a * d:b * d].astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(b - a, d)
+
+    P = 1 << 20
+    pre_S, pre_z = [np.zeros((d, d))], [np.zeros(d)]
+    for a in range(0, N, P):
+        b = min(a + P, N)
+        kk = vals(kb, a, b)
+        _, Sp, zp = ora.noncausal_attention(kk[:1], kk, vals(vb, a, b))
+        pre_S.append(pre_S[-1] + Sp)
+        pre_z.append(pre_z[-1] + zp)
+    ref = np.empty((len(rows), d))
+    for i, t in enumerate(rows):
+        a = t // P * P
+        kk, vv = vals(kb, a, t + 1), vals(vb, a, t + 1)
+        qq = np.zeros_like(kk)
+        qq[-1] = qrows[i]
+        ref[i] = ora.causal_rows(qq, kk, vv, [t - a], S0=pre_S[a // P], z0=pre_z[a // P])[0]
+    _, _, worst = check_close(got, ref, "bf16", f"O rows {rows}")
+    print(f"longest head d={d} N={N}: {len(rows)} rows, worst row relative error {worst:.3e}", flush=True)
+    check_close(S, pre_S[-1], "bf16", "S_N")
+    check_close(z, pre_z[-1], "bf16", "z_N")
+
+
 # ---------------------------------------------------------------- invariants and edges
 
 def test_no_future_leakage_bitwise(lib, span):
