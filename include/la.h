@@ -141,10 +141,10 @@ int la_get_span_tokens(void);
 
 /*
  * How la_forward will run this shape (no device work): *n_span receives the
- * number of spans per head (workgroups per head), *single_pass 1 when a
- * single-pass kernel serves it, 0 for the three-kernel path (span states,
- * span scan, outputs).  Either pointer may be NULL.  Errors as la_forward's
- * shape checks.
+ * number of spans per head (workgroups per head); *single_pass receives 0,
+ * since every shape runs the three-kernel path (span states, span scan,
+ * outputs).  Either pointer may be NULL.  Errors as la_forward's shape
+ * checks.
  */
 la_status la_forward_config(int B, int H, int N, int d, int d_v, int io_dtype, int phi, int r, int causal, int chunk,
                             int *n_span, int *single_pass);
@@ -176,10 +176,8 @@ la_status la_forward(const void *Q, const void *K, const void *V, void *O, int B
 /*
  * la_forward plus timing: events is NULL or an array of 2*LA_FORWARD_KERNELS
  * hipEvent_t created by the caller (see la_event_create); events[2i] is
- * recorded on the stream before kernel i and events[2i+1] after it.  Kernels
- * of the three-kernel path: 0 = per-span state, 1 = span scan, 2 = output;
- * of the single-pass path: 0 = workspace flag reset, 1 = none (empty
- * interval), 2 = the single-pass kernel.
+ * recorded on the stream before kernel i and events[2i+1] after it.
+ * Kernels: 0 = per-span state, 1 = span scan, 2 = output.
  */
 la_status la_forward_timed(const void *Q, const void *K, const void *V, void *O, int B, int H, int N, int d,
                            int d_v, int io_dtype, int phi, int r, const float *omega, int causal, int chunk,
