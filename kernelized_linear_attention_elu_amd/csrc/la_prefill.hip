@@ -1251,14 +1251,20 @@ __global__ __launch_bounds__(CF::NT, DK != kNoDecay ? CF::MINB_DECAY : CF::MINB)
     // two chunks ahead, and each chunk's outputs are stored right away
     publish_state<CF>(sacc, zt, sm.s, sm.z, w, g, li);
     __syncthreads();
+    // every step issues its load (past the span's last chunk it re-reads
+    // that chunk, from L2), so that the counter wait before each step's
+    // phi(Q) waits for that chunk's rows and not for the stores issued
+    // after them
+    if (t_begin >= t_end) return;
+    const int last = t_begin + ((t_end - t_begin - 1) / CF::C) * CF::C;
     QRegs<CF> qa, qb;
     qa.load(hb.q, t_begin, w, g, li);
-    qb.load(hb.q, t_begin + CF::C, w, g, li);  // beyond N: zeros, never stored
+    qb.load(hb.q, min(t_begin + CF::C, last), w, g, li);
     typename CF::OP* scr = sm.scr + w * Scratch<CF>::PER_WAVE;
     auto step = [&](QRegs<CF>& q, int t0) {
       typename QRegs<CF>::frag qf[CF::RBW][CF::R / CF::KS];
       q.to_frags(qf, scr, g, li);
-      if (t0 + 2 * CF::C < t_end) q.load(hb.q, t0 + 2 * CF::C, w, g, li);
+      q.load(hb.q, min(t0 + 2 * CF::C, last), w, g, li);
       chunk_outputs<CF, false>(qf, nullptr, nullptr, sm.s, sm.z, out, w, g, li);
       store_outputs<CF>(out, hb.o, t0, w, g, li, false, scr);
     };
