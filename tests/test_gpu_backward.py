@@ -113,3 +113,22 @@ def test_backward_long_workload_full(lib):
         head, block, row = check_grad(g, r, sc, name)
         print(f"backward long {name}: head RMS error {head:.3e}, block RMS error {block:.3e}, "
               f"worst row {row:.3f} of its bound", flush=True)
+
+
+def test_backward_wide_workload_full(lib):
+    """The wide workload (B2 H16 N65536 d128 bf16) in the bench's launch
+    configuration (eight waves per workgroup, the reverse sums in a pass of
+    their own): dQ, dK, dV at every row of every (batch, head) against the
+    fp64 prefix/suffix gradient loops."""
+    w = synth.WORKLOADS["wide"]
+    q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
+    rng = np.random.default_rng(92)
+    dO = synth.round_to_io(rng.standard_normal((w.B, w.H, w.N, w.dv), dtype=np.float32), "bf16")
+    got = _run(lib, q, k, v, dO)
+    refs = heads.map_heads(_grad_rows_all, q, k, v, dO)
+    scales = heads.map_heads(grad_scales, q, k, v, dO)
+    del q, k, v, dO
+    for name, g, r, sc in zip(("dQ", "dK", "dV"), got, refs, scales):
+        head, block, row = check_grad(g, r, sc, name)
+        print(f"backward wide {name}: head RMS error {head:.3e}, block RMS error {block:.3e}, "
+              f"worst row {row:.3f} of its bound", flush=True)
