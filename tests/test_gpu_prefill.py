@@ -188,17 +188,21 @@ def test_long_bf16_full(lib, span, long_case, causal):
         check_close(to_host(O)[:, :, -1:], refs[True][0][:, :, -1:], "bf16", "last row")
 
 
-def test_wide_bf16_full(lib, span):
+@pytest.mark.parametrize("causal", [True, False])
+def test_wide_bf16_full(lib, span, causal):
     """The wide workload (B2 H16 N65536 d128 bf16): every output of every
-    (batch, head) and the final state."""
+    (batch, head) and the final state (non-causal: the full sums)."""
     w = synth.WORKLOADS["wide"]
     q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
-    O, S, z = _run(lib, q, k, v, "bf16", return_state=True)
+    O, S, z = _run(lib, q, k, v, "bf16", causal=causal, return_state=True)
     O, S, z = to_host(O), to_host(S), to_host(z)
-    ref, S_ref, z_ref = heads.map_heads(_recurrent_head, q, k, v)
+    if causal:
+        ref, S_ref, z_ref = heads.map_heads(_recurrent_head, q, k, v)
+    else:
+        ref, S_ref, z_ref = ora.noncausal_attention(q, k, v)
     del q, k, v
     _, _, worst = check_close(O, ref, "bf16", "O")
-    print(f"wide: worst row relative error {worst:.3e}", flush=True)
+    print(f"wide causal={causal}: worst row relative error {worst:.3e}", flush=True)
     check_close(S, S_ref, "bf16", "S_N")
     check_close(z, z_ref, "bf16", "z_N")
 
