@@ -67,21 +67,21 @@ def _recurrent_favor_head(q, k, v, omega):
     return ora.recurrent_attention(q, k, v, phi="favor", omega=omega)
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_favor_workload_full(lib, omega, causal):
-    """The FAVOR+ workload (B2 H16 N16384): every output of every (batch,
-    head) against the fp64 recurrence (non-causal: the full sums), and the
-    final state."""
+@pytest.mark.parametrize("phi,causal", [("favor", True), ("favor", False), ("favor_precise", True)])
+def test_favor_workload_full(lib, omega, phi, causal):
+    """The FAVOR+ workload (B2 H16 N16384), both forms: every output of every
+    (batch, head) against the fp64 recurrence (non-causal: the full sums),
+    and the final state."""
     w = synth.WORKLOADS["favor"]
     q, k, v = synth.draw_qkv(w.B, w.H, w.N, w.d, w.dv, io=w.io)
-    O, S, z = _run(lib, q, k, v, omega, causal=causal, return_state=True)
+    O, S, z = _run(lib, q, k, v, omega, phi=phi, causal=causal, return_state=True)
     O, S, z = to_host(O), to_host(S), to_host(z)
     if causal:
         ref, S_ref, z_ref = heads.map_heads(_recurrent_favor_head, q, k, v, omega=omega)
     else:
         ref, S_ref, z_ref = ora.noncausal_attention(q, k, v, phi="favor", omega=omega)
     _, _, worst = check_close(O, ref, "bf16", "O")
-    print(f"favor causal={causal}: worst row relative error {worst:.3e}", flush=True)
+    print(f"{phi} causal={causal}: worst row relative error {worst:.3e}", flush=True)
     check_close(S, S_ref, "bf16", "S_N")
     check_close(z, z_ref, "bf16", "z_N")
 
