@@ -70,6 +70,16 @@ def test_longest_sequence_per_head(lib):
         assert cfg(n_max + 1, d, io) == 2, (d, io)                     # LA_ERR_SHAPE
         assert _ws(1, 1, n_max, d=d, dv=d, io=io) > 0
         assert _ws(1, 1, n_max + 1, d=d, dv=d, io=io) == 0
+    # the decayed, gated and backward entry points address the same buffers
+    for d, n_max in ((64, (1 << 24) - 1), (128, (1 << 23) - 1)):
+        for fn in (lib.la_forward_decay_config, lib.la_forward_gated_config, lib.la_backward_config):
+            assert fn(1, 1, n_max, d, d, 1, 0, 0, 64, ctypes.byref(n)) == 0, (fn, d)
+            assert fn(1, 1, n_max + 1, d, d, 1, 0, 0, 64, ctypes.byref(n)) == 2, (fn, d)
+    # per-channel gates: a head's [N + 128][r] fp32 gates must stay below 2^31
+    # bytes as well (chunk 0: the default, 32 at d = 128)
+    for d, n_max in ((64, (1 << 23) - 129), (128, (1 << 22) - 129)):
+        assert lib.la_forward_gla_config(1, 1, n_max, d, d, 1, 0, 0, 0, ctypes.byref(n), None) == 0, d
+        assert lib.la_forward_gla_config(1, 1, n_max + 1, d, d, 1, 0, 0, 0, ctypes.byref(n), None) == 2, d
 
 
 def test_span_setter(lib, span_tokens):
