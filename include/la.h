@@ -43,8 +43,12 @@
  *     (0 is accepted and means d).  For LA_PHI_FAVOR (and
  *     LA_PHI_FAVOR_PRECISE) r is the number of omega rows.
  *   - stream: a hipStream_t (NULL = the default stream).  All work is enqueued
- *     asynchronously on it; the library allocates no memory, keeps no state
- *     between calls and is re-entrant.
+ *     asynchronously on it.  The library allocates no memory at run time
+ *     (la_forward_noalloc's scratch is a static device array) and is
+ *     re-entrant; what persists between calls is the span override of
+ *     la_set_span_tokens (process-wide), a per-device cache of the CU count
+ *     and of the scratch array's address, and the last HIP error string
+ *     (per thread).
  *   - The library links the HIP runtime by its soname (libamdhip64.so.7).  In a
  *     process that also uses PyTorch, load PyTorch first so that both share
  *     the runtime PyTorch brings (the Python binding does this); otherwise two
