@@ -127,7 +127,9 @@ def rel_rms_error(got, ref):
 #     of their terms; the kernels reach them as a difference of rounded
 #     sums, and the dot products inside those sums can cancel as well (the
 #     worst measured row, the second token of a long head, came within
-#     0.046 m).  For typical rows m is three to five times the row's norm.
+#     0.046 m).  Where those dot products cancel almost entirely, m takes
+#     1/16 of their terms' magnitude instead (tests/grad_scales.py).  For
+#     typical rows m is three to five times the row's norm.
 #
 # A head or block whose reference is zero up to 1e-9 of m (a single token)
 # is judged by its rows alone.
