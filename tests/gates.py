@@ -136,12 +136,18 @@ def rel_rms_error(got, ref):
 #     typical rows m is three to five times the row's norm.
 #
 # A head or block whose reference is zero up to 1e-9 of m (a single token)
-# is judged by its rows alone.
+# is judged by its rows alone.  A head of fewer than 16 rows (one block) is
+# held to the larger of its relative gate and 2^-6 of its magnitude m: all
+# of its rows are early rows, which cancel (an fp64 model of the dQ pass's
+# bf16 roundings over 240 random heads of 2 to 200 tokens: relative head
+# error up to 0.14 at 2 tokens and 0.057 at 4, under 0.03 from 5 tokens;
+# head error against m at most 2^-7.6).
 
 GRAD_HEAD = 3e-2
 GRAD_BLOCK = 5e-2
 GRAD_ROW = 1e-1
 GRAD_FLOOR = 2.0 ** -4
+GRAD_SHORT_FLOOR = 2.0 ** -6
 GRAD_BLOCK_ROWS = 64
 GRAD_TAIL_ROWS = 16
 
@@ -152,6 +158,15 @@ def _rel_rms(err2, ref2, m2):
     en, rn, mn = np.sqrt(err2), np.sqrt(ref2), np.sqrt(m2)
     judged = rn > 1e-9 * mn
     return np.where(judged, en / np.where(judged, rn, 1.0), 0.0)
+
+
+def _over(err2, ref2, m2, rel, short):
+    """Which heads or blocks exceed their gate: rel of the reference's norm,
+    or (short heads) 2^-6 of m where that is larger; zero references are
+    left to the row gate."""
+    en, rn, mn = np.sqrt(err2), np.sqrt(ref2), np.sqrt(m2)
+    bound = np.maximum(rel * rn, GRAD_SHORT_FLOOR * mn) if short else rel * rn
+    return (rn > 1e-9 * mn) & (en > bound)
 
 
 def check_grad(got, ref, scale, what=""):
@@ -170,10 +185,11 @@ def check_grad(got, ref, scale, what=""):
     e2 = np.sum((got - ref) ** 2, axis=-1)
     r2 = np.sum(ref ** 2, axis=-1)
     m2 = np.sum(scale ** 2, axis=-1)
-    head = _rel_rms(e2.sum(-1), r2.sum(-1), m2.sum(-1))
-    assert head.max() <= GRAD_HEAD, (
-        f"{what}: head relative RMS error {head.max():.3e} > {GRAD_HEAD:.0e} (per head: {np.round(head.ravel(), 4)})")
     n = e2.shape[-1]
+    short = n < GRAD_TAIL_ROWS
+    head = _rel_rms(e2.sum(-1), r2.sum(-1), m2.sum(-1))
+    assert not _over(e2.sum(-1), r2.sum(-1), m2.sum(-1), GRAD_HEAD, short).any(), (
+        f"{what}: head relative RMS error {head.max():.3e} > {GRAD_HEAD:.0e} (per head: {np.round(head.ravel(), 4)})")
     nb = (n + GRAD_BLOCK_ROWS - 1) // GRAD_BLOCK_ROWS
     # a ragged tail of fewer than GRAD_TAIL_ROWS rows joins the block before it
     if nb > 1 and n - (nb - 1) * GRAD_BLOCK_ROWS < GRAD_TAIL_ROWS:
@@ -182,7 +198,7 @@ def check_grad(got, ref, scale, what=""):
     blk = lambda x: np.stack([x[..., bid == b].sum(-1) for b in range(nb)], axis=-1)
     block = _rel_rms(blk(e2), blk(r2), blk(m2))
     wb = np.unravel_index(np.argmax(block), block.shape)
-    assert block.max() <= GRAD_BLOCK, (
+    assert not _over(blk(e2), blk(r2), blk(m2), GRAD_BLOCK, short).any(), (
         f"{what}: block {wb} (rows {GRAD_BLOCK_ROWS * wb[-1]}..) relative RMS error {block[wb]:.3e} > "
         f"{GRAD_BLOCK:.0e} (blocks over: {int(np.sum(block > GRAD_BLOCK))} of {block.size})")
     er, rr, sr = np.sqrt(e2), np.sqrt(r2), np.sqrt(m2)
